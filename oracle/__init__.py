@@ -1,0 +1,121 @@
+"""Float64 CPU oracle for the RWKV-7 WKV recurrence.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by the
+benchmark's CPU-baseline leg. The GPU library never imports or links it, and it
+imports nothing from the GPU package.
+
+The arithmetic lives in ``wkv7_oracle.c`` (plain C, double precision, compiled
+with ``-O2 -ffp-contract=off``). This module compiles it with gcc and calls it
+through ctypes. What it computes, per (batch, head), with the state S indexed
+[value i, key j]::
+
+    S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T,    y_t = S_t r_t
+
+following the RWKV-7 G0 7.2B notes (lshu.cn/news/198401), section 7.1 (state
+decayed by w, plus state*a*b, plus v k^T, then read out with r) and section
+3.3 (a zero-initialised float32 [H, N, N] state per layer).
+
+Pins (tests/test_oracle_pins.py, all CPU): brute-force matrix products on tiny
+T, the closed forms for a = 0 and for w = 1 with a = 0, an exact rational run,
+delta-rule retrieval, the memoryless case, linearity and row equivariance.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wkv7_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_wkv7.so")
+_lock = threading.Lock()
+_lib = None
+
+IN_F32, IN_BF16, IN_F64 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle_wkv7.so``."""
+    global _lib
+    with _lock:
+        if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+            cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-shared", "-fPIC",
+                   "-pthread", _SRC, "-o", tmp]
+            subprocess.run(cmd, check=True)
+            os.replace(tmp, _LIB_PATH)
+            _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        with _lock:
+            lib = ctypes.CDLL(_LIB_PATH)
+            f = lib.wkv7_oracle_f64
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int] * 3
+            _lib = lib
+    return _lib
+
+
+def _in_dtype(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return IN_F32
+    if x.dtype == np.uint16:  # raw bfloat16 bits
+        return IN_BF16
+    if x.dtype == np.float64:
+        return IN_F64
+    raise TypeError("oracle inputs must be float32, float64 or uint16 (bfloat16 bits), got %s" % x.dtype)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def wkv7(r, w, k, v, a, b, state_in=None, nthreads: int | None = None, want_state: bool = True):
+    """Run the float64 recurrence.
+
+    r, w, k, v, a, b: arrays of shape [B, T, H, N], all float32, all float64 or
+    all uint16 holding bfloat16 bits. state_in: None (zero state) or an array
+    [B, H, N, N] of float32 or float64. Returns (y [B,T,H,N] float64,
+    state_out [B,H,N,N] float64 or None).
+    """
+    lib = _load()
+    ins = [np.ascontiguousarray(x) for x in (r, w, k, v, a, b)]
+    shape = ins[0].shape
+    if len(shape) != 4 or any(x.shape != shape for x in ins):
+        raise ValueError("r,w,k,v,a,b must share one [B,T,H,N] shape")
+    dt = _in_dtype(ins[0])
+    if any(_in_dtype(x) != dt for x in ins):
+        raise TypeError("r,w,k,v,a,b must share one dtype")
+    B, T, H, N = shape
+    s_in = None
+    st_dt = IN_F64
+    if state_in is not None:
+        s_in = np.ascontiguousarray(state_in)
+        if s_in.shape != (B, H, N, N):
+            raise ValueError("state_in must be [B,H,N,N]")
+        if s_in.dtype == np.float32:
+            st_dt = IN_F32
+        elif s_in.dtype == np.float64:
+            st_dt = IN_F64
+        else:
+            raise TypeError("state_in must be float32 or float64")
+    y = np.empty((B, T, H, N), dtype=np.float64)
+    s_out = np.empty((B, H, N, N), dtype=np.float64) if want_state else None
+    p = lambda x: None if x is None else x.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    rc = lib.wkv7_oracle_f64(*(p(x) for x in ins), p(s_in), p(y), p(s_out), B, T, H, N, dt, st_dt,
+                             int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle failed with status %d" % rc)
+    return y, s_out

@@ -1,0 +1,184 @@
+/*
+ * Float64 reference ("oracle") for the RWKV-7 WKV time-mix recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is compiled and called by the test
+ * suite, by the smoke check and by the benchmark's CPU-baseline leg. It shares
+ * no code, header or constant with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * What it computes (per batch b and head h, state S is N x N, row i = value
+ * index, column j = key index):
+ *
+ *     sa_i      = sum_j S_ij a_j                      (S of the previous token)
+ *     S_ij     <- S_ij w_j + sa_i b_j + v_i k_j
+ *     y_i       = sum_j S_ij r_j                      (S after the update)
+ *
+ * i.e. S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T and y_t = S_t r_t.
+ * Sources:
+ *   - RWKV-7 G0 7.2B notes (lshu.cn/news/198401), section 7.1 "x070 architecture,
+ *     the two core operators": the state is decayed by w, gets the state*a*b
+ *     term and the v k^T outer product, and is then read out with r; the kernel
+ *     slots are a = -kk and b = kk*a_lr.
+ *   - same page, section 3.3 "vocabulary and loading details": the per-layer
+ *     WKV state is an [H, N, N] float32 tensor initialised to zero.
+ *   - RWKV-LM README (oa0.com/c/1004164), "RWKV introduction": a state of None
+ *     starts fresh and a returned state resumes the sequence.
+ *
+ * Readings taken where the pages leave a step open:
+ *   - decay multiplies key columns j (right-multiplication by diag(w));
+ *   - sa uses the state before this token's update;
+ *   - y is read after the update;
+ *   - inputs are widened exactly (bf16 bits << 16, or float) to double and every
+ *     accumulation is double, in index order, with no fused multiply-add
+ *     (build with -ffp-contract=off).
+ *
+ * Layouts: r,w,k,v,a,b,y are [B,T,H,N] row-major; state_in / state_out are
+ * [B,H,N,N] row-major with element (i,j) = S_ij.
+ */
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+
+static double widen(const void *p, int dtype, size_t idx)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)p)[idx];
+    if (dtype == ORC_BF16) {
+        /* bfloat16 is the upper half of an IEEE binary32 word. */
+        uint32_t u = ((uint32_t)((const uint16_t *)p)[idx]) << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return ((const double *)p)[idx];
+}
+
+typedef struct {
+    const void *r, *w, *k, *v, *a, *b; /* [B,T,H,N], dtype in_dtype */
+    const void *state_in;              /* [B,H,N,N] or NULL, dtype st_dtype */
+    double *y;                         /* [B,T,H,N] */
+    double *state_out;                 /* [B,H,N,N] or NULL */
+    int64_t B, T, H, N;
+    int in_dtype, st_dtype;
+    int64_t next_unit; /* shared work counter, guarded by lock */
+    pthread_mutex_t lock;
+} job_t;
+
+static void run_unit(job_t *J, int64_t unit, double *S, double *vec)
+{
+    const int64_t N = J->N, T = J->T, H = J->H;
+    const int64_t bb = unit / H, hh = unit % H;
+    double *r = vec, *w = vec + N, *k = vec + 2 * N, *v = vec + 3 * N;
+    double *a = vec + 4 * N, *b = vec + 5 * N;
+
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            S[i * N + j] = J->state_in
+                               ? widen(J->state_in, J->st_dtype, (size_t)(unit * N * N + i * N + j))
+                               : 0.0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        const size_t base = (size_t)(((bb * T + t) * H + hh) * N);
+        for (int64_t j = 0; j < N; ++j) {
+            r[j] = widen(J->r, J->in_dtype, base + j);
+            w[j] = widen(J->w, J->in_dtype, base + j);
+            k[j] = widen(J->k, J->in_dtype, base + j);
+            v[j] = widen(J->v, J->in_dtype, base + j);
+            a[j] = widen(J->a, J->in_dtype, base + j);
+            b[j] = widen(J->b, J->in_dtype, base + j);
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            double *Si = S + i * N;
+            double sa = 0.0;
+            for (int64_t j = 0; j < N; ++j)
+                sa += Si[j] * a[j];
+            for (int64_t j = 0; j < N; ++j)
+                Si[j] = Si[j] * w[j] + sa * b[j] + v[i] * k[j];
+            double yi = 0.0;
+            for (int64_t j = 0; j < N; ++j)
+                yi += Si[j] * r[j];
+            J->y[base + i] = yi;
+        }
+    }
+    if (J->state_out)
+        memcpy(J->state_out + unit * N * N, S, sizeof(double) * (size_t)(N * N));
+}
+
+static void *worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(J->N * J->N));
+    double *vec = (double *)malloc(sizeof(double) * (size_t)(6 * J->N));
+    if (!S || !vec) {
+        free(S);
+        free(vec);
+        return (void *)1;
+    }
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t unit = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (unit >= J->B * J->H)
+            break;
+        run_unit(J, unit, S, vec);
+    }
+    free(S);
+    free(vec);
+    return NULL;
+}
+
+/*
+ * Runs the recurrence over all B*H (batch, head) units with `nthreads` POSIX
+ * threads (each unit is independent). Returns 0 on success, -1 on bad
+ * arguments, -2 if a thread or its buffers could not be created.
+ */
+int wkv7_oracle_f64(const void *r, const void *w, const void *k, const void *v,
+                    const void *a, const void *b, const void *state_in, double *y,
+                    double *state_out, int64_t B, int64_t T, int64_t H, int64_t N,
+                    int in_dtype, int st_dtype, int nthreads)
+{
+    if (!r || !w || !k || !v || !a || !b || !y || B < 0 || T < 0 || H < 0 || N <= 0)
+        return -1;
+    if (in_dtype < ORC_F32 || in_dtype > ORC_F64 || st_dtype < ORC_F32 || st_dtype > ORC_F64 ||
+        st_dtype == ORC_BF16)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    job_t J;
+    J.r = r; J.w = w; J.k = k; J.v = v; J.a = a; J.b = b;
+    J.state_in = state_in; J.y = y; J.state_out = state_out;
+    J.B = B; J.T = T; J.H = H; J.N = N;
+    J.in_dtype = in_dtype; J.st_dtype = st_dtype;
+    J.next_unit = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    if (B * H < nthreads)
+        nthreads = (int)(B * H > 0 ? B * H : 1);
+
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int status = 0, started = 0;
+    if (!tid) {
+        pthread_mutex_destroy(&J.lock);
+        return -2;
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, worker, &J) != 0) {
+            status = -2;
+            break;
+        }
+        ++started;
+    }
+    if (started == 0 && status == 0)
+        status = -2;
+    for (int i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(tid[i], &ret);
+        if (ret)
+            status = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return status;
+}
