@@ -1,0 +1,135 @@
+/*
+ * rwkv7_wkv.h -- C ABI of the MI355X (gfx950) RWKV-7 WKV time-mix library.
+ *
+ * The operation (per batch b and head h; the state S is N x N float32, row i =
+ * value index, column j = key index):
+ *
+ *     S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T
+ *     y_t = S_t r_t                      (read out after the update)
+ *
+ * Source: RWKV-7 G0 7.2B notes (lshu.cn/news/198401), section 7.1, "x070
+ * architecture, the two core operators": the state is decayed by w, receives the
+ * state*a*b transition term and the v k^T outer product, and is then read out
+ * with r; an RWKV-7 layer passes a = -kk (the normalised removal key) and
+ * b = kk * a_lr (kk scaled by the in-context learning rate). The library
+ * computes the formula for any a and b. The head size is fixed at 64 (same page,
+ * sections 3.2 and 3.4: the kernels are built for head size 64 only), and the
+ * state is float32 because w can be very close to 1 (RWKV-LM README,
+ * oa0.com/c/1004164, MiniPile-training section, note on keeping the state and w
+ * in fp32).
+ *
+ * Layout (all row-major, contiguous, device memory):
+ *   r, w, k, v, a, b : [B, T, H, N]   dtype given by `dtype` (all six alike)
+ *   y                : [B, T, H, N]   float32
+ *   state_in/out     : [B, H, N, N]   float32, element (i, j) = S_ij
+ * w is the decay multiplier itself (typically exp(-exp(.)) in (0, 1]), not its log.
+ *
+ * Ownership: every pointer is caller-owned device memory (e.g. torch tensors).
+ * The library never keeps, frees or reallocates them. Calls are asynchronous on
+ * `stream` (a hipStream_t; NULL = the null stream): buffers must stay alive until
+ * the caller synchronises that stream. Device faults surface at that sync.
+ *
+ * Nulls and aliasing:
+ *   state_in  == NULL : start from a zero state (a fresh sequence; same page,
+ *                        section 3.3: the per-layer state starts at zero).
+ *   state_out == NULL : the final state is not written.
+ *   state_out == state_in (exactly) is allowed: the state is updated in place,
+ *   which is how a sequence is resumed (RWKV-LM README, "RWKV introduction":
+ *   passing the returned state back continues the sequence).
+ *   Any other overlap between y / state_out and any input, or between y and
+ *   state_out, is RWKV7_ERR_ALIAS.
+ *   A pointer to a zero-element tensor may be NULL (e.g. y when T == 0).
+ * Alignment: every non-NULL pointer must be 16-byte aligned (RWKV7_ERR_ALIGN).
+ * Empty work: B == 0 or H == 0 does nothing; T == 0 (prefill only) copies
+ * state_in to state_out (zeros when state_in is NULL) and writes no y.
+ *
+ * Errors: every entry point returns RWKV7_OK or a negative code, never throws,
+ * prints or aborts, and validates every argument before its first HIP call.
+ * Entry points are thread-safe; concurrent calls on different streams are
+ * independent.
+ */
+#ifndef RWKV7_WKV_H
+#define RWKV7_WKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define RWKV7_OK 0
+#define RWKV7_ERR_NULL (-1)      /* a required pointer is NULL */
+#define RWKV7_ERR_SHAPE (-2)     /* B, T or H negative; step called with T != 1; sizes overflow */
+#define RWKV7_ERR_HEAD_SIZE (-3) /* N != 64 */
+#define RWKV7_ERR_DTYPE (-4)     /* dtype not one of RWKV7_DTYPE_* */
+#define RWKV7_ERR_ALIGN (-5)     /* a pointer is not 16-byte aligned */
+#define RWKV7_ERR_ALIAS (-6)     /* outputs overlap inputs or each other (other than state_out == state_in) */
+#define RWKV7_ERR_ALGO (-7)      /* unknown algorithm, or one that does not support the arguments */
+#define RWKV7_ERR_HIP (-8)       /* a HIP runtime call or kernel launch failed */
+
+/* Input dtype of r, w, k, v, a, b. y and the state are always float32. */
+#define RWKV7_DTYPE_F32 0
+#define RWKV7_DTYPE_BF16 1
+
+/* Prefill algorithm (rwkv7_wkv_prefill_ex). */
+#define RWKV7_ALGO_AUTO 0       /* library's choice (what rwkv7_wkv_prefill does) */
+#define RWKV7_ALGO_SEQUENTIAL 1 /* token-by-token recurrence, state resident in registers */
+#define RWKV7_ALGO_CHUNKED 2    /* chunked (WY / UT) form with the intra-chunk products on MFMA */
+
+#define RWKV7_HEAD_SIZE 64
+
+/*
+ * Whole-sequence prefill ("GPT mode"; RWKV-7 G0 7.2B notes, section 3.2: one
+ * parallel pass over the prompt, producing the same state as running the tokens
+ * one by one). Runs T tokens for every (b, h) unit, writes y for every token and
+ * the state after token T-1.
+ *
+ *   r, w, k, v, a, b  inputs [B,T,H,N], dtype `dtype`
+ *   state_in          [B,H,N,N] float32 initial state, or NULL for zeros
+ *   y                 [B,T,H,N] float32 output
+ *   state_out         [B,H,N,N] float32 final state, or NULL; may equal state_in
+ *   B, T, H           batch, tokens, heads (>= 0)
+ *   N                 head size; must be 64
+ *   dtype             RWKV7_DTYPE_F32 or RWKV7_DTYPE_BF16
+ *   stream            hipStream_t to launch on (NULL = null stream)
+ *
+ * The automatic choice uses the sequential algorithm for float32 inputs and the
+ * chunked algorithm for bfloat16 inputs.
+ */
+int rwkv7_wkv_prefill(const void *r, const void *w, const void *k, const void *v, const void *a,
+                      const void *b, const float *state_in, float *y, float *state_out, int64_t B,
+                      int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * Batched single-token step ("RNN mode"; RWKV-7 G0 7.2B notes, sections 3.2
+ * and 7.1: the single-step kernel applies the same formula to one token with the
+ * state carried in and out). Same arguments and layouts as rwkv7_wkv_prefill
+ * with T == 1 (else RWKV7_ERR_SHAPE). Typical use updates the state in place
+ * (state_out == state_in). The result is bit-identical to the sequential
+ * prefill run over the same tokens one call at a time.
+ */
+int rwkv7_wkv_step(const void *r, const void *w, const void *k, const void *v, const void *a,
+                   const void *b, const float *state_in, float *y, float *state_out, int64_t B,
+                   int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * Prefill with an explicit algorithm (RWKV7_ALGO_*), so a caller or a test can
+ * force one kernel. RWKV7_ALGO_CHUNKED takes logarithms of w: it requires
+ * 0 < w <= 1 and treats any w below 2^-14 as 2^-14 (a decay below that floor
+ * changes the result by at most that fraction of the decayed state); use the
+ * sequential algorithm for inputs outside that domain. Other arguments as for
+ * rwkv7_wkv_prefill.
+ */
+int rwkv7_wkv_prefill_ex(const void *r, const void *w, const void *k, const void *v, const void *a,
+                         const void *b, const float *state_in, float *y, float *state_out, int64_t B,
+                         int64_t T, int64_t H, int64_t N, int dtype, int algo, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *rwkv7_wkv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKV7_WKV_H */

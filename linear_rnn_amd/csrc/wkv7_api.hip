@@ -1,0 +1,127 @@
+// C ABI of the WKV-7 library: argument validation and kernel dispatch.
+// Every check runs before the first HIP call, so invalid calls are rejected
+// without touching the device.
+#include <stdint.h>
+
+#include "rwkv7_wkv.h"
+#include "wkv7_internal.hpp"
+
+namespace {
+
+using rwkv7::WkvCall;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+bool overlap(Range x, Range y) { return !x.empty() && !y.empty() && x.lo < y.hi && y.lo < x.hi; }
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, p ? lo + (uintptr_t)bytes : lo};
+}
+
+int validate(const void* const in[6], const float* s_in, const float* y, const float* s_out, int64_t B,
+             int64_t T, int64_t H, int64_t N, int dtype) {
+  if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
+  if (N != RWKV7_HEAD_SIZE) return RWKV7_ERR_HEAD_SIZE;
+  // Size limits: workgroup counts up to B*H*16 must fit a 31-bit grid, and every
+  // byte offset must fit in int64 with room to spare.
+  int64_t units = 0, tok_heads = 0, elems = 0;
+  if (__builtin_mul_overflow(B, H, &units) || units > (int64_t(1) << 26)) return RWKV7_ERR_SHAPE;
+  if (__builtin_mul_overflow(units, T, &tok_heads) || __builtin_mul_overflow(tok_heads, int64_t(64), &elems) ||
+      elems > (int64_t(1) << 58))
+    return RWKV7_ERR_SHAPE;
+
+  const int64_t esz = dtype == RWKV7_DTYPE_BF16 ? 2 : 4;
+  const int64_t in_bytes = elems * esz;
+  const int64_t y_bytes = elems * 4;
+  const int64_t st_bytes = units * 64 * 64 * 4;
+
+  if (elems > 0) {
+    for (int i = 0; i < 6; ++i)
+      if (!in[i]) return RWKV7_ERR_NULL;
+    if (!y) return RWKV7_ERR_NULL;
+  }
+  const void* ptrs[9] = {in[0], in[1], in[2], in[3], in[4], in[5], s_in, y, s_out};
+  for (const void* q : ptrs)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return RWKV7_ERR_ALIGN;
+
+  const Range ry = range_of(y, y_bytes);
+  const Range rsi = range_of(s_in, st_bytes);
+  const Range rso = range_of(s_out, st_bytes);
+  for (int i = 0; i < 6; ++i) {
+    const Range ri = range_of(in[i], in_bytes);
+    if (overlap(ry, ri) || overlap(rso, ri)) return RWKV7_ERR_ALIAS;
+  }
+  if (overlap(ry, rsi) || overlap(ry, rso)) return RWKV7_ERR_ALIAS;
+  if (s_out && s_in && s_out != s_in && overlap(rso, rsi)) return RWKV7_ERR_ALIAS;
+  return RWKV7_OK;
+}
+
+int run(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
+        const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
+        int dtype, int algo, bool step, void* stream) {
+  const void* in[6] = {r, w, k, v, a, b};
+  if (algo < RWKV7_ALGO_AUTO || algo > RWKV7_ALGO_CHUNKED) return RWKV7_ERR_ALGO;
+  const int st = validate(in, state_in, y, state_out, B, T, H, N, dtype);
+  if (st != RWKV7_OK) return st;
+  if (step && T != 1) return RWKV7_ERR_SHAPE;
+
+  WkvCall c{{r, w, k, v, a, b}, state_in, y, state_out, B, T, H, dtype, static_cast<hipStream_t>(stream)};
+  if (B * H == 0) return RWKV7_OK;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (state_out && state_out != state_in) e = rwkv7::launch_state_copy(state_in, state_out, B * H, c.stream);
+    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+  }
+  if (step) {
+    e = rwkv7::launch_sequential(c, /*decode_shape=*/true);
+  } else {
+    if (algo == RWKV7_ALGO_AUTO) algo = RWKV7_ALGO_SEQUENTIAL;
+    e = algo == RWKV7_ALGO_CHUNKED ? rwkv7::launch_chunked(c) : rwkv7::launch_sequential(c, false);
+  }
+  if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;
+  return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rwkv7_wkv_prefill(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
+                      const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H,
+                      int64_t N, int dtype, void* stream) {
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_ALGO_AUTO, false, stream);
+}
+
+int rwkv7_wkv_step(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
+                   const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
+                   int dtype, void* stream) {
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_ALGO_SEQUENTIAL, true, stream);
+}
+
+int rwkv7_wkv_prefill_ex(const void* r, const void* w, const void* k, const void* v, const void* a,
+                         const void* b, const float* state_in, float* y, float* state_out, int64_t B, int64_t T,
+                         int64_t H, int64_t N, int dtype, int algo, void* stream) {
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, algo, false, stream);
+}
+
+const char* rwkv7_wkv_strerror(int status) {
+  switch (status) {
+    case RWKV7_OK: return "success";
+    case RWKV7_ERR_NULL: return "a required pointer is NULL";
+    case RWKV7_ERR_SHAPE: return "invalid shape (negative B/T/H, T != 1 for a step, or sizes too large)";
+    case RWKV7_ERR_HEAD_SIZE: return "head size N must be 64";
+    case RWKV7_ERR_DTYPE: return "unknown input dtype";
+    case RWKV7_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case RWKV7_ERR_ALIAS: return "outputs overlap inputs or each other";
+    case RWKV7_ERR_ALGO: return "unknown or unsupported algorithm for these arguments";
+    case RWKV7_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rwkv7 {
+
+// One validated call. Input order in `in`: r, w, k, v, a, b.
+struct WkvCall {
+  const void* in[6];
+  const float* s_in;  // may be null (zero state)
+  float* y;
+  float* s_out;  // may be null
+  int64_t B, T, H;
+  int dtype;  // RWKV7_DTYPE_*
+  hipStream_t stream;
+};
+
+// Token-by-token recurrence with the state resident in registers. Also the
+// single-token step (T == 1). Returns the launch status.
+hipError_t launch_sequential(const WkvCall& c, bool decode_shape);
+
+// Chunked (WY / UT) prefill with the intra-chunk products on MFMA.
+hipError_t launch_chunked(const WkvCall& c);
+
+// state_out <- state_in (zeros when state_in is null) for B*H heads.
+hipError_t launch_state_copy(const float* s_in, float* s_out, int64_t units, hipStream_t stream);
+
+}  // namespace rwkv7

@@ -1,0 +1,255 @@
+// Sequential WKV-7 kernel: the recurrence token by token with the 64x64 float32
+// state held in VGPRs. Serves the whole-sequence prefill for float32 inputs and
+// the batched single-token step (RNN mode).
+//
+// Per token and head (RWKV-7 G0 7.2B notes, lshu.cn/news/198401, section 7.1):
+//   sa_i = sum_j S_ij a_j,  S_ij <- S_ij w_j + sa_i b_j + v_i k_j,  y_i = sum_j S_ij r_j.
+//
+// Work decomposition. The value rows of S evolve independently (row i needs
+// only its own state row, v_i and the shared key-space vectors r, w, k, a, b),
+// so a head's 64 rows are split over WAVES*RPW-row workgroups. Inside a wave,
+// lane = 16*ri + c holds columns 4c..4c+3 of the RPW/4 rows {4m + ri}; the two
+// row dot products (S a and S r) are a 4-term in-lane partial followed by a
+// 16-lane DPP butterfly, which leaves the identical sum in every lane of the row.
+// State loads and stores are float4 per lane and cover 1 KiB contiguous per
+// wave instruction.
+//
+// Inputs are staged through LDS in blocks of TB tokens: the whole workgroup
+// issues coalesced 16-byte loads for block n+1 into registers while it computes
+// block n from LDS, where the inputs sit widened to float32.
+//
+// Arithmetic order is fixed (explicit fmaf, built with -ffp-contract=off) and
+// does not depend on RPW, WAVES or TB, so prefill and step give identical bits.
+#include "wkv7_device.hpp"
+#include "wkv7_internal.hpp"
+
+namespace rwkv7 {
+namespace {
+
+struct SeqParams {
+  const void* r;
+  const void* w;
+  const void* k;
+  const void* v;
+  const void* a;
+  const void* b;
+  const float* s_in;
+  float* y;
+  float* s_out;
+  int64_t T;
+  int32_t H;
+};
+
+template <bool BF16>
+struct InTraits;
+template <>
+struct InTraits<true> {
+  static constexpr int kEpv = 8;  // elements per 16-byte load
+  // Widen 8 bfloat16 values to float32 and write them as two float4.
+  __device__ static void store(float* dst, const uint4 q) {
+    float4 lo = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+    float4 hi = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+    reinterpret_cast<float4*>(dst)[0] = lo;
+    reinterpret_cast<float4*>(dst)[1] = hi;
+  }
+};
+template <>
+struct InTraits<false> {
+  static constexpr int kEpv = 4;
+  __device__ static void store(float* dst, const uint4 q) {
+    *reinterpret_cast<uint4*>(dst) = q;
+  }
+};
+
+template <bool BF16, int WAVES, int RPW, int TB>
+__global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
+  using Tr = InTraits<BF16>;
+  constexpr int kThreads = kWave * WAVES;
+  constexpr int kRpb = WAVES * RPW;     // rows per workgroup
+  constexpr int kNrb = kN / kRpb;       // workgroups per head
+  constexpr int kMr = RPW / 4;          // rows per lane
+  constexpr int kEpv = Tr::kEpv;
+  constexpr int kKseg = kN / kEpv;      // 16-byte segments per key-space vector
+  constexpr int kVseg = kRpb / kEpv;    // 16-byte segments of this workgroup's v rows
+  constexpr int kEsz = BF16 ? 2 : 4;
+  constexpr int kNqk = (TB * kKseg + kThreads - 1) / kThreads;
+  constexpr int kNqv = (TB * kVseg + kThreads - 1) / kThreads;
+  static_assert(kN % kRpb == 0 && RPW % 4 == 0 && kRpb % kEpv == 0, "bad tiling");
+
+  // [token][r, w, k, a, b][column] and [token][row of this workgroup]
+  __shared__ __align__(16) float kv_lds[TB][5][kN];
+  __shared__ __align__(16) float v_lds[TB][kRpb];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int c = lane & 15;
+  const int ri = lane >> 4;
+
+  const uint32_t logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int64_t unit = logical / kNrb;
+  const int rb = logical % kNrb;
+  const int64_t bb = unit / p.H;
+  const int64_t hh = unit % p.H;
+  const int64_t T = p.T;
+  const int64_t tok_stride = (int64_t)p.H * kN;           // elements between tokens
+  const int64_t seq_base = (bb * T * p.H + hh) * kN;      // element offset of token 0
+  const int row_wg = rb * kRpb;                           // first row of this workgroup
+  const int row0 = row_wg + wave * RPW;                   // first row of this wave
+
+  const char* src[5] = {static_cast<const char*>(p.r), static_cast<const char*>(p.w),
+                        static_cast<const char*>(p.k), static_cast<const char*>(p.a),
+                        static_cast<const char*>(p.b)};
+  const char* vsrc = static_cast<const char*>(p.v);
+
+  // ---- state in
+  float4 S[kMr];
+#pragma unroll
+  for (int m = 0; m < kMr; ++m) {
+    const int row = row0 + 4 * m + ri;
+    if (p.s_in)
+      S[m] = *reinterpret_cast<const float4*>(p.s_in + (unit * kN + row) * kN + 4 * c);
+    else
+      S[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  uint4 stk[5][kNqk];
+  uint4 stv[kNqv];
+  auto issue = [&](int64_t t0) {
+#pragma unroll
+    for (int x = 0; x < 5; ++x) {
+#pragma unroll
+      for (int q = 0; q < kNqk; ++q) {
+        const int e = tid + kThreads * q;
+        const int tok = e / kKseg, seg = e % kKseg;
+        if (e < TB * kKseg && t0 + tok < T) {
+          const int64_t off = seq_base + (t0 + tok) * tok_stride + seg * kEpv;
+          stk[x][q] = *reinterpret_cast<const uint4*>(src[x] + off * kEsz);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kNqv; ++q) {
+      const int e = tid + kThreads * q;
+      const int tok = e / kVseg, seg = e % kVseg;
+      if (e < TB * kVseg && t0 + tok < T) {
+        const int64_t off = seq_base + (t0 + tok) * tok_stride + row_wg + seg * kEpv;
+        stv[q] = *reinterpret_cast<const uint4*>(vsrc + off * kEsz);
+      }
+    }
+  };
+  auto commit = [&](int64_t t0) {
+#pragma unroll
+    for (int x = 0; x < 5; ++x) {
+#pragma unroll
+      for (int q = 0; q < kNqk; ++q) {
+        const int e = tid + kThreads * q;
+        const int tok = e / kKseg, seg = e % kKseg;
+        if (e < TB * kKseg && t0 + tok < T) Tr::store(&kv_lds[tok][x][seg * kEpv], stk[x][q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kNqv; ++q) {
+      const int e = tid + kThreads * q;
+      const int tok = e / kVseg, seg = e % kVseg;
+      if (e < TB * kVseg && t0 + tok < T) Tr::store(&v_lds[tok][seg * kEpv], stv[q]);
+    }
+  };
+
+  if (T > 0) issue(0);
+  for (int64_t t0 = 0; t0 < T; t0 += TB) {
+    __syncthreads();  // every wave is done reading the previous block
+    commit(t0);
+    __syncthreads();
+    if (t0 + TB < T) issue(t0 + TB);  // in flight while this block is computed
+    const int ntok = (T - t0 < TB) ? (int)(T - t0) : TB;
+    for (int tt = 0; tt < ntok; ++tt) {
+      const float4 r4 = *reinterpret_cast<const float4*>(&kv_lds[tt][0][4 * c]);
+      const float4 w4 = *reinterpret_cast<const float4*>(&kv_lds[tt][1][4 * c]);
+      const float4 k4 = *reinterpret_cast<const float4*>(&kv_lds[tt][2][4 * c]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&kv_lds[tt][3][4 * c]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&kv_lds[tt][4][4 * c]);
+      float vm[kMr], sa[kMr], yp[kMr];
+#pragma unroll
+      for (int m = 0; m < kMr; ++m) vm[m] = v_lds[tt][wave * RPW + 4 * m + ri];
+      // sa = S_{t-1} a  (4 in-lane terms, then the 16-lane butterfly)
+#pragma unroll
+      for (int m = 0; m < kMr; ++m)
+        sa[m] = fmaf(S[m].w, a4.w, fmaf(S[m].z, a4.z, fmaf(S[m].y, a4.y, S[m].x * a4.x)));
+#pragma unroll
+      for (int m = 0; m < kMr; ++m) sa[m] = row16_sum(sa[m]);
+      // S <- S diag(w) + sa b^T + v k^T
+#pragma unroll
+      for (int m = 0; m < kMr; ++m) {
+        S[m].x = fmaf(S[m].x, w4.x, fmaf(sa[m], b4.x, vm[m] * k4.x));
+        S[m].y = fmaf(S[m].y, w4.y, fmaf(sa[m], b4.y, vm[m] * k4.y));
+        S[m].z = fmaf(S[m].z, w4.z, fmaf(sa[m], b4.z, vm[m] * k4.z));
+        S[m].w = fmaf(S[m].w, w4.w, fmaf(sa[m], b4.w, vm[m] * k4.w));
+      }
+      // y = S_t r
+#pragma unroll
+      for (int m = 0; m < kMr; ++m)
+        yp[m] = fmaf(S[m].w, r4.w, fmaf(S[m].z, r4.z, fmaf(S[m].y, r4.y, S[m].x * r4.x)));
+#pragma unroll
+      for (int m = 0; m < kMr; ++m) yp[m] = row16_sum(yp[m]);
+      // lane c < RPW/4 writes row 4c + ri: the wave's RPW rows are contiguous.
+      float yo = yp[0];
+#pragma unroll
+      for (int m = 1; m < kMr; ++m) yo = (c == m) ? yp[m] : yo;
+      if (c < kMr) p.y[seq_base + (t0 + tt) * tok_stride + row0 + 4 * c + ri] = yo;
+    }
+  }
+
+  // ---- state out
+  if (p.s_out) {
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      const int row = row0 + 4 * m + ri;
+      *reinterpret_cast<float4*>(p.s_out + (unit * kN + row) * kN + 4 * c) = S[m];
+    }
+  }
+}
+
+__global__ void state_copy_kernel(const float4* __restrict__ src, float4* __restrict__ dst, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n4) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <bool BF16, int WAVES, int RPW, int TB>
+hipError_t launch_seq_cfg(const WkvCall& c) {
+  SeqParams p{c.in[0], c.in[1], c.in[2], c.in[3], c.in[4], c.in[5], c.s_in, c.y, c.s_out, c.T, (int32_t)c.H};
+  constexpr int kNrb = kN / (WAVES * RPW);
+  const int64_t blocks = c.B * c.H * kNrb;
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_seq_kernel<BF16, WAVES, RPW, TB>),
+                         dim3((uint32_t)blocks), dim3(kWave * WAVES), args, 0, c.stream);
+}
+
+template <bool BF16>
+hipError_t launch_seq_dtype(const WkvCall& c, bool decode_shape) {
+  if (decode_shape) return launch_seq_cfg<BF16, 4, 16, 1>(c);  // one head per workgroup
+  // Prefill: the token loop is serial, so spread each head's rows over more
+  // waves when there are few heads.
+  const int64_t units = c.B * c.H;
+  if (units >= 2048) return launch_seq_cfg<BF16, 4, 16, 16>(c);
+  return launch_seq_cfg<BF16, 4, 4, 32>(c);
+}
+
+}  // namespace
+
+hipError_t launch_sequential(const WkvCall& c, bool decode_shape) {
+  return c.dtype == 1 ? launch_seq_dtype<true>(c, decode_shape) : launch_seq_dtype<false>(c, decode_shape);
+}
+
+hipError_t launch_state_copy(const float* s_in, float* s_out, int64_t units, hipStream_t stream) {
+  const int64_t n4 = units * kN * kN / 4;
+  const int threads = 256;
+  const int64_t blocks = (n4 + threads - 1) / threads;
+  const float4* src = reinterpret_cast<const float4*>(s_in);
+  float4* dst = reinterpret_cast<float4*>(s_out);
+  void* args[] = {&src, &dst, const_cast<int64_t*>(&n4)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&state_copy_kernel), dim3((uint32_t)blocks),
+                         dim3(threads), args, 0, stream);
+}
+
+}  // namespace rwkv7

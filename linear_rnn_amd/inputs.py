@@ -36,7 +36,7 @@ from dataclasses import dataclass
 import numpy as np
 
 HEAD_SIZE = 64
-_SLAB_ROWS = 1 << 15  # rows of 64 elements per independently seeded slab
+_SLAB_ROWS = 1 << 12  # rows of 64 elements per independently seeded slab
 
 
 @dataclass(frozen=True)
@@ -179,7 +179,7 @@ def make_inputs(cfg: WkvConfig, step: int | None = None, B: int | None = None, T
         res["b"][lo:lo + n] = _cast(kk * alr, cfg.dtype)
 
     nthr = _threads()
-    if rows * N >= (1 << 22) and nthr > 1:
+    if rows * N >= (1 << 18) and nthr > 1:
         with _cf.ThreadPoolExecutor(nthr) as ex:
             list(ex.map(run_simple, tasks))
             list(ex.map(run_ab, range(len(kk_jobs))))

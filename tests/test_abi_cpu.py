@@ -1,0 +1,146 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad arguments (CPU only).
+
+Every call here fails validation or has no work, so no HIP call is made.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_rnn_amd import wkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rwkv7_wkv.h")
+
+F32, BF16 = wkv.RWKV7_DTYPE_F32, wkv.RWKV7_DTYPE_BF16
+OK, E_NULL, E_SHAPE, E_HEAD, E_DTYPE, E_ALIGN, E_ALIAS, E_ALGO = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(rwkv7_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wkv.LIB_PATH):
+        pytest.skip("HIP library not built")
+    return wkv.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(wkv.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", wkv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (rwkv7_\w+)", out))
+    assert set(names) <= exported, (names, exported)
+
+
+def test_strerror_never_null(L):
+    for code in range(-12, 3):
+        assert isinstance(wkv.rwkv7_wkv_strerror(code), str) and wkv.rwkv7_wkv_strerror(code)
+
+
+# Fake device addresses: distinct, 16-byte aligned, far apart. Never dereferenced,
+# because every call below is rejected or has no work.
+BASE = 1 << 40
+GAP = 1 << 34
+
+
+def ptrs(n=9):
+    return [BASE + i * GAP for i in range(n)]
+
+
+def call(L, fn="rwkv7_wkv_prefill", p=None, B=2, T=3, H=4, N=64, dtype=BF16, algo=None):
+    p = ptrs() if p is None else p
+    args = list(p) + [B, T, H, N, dtype]
+    if fn == "rwkv7_wkv_prefill_ex":
+        args.append(algo)
+    args.append(None)
+    return getattr(L, fn)(*args)
+
+
+def test_bad_dtype(L):
+    assert call(L, dtype=7) == E_DTYPE
+
+
+@pytest.mark.parametrize("B,T,H", [(-1, 3, 4), (2, -1, 4), (2, 3, -4), (1 << 30, 1, 1 << 10), (1, 1 << 60, 1)])
+def test_bad_shape(L, B, T, H):
+    assert call(L, B=B, T=T, H=H) == E_SHAPE
+
+
+@pytest.mark.parametrize("N", [0, 32, 63, 65, 128])
+def test_head_size_must_be_64(L, N):
+    assert call(L, N=N) == E_HEAD
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_null_required_pointer(L, idx):
+    if idx == 6:  # state_in may be NULL
+        return
+    p = ptrs()
+    p[idx] = None
+    assert call(L, p=p) == E_NULL
+
+
+@pytest.mark.parametrize("idx", range(9))
+def test_misaligned_pointer(L, idx):
+    p = ptrs()
+    p[idx] += 4
+    assert call(L, p=p) == E_ALIGN
+
+
+def test_output_overlapping_input(L):
+    p = ptrs()
+    p[7] = p[2] + 64  # y inside k
+    assert call(L, p=p) == E_ALIAS
+    p = ptrs()
+    p[8] = p[0]  # state_out on r
+    assert call(L, p=p) == E_ALIAS
+    p = ptrs()
+    p[8] = p[7] + 256  # state_out inside y
+    assert call(L, p=p) == E_ALIAS
+    p = ptrs()
+    p[8] = p[6] + 1024  # partial overlap of state_out and state_in
+    assert call(L, p=p) == E_ALIAS
+    p = ptrs()
+    p[7] = p[6]  # y on state_in
+    assert call(L, p=p) == E_ALIAS
+
+
+def test_adjacent_buffers_are_not_alias(L):
+    # y directly after k: touching but not overlapping; use B*H == 0 so nothing launches
+    p = ptrs()
+    assert call(L, p=p, B=0) == OK
+
+
+def test_step_requires_one_token(L):
+    assert call(L, fn="rwkv7_wkv_step", T=2) == E_SHAPE
+    assert call(L, fn="rwkv7_wkv_step", T=0) == E_SHAPE
+
+
+@pytest.mark.parametrize("algo", [-1, 3, 99])
+def test_unknown_algo(L, algo):
+    assert call(L, fn="rwkv7_wkv_prefill_ex", algo=algo) == E_ALGO
+
+
+def test_empty_work_is_ok_without_device(L):
+    assert call(L, B=0) == OK
+    assert call(L, H=0) == OK
+    p = ptrs()
+    p[8] = None  # T == 0 with no state_out: nothing to do
+    assert call(L, p=p, T=0) == OK
+    p = ptrs()
+    p[8] = p[6]  # T == 0, state_out == state_in: nothing to copy
+    assert call(L, p=p, T=0) == OK
+    # zero-element tensors may be NULL
+    p = [None] * 9
+    assert call(L, p=p, B=0) == OK
+
+
+def test_binding_error_message(L):
+    with pytest.raises(wkv.Rwkv7Error) as ei:
+        wkv._check(E_HEAD)
+    assert "64" in str(ei.value) and ei.value.status == E_HEAD
