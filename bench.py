@@ -1,0 +1,269 @@
+"""Benchmark of the WKV-7 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline]
+
+One timed step = one whole-sequence prefill of the L12-D768 layer workload
+(B=8, T=4096, H=12, N=64, bfloat16 inputs, float32 state carried in and out)
+through the C ABI with the library's default algorithm. The batched decode
+step (D2048 shape: B=512, H=32, 256 consecutive in-place steps) is timed in the
+same run and reported under "decode". Inputs are seeded synthetic tensors,
+resident in HBM before timing starts.
+
+Prints one JSON line. "value" is prefill tokens*heads per second. "roofline"
+relates the dominant kernel's algorithmic bytes (or flops) per launch to its
+mean launch time (HIP events on the launch stream) and to MI355X's published
+peak. "cpu_baseline" is the float64 oracle timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+N = 64
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+FLOP_REC = 9 * N * N  # per token*head: S a (2N^2), update (5N^2), S r (2N^2)
+METRIC = "WKV7 tokens*heads/sec (prefill & decode step) + % of HBM/MFMA roofline"
+UNIT = "tokens*heads/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algo_bytes(B, T, H, in_bytes=2):
+    """Algorithmic HBM bytes of one call: six inputs and fp32 y per token*head, fp32 state in and out."""
+    return B * T * H * (6 * N * in_bytes + N * 4) + 2 * B * H * N * N * 4
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_files):
+    """HBM bytes per launch from the committed counter runs, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tab = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel_key)
+    if not ent or ent.get("src_sha") != source_hash(src_files):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def to_dev(x, torch):
+    import numpy as np
+    out = {}
+    for n in "rwkvab":
+        a = x[n]
+        out[n] = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a).cuda()
+    return out
+
+
+def time_region(torch, fn, reps):
+    """Mean ms per call of `fn` over `reps` back-to-back calls, HIP events on the current stream."""
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the WKV-7 units (batch, head) are independent, so a "
+              "multi-GPU run would shard batch or heads with no communication; run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from linear_rnn_amd import wkv
+    from linear_rnn_amd.inputs import CONFIGS, make_inputs
+
+    wkv.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev_name = torch.cuda.get_device_name(0)
+
+    # ------------------------------------------------------------------ prefill
+    cfg = CONFIGS[1]
+    B, T, H = cfg.B, cfg.T, cfg.H
+    x = make_inputs(cfg)
+    d = to_dev(x, torch)
+    s_in = torch.from_numpy(x["state_in"]).cuda()
+    y = torch.empty((B, T, H, N), dtype=torch.float32, device="cuda")
+    s_out = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
+    algo = args.algo if args.algo else (wkv.RWKV7_ALGO_CHUNKED if chunked_available(wkv, torch) else
+                                        wkv.RWKV7_ALGO_SEQUENTIAL)
+
+    def prefill():
+        wkv.rwkv7_wkv_prefill_ex(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], s_in, y, s_out, algo=algo)
+
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_region(torch, prefill, args.steps)
+    wall = time.perf_counter() - t0
+    tok_heads = B * T * H
+    value = tok_heads / (ms * 1e-3)
+
+    nbytes = algo_bytes(B, T, H)
+    if algo == wkv.RWKV7_ALGO_SEQUENTIAL:
+        kname, src = "wkv7_seq_kernel", ["linear_rnn_amd/csrc/wkv7_seq.hip", "linear_rnn_amd/csrc/wkv7_device.hpp"]
+        flops = FLOP_REC * tok_heads
+        roof = {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VECTOR_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        kname, src = "wkv7_chunk_kernel", ["linear_rnn_amd/csrc/wkv7_chunk.hip",
+                                           "linear_rnn_amd/csrc/wkv7_device.hpp"]
+        roof = {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(kname + ":" + cfg.name, src)
+    roof["kernel"] = kname
+    roof["algorithmic_bytes"] = nbytes
+    roof["hbm_frac_of_peak"] = nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS
+
+    out = {
+        "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if algo == wkv.RWKV7_ALGO_SEQUENTIAL else "bf16",
+        "data": "synthetic (seeded; RWKV-7 layer-shaped distributions)",
+        "config": {"workload": "%s: B=%d T=%d H=%d N=%d bf16 inputs, fp32 state in/out" % (cfg.name, B, T, H, N),
+                   "B": B, "T": T, "H": H, "N": N, "algo": {1: "sequential", 2: "chunked"}[algo]},
+        "roofline": roof, "device": dev_name, "timed_wall_s": wall,
+    }
+
+    # ------------------------------------------------------------------ decode
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, wkv, make_inputs, CONFIGS[3], args)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": a.numel() * 4, "write": a.numel() * 4}
+
+    # ------------------------------------------------------------------ CPU oracle
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def chunked_available(wkv, torch):
+    """True if the library accepts the chunked algorithm (probed on a 1-token call)."""
+    z = torch.zeros((1, 1, 1, N), dtype=torch.bfloat16, device="cuda")
+    yy = torch.empty((1, 1, 1, N), dtype=torch.float32, device="cuda")
+    try:
+        wkv.rwkv7_wkv_prefill_ex(z, z, z, z, z, z, None, yy, None, algo=wkv.RWKV7_ALGO_CHUNKED)
+        torch.cuda.synchronize()
+        return True
+    except wkv.Rwkv7Error:
+        return False
+
+
+def bench_decode(torch, wkv, make_inputs, cfg, args):
+    B, H, S = cfg.B, cfg.H, args.decode_steps
+    steps = []
+    for s in range(S):
+        xs = make_inputs(cfg, step=s, with_state=(s == 0))
+        if s == 0:
+            state = torch.from_numpy(xs["state_in"]).cuda()
+        steps.append(to_dev(xs, torch))
+    y = torch.empty((B, 1, H, N), dtype=torch.float32, device="cuda")
+
+    def run_all():
+        for dd in steps:
+            wkv.rwkv7_wkv_step(dd["r"], dd["w"], dd["k"], dd["v"], dd["a"], dd["b"], state, y, state)
+
+    run_all()  # warm-up pass
+    torch.cuda.synchronize()
+    per_step = []
+    for _ in range(args.decode_reps):
+        per_step.append(time_region(torch, run_all, 1) / S)
+    ms = float(sorted(per_step)[len(per_step) // 2])
+    nbytes = algo_bytes(B, 1, H)
+    src = ["linear_rnn_amd/csrc/wkv7_seq.hip", "linear_rnn_amd/csrc/wkv7_device.hpp"]
+    return {
+        "value": B * H / (ms * 1e-3), "unit": UNIT, "ms_per_step": ms, "steps_per_rep": S,
+        "reps": args.decode_reps, "ms_per_step_all_reps": per_step,
+        "config": {"workload": "%s: B=%d H=%d N=%d, %d consecutive in-place steps, bf16 inputs, fp32 state"
+                   % (cfg.name, B, H, N, S), "B": B, "H": H, "N": N},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("wkv7_seq_kernel:" + cfg.name, src),
+                     "kernel": "wkv7_seq_kernel (step shape)", "algorithmic_bytes": nbytes},
+    }
+
+
+def cpu_baseline(x):
+    """Time the float64 oracle (as it stands) on the prefill workload, on every host core."""
+    import oracle
+    oracle.build(force=False)
+    th = oracle.default_threads()
+    B, T, H = x["r"].shape[:3]
+    times = []
+    budget = 20.0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"], nthreads=th)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 5 or time.perf_counter() - t_start > budget / 2:
+            break
+    sec = sorted(times)[len(times) // 2]
+    return {"value": B * T * H / sec, "unit": UNIT, "cores": th, "kind": "oracle",
+            "sample": "whole prefill workload (B=%d T=%d H=%d), float64, median of %d runs, %.3f s each"
+                      % (B, T, H, len(times), sec),
+            "cpu_model": cpu_model()}
+
+
+if __name__ == "__main__":
+    sys.exit(main())
