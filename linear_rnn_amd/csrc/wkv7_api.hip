@@ -80,7 +80,7 @@ int run(const void* r, const void* w, const void* k, const void* v, const void* 
   if (step) {
     e = rwkv7::launch_sequential(c, /*decode_shape=*/true);
   } else {
-    if (algo == RWKV7_ALGO_AUTO) algo = RWKV7_ALGO_SEQUENTIAL;
+    if (algo == RWKV7_ALGO_AUTO) algo = dtype == RWKV7_DTYPE_BF16 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SEQUENTIAL;
     e = algo == RWKV7_ALGO_CHUNKED ? rwkv7::launch_chunked(c) : rwkv7::launch_sequential(c, false);
   }
   if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;

@@ -33,6 +33,14 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Workgroup barrier for data exchanged through LDS only: wait for this wave's
+// LDS operations, then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding global loads, so prefetches stay in flight across the barrier
+// (their consumers wait on them through the usual register dependencies).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // The dispatcher deals consecutive workgroup ids to the XCDs round-robin.
 // Renumber so that each run of nblocks/8 consecutive logical ids executes on a
 // single XCD; workgroups that read the same data then share one L2. Ids in the
