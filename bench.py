@@ -136,8 +136,8 @@ def main(argv=None):
     s_in = torch.from_numpy(x["state_in"]).cuda()
     y = torch.empty((B, T, H, N), dtype=torch.float32, device="cuda")
     s_out = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
-    algo = args.algo if args.algo else (wkv.RWKV7_ALGO_CHUNKED if chunked_available(wkv, torch) else
-                                        wkv.RWKV7_ALGO_SEQUENTIAL)
+    # the library's default for bfloat16 inputs is the chunked algorithm
+    algo = args.algo if args.algo else wkv.RWKV7_ALGO_CHUNKED
 
     def prefill():
         wkv.rwkv7_wkv_prefill_ex(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], s_in, y, s_out, algo=algo)
@@ -195,18 +195,6 @@ def main(argv=None):
 
     print(json.dumps(out), flush=True)
     return 0
-
-
-def chunked_available(wkv, torch):
-    """True if the library accepts the chunked algorithm (probed on a 1-token call)."""
-    z = torch.zeros((1, 1, 1, N), dtype=torch.bfloat16, device="cuda")
-    yy = torch.empty((1, 1, 1, N), dtype=torch.float32, device="cuda")
-    try:
-        wkv.rwkv7_wkv_prefill_ex(z, z, z, z, z, z, None, yy, None, algo=wkv.RWKV7_ALGO_CHUNKED)
-        torch.cuda.synchronize()
-        return True
-    except wkv.Rwkv7Error:
-        return False
 
 
 def bench_decode(torch, wkv, make_inputs, cfg, args):
