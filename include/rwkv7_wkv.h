@@ -115,11 +115,19 @@ int rwkv7_wkv_step(const void *r, const void *w, const void *k, const void *v, c
 
 /*
  * Prefill with an explicit algorithm (RWKV7_ALGO_*), so a caller or a test can
- * force one kernel. RWKV7_ALGO_CHUNKED takes logarithms of w: it requires
- * 0 < w <= 1 and treats any w below 2^-14 as 2^-14 (a decay below that floor
- * changes the result by at most that fraction of the decayed state); use the
- * sequential algorithm for inputs outside that domain. Other arguments as for
- * rwkv7_wkv_prefill.
+ * force one kernel. Other arguments as for rwkv7_wkv_prefill.
+ *
+ * Domain of RWKV7_ALGO_CHUNKED (the sequential algorithm has none beyond
+ * finite inputs):
+ *   - 0 <= w <= 1; any w below 2^-15 is treated as 2^-15, which changes a
+ *     decayed term by at most 2^-15 of its size;
+ *   - the decay-scaled inputs, the state and the intermediate chunk products
+ *     are rounded to float16 as matrix-core operands, so their magnitudes must
+ *     stay below 2^15 (RWKV-7 activations and states are far smaller);
+ *   - T * H * 64 must be below 2^31 (32-bit in-sequence offsets);
+ *     otherwise the call returns RWKV7_ERR_ALGO and launches nothing.
+ * Results agree with the sequential algorithm to about 1e-3 relative (max-norm
+ * over a tensor) rather than bit for bit.
  */
 int rwkv7_wkv_prefill_ex(const void *r, const void *w, const void *k, const void *v, const void *a,
                          const void *b, const float *state_in, float *y, float *state_out, int64_t B,
