@@ -6,8 +6,9 @@ One timed step = one whole-sequence prefill of the L12-D768 layer workload
 (B=8, T=4096, H=12, N=64, bfloat16 inputs, float32 state carried in and out)
 through the C ABI with the library's default algorithm. The batched decode
 step (D2048 shape: B=512, H=32, 256 consecutive in-place steps) is timed in the
-same run and reported under "decode". Inputs are seeded synthetic tensors,
-resident in HBM before timing starts.
+same run and reported under "decode", and again with the state stored as
+bfloat16 and as float16 ("decode_state_bf16", "decode_state_f16"). Inputs are
+seeded synthetic tensors, resident in HBM before timing starts.
 
 Prints one JSON line. "value" is prefill tokens*heads per second. "roofline"
 relates the dominant kernel's algorithmic bytes (or flops) per launch to its
@@ -38,9 +39,9 @@ UNIT = "tokens*heads/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def algo_bytes(B, T, H, in_bytes=2):
-    """Algorithmic HBM bytes of one call: six inputs and fp32 y per token*head, fp32 state in and out."""
-    return B * T * H * (6 * N * in_bytes + N * 4) + 2 * B * H * N * N * 4
+def algo_bytes(B, T, H, in_bytes=2, state_bytes=4):
+    """Algorithmic HBM bytes of one call: six inputs and fp32 y per token*head, the state in and out."""
+    return B * T * H * (6 * N * in_bytes + N * 4) + 2 * B * H * N * N * state_bytes
 
 
 def source_hash(files):
@@ -106,6 +107,7 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode-16bit", action="store_true", help="skip the bf16 / f16 stored-state decode legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -180,6 +182,9 @@ def main(argv=None):
     # ------------------------------------------------------------------ decode
     if not args.no_decode:
         out["decode"] = bench_decode(torch, wkv, make_inputs, CONFIGS[3], args)
+        if not args.no_decode_16bit:
+            for fmt in ("bf16", "f16"):
+                out["decode_state_" + fmt] = bench_decode(torch, wkv, make_inputs, CONFIGS[3], args, fmt)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -197,19 +202,23 @@ def main(argv=None):
     return 0
 
 
-def bench_decode(torch, wkv, make_inputs, cfg, args):
+def bench_decode(torch, wkv, make_inputs, cfg, args, fmt="f32"):
+    """Consecutive in-place single-token steps; fmt is the stored-state format (f32, bf16, f16)."""
     B, H, S = cfg.B, cfg.H, args.decode_steps
     steps = []
     for s in range(S):
         xs = make_inputs(cfg, step=s, with_state=(s == 0))
         if s == 0:
             state = torch.from_numpy(xs["state_in"]).cuda()
+            if fmt != "f32":
+                state = state.to({"bf16": torch.bfloat16, "f16": torch.float16}[fmt])
         steps.append(to_dev(xs, torch))
     y = torch.empty((B, 1, H, N), dtype=torch.float32, device="cuda")
+    step = wkv.rwkv7_wkv_step if fmt == "f32" else wkv.rwkv7_wkv_step_q
 
     def run_all():
         for dd in steps:
-            wkv.rwkv7_wkv_step(dd["r"], dd["w"], dd["k"], dd["v"], dd["a"], dd["b"], state, y, state)
+            step(dd["r"], dd["w"], dd["k"], dd["v"], dd["a"], dd["b"], state, y, state)
 
     run_all()  # warm-up pass
     torch.cuda.synchronize()
@@ -217,17 +226,19 @@ def bench_decode(torch, wkv, make_inputs, cfg, args):
     for _ in range(args.decode_reps):
         per_step.append(time_region(torch, run_all, 1) / S)
     ms = float(sorted(per_step)[len(per_step) // 2])
-    nbytes = algo_bytes(B, 1, H)
+    nbytes = algo_bytes(B, 1, H, state_bytes=4 if fmt == "f32" else 2)
     src = ["linear_rnn_amd/csrc/wkv7_seq.hip", "linear_rnn_amd/csrc/wkv7_device.hpp"]
+    kern = "wkv7_seq_kernel" if fmt == "f32" else "wkv7_step_kernel"
+    key = kern + ":" + cfg.name + ("" if fmt == "f32" else ":state-" + fmt)
     return {
         "value": B * H / (ms * 1e-3), "unit": UNIT, "ms_per_step": ms, "steps_per_rep": S,
         "reps": args.decode_reps, "ms_per_step_all_reps": per_step,
-        "config": {"workload": "%s: B=%d H=%d N=%d, %d consecutive in-place steps, bf16 inputs, fp32 state"
-                   % (cfg.name, B, H, N, S), "B": B, "H": H, "N": N},
+        "config": {"workload": "%s: B=%d H=%d N=%d, %d consecutive in-place steps, bf16 inputs, %s stored state"
+                   % (cfg.name, B, H, N, S, fmt), "B": B, "H": H, "N": N, "state": fmt},
         "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": measured_traffic("wkv7_seq_kernel:" + cfg.name, src),
-                     "kernel": "wkv7_seq_kernel (step shape)", "algorithmic_bytes": nbytes},
+                     "traffic": measured_traffic(key, src),
+                     "kernel": "%s (%s state)" % (kern, fmt), "algorithmic_bytes": nbytes},
     }
 
 

@@ -62,15 +62,20 @@ extern "C" {
 #define RWKV7_ERR_NULL (-1)      /* a required pointer is NULL */
 #define RWKV7_ERR_SHAPE (-2)     /* B, T or H negative; step called with T != 1; sizes overflow */
 #define RWKV7_ERR_HEAD_SIZE (-3) /* N != 64 */
-#define RWKV7_ERR_DTYPE (-4)     /* dtype not one of RWKV7_DTYPE_* */
+#define RWKV7_ERR_DTYPE (-4)     /* dtype not one of RWKV7_DTYPE_*, or state dtype not one of RWKV7_STATE_* */
 #define RWKV7_ERR_ALIGN (-5)     /* a pointer is not 16-byte aligned */
 #define RWKV7_ERR_ALIAS (-6)     /* outputs overlap inputs or each other (other than state_out == state_in) */
 #define RWKV7_ERR_ALGO (-7)      /* unknown algorithm, or one that does not support the arguments */
 #define RWKV7_ERR_HIP (-8)       /* a HIP runtime call or kernel launch failed */
 
-/* Input dtype of r, w, k, v, a, b. y and the state are always float32. */
+/* Input dtype of r, w, k, v, a, b. y is always float32; so is the state except in rwkv7_wkv_step_q. */
 #define RWKV7_DTYPE_F32 0
 #define RWKV7_DTYPE_BF16 1
+
+/* Stored-state element format (rwkv7_wkv_step_q). The other entry points use float32. */
+#define RWKV7_STATE_F32 0
+#define RWKV7_STATE_BF16 1
+#define RWKV7_STATE_F16 2
 
 /* Prefill algorithm (rwkv7_wkv_prefill_ex). */
 #define RWKV7_ALGO_AUTO 0       /* library's choice (what rwkv7_wkv_prefill does) */
@@ -112,6 +117,35 @@ int rwkv7_wkv_prefill(const void *r, const void *w, const void *k, const void *v
 int rwkv7_wkv_step(const void *r, const void *w, const void *k, const void *v, const void *a,
                    const void *b, const float *state_in, float *y, float *state_out, int64_t B,
                    int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * Single-token step with the state stored in a 16-bit format (reduced-precision
+ * decode state). The RWKV-8 ROSA note (trdm.cn/news/547794, "why states are
+ * worth quantising") writes the state size as a function of batch, heads, head
+ * size, layers and Q, the bits per state element, and names lowering Q as the
+ * direct way to raise the batch that fits; Q = 16 halves the state bytes that
+ * this HBM-bound step reads and writes.
+ *
+ *   state_in   [B,H,N,N] in `state_dtype`, or NULL for zeros; widened exactly
+ *   state_out  [B,H,N,N] in `state_dtype`, or NULL; may equal state_in
+ *   state_dtype RWKV7_STATE_F32 (then identical to rwkv7_wkv_step),
+ *              RWKV7_STATE_BF16 or RWKV7_STATE_F16
+ *   all other arguments as for rwkv7_wkv_step (T == 1, inputs in `dtype`,
+ *   y float32).
+ *
+ * The token is computed in float32 exactly as rwkv7_wkv_step does; y is read
+ * from that float32 state, and the new state is rounded to nearest-even when
+ * it is stored (float16: magnitudes must stay below 65504, and values below
+ * 2^-14 keep fewer bits). The README's fp32 note (oa0.com/c/1004164: the state
+ * update must be float32 because w can be very close to 1) is why float32
+ * stays the default: with a 16-bit stored state, a decay that changes an
+ * element by less than half a unit in its last place is lost at each store,
+ * so the state drifts from the float32 trajectory over many steps. Callers
+ * choose the trade-off.
+ */
+int rwkv7_wkv_step_q(const void *r, const void *w, const void *k, const void *v, const void *a,
+                     const void *b, const void *state_in, float *y, void *state_out, int64_t B,
+                     int64_t T, int64_t H, int64_t N, int dtype, int state_dtype, void *stream);
 
 /*
  * Prefill with an explicit algorithm (RWKV7_ALGO_*), so a caller or a test can

@@ -22,9 +22,11 @@ Range range_of(const void* p, int64_t bytes) {
   return Range{lo, p ? lo + (uintptr_t)bytes : lo};
 }
 
-int validate(const void* const in[6], const float* s_in, const float* y, const float* s_out, int64_t B,
-             int64_t T, int64_t H, int64_t N, int dtype) {
+int validate(const void* const in[6], const void* s_in, const float* y, const void* s_out, int64_t B,
+             int64_t T, int64_t H, int64_t N, int dtype, int sdtype) {
   if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
+  if (sdtype != RWKV7_STATE_F32 && sdtype != RWKV7_STATE_BF16 && sdtype != RWKV7_STATE_F16)
+    return RWKV7_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
   if (N != RWKV7_HEAD_SIZE) return RWKV7_ERR_HEAD_SIZE;
   // Size limits: workgroup counts up to B*H*16 must fit a 31-bit grid, and every
@@ -38,7 +40,7 @@ int validate(const void* const in[6], const float* s_in, const float* y, const f
   const int64_t esz = dtype == RWKV7_DTYPE_BF16 ? 2 : 4;
   const int64_t in_bytes = elems * esz;
   const int64_t y_bytes = elems * 4;
-  const int64_t st_bytes = units * 64 * 64 * 4;
+  const int64_t st_bytes = units * 64 * 64 * (sdtype == RWKV7_STATE_F32 ? 4 : 2);
 
   if (elems > 0) {
     for (int i = 0; i < 6; ++i)
@@ -62,19 +64,21 @@ int validate(const void* const in[6], const float* s_in, const float* y, const f
 }
 
 int run(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
-        const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
-        int dtype, int algo, bool step, void* stream) {
+        const void* state_in, float* y, void* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
+        int dtype, int sdtype, int algo, bool step, void* stream) {
   const void* in[6] = {r, w, k, v, a, b};
   if (algo < RWKV7_ALGO_AUTO || algo > RWKV7_ALGO_CHUNKED) return RWKV7_ERR_ALGO;
-  const int st = validate(in, state_in, y, state_out, B, T, H, N, dtype);
+  const int st = validate(in, state_in, y, state_out, B, T, H, N, dtype, sdtype);
   if (st != RWKV7_OK) return st;
   if (step && T != 1) return RWKV7_ERR_SHAPE;
 
-  WkvCall c{{r, w, k, v, a, b}, state_in, y, state_out, B, T, H, dtype, static_cast<hipStream_t>(stream)};
+  WkvCall c{{r, w, k, v, a, b}, state_in, y, state_out, B, T, H, dtype, sdtype, static_cast<hipStream_t>(stream)};
   if (B * H == 0) return RWKV7_OK;
   hipError_t e = hipSuccess;
-  if (T == 0) {
-    if (state_out && state_out != state_in) e = rwkv7::launch_state_copy(state_in, state_out, B * H, c.stream);
+  if (T == 0) {  // prefill only, float32 state
+    if (state_out && state_out != state_in)
+      e = rwkv7::launch_state_copy(static_cast<const float*>(state_in), static_cast<float*>(state_out), B * H,
+                                   c.stream);
     return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
   }
   if (step) {
@@ -94,19 +98,28 @@ extern "C" {
 int rwkv7_wkv_prefill(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
                       const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H,
                       int64_t N, int dtype, void* stream) {
-  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_ALGO_AUTO, false, stream);
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_STATE_F32, RWKV7_ALGO_AUTO, false,
+             stream);
 }
 
 int rwkv7_wkv_step(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
                    const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
                    int dtype, void* stream) {
-  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_ALGO_SEQUENTIAL, true, stream);
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_STATE_F32, RWKV7_ALGO_SEQUENTIAL,
+             true, stream);
+}
+
+int rwkv7_wkv_step_q(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
+                     const void* state_in, float* y, void* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
+                     int dtype, int state_dtype, void* stream) {
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, state_dtype, RWKV7_ALGO_SEQUENTIAL, true,
+             stream);
 }
 
 int rwkv7_wkv_prefill_ex(const void* r, const void* w, const void* k, const void* v, const void* a,
                          const void* b, const float* state_in, float* y, float* state_out, int64_t B, int64_t T,
                          int64_t H, int64_t N, int dtype, int algo, void* stream) {
-  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, algo, false, stream);
+  return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_STATE_F32, algo, false, stream);
 }
 
 const char* rwkv7_wkv_strerror(int status) {
@@ -115,7 +128,7 @@ const char* rwkv7_wkv_strerror(int status) {
     case RWKV7_ERR_NULL: return "a required pointer is NULL";
     case RWKV7_ERR_SHAPE: return "invalid shape (negative B/T/H, T != 1 for a step, or sizes too large)";
     case RWKV7_ERR_HEAD_SIZE: return "head size N must be 64";
-    case RWKV7_ERR_DTYPE: return "unknown input dtype";
+    case RWKV7_ERR_DTYPE: return "unknown input or state dtype";
     case RWKV7_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case RWKV7_ERR_ALIAS: return "outputs overlap inputs or each other";
     case RWKV7_ERR_ALGO: return "unknown or unsupported algorithm for these arguments";

@@ -565,8 +565,8 @@ hipError_t launch_chunk_dtype(const WkvCall& c) {
   // Opt in to more than 64 KiB of LDS once per process (the attribute is per function).
   static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (attr != hipSuccess) return attr;
-  ChunkParams p{{c.in[0], c.in[1], c.in[2], c.in[3], c.in[4], c.in[5]}, c.s_in, c.y, c.s_out, (int32_t)c.T,
-                (int32_t)c.H};
+  ChunkParams p{{c.in[0], c.in[1], c.in[2], c.in[3], c.in[4], c.in[5]}, static_cast<const float*>(c.s_in), c.y,
+                static_cast<float*>(c.s_out), (int32_t)c.T, (int32_t)c.H};
   void* args[] = {&p};
   return hipLaunchKernel(fn, dim3((uint32_t)(c.B * c.H)), dim3(kThreads), args, bytes, c.stream);
 }

@@ -9,16 +9,18 @@ namespace rwkv7 {
 // One validated call. Input order in `in`: r, w, k, v, a, b.
 struct WkvCall {
   const void* in[6];
-  const float* s_in;  // may be null (zero state)
+  const void* s_in;  // may be null (zero state); element type given by sdtype
   float* y;
-  float* s_out;  // may be null
+  void* s_out;  // may be null
   int64_t B, T, H;
-  int dtype;  // RWKV7_DTYPE_*
+  int dtype;   // RWKV7_DTYPE_*
+  int sdtype;  // RWKV7_STATE_*: float32 unless a reduced-precision step
   hipStream_t stream;
 };
 
 // Token-by-token recurrence with the state resident in registers. Also the
-// single-token step (T == 1). Returns the launch status.
+// single-token step (T == 1), the only shape that takes a 16-bit stored state.
+// Returns the launch status.
 hipError_t launch_sequential(const WkvCall& c, bool decode_shape);
 
 // Chunked (WY / UT) prefill with the intra-chunk products on MFMA.

@@ -19,11 +19,15 @@ LIB_PATH = os.path.join(PKG, "librwkv7_wkv.so")
 RWKV7_OK = 0
 RWKV7_DTYPE_F32 = 0
 RWKV7_DTYPE_BF16 = 1
+RWKV7_STATE_F32 = 0
+RWKV7_STATE_BF16 = 1
+RWKV7_STATE_F16 = 2
 RWKV7_ALGO_AUTO = 0
 RWKV7_ALGO_SEQUENTIAL = 1
 RWKV7_ALGO_CHUNKED = 2
 
-EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_prefill_ex", "rwkv7_wkv_strerror")
+EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
+            "rwkv7_wkv_strerror")
 
 _lib = None
 _lock = threading.Lock()
@@ -49,6 +53,8 @@ def lib() -> ctypes.CDLL:
                 f = getattr(L, name)
                 f.restype = ci
                 f.argtypes = sig + [vp]
+            L.rwkv7_wkv_step_q.restype = ci
+            L.rwkv7_wkv_step_q.argtypes = sig + [ci, vp]
             L.rwkv7_wkv_prefill_ex.restype = ci
             L.rwkv7_wkv_prefill_ex.argtypes = sig + [ci, vp]
             L.rwkv7_wkv_strerror.restype = ctypes.c_char_p
@@ -105,6 +111,24 @@ def rwkv7_wkv_prefill(r, w, k, v, a, b, state_in, y, state_out, stream=None):
 def rwkv7_wkv_step(r, w, k, v, a, b, state_in, y, state_out, stream=None):
     """Single-token step (T == 1); state_out may be state_in for an in-place update."""
     _check(lib().rwkv7_wkv_step(*_args(r, w, k, v, a, b, state_in, y, state_out), _stream(stream)))
+
+
+def _state_code(*states) -> int:
+    import torch
+    codes = {torch.float32: RWKV7_STATE_F32, torch.bfloat16: RWKV7_STATE_BF16, torch.float16: RWKV7_STATE_F16}
+    found = {codes.get(s.dtype, -1) for s in states if s is not None}
+    if len(found) > 1:
+        raise ValueError("state_in and state_out must share one dtype")
+    return found.pop() if found else RWKV7_STATE_F32
+
+
+def rwkv7_wkv_step_q(r, w, k, v, a, b, state_in, y, state_out, state_dtype=None, stream=None):
+    """Single-token step with a float32, bfloat16 or float16 stored state (RWKV7_STATE_*).
+
+    The state format is taken from the state tensors' dtype unless `state_dtype` is given.
+    """
+    sd = _state_code(state_in, state_out) if state_dtype is None else int(state_dtype)
+    _check(lib().rwkv7_wkv_step_q(*_args(r, w, k, v, a, b, state_in, y, state_out), sd, _stream(stream)))
 
 
 def rwkv7_wkv_prefill_ex(r, w, k, v, a, b, state_in, y, state_out, algo=RWKV7_ALGO_AUTO, stream=None):

@@ -34,7 +34,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle_wkv7.so")
 _lock = threading.Lock()
 _lib = None
 
-IN_F32, IN_BF16, IN_F64 = 0, 1, 2
+IN_F32, IN_BF16, IN_F64, IN_F16 = 0, 1, 2, 3
+STATE_FORMATS = {"bf16": IN_BF16, "f16": IN_F16}  # 16-bit stored-state encodings (raw uint16 bits)
 
 
 def build(force: bool = True) -> str:
@@ -44,7 +45,7 @@ def build(force: bool = True) -> str:
         if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             tmp = _LIB_PATH + ".tmp%d" % os.getpid()
             cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-shared", "-fPIC",
-                   "-pthread", _SRC, "-o", tmp]
+                   "-pthread", _SRC, "-o", tmp, "-lm"]
             subprocess.run(cmd, check=True)
             os.replace(tmp, _LIB_PATH)
             _lib = None
@@ -61,6 +62,10 @@ def _load():
             f = lib.wkv7_oracle_f64
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int] * 3
+            for name in ("wkv7_oracle_round16", "wkv7_oracle_widen16"):
+                g = getattr(lib, name)
+                g.restype = ctypes.c_int
+                g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -82,13 +87,15 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def wkv7(r, w, k, v, a, b, state_in=None, nthreads: int | None = None, want_state: bool = True):
+def wkv7(r, w, k, v, a, b, state_in=None, nthreads: int | None = None, want_state: bool = True,
+         state_format: str | None = None):
     """Run the float64 recurrence.
 
     r, w, k, v, a, b: arrays of shape [B, T, H, N], all float32, all float64 or
     all uint16 holding bfloat16 bits. state_in: None (zero state) or an array
-    [B, H, N, N] of float32 or float64. Returns (y [B,T,H,N] float64,
-    state_out [B,H,N,N] float64 or None).
+    [B, H, N, N] of float32 or float64, or of uint16 encodings in
+    `state_format` ("bf16" or "f16"), widened exactly. Returns (y [B,T,H,N]
+    float64, state_out [B,H,N,N] float64 or None).
     """
     lib = _load()
     ins = [np.ascontiguousarray(x) for x in (r, w, k, v, a, b)]
@@ -109,8 +116,10 @@ def wkv7(r, w, k, v, a, b, state_in=None, nthreads: int | None = None, want_stat
             st_dt = IN_F32
         elif s_in.dtype == np.float64:
             st_dt = IN_F64
+        elif s_in.dtype == np.uint16 and state_format in STATE_FORMATS:
+            st_dt = STATE_FORMATS[state_format]
         else:
-            raise TypeError("state_in must be float32 or float64")
+            raise TypeError("state_in must be float32, float64, or uint16 with state_format 'bf16' or 'f16'")
     y = np.empty((B, T, H, N), dtype=np.float64)
     s_out = np.empty((B, H, N, N), dtype=np.float64) if want_state else None
     p = lambda x: None if x is None else x.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
@@ -119,3 +128,34 @@ def wkv7(r, w, k, v, a, b, state_in=None, nthreads: int | None = None, want_stat
     if rc != 0:
         raise RuntimeError("oracle failed with status %d" % rc)
     return y, s_out
+
+
+def round16(x, fmt: str) -> np.ndarray:
+    """Round float64 values to a 16-bit state format ("bf16" or "f16"), ties to even; return the uint16 bits."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    if lib.wkv7_oracle_round16(x.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p), x.size,
+                               STATE_FORMATS[fmt]) != 0:
+        raise RuntimeError("round16 failed")
+    return out
+
+
+def widen16(bits, fmt: str) -> np.ndarray:
+    """Widen 16-bit state encodings ("bf16" or "f16") exactly to float64."""
+    lib = _load()
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    if lib.wkv7_oracle_widen16(bits.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p),
+                               bits.size, STATE_FORMATS[fmt]) != 0:
+        raise RuntimeError("widen16 failed")
+    return out
+
+
+def step_q(r, w, k, v, a, b, state_bits, fmt: str, nthreads: int | None = None):
+    """One call of the step with a 16-bit stored state: widen the state, run the
+    float64 recurrence over the given tokens, read y from the unrounded state,
+    and round the new state to `fmt`. state_bits None means a zero state.
+    Returns (y float64, new state bits uint16)."""
+    y, s = wkv7(r, w, k, v, a, b, state_in=state_bits, nthreads=nthreads, state_format=fmt)
+    return y, round16(s, fmt)

@@ -34,18 +34,43 @@
  *
  * Layouts: r,w,k,v,a,b,y are [B,T,H,N] row-major; state_in / state_out are
  * [B,H,N,N] row-major with element (i,j) = S_ij.
+ *
+ * 16-bit stored states (the reduced-precision decode state; the RWKV-8 ROSA
+ * note, trdm.cn/news/547794, "why states are worth quantising", gives the state
+ * size as a function of the bits per element Q): state_in may be bfloat16 or
+ * IEEE binary16 bits, widened exactly, and wkv7_oracle_round16 rounds a float64
+ * state to either format, to nearest with ties to even, as the definition of
+ * that rounding states it (scale by the quantum of the value's binade, round
+ * the quotient to the nearest integer, even on ties, scale back).
  */
+#include <math.h>
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2, ORC_F16 = 3 };
+
+/* IEEE binary16: sign bit, 5 exponent bits with bias 15, 10 fraction bits;
+ * exponent field 0 holds zero and the subnormals (fraction * 2^-24). */
+static double widen_f16(uint16_t h)
+{
+    const double sign = (h & 0x8000u) ? -1.0 : 1.0;
+    const int e = (h >> 10) & 31;
+    const int m = h & 1023;
+    if (e == 0)
+        return sign * ldexp((double)m, -24);
+    if (e == 31)
+        return m ? NAN : sign * INFINITY;
+    return sign * ldexp((double)(1024 + m), e - 25);
+}
 
 static double widen(const void *p, int dtype, size_t idx)
 {
     if (dtype == ORC_F32)
         return (double)((const float *)p)[idx];
+    if (dtype == ORC_F16)
+        return widen_f16(((const uint16_t *)p)[idx]);
     if (dtype == ORC_BF16) {
         /* bfloat16 is the upper half of an IEEE binary32 word. */
         uint32_t u = ((uint32_t)((const uint16_t *)p)[idx]) << 16;
@@ -142,8 +167,7 @@ int wkv7_oracle_f64(const void *r, const void *w, const void *k, const void *v,
 {
     if (!r || !w || !k || !v || !a || !b || !y || B < 0 || T < 0 || H < 0 || N <= 0)
         return -1;
-    if (in_dtype < ORC_F32 || in_dtype > ORC_F64 || st_dtype < ORC_F32 || st_dtype > ORC_F64 ||
-        st_dtype == ORC_BF16)
+    if (in_dtype < ORC_F32 || in_dtype > ORC_F64 || st_dtype < ORC_F32 || st_dtype > ORC_F16)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -181,4 +205,84 @@ int wkv7_oracle_f64(const void *r, const void *w, const void *k, const void *v,
     free(tid);
     pthread_mutex_destroy(&J.lock);
     return status;
+}
+
+/*
+ * Round x to the nearest number with `prec` significant bits whose leading bit
+ * weighs at least 2^emin (below that the quantum stays 2^(emin - prec + 1):
+ * the subnormal range), ties to even; anything beyond maxv becomes infinite.
+ */
+static double round_to_format(double x, int prec, int emin, double maxv)
+{
+    if (x == 0.0 || isnan(x) || isinf(x))
+        return x;
+    int e;
+    frexp(x, &e); /* |x| = f 2^e with 0.5 <= f < 1: the leading bit weighs 2^(e-1) */
+    int lead = e - 1;
+    if (lead < emin)
+        lead = emin;
+    const double quantum = ldexp(1.0, lead - (prec - 1));
+    const double r = rint(x / quantum) * quantum; /* rint: nearest, ties to even */
+    return fabs(r) > maxv ? copysign(INFINITY, x) : r;
+}
+
+static uint16_t encode_bf16(double r)
+{
+    if (isnan(r))
+        return 0x7FC0u;
+    const float f = (float)r; /* exact: every bfloat16 value is a binary32 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+static uint16_t encode_f16(double r)
+{
+    if (isnan(r))
+        return 0x7E00u;
+    const uint16_t sign = signbit(r) ? 0x8000u : 0u;
+    const double m = fabs(r);
+    if (isinf(m))
+        return sign | 0x7C00u;
+    if (m < ldexp(1.0, -14)) /* zero or subnormal: fraction = m / 2^-24 */
+        return sign | (uint16_t)(m * ldexp(1.0, 24));
+    int e;
+    frexp(m, &e);
+    const int lead = e - 1; /* -14 .. 15 */
+    const uint16_t frac = (uint16_t)((m * ldexp(1.0, -lead) - 1.0) * 1024.0);
+    return sign | (uint16_t)((lead + 15) << 10) | frac;
+}
+
+/*
+ * Round n float64 values to a 16-bit state format and write the encodings.
+ * fmt 1: bfloat16 (8 significant bits, binary32 exponent range, largest finite
+ * value (2 - 2^-7) 2^127); fmt 3: IEEE binary16 (11 significant bits, normal
+ * leading exponents -14..15, largest finite value 65504). Returns 0, or -1 for
+ * an unknown format or bad arguments.
+ */
+int wkv7_oracle_round16(const double *x, uint16_t *out, int64_t n, int fmt)
+{
+    if ((!x || !out) && n > 0)
+        return -1;
+    if (fmt != ORC_BF16 && fmt != ORC_F16)
+        return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        if (fmt == ORC_BF16)
+            out[i] = encode_bf16(round_to_format(x[i], 8, -126, ldexp(255.0, 120)));
+        else
+            out[i] = encode_f16(round_to_format(x[i], 11, -14, 65504.0));
+    }
+    return 0;
+}
+
+/* Widen n 16-bit state encodings (fmt 1 bfloat16, fmt 3 binary16) to float64. */
+int wkv7_oracle_widen16(const uint16_t *bits, double *out, int64_t n, int fmt)
+{
+    if ((!bits || !out) && n > 0)
+        return -1;
+    if (fmt != ORC_BF16 && fmt != ORC_F16)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = widen(bits, fmt, (size_t)i);
+    return 0;
 }

@@ -275,3 +275,78 @@ def cast_inputs(x, dtype):
         out[n_] = x32 if dtype == "f32" else f32_to_bf16_bits(x32)
     out["state_in"] = x["state_in"].astype(np.float32)
     return out
+
+
+# ---- 16-bit stored-state encodings (reduced-precision decode state)
+
+def _f16_table():
+    """Every finite binary16 value, as float64, from numpy's own decoding."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    return bits, vals
+
+
+def pin_widen16(orc) -> float:
+    """Fraction of the 65536 encodings (each format) that the oracle widens differently
+    from numpy's float16 decoding and from the input module's bfloat16 decoding."""
+    from linear_rnn_amd.inputs import bf16_bits_to_f32
+    bits, f16 = _f16_table()
+    with np.errstate(invalid="ignore"):
+        bf = bf16_bits_to_f32(bits).astype(np.float64)
+    bad = 0
+    for fmt, ref in (("f16", f16), ("bf16", bf)):
+        got = orc.widen16(bits, fmt)
+        same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+        same &= (np.signbit(got) == np.signbit(ref)) | np.isnan(ref)  # a NaN's sign carries nothing
+        bad += int((~same).sum())
+    return bad / (2 << 16)
+
+
+def round16_cases(seed=31, n=20000):
+    """Doubles that exercise 16-bit rounding: log-uniform magnitudes over both
+    formats' normal, subnormal and overflow ranges, random signs, and exact
+    midpoints between neighbouring binary16 values (ties)."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.uniform(-30, 17, n))
+    x = mag * rng.choice([-1.0, 1.0], n)
+    _, f16 = _f16_table()
+    fin = np.unique(f16[np.isfinite(f16)])
+    mids = (fin[:-1] + fin[1:]) / 2  # exact in float64
+    pick = rng.choice(len(mids), 4000, replace=False)
+    edges = np.array([65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25, 2.0 ** -26,
+                      2.0 ** -14, (1 - 2.0 ** -11) * 2.0 ** -14, 0.0, -0.0])
+    return np.concatenate([x, mids[pick], edges, -edges])
+
+
+def pin_round16(orc, seed=31) -> float:
+    """Fraction of cases where the oracle's rounding disagrees with an independent rule.
+
+    binary16: numpy's float64 -> float16 conversion (round to nearest, ties to
+    even, with subnormals and overflow to infinity).
+    bfloat16: for float32-exact inputs, the input module's float32 -> bfloat16
+    rounding; for arbitrary doubles, exact rational comparison with the two
+    neighbouring bfloat16 values (nearest wins, ties go to the even encoding).
+    """
+    from linear_rnn_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    x = round16_cases(seed)
+    with np.errstate(over="ignore"):
+        ref16 = x.astype(np.float16).view(np.uint16)
+    bad = int((orc.round16(x, "f16") != ref16).sum())
+    # bfloat16 on float32-exact values
+    rng = np.random.default_rng(seed + 1)
+    f32 = (np.exp2(rng.uniform(-140, 127, 20000)) * rng.choice([-1.0, 1.0], 20000)).astype(np.float32)
+    f32 = np.concatenate([f32, bf16_bits_to_f32(np.arange(0, 0x7f80, 7, dtype=np.uint16)) * np.float32(1 + 2 ** -8)])
+    bad += int((orc.round16(f32.astype(np.float64), "bf16") != f32_to_bf16_bits(f32)).sum())
+    # bfloat16 on doubles that are not float32 values: exact nearest-neighbour check
+    d = np.exp2(rng.uniform(-130, 120, 600)) * (1 + rng.uniform(0, 2.0 ** -30, 600))
+    got = orc.round16(d, "bf16")
+    for xi, gi in zip(d, got):
+        cands = [int(gi) - 1, int(gi), int(gi) + 1]
+        vals = {c: Fraction(float(bf16_bits_to_f32(np.array([c], dtype=np.uint16))[0])) for c in cands
+                if 0 <= c < 0x7f80}
+        xf = Fraction(float(xi))
+        best = min(abs(xf - v) for v in vals.values())
+        winners = [c for c, v in vals.items() if abs(xf - v) == best]
+        ok = int(gi) in winners and (len(winners) == 1 or int(gi) % 2 == 0)
+        bad += 0 if ok else 1
+    return bad / (len(x) + len(f32) + len(d))

@@ -53,11 +53,13 @@ def ptrs(n=9):
     return [BASE + i * GAP for i in range(n)]
 
 
-def call(L, fn="rwkv7_wkv_prefill", p=None, B=2, T=3, H=4, N=64, dtype=BF16, algo=None):
+def call(L, fn="rwkv7_wkv_prefill", p=None, B=2, T=3, H=4, N=64, dtype=BF16, algo=None, sdtype=None):
     p = ptrs() if p is None else p
     args = list(p) + [B, T, H, N, dtype]
     if fn == "rwkv7_wkv_prefill_ex":
         args.append(algo)
+    if fn == "rwkv7_wkv_step_q":
+        args.append(sdtype)
     args.append(None)
     return getattr(L, fn)(*args)
 
@@ -144,3 +146,29 @@ def test_binding_error_message(L):
     with pytest.raises(wkv.Rwkv7Error) as ei:
         wkv._check(E_HEAD)
     assert "64" in str(ei.value) and ei.value.status == E_HEAD
+
+
+@pytest.mark.parametrize("sdtype", [-1, 3, 7])
+def test_step_q_rejects_unknown_state_dtype(L, sdtype):
+    assert call(L, fn="rwkv7_wkv_step_q", T=1, sdtype=sdtype) == E_DTYPE
+
+
+@pytest.mark.parametrize("sdtype", [wkv.RWKV7_STATE_F32, wkv.RWKV7_STATE_BF16, wkv.RWKV7_STATE_F16])
+def test_step_q_validation(L, sdtype):
+    assert call(L, fn="rwkv7_wkv_step_q", T=2, sdtype=sdtype) == E_SHAPE
+    assert call(L, fn="rwkv7_wkv_step_q", T=1, N=32, sdtype=sdtype) == E_HEAD
+    assert call(L, fn="rwkv7_wkv_step_q", T=1, B=0, sdtype=sdtype) == OK
+    p = ptrs()
+    p[6] += 8  # 8-byte aligned state_in
+    assert call(L, fn="rwkv7_wkv_step_q", p=p, T=1, sdtype=sdtype) == E_ALIGN
+
+
+def test_step_q_alias_uses_16_bit_state_size(L):
+    """state_out starting half-way into a 16-bit state_in overlaps it (rejected before any launch)."""
+    B, H = 2, 4
+    st16 = B * H * 64 * 64 * 2
+    p = ptrs()
+    p[8] = p[6] + st16 // 2
+    assert call(L, fn="rwkv7_wkv_step_q", p=p, T=1, B=B, H=H, sdtype=wkv.RWKV7_STATE_BF16) == E_ALIAS
+    p[8] = p[6] + st16 - 16
+    assert call(L, fn="rwkv7_wkv_step_q", p=p, T=1, B=B, H=H, sdtype=wkv.RWKV7_STATE_F16) == E_ALIAS

@@ -31,6 +31,13 @@ MUTANTS = [
     ("previous_token_k", "k[j] = widen(J->k, J->in_dtype, base + j);",
      "k[j] = widen(J->k, J->in_dtype, (t ? base - (size_t)(H * N) : base) + j);"),
     ("bf16_shift", "<< 16;", "<< 15;"),
+    ("round_half_away", "rint(x / quantum)", "round(x / quantum)"),
+    ("round_toward_zero", "rint(x / quantum)", "trunc(x / quantum)"),
+    ("f16_subnormal_floor", "round_to_format(x[i], 11, -14, 65504.0)", "round_to_format(x[i], 11, -15, 65504.0)"),
+    ("f16_precision", "round_to_format(x[i], 11, -14, 65504.0)", "round_to_format(x[i], 10, -14, 65504.0)"),
+    ("f16_no_overflow", "fabs(r) > maxv ?", "fabs(r) > 2 * maxv ?"),
+    ("f16_widen_bias", "e - 25);", "e - 24);"),
+    ("f16_encode_bias", "(lead + 15) << 10", "(lead + 14) << 10"),
 ]
 
 
@@ -42,7 +49,7 @@ def _build_mutant(tmp_path, name, old, new):
     so = tmp_path / (name + ".so")
     c.write_text(mut)
     subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-std=c11", "-shared", "-fPIC", "-pthread", str(c),
-                    "-o", str(so)], check=True)
+                    "-o", str(so), "-lm"], check=True)
     return str(so)
 
 
@@ -54,15 +61,28 @@ class _MutantOracle:
         f = lib.wkv7_oracle_f64
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int] * 3
+        for name in ("wkv7_oracle_round16", "wkv7_oracle_widen16"):
+            g = getattr(lib, name)
+            g.restype = ctypes.c_int
+            g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
         self._lib = lib
 
-    def wkv7(self, *args, **kw):
+    def _bound(self, fn, *args, **kw):
         saved = oracle._lib
         oracle._lib = self._lib
         try:
-            return oracle.wkv7(*args, **kw)
+            return fn(*args, **kw)
         finally:
             oracle._lib = saved
+
+    def wkv7(self, *args, **kw):
+        return self._bound(oracle.wkv7, *args, **kw)
+
+    def round16(self, *args, **kw):
+        return self._bound(oracle.round16, *args, **kw)
+
+    def widen16(self, *args, **kw):
+        return self._bound(oracle.widen16, *args, **kw)
 
 
 def _all_pins(orc):
@@ -81,6 +101,8 @@ def _all_pins(orc):
     ye, se, _ = pins.exact_fraction_run(x)
     y, s = pins.call(orc, pins.cast_inputs(x, "bf16"))
     res["exact_bf16"] = max(pins.rel(y, ye), pins.rel(s, se))
+    res["widen16"] = pins.pin_widen16(orc)
+    res["round16"] = pins.pin_round16(orc)
     return res
 
 
