@@ -153,6 +153,8 @@ int rwkv7_wkv_step_q(const void *r, const void *w, const void *k, const void *v,
  *
  * Domain of RWKV7_ALGO_CHUNKED (the sequential algorithm has none beyond
  * finite inputs):
+ *   - bfloat16 inputs only (dtype RWKV7_DTYPE_BF16); float32 inputs return
+ *     RWKV7_ERR_ALGO (their 1e-5 accuracy needs the sequential algorithm);
  *   - 0 <= w <= 1; any w below 2^-15 is treated as 2^-15, which changes a
  *     decayed term by at most 2^-15 of its size;
  *   - the decay-scaled inputs, the state and the intermediate chunk products

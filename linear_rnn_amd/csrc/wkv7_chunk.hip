@@ -23,15 +23,21 @@
 // MFMA stages (U, Y and the update) touch the state.
 //
 // Software pipeline. One workgroup (8 waves, two per SIMD) owns one head. In
-// loop iteration i, between two barriers, the waves work on five chunks at once:
+// loop iteration i, between two barriers, the waves work on six chunks at once:
 //   waves 0-3  S: state phase of chunk i (wave = 16-value block)
 //              P: fused products of chunk i+1 (wave = 16-key tile)
-//              staging of chunk i+4's inputs from HBM into LDS
+//              staging of chunk i+5's six inputs from HBM into LDS
 //   wave 4     F: decay factors of chunk i+4;  A^, R^ fragments of chunk i+3
 //   wave 5     B: rows of T and M_r of chunk i+2; B-, K-, V fragments of chunk i+3
 //   waves 6,7  G: Grams of chunk i+3 (keys 0-31 and 32-63 as two partial sums)
 // Each stage reads what an earlier iteration wrote into LDS rings deep enough
-// for it, so one barrier per iteration suffices.
+// for it, so one barrier per iteration suffices. Only the staging waves issue
+// global loads: every other role works from LDS, so no wave ever has a load in
+// flight into registers that another role's code also uses (the compiler's
+// wait-count insertion cannot tell the roles apart and would otherwise make
+// the staging waves wait for their own earlier stores). Within a stage, all LDS
+// reads are issued before its first LDS write, so each stage pays about one
+// LDS round trip rather than one per fragment.
 //
 // Numerics. Decay factors are running products of w: every factor that
 // multiplies the state is <= 1. Each Gram factors e^{gamma_x - gamma_y} through
@@ -83,6 +89,7 @@ __device__ __forceinline__ f32x4 to_f4(half4 h) {
   return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
 
 // hi + lo bfloat16 split of 8 floats: hi keeps the top 16 bits (truncation), lo
 // is the rounded remainder, so x = hi + lo to ~2^-17 relative.
@@ -153,16 +160,17 @@ struct ChunkParams {
   int32_t H;
 };
 
-// Tensors staged through LDS (w goes straight to the factor wave's registers).
-enum { kR = 0, kK = 1, kV = 2, kA = 3, kB = 4, kStaged = 5 };
-constexpr int kSrc[kStaged] = {0, 2, 3, 4, 5};  // index into ChunkParams::in
+// Tensors staged through LDS, in slot order.
+enum { kR = 0, kK = 1, kV = 2, kA = 3, kB = 4, kW = 5, kStaged = 6 };
+constexpr int kSrc[kStaged] = {0, 2, 3, 4, 5, 1};  // index into ChunkParams::in
+constexpr int kRing = 3;  // input slots: chunks i+3 (fragments, Grams), i+4 (factors), i+5 (being filled)
 enum { kFacE = 0, kFacS = 1, kFacG = 2, kFacF = 3 };
 enum { kLab = 0, kLak = 1, kLrb = 2, kLrk = 3 };
 
 template <bool BF16>
 struct Pipe {
   using IT = typename In<BF16>::T;
-  IT X[2][kStaged][kC][In<BF16>::kRow];  // raw inputs of chunks i+3 (read) and i+4 (being filled)
+  IT X[kRing][kStaged][kC][In<BF16>::kRow];  // raw inputs, slot = chunk % kRing
   float fac[2][4][kC + 1][kNP];           // E (row t+1 = e^{gamma_t}, row 0 = 1), Suf, G (row t+1 = e^{gamma_t-gamma_7}), F
   float gp[2][2][4][kC][kC];              // Gram partial sums (key halves) [t][s]
   float lk[2][2][kC][kC];                 // summed L_ak^T [s][t] and L_rk [t][s]
@@ -196,7 +204,6 @@ __global__ __launch_bounds__(kThreads) void wkv7_chunk_kernel(ChunkParams p) {
   const int64_t seq_base = ((int64_t)bb * T * p.H + hh) * kN;
   const int nch = (T + kC - 1) / kC;
   // Per-head bases (uniform); every in-head offset below fits in 32 bits.
-  const IT* win = static_cast<const IT*>(p.in[1]) + seq_base;
   float* yout = p.y + seq_base;
   const bool state_wave = wave < 4;
 
@@ -212,76 +219,97 @@ __global__ __launch_bounds__(kThreads) void wkv7_chunk_kernel(ChunkParams p) {
       St[kt] = f32x4{q.x, q.y, q.z, q.w};
     }
   }
+  // Complete the state loads here, once: otherwise the loop's wait counts must
+  // allow for them on every iteration and end up waiting for unrelated stores.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // ---- loaders (global -> registers at the top of an iteration, consumed at its
-  // end or at the top of the next one; past-the-end tokens are clamped to T-1
-  // and replaced at use by an identity token: w = 1, everything else 0).
-  // Staging: state wave w loads all of tensor w and a quarter of tensor 4, so
+  // ---- staging (global -> registers at the top of an iteration, -> LDS at its
+  // end; past-the-end tokens are clamped to T-1 and stored as zeros, and the
+  // factor stage turns them into identity tokens: w = 1, everything else 0).
+  // State wave w loads all of tensor w and a quarter of tensors 4 and 5, so
   // every load instruction has a wave-uniform base.
   constexpr int kPerTensor = kC * kSeg;            // 16-byte loads per tensor per chunk
   constexpr int kOwn = kPerTensor / kWave;         // own-tensor loads per lane (2 or 4)
-  constexpr int kShared = kPerTensor / 4;          // loads of tensor 4 per wave (32 or 64)
+  constexpr int kQuarter = kPerTensor / 4;         // loads of tensor 4 (and of 5) per wave (32 or 64)
+  constexpr int kShr = 2 * kQuarter / kWave;       // shared loads per lane (1 or 2)
   constexpr uint32_t kEsz = sizeof(IT);
-  uint4 stg[kOwn + 1];
-  auto stage_slot = [&](int q, int& x, int& tok, int& seg) {  // q = kOwn: the shared tensor
-    const int e = q < kOwn ? lane + kWave * q : kShared * wave + lane;
-    x = q < kOwn ? wave : 4;
+  uint4 stg[kOwn + kShr];
+  auto stage_slot = [&](int q, int& x, int& tok, int& seg) {
+    int e;
+    if (q < kOwn) {
+      e = lane + kWave * q;
+      x = wave;
+    } else {
+      const int e2 = lane + kWave * (q - kOwn);  // 0 .. 2 * kQuarter - 1
+      x = 4 + e2 / kQuarter;
+      e = kQuarter * wave + e2 % kQuarter;
+    }
     tok = e / kSeg;
     seg = e % kSeg;
   };
   auto issue_stage = [&](int c) {
 #pragma unroll
-    for (int q = 0; q <= kOwn; ++q) {
+    for (int q = 0; q < kOwn + kShr; ++q) {
       int x, tok, seg;
       stage_slot(q, x, tok, seg);
-      if (q < kOwn || lane < kShared) {
-        const int t = min(c * kC + tok, T - 1);
-        const void* base = static_cast<const IT*>(q < kOwn ? p.in[kSrc[0]] : p.in[kSrc[4]]) + seq_base;
-        if (q < kOwn) {  // own tensor: pick the wave's pointer (uniform)
-          const void* b1 = static_cast<const IT*>(p.in[kSrc[1]]) + seq_base;
-          const void* b2 = static_cast<const IT*>(p.in[kSrc[2]]) + seq_base;
-          const void* b3 = static_cast<const IT*>(p.in[kSrc[3]]) + seq_base;
-          base = wave == 1 ? b1 : wave == 2 ? b2 : wave == 3 ? b3 : base;
-        }
-        stg[q] = ld_off<uint4>(base, (uint32_t)(t * tok_stride + seg * kEpv) * kEsz);
+      const int t = min(c * kC + tok, T - 1);
+      const void* base;
+      if (q < kOwn) {  // own tensor: pick the wave's pointer (uniform)
+        const void* b1 = static_cast<const IT*>(p.in[kSrc[1]]) + seq_base;
+        const void* b2 = static_cast<const IT*>(p.in[kSrc[2]]) + seq_base;
+        const void* b3 = static_cast<const IT*>(p.in[kSrc[3]]) + seq_base;
+        const void* b0 = static_cast<const IT*>(p.in[kSrc[0]]) + seq_base;
+        base = wave == 1 ? b1 : wave == 2 ? b2 : wave == 3 ? b3 : b0;
+      } else {  // tensor 4 or 5: uniform per instruction when kQuarter is a multiple of the wave
+        const void* b4 = static_cast<const IT*>(p.in[kSrc[4]]) + seq_base;
+        const void* b5 = static_cast<const IT*>(p.in[kSrc[5]]) + seq_base;
+        base = x == 4 ? b4 : b5;
       }
+      stg[q] = ld_off<uint4>(base, (uint32_t)(t * tok_stride + seg * kEpv) * kEsz);
     }
   };
   auto commit_stage = [&](int c) {
+    const bool tail = (c + 1) * kC > T;  // uniform: only the last chunk has dead tokens
 #pragma unroll
-    for (int q = 0; q <= kOwn; ++q) {
+    for (int q = 0; q < kOwn + kShr; ++q) {
       int x, tok, seg;
       stage_slot(q, x, tok, seg);
-      if (q < kOwn || lane < kShared) {
+      uint4 v = stg[q];
+      if (tail) {  // component-wise select (a whole-vector select is lowered through scratch memory)
         const bool live = c * kC + tok < T;
-        uint4 v;  // component-wise select (a whole-vector select is lowered through scratch memory)
-        v.x = live ? stg[q].x : 0u;
-        v.y = live ? stg[q].y : 0u;
-        v.z = live ? stg[q].z : 0u;
-        v.w = live ? stg[q].w : 0u;
-        *reinterpret_cast<uint4*>(&sm.X[c & 1][x][tok][seg * kEpv]) = v;
+        v.x = live ? v.x : 0u;
+        v.y = live ? v.y : 0u;
+        v.z = live ? v.z : 0u;
+        v.w = live ? v.w : 0u;
       }
+      *reinterpret_cast<uint4*>(&sm.X[c % kRing][x][tok][seg * kEpv]) = v;
     }
   };
-  // factor wave: raw bits of w (lane = key column) for the next chunk, kept at
-  // their loaded width so nothing touches them before the next iteration
-  using WRaw = typename std::conditional<BF16, uint16_t, uint32_t>::type;
-  WRaw wraw[kC];
-  auto issue_w = [&](int c) {
+
+  // y of chunk ychunk: yout4[e] = y[t = 4g + e][i = 16 wave + li]. The state phase
+  // leaves it in registers and the next iteration stores it right after issuing
+  // its staging loads: loads and stores share one wait counter, so stores issued
+  // late in an iteration would hold up the commit's wait (or the next loads).
+  f32x4 yout4 = zero4();
+  int ychunk = -1;
+  auto store_y = [&]() {
+    if (ychunk >= 0) {
+      const int t0 = ychunk * kC + 4 * g;
 #pragma unroll
-    for (int t = 0; t < kC; ++t)
-      wraw[t] = ld_off<WRaw>(win, (uint32_t)(min(c * kC + t, T - 1) * tok_stride + lane) * kEsz);
+      for (int e = 0; e < 4; ++e)
+        if (t0 + e < T) st_off<float>(yout, (uint32_t)((t0 + e) * tok_stride + 16 * wave + li) * 4u, yout4[e]);
+      ychunk = -1;
+    }
   };
 
-  if (wave == 4) issue_w(0);
-
-  for (int it = -4; it < nch; ++it) {
-    const int cF = it + 4, cG = it + 3, cB = it + 2, cP = it + 1, cS = it;
-    const bool doF = cF < nch, doG = cG >= 0 && cG < nch, doB = cB >= 0 && cB < nch;
-    const bool doP = cP >= 0 && cP < nch, doS = cS >= 0;
+  for (int it = -5; it < nch; ++it) {
+    const int cX = it + 5, cF = it + 4, cG = it + 3, cB = it + 2, cP = it + 1, cS = it;
+    const bool doF = cF >= 0 && cF < nch, doG = cG >= 0 && cG < nch, doB = cB >= 0 && cB < nch;
+    const bool doP = cP >= 0 && cP < nch, doS = cS >= 0, doX = cX < nch;
 
     if (state_wave) {
-      issue_stage(cF);  // unconditional (clamped), committed at the end of this iteration
+      issue_stage(cX);  // unconditional (clamped), committed at the end of this iteration
+      store_y();
 
       // ================= P: fused products of chunk cP (wave = key tile; wave 0 also the 16x16 ones)
       if (doP) {
@@ -327,88 +355,92 @@ __global__ __launch_bounds__(kThreads) void wkv7_chunk_kernel(ChunkParams p) {
           St[kt] = mfma16(sm.ob[os][0][kt][lane], uB, St[kt]);
           St[kt] = mfma16(sm.ob[os][1][kt][lane], vB, St[kt]);
         }
-        // yv[e] = y[t = 4g + e][i = 16 wave + li]
-        const int t0 = cS * kC + 4 * g;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (t0 + e < T) st_off<float>(yout, (uint32_t)((t0 + e) * tok_stride + 16 * wave + li) * 4u, yv[e]);
+        yout4 = yv;  // stored at the top of the next iteration
+        ychunk = cS;
       }
 
-      if (doF) commit_stage(cF);
+      if (doX) commit_stage(cX);
     } else if (wave == 4) {
       // ================= F: decay factors of chunk cF (lane = key column j)
-      float wc[kC];
-#pragma unroll
-      for (int t = 0; t < kC; ++t) wc[t] = cF * kC + t < T ? fmaxf(IO::widen(wraw[t]), kWMin) : 1.f;
-      // keep the next loads after this use, so they can land in the same registers
-      // (otherwise the loop-carried copy of wraw would wait for them)
-      __builtin_amdgcn_sched_barrier(0);
-      issue_w(cF + 1);
       if (doF) {
-        float(*f)[kC + 1][kNP] = sm.fac[cF & 1];
-        const int j = lane;
-        float e = 1.f;
-        f[kFacE][0][j] = 1.f;
+        const IT* wrow = &sm.X[cF % kRing][kW][0][lane];
+        IT wr[kC];
+#pragma unroll
+        for (int t = 0; t < kC; ++t) wr[t] = wrow[t * In<BF16>::kRow];
+        float wc[kC], rc[kC];
 #pragma unroll
         for (int t = 0; t < kC; ++t) {
-          e *= wc[t];
-          f[kFacE][t + 1][j] = e;
+          float x = IO::widen(wr[t]);
+          x = x < kWMin ? kWMin : x;                 // clamp (a NaN passes through)
+          wc[t] = cF * kC + t < T ? x : 1.f;         // identity token past the end
+          rc[t] = __builtin_amdgcn_rcpf(wc[t]);
         }
-        float s = 1.f;
+        // Six running products, advanced together so their latencies overlap:
+        //   E row t+1 = e^{gamma_t} (prefix), S row t = e^{gamma_15 - gamma_t} (suffix),
+        //   G row t+1 = e^{gamma_t - gamma_7}, F row s = e^{gamma_7 - gamma_s}.
+        float(*f)[kC + 1][kNP] = sm.fac[cF & 1];
+        const int j = lane;
+        float e = 1.f, sf = 1.f, gu = 1.f, gd = 1.f, fd = 1.f, fu = 1.f;
+        f[kFacE][0][j] = 1.f;
         f[kFacS][kC - 1][j] = 1.f;
-#pragma unroll
-        for (int t = kC - 2; t >= 0; --t) {
-          s *= wc[t + 1];
-          f[kFacS][t][j] = s;
-        }
-        float rc[kC];
-#pragma unroll
-        for (int t = 0; t < kC; ++t) rc[t] = __builtin_amdgcn_rcpf(wc[t]);
-        float gv = 1.f;  // G row t+1: e^{gamma_t - gamma_7}
         f[kFacG][kMid + 1][j] = 1.f;
-#pragma unroll
-        for (int t = kMid + 1; t < kC; ++t) {
-          gv *= wc[t];
-          f[kFacG][t + 1][j] = gv;
-        }
-        gv = 1.f;
-#pragma unroll
-        for (int t = kMid - 1; t >= -1; --t) {
-          gv *= rc[t + 1];
-          f[kFacG][t + 1][j] = gv;
-        }
-        float fv = 1.f;  // F row s: e^{gamma_7 - gamma_s}
         f[kFacF][kMid][j] = 1.f;
 #pragma unroll
-        for (int s2 = kMid - 1; s2 >= 0; --s2) {
-          fv *= wc[s2 + 1];
-          f[kFacF][s2][j] = fv;
-        }
-        fv = 1.f;
-#pragma unroll
-        for (int s2 = kMid + 1; s2 < kC; ++s2) {
-          fv *= rc[s2];
-          f[kFacF][s2][j] = fv;
+        for (int q = 0; q < kC; ++q) {
+          e *= wc[q];
+          f[kFacE][q + 1][j] = e;
+          if (q < kC - 1) {  // S row kC-2-q
+            sf *= wc[kC - 1 - q];
+            f[kFacS][kC - 2 - q][j] = sf;
+          }
+          if (q < kC - 1 - kMid) {  // G rows kMid+2 .. kC: token t = kMid+1+q
+            gu *= wc[kMid + 1 + q];
+            f[kFacG][kMid + 2 + q][j] = gu;
+          }
+          if (q <= kMid) {  // G rows kMid .. 0: token t = kMid-1-q, factor 1 / w_{t+1}
+            gd *= rc[kMid - q];
+            f[kFacG][kMid - q][j] = gd;
+          }
+          if (q < kMid) {  // F rows kMid-1 .. 0: s = kMid-1-q, factor w_{s+1}
+            fd *= wc[kMid - q];
+            f[kFacF][kMid - 1 - q][j] = fd;
+          }
+          if (q < kC - 1 - kMid) {  // F rows kMid+1 .. kC-1: s = kMid+1+q, factor 1 / w_s
+            fu *= rc[kMid + 1 + q];
+            f[kFacF][kMid + 1 + q][j] = fu;
+          }
         }
       }
-      // ================= A^ A-fragments (M = key, K = token) and R^ seeds (D layout) of chunk cG
+      // ================= A^ A-fragments (M = key, K = token) and R^ seeds (D layout) of chunk cG,
+      // key tiles 2h and 2h+1 for h = 0, 1
+      // (each half reads all it needs before its fragment writes)
       if (doG) {
-        const int xs = cG & 1, os = cG % 3;
-        const float(*fE)[kNP] = sm.fac[cG & 1][kFacE];
+        for (int h = 0; h < 2; ++h) {
+          const int xs = cG % kRing, os = cG % 3;
+          const float(*fE)[kNP] = sm.fac[cG & 1][kFacE];
+          IT araw[2][4];
+          float ea[2][4], rv[2][4];
+          float4 er[2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const int j = 16 * kt + li;
-          float av[4];
+          for (int u = 0; u < 2; ++u) {
+            const int kt = 2 * h + u;
+            const int j = 16 * kt + li;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 4 * g + e;
-            av[e] = IO::get(&sm.X[xs][kA][t][j]) * fE[t][j];
+            for (int e = 0; e < 4; ++e) {
+              araw[u][e] = sm.X[xs][kA][4 * g + e][j];
+              ea[u][e] = fE[4 * g + e][j];
+            }
+            IO::get4(&sm.X[xs][kR][li][16 * kt + 4 * g], rv[u]);
+            er[u] = *reinterpret_cast<const float4*>(&fE[li + 1][16 * kt + 4 * g]);
           }
-          sm.oa[os][0][kt][lane] = to_h4(av[0], av[1], av[2], av[3]);
-          float rv[4];
-          IO::get4(&sm.X[xs][kR][li][16 * kt + 4 * g], rv);
-          const float4 ef = *reinterpret_cast<const float4*>(&fE[li + 1][16 * kt + 4 * g]);
-          sm.oa[os][1][kt][lane] = to_h4(rv[0] * ef.x, rv[1] * ef.y, rv[2] * ef.z, rv[3] * ef.w);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int kt = 2 * h + u;
+            sm.oa[os][0][kt][lane] = to_h4(IO::widen(araw[u][0]) * ea[u][0], IO::widen(araw[u][1]) * ea[u][1],
+                                           IO::widen(araw[u][2]) * ea[u][2], IO::widen(araw[u][3]) * ea[u][3]);
+            sm.oa[os][1][kt][lane] =
+                to_h4(rv[u][0] * er[u].x, rv[u][1] * er[u].y, rv[u][2] * er[u].z, rv[u][3] * er[u].w);
+          }
         }
       }
     } else if (wave == 5) {
@@ -466,31 +498,44 @@ __global__ __launch_bounds__(kThreads) void wkv7_chunk_kernel(ChunkParams p) {
       }
       // ================= B- and K- A-fragments (M = key, K = token), V B-fragments, gamma_15 of chunk cG
       if (doG) {
-        const int xs = cG & 1, os = cG & 3;
+        const int xs = cG % kRing, os = cG & 3;
         const float(*fS)[kNP] = sm.fac[cG & 1][kFacS];
+        // every LDS read of the stage first, then the arithmetic and the fragment writes
+        IT braw[4][4], kraw[4][4], vraw[4][4];
+        float suf[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           const int j = 16 * kt + li;
-          float bv[4], kv[4], vv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = 4 * g + e;
-            const float suf = fS[t][j];
-            bv[e] = IO::get(&sm.X[xs][kB][t][j]) * suf;
-            kv[e] = IO::get(&sm.X[xs][kK][t][j]) * suf;
-            vv[e] = IO::get(&sm.X[xs][kV][t][j]);  // value index i = j
+            suf[kt][e] = fS[t][j];
+            braw[kt][e] = sm.X[xs][kB][t][j];
+            kraw[kt][e] = sm.X[xs][kK][t][j];
+            vraw[kt][e] = sm.X[xs][kV][t][j];  // value index i = j
+          }
+        }
+        const float g15 = sm.fac[cG & 1][kFacE][kC][lane];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          float bv[4], kv[4], vv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bv[e] = IO::widen(braw[kt][e]) * suf[kt][e];
+            kv[e] = IO::widen(kraw[kt][e]) * suf[kt][e];
+            vv[e] = IO::widen(vraw[kt][e]);
           }
           sm.ob[os][0][kt][lane] = to_h4(bv[0], bv[1], bv[2], bv[3]);
           sm.ob[os][1][kt][lane] = to_h4(kv[0], kv[1], kv[2], kv[3]);
           sm.ob[os][2][kt][lane] = to_h4(vv[0], vv[1], vv[2], vv[3]);
         }
-        sm.gam[os][lane] = sm.fac[cG & 1][kFacE][kC][lane];
+        sm.gam[os][lane] = g15;
       }
     } else {
       // ================= G: Gram partial sums of chunk cG over keys 32h..32h+31 (h = wave - 6)
       if (doG) {
         const int h = wave - 6;
-        const int xs = cG & 1;
+        const int xs = cG % kRing;
         const float(*fG)[kNP] = sm.fac[cG & 1][kFacG];
         const float(*fF)[kNP] = sm.fac[cG & 1][kFacF];
         const int j0 = 32 * h + 8 * g;
@@ -547,6 +592,7 @@ __global__ __launch_bounds__(kThreads) void wkv7_chunk_kernel(ChunkParams p) {
     lds_barrier();
   }
 
+  if (state_wave) store_y();
   if (state_wave && p.s_out) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -574,7 +620,9 @@ hipError_t launch_chunk_dtype(const WkvCall& c) {
 }  // namespace
 
 hipError_t launch_chunked(const WkvCall& c) {
-  return c.dtype == 1 ? launch_chunk_dtype<true>(c) : launch_chunk_dtype<false>(c);
+  // bfloat16 inputs only: float32 inputs keep float32 accuracy on the sequential
+  // kernel, and their six staged input slots would not fit the LDS ring.
+  return c.dtype == 1 ? launch_chunk_dtype<true>(c) : hipErrorNotSupported;
 }
 
 }  // namespace rwkv7

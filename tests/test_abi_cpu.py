@@ -172,3 +172,7 @@ def test_step_q_alias_uses_16_bit_state_size(L):
     assert call(L, fn="rwkv7_wkv_step_q", p=p, T=1, B=B, H=H, sdtype=wkv.RWKV7_STATE_BF16) == E_ALIAS
     p[8] = p[6] + st16 - 16
     assert call(L, fn="rwkv7_wkv_step_q", p=p, T=1, B=B, H=H, sdtype=wkv.RWKV7_STATE_F16) == E_ALIAS
+
+
+def test_chunked_refuses_f32_inputs_before_any_launch(L):
+    assert call(L, fn="rwkv7_wkv_prefill_ex", dtype=F32, algo=wkv.RWKV7_ALGO_CHUNKED) == E_ALGO

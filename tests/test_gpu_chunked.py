@@ -44,12 +44,13 @@ def test_zero_initial_state(torch):
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16
 
 
-def test_f32_inputs(torch):
-    say("chunked, f32 inputs")
+def test_f32_inputs_are_refused(torch):
+    """The chunked algorithm takes bfloat16 inputs only; float32 inputs stay on the sequential kernel."""
+    say("chunked, f32 inputs refused")
     x = make_inputs(CONFIGS[0])
-    y, s = run(torch, to_dev(x))
-    yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=None)
-    assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16
+    with pytest.raises(wkv.Rwkv7Error) as ei:
+        run(torch, to_dev(x))
+    assert ei.value.status == -7
 
 
 def test_config1_full(torch):
