@@ -109,7 +109,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-16bit", action="store_true", help="skip the bf16 / f16 stored-state decode legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked")
+    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked (fused), 3 chunked (split)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -138,8 +138,8 @@ def main(argv=None):
     s_in = torch.from_numpy(x["state_in"]).cuda()
     y = torch.empty((B, T, H, N), dtype=torch.float32, device="cuda")
     s_out = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
-    # the library's default for bfloat16 inputs is the chunked algorithm
-    algo = args.algo if args.algo else wkv.RWKV7_ALGO_CHUNKED
+    # the library's default for bfloat16 inputs is the split chunked algorithm
+    algo = args.algo if args.algo else wkv.RWKV7_ALGO_CHUNKED_SPLIT
 
     def prefill():
         wkv.rwkv7_wkv_prefill_ex(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], s_in, y, s_out, algo=algo)
@@ -159,9 +159,13 @@ def main(argv=None):
         flops = FLOP_REC * tok_heads
         roof = {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VECTOR_TFLOPS,
                 "unit": "TFLOP/s"}
-    else:
+    elif algo == wkv.RWKV7_ALGO_CHUNKED:
         kname, src = "wkv7_chunk_kernel", ["linear_rnn_amd/csrc/wkv7_chunk.hip",
                                            "linear_rnn_amd/csrc/wkv7_device.hpp"]
+        roof = {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        kname, src = "wkv7_prep_kernel+wkv7_scan_kernel", ["linear_rnn_amd/csrc/wkv7_split.hip",
+                                                           "linear_rnn_amd/csrc/wkv7_device.hpp"]
         roof = {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(kname + ":" + cfg.name, src)
@@ -175,7 +179,7 @@ def main(argv=None):
         "vs_baseline": None, "dtype": "f32" if algo == wkv.RWKV7_ALGO_SEQUENTIAL else "bf16",
         "data": "synthetic (seeded; RWKV-7 layer-shaped distributions)",
         "config": {"workload": "%s: B=%d T=%d H=%d N=%d bf16 inputs, fp32 state in/out" % (cfg.name, B, T, H, N),
-                   "B": B, "T": T, "H": H, "N": N, "algo": {1: "sequential", 2: "chunked"}[algo]},
+                   "B": B, "T": T, "H": H, "N": N, "algo": {1: "sequential", 2: "chunked-fused", 3: "chunked-split"}[algo]},
         "roofline": roof, "device": dev_name, "timed_wall_s": wall,
     }
 

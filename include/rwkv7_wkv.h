@@ -80,7 +80,9 @@ extern "C" {
 /* Prefill algorithm (rwkv7_wkv_prefill_ex). */
 #define RWKV7_ALGO_AUTO 0       /* library's choice (what rwkv7_wkv_prefill does) */
 #define RWKV7_ALGO_SEQUENTIAL 1 /* token-by-token recurrence, state resident in registers */
-#define RWKV7_ALGO_CHUNKED 2    /* chunked (WY / UT) form with the intra-chunk products on MFMA */
+#define RWKV7_ALGO_CHUNKED 2    /* chunked (WY / UT) form, one workgroup per head doing every stage */
+#define RWKV7_ALGO_CHUNKED_SPLIT 3 /* chunked form split into a chunk-parallel prep kernel and a
+                                      per-head scan kernel (uses a cached device workspace) */
 
 #define RWKV7_HEAD_SIZE 64
 
@@ -100,7 +102,7 @@ extern "C" {
  *   stream            hipStream_t to launch on (NULL = null stream)
  *
  * The automatic choice uses the sequential algorithm for float32 inputs and the
- * chunked algorithm for bfloat16 inputs.
+ * split chunked algorithm (RWKV7_ALGO_CHUNKED_SPLIT) for bfloat16 inputs.
  */
 int rwkv7_wkv_prefill(const void *r, const void *w, const void *k, const void *v, const void *a,
                       const void *b, const float *state_in, float *y, float *state_out, int64_t B,
@@ -151,8 +153,8 @@ int rwkv7_wkv_step_q(const void *r, const void *w, const void *k, const void *v,
  * Prefill with an explicit algorithm (RWKV7_ALGO_*), so a caller or a test can
  * force one kernel. Other arguments as for rwkv7_wkv_prefill.
  *
- * Domain of RWKV7_ALGO_CHUNKED (the sequential algorithm has none beyond
- * finite inputs):
+ * Domain of RWKV7_ALGO_CHUNKED and RWKV7_ALGO_CHUNKED_SPLIT (the sequential
+ * algorithm has none beyond finite inputs):
  *   - bfloat16 inputs only (dtype RWKV7_DTYPE_BF16); float32 inputs return
  *     RWKV7_ERR_ALGO (their 1e-5 accuracy needs the sequential algorithm);
  *   - 0 <= w <= 1; any w below 2^-15 is treated as 2^-15, which changes a
@@ -164,6 +166,14 @@ int rwkv7_wkv_step_q(const void *r, const void *w, const void *k, const void *v,
  *     otherwise the call returns RWKV7_ERR_ALGO and launches nothing.
  * Results agree with the sequential algorithm to about 1e-3 relative (max-norm
  * over a tensor) rather than bit for bit.
+ *
+ * Workspace of RWKV7_ALGO_CHUNKED_SPLIT (also the automatic choice for
+ * bfloat16 inputs): the chunk records that pass from its first kernel to its
+ * second live in a device buffer that the library allocates on the first call
+ * that needs it and keeps for later calls, one buffer per (device, stream),
+ * grown when a call needs more (about 96 MiB for long sequences: the sequence
+ * is processed in slabs of chunks that fit it). Growing it synchronises that
+ * stream; an allocation failure returns RWKV7_ERR_HIP before any launch.
  */
 int rwkv7_wkv_prefill_ex(const void *r, const void *w, const void *k, const void *v, const void *a,
                          const void *b, const float *state_in, float *y, float *state_out, int64_t B,

@@ -67,7 +67,7 @@ int run(const void* r, const void* w, const void* k, const void* v, const void* 
         const void* state_in, float* y, void* state_out, int64_t B, int64_t T, int64_t H, int64_t N,
         int dtype, int sdtype, int algo, bool step, void* stream) {
   const void* in[6] = {r, w, k, v, a, b};
-  if (algo < RWKV7_ALGO_AUTO || algo > RWKV7_ALGO_CHUNKED) return RWKV7_ERR_ALGO;
+  if (algo < RWKV7_ALGO_AUTO || algo > RWKV7_ALGO_CHUNKED_SPLIT) return RWKV7_ERR_ALGO;
   const int st = validate(in, state_in, y, state_out, B, T, H, N, dtype, sdtype);
   if (st != RWKV7_OK) return st;
   if (step && T != 1) return RWKV7_ERR_SHAPE;
@@ -84,8 +84,10 @@ int run(const void* r, const void* w, const void* k, const void* v, const void* 
   if (step) {
     e = rwkv7::launch_sequential(c, /*decode_shape=*/true);
   } else {
-    if (algo == RWKV7_ALGO_AUTO) algo = dtype == RWKV7_DTYPE_BF16 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SEQUENTIAL;
-    e = algo == RWKV7_ALGO_CHUNKED ? rwkv7::launch_chunked(c) : rwkv7::launch_sequential(c, false);
+    if (algo == RWKV7_ALGO_AUTO) algo = dtype == RWKV7_DTYPE_BF16 ? RWKV7_ALGO_CHUNKED_SPLIT : RWKV7_ALGO_SEQUENTIAL;
+    e = algo == RWKV7_ALGO_CHUNKED         ? rwkv7::launch_chunked(c)
+        : algo == RWKV7_ALGO_CHUNKED_SPLIT ? rwkv7::launch_chunked_split(c)
+                                           : rwkv7::launch_sequential(c, false);
   }
   if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;
   return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;

@@ -23,8 +23,13 @@ struct WkvCall {
 // Returns the launch status.
 hipError_t launch_sequential(const WkvCall& c, bool decode_shape);
 
-// Chunked (WY / UT) prefill with the intra-chunk products on MFMA.
+// Chunked (WY / UT) prefill with the intra-chunk products on MFMA, one
+// workgroup per head doing every stage.
 hipError_t launch_chunked(const WkvCall& c);
+
+// Chunked prefill split into a chunk-parallel prep kernel and a per-head scan
+// kernel, with a record buffer cached per (device, stream).
+hipError_t launch_chunked_split(const WkvCall& c);
 
 // state_out <- state_in (zeros when state_in is null) for B*H heads.
 hipError_t launch_state_copy(const float* s_in, float* s_out, int64_t units, hipStream_t stream);

@@ -1,0 +1,677 @@
+// Chunked WKV-7 prefill in two kernels, so that the chunk-parallel half of the
+// work uses the whole chip whatever the number of heads.
+//
+// Recurrence (RWKV-7 G0 7.2B notes, lshu.cn/news/198401, section 7.1), per head:
+//   S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T,   y_t = S_t r_t.
+//
+// Chunk form (derived; WY / "DPLR" style). Tokens t = 0..15 of a chunk, state S0
+// at its start, gamma_t = sum_{u<=t} log w_u per key column j:
+//   U[t]  = S_{t-1} a_t                       (the "state*a" term, a row over values i)
+//   U     = A' S0^T + G_u V,   Y = R' S0^T + G_y V,
+//   S_C^T = diag(e^{gamma_15}) S0^T + B- U + K- V
+// with
+//   A^[t] = a_t e^{gamma_{t-1}},  R^[t] = r_t e^{gamma_t},
+//   B-[s] = b_s e^{gamma_15 - gamma_s},  K-[s] = k_s e^{gamma_15 - gamma_s},
+//   L_ab[t][s] = sum_j a_t,j b_s,j e^{gamma_{t-1} - gamma_s}  (s <  t), L_ak likewise with k,
+//   L_rb[t][s] = sum_j r_t,j b_s,j e^{gamma_t - gamma_s}      (s <= t), L_rk likewise with k,
+//   T = (I - L_ab)^{-1},  M_r = L_rb T,
+//   A' = T A^,  R' = R^ + M_r A^,  G_u = T L_ak,  G_y = M_r L_ak + L_rk.
+// Everything except S0 and V is a function of the chunk's own r, w, k, a, b.
+//
+// Kernel 1 (prep) runs one wave per (head, chunk), all chunks in parallel. It
+// computes the decay factors, the four Grams (float32 MFMA), T and M_r (float32
+// back substitution) and the products above, and writes a 9,472-byte record per
+// chunk: A', R', G_u, G_y, B-, K- as float16 MFMA fragments in the exact register
+// layout that kernel 2 consumes, plus e^{gamma_15} in float32.
+//
+// Kernel 2 (scan) carries the float32 state through the chunks. A head's 64
+// value rows are independent, so it is split over two workgroups; each has two
+// compute waves (16 value rows each, one SIMD each) that advance the state with
+// ten 16x16x32 MFMAs per chunk, and four loader waves that stream the records
+// and the needed v columns into a five-slot LDS ring, each load issued eight
+// chunk periods before it is needed. One LDS barrier per chunk.
+//
+// Every dependent MFMA chain keeps one instruction shape: chains that mixed
+// 16x16x32 and 16x16x16 f16 products gave wrong results on gfx950 (in whichever
+// product the register allocation placed last), the same chains in one shape
+// are exact.
+//
+// A long sequence is processed in slabs of chunks (prep of a slab, then its
+// scan), so the record buffer stays a bounded workspace; the scan of slab s+1
+// starts from the state that slab s stored.
+//
+// Numerics. Decay factors are running products of w (clamped below at 2^-15):
+// factors that multiply the state are <= 1, and the Gram factors pass through
+// the decay at token 7, so no factor exceeds w_min^-8. The Grams are float32
+// products with float32 accumulation; T and M_r are float32; A', R', G_u, G_y,
+// B-, K-, the state operand and U are rounded once to float16 as MFMA operands
+// (float32 accumulation), so magnitudes must stay below 2^15. The carried state
+// is float32 throughout.
+//
+// MFMA layouts (gfx950, wave64; l = lane, li = l % 16, g = l / 16):
+//   16x16x4  f32 : A[m=li][k=g],      B[k=g][n=li]
+//   16x16x16 f16 : A[m=li][k=4g+e],   B[k=4g+e][n=li]   (e = 0..3)
+//   16x16x32 f16 : A[m=li][k=8g+e],   B[k=8g+e][n=li]   (e = 0..7)
+//   all          : D[m=4g+e][n=li]
+// A D result is unchanged a B operand with K = 16, and a product with the
+// identity as B turns an A-layout tile into the D layout (a transpose).
+// Contractions may permute their K index freely as long as both operands use
+// the same permutation: the 64-key contractions below take key 16kt + 4g + e for
+// (step, lane group, element), matching the state tiles' D layout.
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "wkv7_device.hpp"
+#include "wkv7_internal.hpp"
+
+namespace rwkv7 {
+namespace {
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 16;   // tokens per chunk
+constexpr float kWMin = 0x1p-15f;
+
+// Record of one (head, chunk): nine 1 KiB fragment blocks (16 bytes per lane),
+// then e^{gamma_15} for the 64 key columns.
+enum { kRecA0 = 0, kRecA1 = 1, kRecR0 = 2, kRecR1 = 3, kRecG = 4, kRecBK = 5, kRecBlocks = 9 };
+constexpr int kRecD = kRecBlocks * 1024;
+constexpr int kRecBytes = kRecD + kN * 4;  // 9472
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(half4 a, half4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ half4 to_h4(f32x4 x) {
+  return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+__device__ __forceinline__ half8 cat8(half4 lo, half4 hi) {
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ half4 lo4(half8 x) { return half4{x[0], x[1], x[2], x[3]}; }
+__device__ __forceinline__ half4 hi4(half8 x) { return half4{x[4], x[5], x[6], x[7]}; }
+// bfloat16 bits (low 16 bits of the argument) widened to float32, exactly
+__device__ __forceinline__ float bfw(uint32_t raw16) { return __uint_as_float(raw16 << 16); }
+// element e (0..3) of four bfloat16 packed in a uint2
+__device__ __forceinline__ float bf4(uint2 q, int e) {
+  const uint32_t u = e < 2 ? q.x : q.y;
+  return (e & 1) ? __uint_as_float(u & 0xffff0000u) : __uint_as_float(u << 16);
+}
+
+// Workgroup barrier for data exchanged through LDS: an explicit lgkmcnt(0) that
+// the compiler's wait-count pass sees (so it knows every earlier LDS read has
+// completed and does not wait on them again after the barrier), then s_barrier
+// as inline assembly, which adds no wait on outstanding global loads or stores.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <class V>
+__device__ __forceinline__ V ld_off(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
+}
+template <class V>
+__device__ __forceinline__ void st_off(void* base, uint32_t byte_off, V v) {
+  *reinterpret_cast<V*>(static_cast<char*>(base) + byte_off) = v;
+}
+
+// ============================================================================ kernel 1: prep
+
+struct PrepParams {
+  const uint16_t* r;
+  const uint16_t* w;
+  const uint16_t* k;
+  const uint16_t* a;
+  const uint16_t* b;
+  unsigned char* rec;  // [unit][chunk of slab][kRecBytes]
+  int32_t T, H;
+  int32_t c0;     // first chunk of the slab
+  int32_t nc;     // chunks in the slab
+  int32_t items;  // B * H * nc
+};
+
+constexpr int kPrepWaves = 4;
+constexpr int kFacRow = kN + 4;  // padded float row
+// Factor rows (float32, [row][key]): E row t+1 = e^{gamma_t} (row 0 = 1), Suf row s =
+// e^{gamma_15 - gamma_s}, Gq row t+1 = e^{gamma_t - gamma_7} (row 0 for t = -1),
+// Fk row s = e^{gamma_7 - gamma_s}.
+constexpr int kRowE = 0, kRowS = 17, kRowG = 33, kRowF = 50, kFacRows = 66;
+constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 17,952 bytes
+// After the factors are consumed the same wave area holds L_ab and L_rb ([t][s],
+// float32) and the rows of T and M_r (float16).
+constexpr int kLabOff = 0, kLrbOff = 16 * 16, kTmOffBytes = 2 * 16 * 16 * 4;
+
+__global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int item = (int)blockIdx.x * kPrepWaves + wave;
+  if (item >= p.items) return;  // wave-uniform; this kernel has no workgroup barrier
+  float* fac = reinterpret_cast<float*>(smem_raw + wave * kPrepLdsPerWave);
+
+  // item = (b * nc + chunk) * H + h: neighbouring waves read neighbouring heads of one token block
+  const int h = item % p.H;
+  const int rest = item / p.H;
+  const int cl = rest % p.nc;
+  const int bb = rest / p.nc;
+  const int unit = bb * p.H + h;
+  const int t0 = (p.c0 + cl) * kC;
+  const int nt = min(kC, p.T - t0);  // live tokens, >= 1
+  const int64_t base = ((int64_t)bb * p.T + t0) * p.H * kN + (int64_t)h * kN;  // element offset of token t0
+  const uint32_t tstride = (uint32_t)p.H * kN;                                // elements between tokens
+  unsigned char* rec = p.rec + ((int64_t)unit * p.nc + cl) * kRecBytes;
+
+  // ---- raw r, a, b, k in the token layout: lane (t = li, g) holds columns 16kt + 4g .. 4g+3.
+  // Past-the-end tokens read token nt-1 and are zeroed below (identity tokens).
+  const int tl = min(li, nt - 1);
+  const bool live = li < nt;
+  uint2 rr[4], ar[4], br[4], kr[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const uint32_t off = (uint32_t)(tl * tstride + 16 * kt + 4 * g) * 2u;
+    rr[kt] = ld_off<uint2>(p.r + base, off);
+    ar[kt] = ld_off<uint2>(p.a + base, off);
+    br[kt] = ld_off<uint2>(p.b + base, off);
+    kr[kt] = ld_off<uint2>(p.k + base, off);
+  }
+  // ---- w in the key layout: lane = key column j, all 16 tokens (past the end: w = 1)
+  float wc[kC], rc[kC];
+#pragma unroll
+  for (int t = 0; t < kC; ++t) {
+    const int tt = min(t, nt - 1);
+    float x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
+    x = x < kWMin ? kWMin : x;  // clamp (a NaN passes through)
+    wc[t] = t < nt ? x : 1.f;
+    rc[t] = __builtin_amdgcn_rcpf(wc[t]);
+  }
+
+  // ---- decay factors (lane = j): running products, advanced together
+  {
+    const int j = lane;
+    float e = 1.f, sf = 1.f, gu = 1.f, gd = 1.f, fd = 1.f, fu = 1.f;
+    fac[kRowE * kFacRow + j] = 1.f;
+    fac[(kRowS + kC - 1) * kFacRow + j] = 1.f;
+    fac[(kRowG + 8) * kFacRow + j] = 1.f;  // Gq_7
+    fac[(kRowF + 7) * kFacRow + j] = 1.f;  // Fk_7
+#pragma unroll
+    for (int q = 0; q < kC; ++q) {
+      e *= wc[q];
+      fac[(kRowE + q + 1) * kFacRow + j] = e;  // E_q
+      if (q < kC - 1) {                        // Suf_s, s = 14 - q: times w_{s+1}
+        sf *= wc[kC - 1 - q];
+        fac[(kRowS + kC - 2 - q) * kFacRow + j] = sf;
+      }
+      if (q < 8) {  // Gq_t, t = 8 + q: times w_t
+        gu *= wc[8 + q];
+        fac[(kRowG + 9 + q) * kFacRow + j] = gu;
+        gd *= rc[7 - q];  // Gq_t, t = 6 - q: divided by w_{t+1}
+        fac[(kRowG + 7 - q) * kFacRow + j] = gd;
+        fu *= rc[8 + q];  // Fk_s, s = 8 + q: divided by w_s
+        fac[(kRowF + 8 + q) * kFacRow + j] = fu;
+      }
+      if (q < 7) {  // Fk_s, s = 6 - q: times w_{s+1}
+        fd *= wc[7 - q];
+        fac[(kRowF + 6 - q) * kFacRow + j] = fd;
+      }
+    }
+    st_off<float>(rec, (uint32_t)(kRecD + 4 * j), e);  // e^{gamma_15}
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS before other lanes read them
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- token layout: factors and operands. q = 4kt + e indexes key 16kt + 4g + e.
+  float ah[16], rh[16], bh[16], kh[16];  // Gram operands
+  half4 Ahat[4], Bbar[4], Kbar[4];
+  f32x4 Rhat[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int col = 16 * kt + 4 * g;
+    const float4 gqm1 = *reinterpret_cast<const float4*>(&fac[(kRowG + li) * kFacRow + col]);
+    const float4 gq = *reinterpret_cast<const float4*>(&fac[(kRowG + li + 1) * kFacRow + col]);
+    const float4 fk = *reinterpret_cast<const float4*>(&fac[(kRowF + li) * kFacRow + col]);
+    const float4 em1 = *reinterpret_cast<const float4*>(&fac[(kRowE + li) * kFacRow + col]);
+    const float4 e0 = *reinterpret_cast<const float4*>(&fac[(kRowE + li + 1) * kFacRow + col]);
+    const float4 sf = *reinterpret_cast<const float4*>(&fac[(kRowS + li) * kFacRow + col]);
+    const float fgqm1[4] = {gqm1.x, gqm1.y, gqm1.z, gqm1.w}, fgq[4] = {gq.x, gq.y, gq.z, gq.w};
+    const float ffk[4] = {fk.x, fk.y, fk.z, fk.w}, fem1[4] = {em1.x, em1.y, em1.z, em1.w};
+    const float fe0[4] = {e0.x, e0.y, e0.z, e0.w}, fsf[4] = {sf.x, sf.y, sf.z, sf.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float av = live ? bf4(ar[kt], e) : 0.f;
+      const float rv = live ? bf4(rr[kt], e) : 0.f;
+      const float bv = live ? bf4(br[kt], e) : 0.f;
+      const float kv = live ? bf4(kr[kt], e) : 0.f;
+      const int q = 4 * kt + e;
+      ah[q] = av * fgqm1[e];
+      rh[q] = rv * fgq[e];
+      bh[q] = bv * ffk[e];
+      kh[q] = kv * ffk[e];
+      Ahat[kt][e] = (_Float16)(av * fem1[e]);
+      Rhat[kt][e] = rv * fe0[e];
+      Bbar[kt][e] = (_Float16)(bv * fsf[e]);
+      Kbar[kt][e] = (_Float16)(kv * fsf[e]);
+    }
+  }
+
+  // ---- Grams on float32 MFMA: L[t][s] in D layout (lane (s = li, g) holds t = 4g + e);
+  // L_rk is formed transposed (operands swapped) because it is needed as a D-layout seed.
+  f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    Lab = mfma4(ah[q], bh[q], Lab);
+    Lak = mfma4(ah[q], kh[q], Lak);
+    Lrb = mfma4(rh[q], bh[q], Lrb);
+    LrkT = mfma4(kh[q], rh[q], LrkT);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = 4 * g + e;                 // row of Lab, Lak, Lrb; column li is s
+    Lab[e] = li < t ? Lab[e] : 0.f;          // strictly lower
+    Lak[e] = li < t ? Lak[e] : 0.f;
+    Lrb[e] = li <= t ? Lrb[e] : 0.f;         // lower with the diagonal
+    LrkT[e] = t <= li ? LrkT[e] : 0.f;       // element (s = 4g+e, t = li) of L_rk^T
+  }
+
+  // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
+  // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
+  // every x[s], s < s2. The factor rows are no longer read, so their area is reused.
+  float* lab = fac + kLabOff;
+  float* lrb = fac + kLrbOff;
+  // every factor read of this wave has completed before the area is overwritten
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lab[(4 * g + e) * 16 + li] = Lab[e];
+    lrb[(4 * g + e) * 16 + li] = Lrb[e];
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const int row = li;
+  float x[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(&lrb[row * 16 + 4 * q]);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * q + e] = g == 0 ? (4 * q + e == row ? 1.f : 0.f) : vv[e];
+  }
+#pragma unroll
+  for (int s2 = kC - 1; s2 >= 1; --s2) {
+    float lrow[16];
+#pragma unroll
+    for (int q = 0; q < (s2 + 3) / 4; ++q)
+      *reinterpret_cast<float4*>(&lrow[4 * q]) = *reinterpret_cast<const float4*>(&lab[s2 * 16 + 4 * q]);
+#pragma unroll
+    for (int s = 0; s < s2; ++s) x[s] = fmaf(x[s2], lrow[s], x[s]);
+  }
+  _Float16* tm = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(fac) + kTmOffBytes);
+  if (g < 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<half4*>(&tm[(g * 16 + row) * 16 + 4 * q]) =
+          half4{(_Float16)x[4 * q], (_Float16)x[4 * q + 1], (_Float16)x[4 * q + 2], (_Float16)x[4 * q + 3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const half4 tB = *reinterpret_cast<const half4*>(&tm[li * 16 + 4 * g]);         // T[t = li][4g..]: T^T as B
+  const half4 mB = *reinterpret_cast<const half4*>(&tm[(16 + li) * 16 + 4 * g]);  // M_r^T as B
+
+  // ---- products. Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
+  half4 eye;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
+  half4 ApT[4], RpT[4], BT[4], KT[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const half4 AT = to_h4(mfma16(Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
+    ApT[kt] = to_h4(mfma16(AT, tB, zero4()));                // lane (t = li, g): A'[t][16kt + 4g + e]
+    RpT[kt] = to_h4(mfma16(AT, mB, Rhat[kt]));               // R'[t][16kt + 4g + e]
+    BT[kt] = to_h4(mfma16(Bbar[kt], eye, zero4()));          // lane (j = li, g): B-[4g+e][16kt + li]
+    KT[kt] = to_h4(mfma16(Kbar[kt], eye, zero4()));
+  }
+  const half4 LakH = to_h4(Lak);  // as an A operand: L_ak^T (M = s', K = s)
+  const half4 GuT = to_h4(mfma16(LakH, tB, zero4()));  // lane (t = li, g): G_u[t][4g + e]
+  const half4 GyT = to_h4(mfma16(LakH, mB, LrkT));     // G_y[t][4g + e]
+
+  // ---- record: 16 bytes per lane per block
+  const uint32_t lo = (uint32_t)lane * 16u;
+  st_off<half8>(rec, kRecA0 * 1024 + lo, cat8(ApT[0], ApT[1]));
+  st_off<half8>(rec, kRecA1 * 1024 + lo, cat8(ApT[2], ApT[3]));
+  st_off<half8>(rec, kRecR0 * 1024 + lo, cat8(RpT[0], RpT[1]));
+  st_off<half8>(rec, kRecR1 * 1024 + lo, cat8(RpT[2], RpT[3]));
+  st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT[kt], KT[kt]));
+}
+
+// ============================================================================ kernel 2: scan
+
+struct ScanParams {
+  const unsigned char* rec;  // records of the slab [unit][chunk of slab][kRecBytes]
+  const uint16_t* v;
+  float* y;
+  const float* s_src;  // state at the slab start, or null for zeros
+  float* s_dst;        // state at the slab end, or null
+  int32_t T, H;
+  int32_t c0, nc;
+};
+
+// A head's 64 value rows are independent; they are split over kWgPerHead
+// workgroups of kCompute compute waves (16 rows each) and kLoaders loader waves.
+// One workgroup per CU leaves every compute wave a SIMD of its own.
+constexpr int kCompute = 2;
+constexpr int kWgPerHead = 4 / kCompute;
+constexpr int kLoaders = 4;
+constexpr int kAhead = 4;                          // chunks committed ahead of the compute waves
+constexpr int kRing = kAhead + 1;                  // LDS slots
+constexpr int kVCols = 16 * kCompute;              // value columns of v this workgroup needs
+constexpr int kVBytes = kC * kVCols * 2;           // bfloat16, [token][kVCols]
+constexpr int kSlotBytes = kRecBytes + kVBytes;    // 10,496
+constexpr int kRecPieces = kRecBytes / 16;         // 592
+constexpr int kVSegs = kVCols * 2 / 16;            // 16-byte pieces per token row of v
+constexpr int kPieces = kSlotBytes / 16;           // 656
+constexpr int kLoadsPerLane = (kPieces + 63) / 64;  // 11
+constexpr int kScanThreads = 64 * (kCompute + kLoaders);
+
+__device__ __forceinline__ f32x4 mfma32(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
+  extern __shared__ __align__(16) unsigned char ring[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  // consecutive logical ids (the workgroups of one head) run on one XCD and share its L2
+  const int lid = (int)xcd_swizzle(blockIdx.x, gridDim.x);
+  const int unit = lid / kWgPerHead, part = lid % kWgPerHead;
+  const int bb = unit / p.H, hh = unit % p.H;
+  const int nc = p.nc;
+  const uint32_t tstride = (uint32_t)p.H * kN;
+  const unsigned char* recs = p.rec + (int64_t)unit * nc * kRecBytes;
+  const int64_t seq_base =
+      ((int64_t)bb * p.T + (int64_t)p.c0 * kC) * p.H * kN + (int64_t)hh * kN + kVCols * part;
+  const uint16_t* vbase = p.v + seq_base;  // this workgroup's value columns
+  float* ybase = p.y + seq_base;
+
+  // The two roles run separate loops with the same number of barriers. One shared
+  // loop would let the compiler give the loaders' in-flight load registers and the
+  // compute waves' temporaries the same physical registers, and its wait-count
+  // insertion would then make the compute waves wait for their own y stores.
+  if (wave >= kCompute) {
+    // ---- loader m serves chunks x = m (mod 4) with two register buffers (buffer
+    // (x / 4) % 2): it issues chunk x's loads at iteration x - 12 and commits them
+    // to the ring at iteration x - 4, so each load has eight chunk periods to arrive.
+    const int m = wave - kCompute;
+    uint4 buf[2][kLoadsPerLane];
+    auto issue = [&](int x, uint4* bf) {
+      const int nt = min(kC, p.T - (p.c0 + x) * kC);
+#pragma unroll
+      for (int q = 0; q < kLoadsPerLane; ++q) {
+        const int piece = lane + 64 * q;
+        if (piece < kRecPieces) {
+          bf[q] = ld_off<uint4>(recs, (uint32_t)(x * kRecBytes + piece * 16));
+        } else if (piece < kPieces) {
+          const int vi = piece - kRecPieces;  // token vi / kVSegs, 16-byte piece vi % kVSegs of its row
+          const int tok = min(vi / kVSegs, nt - 1);
+          bf[q] = ld_off<uint4>(vbase, (uint32_t)(((x * kC + tok) * tstride + (vi % kVSegs) * 8) * 2u));
+        }
+      }
+    };
+    auto commit = [&](int x, const uint4* bf) {
+      const int nt = min(kC, p.T - (p.c0 + x) * kC);
+      unsigned char* slot = ring + (x % kRing) * kSlotBytes;
+#pragma unroll
+      for (int q = 0; q < kLoadsPerLane; ++q) {
+        const int piece = lane + 64 * q;
+        if (piece < kPieces) {
+          uint4 val = bf[q];
+          if (piece >= kRecPieces && (piece - kRecPieces) / kVSegs >= nt) val = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(slot + piece * 16) = val;
+        }
+      }
+    };
+    if (m < nc) {
+      issue(m, buf[0]);
+      commit(m, buf[0]);
+    }
+    if (m + 4 < nc) issue(m + 4, buf[1]);
+    if (m + 8 < nc) issue(m + 8, buf[0]);
+    lds_sync();
+    // unrolled by eight iterations so that the buffer of every commit is static
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = c0 + j;
+        if (c < nc) {
+          if (((j + kAhead) & 3) == m) {  // chunk x = c + 4 is this loader's, buffer ((j + 4) / 4) % 2
+            const int x = c + kAhead;
+            uint4* bf = buf[((j + kAhead) >> 2) & 1];
+            if (x < nc) commit(x, bf);
+            if (x + 8 < nc) issue(x + 8, bf);
+          }
+          lds_sync();
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- compute wave: value rows 16 rb .. 16 rb + 15 of the head,
+  // element e of St[kt] = S[i = 16 rb + li][j = 16kt + 4g + e]
+  const int rb = kCompute * part + wave;
+  f32x4 St[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) St[kt] = zero4();
+  if (p.s_src) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const float4 s = *reinterpret_cast<const float4*>(p.s_src + ((int64_t)unit * kN + 16 * rb + li) * kN +
+                                                        16 * kt + 4 * g);
+      St[kt] = f32x4{s.x, s.y, s.z, s.w};
+    }
+  }
+  lds_sync();
+
+  // fragments of one chunk, read from its ring slot one iteration ahead
+  struct Frag {
+    half8 a0, a1, r0, r1, gl, bk[4];
+    float4 dv[4];
+    uint32_t v[4];  // V[t = 4g + e][i = 16 rb + li], raw bfloat16 bits (widened when used)
+  };
+  const uint32_t lo = (uint32_t)lane * 16u;
+  auto read = [&](int c, Frag& f) {
+    const unsigned char* slot = ring + (c % kRing) * kSlotBytes;
+    f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
+    f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
+    f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
+    f.r1 = *reinterpret_cast<const half8*>(slot + kRecR1 * 1024 + lo);
+    f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
+      f.dv[kt] = *reinterpret_cast<const float4*>(slot + kRecD + (16 * kt + 4 * g) * 4);
+    }
+    const uint16_t* vr = reinterpret_cast<const uint16_t*>(slot + kRecBytes);  // [token][kVCols]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.v[e] = vr[(4 * g + e) * kVCols + 16 * wave + li];
+  };
+  const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+  auto step = [&](int c, const Frag& f) {
+    half4 vB;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
+    // K = 32 products (16x16x32 only: every dependent chain keeps one MFMA shape).
+    //   U = A' S0^T + G_u V and Y = R' S0^T + G_y V: two key halves, then the
+    //   G V term (the record's G block holds G_u | G_y, so a B operand of V | 0
+    //   or 0 | V selects one of them);
+    //   S^T <- diag(e^{gamma_15}) S^T + [B- | K-] [U ; V] per key tile.
+    const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
+    const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
+    f32x4 u = mfma32(f.a0, sB0, zero4());
+    f32x4 yv = mfma32(f.r0, sB0, zero4());
+    u = mfma32(f.a1, sB1, u);
+    yv = mfma32(f.r1, sB1, yv);
+    u = mfma32(f.gl, cat8(vB, hz), u);
+    yv = mfma32(f.gl, cat8(hz, vB), yv);
+    const half8 uv = cat8(to_h4(u), vB);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      St[kt][0] *= f.dv[kt].x;
+      St[kt][1] *= f.dv[kt].y;
+      St[kt][2] *= f.dv[kt].z;
+      St[kt][3] *= f.dv[kt].w;
+      St[kt] = mfma32(f.bk[kt], uv, St[kt]);
+    }
+    // y[t = 4g + e][i = 16 rb + li]
+    const int nt = min(kC, p.T - (p.c0 + c) * kC);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g + e;
+      if (t < nt) st_off<float>(ybase, (uint32_t)(((c * kC + t) * tstride + 16 * wave + li) * 4u), yv[e]);
+    }
+  };
+
+  // Two register sets alternate (the loop is unrolled by two), so the next
+  // chunk's LDS reads are in flight while this chunk's MFMAs run.
+  Frag fa, fb;
+  if (nc > 0) read(0, fa);
+  // nothing is in flight from LDS when the loop starts: the wait-count pass then
+  // never holds this chunk's operands back behind the next chunk's reads
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  for (int c = 0; c < nc; c += 2) {
+    if (c + 1 < nc) read(c + 1, fb);
+    step(c, fa);
+    lds_sync();
+    if (c + 1 < nc) {
+      if (c + 2 < nc) read(c + 2, fa);
+      step(c + 1, fb);
+      lds_sync();
+    }
+  }
+
+  if (p.s_dst) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      *reinterpret_cast<float4*>(p.s_dst + ((int64_t)unit * kN + 16 * rb + li) * kN + 16 * kt + 4 * g) =
+          make_float4(St[kt][0], St[kt][1], St[kt][2], St[kt][3]);
+  }
+}
+
+// ============================================================================ host side
+
+// Record buffer (and, if needed, a carried-state buffer) cached per (device, stream):
+// calls on one stream run in order, so they can share it; calls on different
+// streams get different buffers. Grown on demand, never shrunk.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
+  if (ws.bytes < bytes) {
+    if (ws.ptr) {
+      // work already queued on this stream may still use the old buffer
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return e;
+      e = hipFree(ws.ptr);
+      if (e != hipSuccess) return e;
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    e = hipMalloc(&ws.ptr, bytes);
+    if (e != hipSuccess) {
+      ws.ptr = nullptr;
+      return e;
+    }
+    ws.bytes = bytes;
+  }
+  *out = ws.ptr;
+  return hipSuccess;
+}
+
+// Record-buffer budget per slab: the scan of a slab reads what its prep wrote
+// just before, so a slab that fits the 256 MB last-level (MALL) cache with room
+// to spare is read back without a second HBM round trip.
+size_t slab_budget_bytes() {
+  static const size_t mb = [] {
+    const char* s = std::getenv("RWKV7_SPLIT_SLAB_MB");
+    const long v = s ? std::atol(s) : 0;
+    return v > 0 ? (size_t)v : (size_t)96;
+  }();
+  return mb << 20;
+}
+
+}  // namespace
+
+hipError_t launch_chunked_split(const WkvCall& c) {
+  if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
+  const int64_t units = c.B * c.H;
+  const int64_t nch = (c.T + kC - 1) / kC;
+  // In-sequence offsets are 32-bit: T * H * 64 elements must stay below 2^31.
+  if (c.T * c.H * kN >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  const int64_t per_chunk = units * kRecBytes;
+  int64_t slab = (int64_t)(slab_budget_bytes() / (size_t)per_chunk);
+  slab = slab < 1 ? 1 : (slab > nch ? nch : slab);
+  const int64_t nslab = (nch + slab - 1) / slab;
+  slab = (nch + nslab - 1) / nslab;  // balance the slabs
+  if (units * slab > (int64_t(1) << 30)) return hipErrorNotSupported;
+  const bool tmp_state = nslab > 1 && c.s_out == nullptr;
+  const size_t rec_bytes = (size_t)(units * slab * kRecBytes);
+  const size_t bytes = rec_bytes + (tmp_state ? (size_t)units * kN * kN * 4 : 0);
+  void* ws = nullptr;
+  hipError_t e = workspace(c.stream, bytes, &ws);
+  if (e != hipSuccess) return e;
+  unsigned char* rec = static_cast<unsigned char*>(ws);
+  float* carry = tmp_state ? reinterpret_cast<float*>(rec + rec_bytes) : static_cast<float*>(c.s_out);
+
+  const void* prep_fn = reinterpret_cast<const void*>(&wkv7_prep_kernel);
+  const void* scan_fn = reinterpret_cast<const void*>(&wkv7_scan_kernel);
+  const int prep_lds = kPrepWaves * kPrepLdsPerWave;
+  const int scan_lds = kRing * kSlotBytes;
+  static const hipError_t a1 = hipFuncSetAttribute(prep_fn, hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
+  static const hipError_t a2 = hipFuncSetAttribute(scan_fn, hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
+
+  for (int64_t s = 0; s < nslab; ++s) {
+    const int64_t c0 = s * slab;
+    const int64_t ncs = (nch - c0 < slab) ? nch - c0 : slab;
+    PrepParams pp{static_cast<const uint16_t*>(c.in[0]), static_cast<const uint16_t*>(c.in[1]),
+                  static_cast<const uint16_t*>(c.in[2]), static_cast<const uint16_t*>(c.in[4]),
+                  static_cast<const uint16_t*>(c.in[5]), rec, (int32_t)c.T, (int32_t)c.H, (int32_t)c0,
+                  (int32_t)ncs, (int32_t)(units * ncs)};
+    void* pargs[] = {&pp};
+    const uint32_t pblocks = (uint32_t)((units * ncs + kPrepWaves - 1) / kPrepWaves);
+    e = hipLaunchKernel(prep_fn, dim3(pblocks), dim3(64 * kPrepWaves), pargs, prep_lds, c.stream);
+    if (e != hipSuccess) return e;
+    ScanParams sp{rec, static_cast<const uint16_t*>(c.in[3]), c.y,
+                  s == 0 ? static_cast<const float*>(c.s_in) : carry,
+                  s == nslab - 1 ? static_cast<float*>(c.s_out) : carry, (int32_t)c.T, (int32_t)c.H,
+                  (int32_t)c0, (int32_t)ncs};
+    void* sargs[] = {&sp};
+    e = hipLaunchKernel(scan_fn, dim3((uint32_t)(units * kWgPerHead)), dim3(kScanThreads), sargs, scan_lds,
+                        c.stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rwkv7

@@ -25,6 +25,7 @@ RWKV7_STATE_F16 = 2
 RWKV7_ALGO_AUTO = 0
 RWKV7_ALGO_SEQUENTIAL = 1
 RWKV7_ALGO_CHUNKED = 2
+RWKV7_ALGO_CHUNKED_SPLIT = 3
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
             "rwkv7_wkv_strerror")

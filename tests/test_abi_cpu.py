@@ -123,7 +123,7 @@ def test_step_requires_one_token(L):
     assert call(L, fn="rwkv7_wkv_step", T=0) == E_SHAPE
 
 
-@pytest.mark.parametrize("algo", [-1, 3, 99])
+@pytest.mark.parametrize("algo", [-1, 4, 99])
 def test_unknown_algo(L, algo):
     assert call(L, fn="rwkv7_wkv_prefill_ex", algo=algo) == E_ALGO
 
@@ -176,3 +176,4 @@ def test_step_q_alias_uses_16_bit_state_size(L):
 
 def test_chunked_refuses_f32_inputs_before_any_launch(L):
     assert call(L, fn="rwkv7_wkv_prefill_ex", dtype=F32, algo=wkv.RWKV7_ALGO_CHUNKED) == E_ALGO
+    assert call(L, fn="rwkv7_wkv_prefill_ex", dtype=F32, algo=wkv.RWKV7_ALGO_CHUNKED_SPLIT) == E_ALGO

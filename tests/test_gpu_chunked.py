@@ -1,4 +1,7 @@
-"""GPU parity of the chunked (MFMA) prefill against the float64 oracle and the sequential kernel."""
+"""GPU parity of the chunked (MFMA) prefill against the float64 oracle and the sequential kernel.
+
+Every test runs both chunked variants: the fused one (one workgroup per head) and the split
+one (chunk-parallel prep kernel, per-head scan kernel)."""
 import numpy as np
 import pytest
 
@@ -8,8 +11,13 @@ from linear_rnn_amd.inputs import CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, m
 from tests.gpu_util import TOL_BF16, oracle_units, rel, sample_units, say, to_dev
 
 pytestmark = pytest.mark.gpu
-CH = wkv.RWKV7_ALGO_CHUNKED
 SEQ = wkv.RWKV7_ALGO_SEQUENTIAL
+VARIANTS = {"fused": wkv.RWKV7_ALGO_CHUNKED, "split": wkv.RWKV7_ALGO_CHUNKED_SPLIT}
+
+
+@pytest.fixture(params=sorted(VARIANTS), scope="module")
+def CH(request):
+    return VARIANTS[request.param]
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +28,7 @@ def torch():
     return t
 
 
-def run(torch, d, algo=CH, state=True):
+def run(torch, d, algo, state=True):
     y, s = wkv.wkv7(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state_in"] if state else None, algo=algo)
     torch.cuda.synchronize()
     return y.cpu().numpy(), s.cpu().numpy()
@@ -28,49 +36,49 @@ def run(torch, d, algo=CH, state=True):
 
 @pytest.mark.parametrize("B,T,H", [(1, 1, 1), (1, 15, 2), (2, 16, 3), (1, 17, 2), (2, 33, 3), (3, 100, 5),
                                    (2, 1000, 12)])
-def test_ragged_vs_oracle(torch, B, T, H):
-    say("chunked ragged", B, T, H)
+def test_ragged_vs_oracle(torch, CH, B, T, H):
+    say("algo", CH, "chunked ragged", B, T, H)
     x = make_inputs(CONFIGS[1], B=B, T=T, H=H, seed=200 + T)
-    y, s = run(torch, to_dev(x))
+    y, s = run(torch, to_dev(x), CH)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
 
 
-def test_zero_initial_state(torch):
-    say("chunked, state_in NULL")
+def test_zero_initial_state(torch, CH):
+    say("algo", CH, "chunked, state_in NULL")
     x = make_inputs(CONFIGS[1], B=2, T=77, H=4, seed=3)
-    y, s = run(torch, to_dev(x), state=False)
+    y, s = run(torch, to_dev(x), CH, state=False)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=None)
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16
 
 
-def test_f32_inputs_are_refused(torch):
+def test_f32_inputs_are_refused(torch, CH):
     """The chunked algorithm takes bfloat16 inputs only; float32 inputs stay on the sequential kernel."""
-    say("chunked, f32 inputs refused")
+    say("algo", CH, "chunked, f32 inputs refused")
     x = make_inputs(CONFIGS[0])
     with pytest.raises(wkv.Rwkv7Error) as ei:
-        run(torch, to_dev(x))
+        run(torch, to_dev(x), CH)
     assert ei.value.status == -7
 
 
-def test_config1_full(torch):
+def test_config1_full(torch, CH):
     cfg = CONFIGS[1]
-    say("chunked config 1 full", cfg)
+    say("algo", CH, "chunked config 1 full", cfg)
     x = make_inputs(cfg)
-    y, s = run(torch, to_dev(x))
+    y, s = run(torch, to_dev(x), CH)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     e = (rel(y, yr), rel(s, sr))
     say("config 1 chunked errors", e)
     assert e[0] <= TOL_BF16 and e[1] <= TOL_BF16, e
 
 
-def test_config2_full_and_resume(torch):
+def test_config2_full_and_resume(torch, CH):
     """One pass and 4 x 1024-token segments with the state carried, each against the oracle."""
     cfg = CONFIGS[2]
-    say("chunked config 2 full + resume", cfg)
+    say("algo", CH, "chunked config 2 full + resume", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
-    y1, s1 = run(torch, d)
+    y1, s1 = run(torch, d, CH)
     st = d["state_in"].clone()
     ys = []
     for i in range(4):
@@ -89,8 +97,8 @@ def test_config2_full_and_resume(torch):
     assert np.array_equal(y4, y1) and np.array_equal(s4, s1)
 
 
-def test_unaligned_resume(torch):
-    say("chunked unaligned resume")
+def test_unaligned_resume(torch, CH):
+    say("algo", CH, "chunked unaligned resume")
     x = make_inputs(CONFIGS[1], B=2, T=300, H=3, seed=11)
     d = to_dev(x)
     st = d["state_in"].clone()
@@ -106,9 +114,9 @@ def test_unaligned_resume(torch):
     assert max(e) <= TOL_BF16, e
 
 
-def test_config4_sampled_heads_and_vs_sequential(torch):
+def test_config4_sampled_heads_and_vs_sequential(torch, CH):
     cfg = CONFIGS[4]
-    say("chunked config 4 full, 16 sampled heads + sequential comparison", cfg)
+    say("algo", CH, "chunked config 4 full, 16 sampled heads + sequential comparison", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
     y, s = wkv.wkv7(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state_in"], algo=CH)
@@ -130,22 +138,22 @@ def test_config4_sampled_heads_and_vs_sequential(torch):
     assert max(e) <= TOL_BF16, e
 
 
-def test_extreme_decays(torch):
+def test_extreme_decays(torch, CH):
     """w in {0, 1e-6, 1e-2, 0.5, 1}: below 2^-15 the chunked form clamps, which moves a decayed
     term by at most 2^-15 of its size."""
-    say("chunked extreme decays")
+    say("algo", CH, "chunked extreme decays")
     x = make_inputs(CONFIGS[1], B=2, T=90, H=3, seed=17)
     rng = np.random.default_rng(17)
     choices = np.array([0.0, 1e-6, 1e-2, 0.5, 1.0], dtype=np.float32)
     x["w"] = f32_to_bf16_bits(choices[rng.integers(0, 5, size=x["w"].shape)])
-    y, s = run(torch, to_dev(x))
+    y, s = run(torch, to_dev(x), CH)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
 
 
-def test_delta_rule_retrieval(torch):
+def test_delta_rule_retrieval(torch, CH):
     """w = 1, a = -kk, b = kk, k = r = kk (unit): y_t = v_t."""
-    say("chunked delta rule")
+    say("algo", CH, "chunked delta rule")
     rng = np.random.default_rng(23)
     B, T, H = 1, 64, 2
     kk = rng.standard_normal((B, T, H, 64))
@@ -154,19 +162,19 @@ def test_delta_rule_retrieval(torch):
     x = {n: f32_to_bf16_bits(a.astype(np.float32)) for n, a in
          dict(r=kk, k=kk, a=-kk, b=kk, w=np.ones_like(kk), v=v).items()}
     x["state_in"] = (rng.standard_normal((B, H, 64, 64)) * 0.3).astype(np.float32)
-    y, _ = run(torch, to_dev(x))
+    y, _ = run(torch, to_dev(x), CH)
     yr, _ = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= TOL_BF16
     # against v itself, up to the bfloat16 rounding of the keys (|kk|^2 != 1 exactly)
     assert rel(y, bf16_bits_to_f32(x["v"])) <= 2e-2
 
 
-def test_deterministic(torch):
-    say("chunked determinism")
+def test_deterministic(torch, CH):
+    say("algo", CH, "chunked determinism")
     x = make_inputs(CONFIGS[1], B=2, T=300, H=6, seed=8)
     d = to_dev(x)
-    y1, s1 = run(torch, d)
-    y2, s2 = run(torch, d)
+    y1, s1 = run(torch, d, CH)
+    y2, s2 = run(torch, d, CH)
     assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
 
 
@@ -176,6 +184,6 @@ def test_auto_uses_chunked_for_bf16(torch):
     d = to_dev(x)
     y_auto = torch.empty((1, 40, 2, 64), dtype=torch.float32, device="cuda")
     wkv.rwkv7_wkv_prefill(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state_in"], y_auto, None)
-    y_ch, _ = run(torch, d)
+    y_ch, _ = run(torch, d, wkv.RWKV7_ALGO_CHUNKED_SPLIT)
     torch.cuda.synchronize()
     assert np.array_equal(y_auto.cpu().numpy(), y_ch)
