@@ -203,3 +203,44 @@ def widen(x: np.ndarray) -> np.ndarray:
     if x.dtype == np.uint16:
         return bf16_bits_to_f32(x).astype(np.float64)
     return x.astype(np.float64)
+
+
+def make_tmix_inputs(cfg: WkvConfig, step: int | None = None, B: int | None = None, T: int | None = None,
+                     H: int | None = None, seed: int | None = None, with_state: bool | None = None) -> dict:
+    """Raw inputs of the time-mix operator with its prologue and epilogue, [B, T, H, N] each.
+
+    r, v ~ N(0, 1) and k ~ N(0, 1) / 8 in the config's dtype; w_raw = u ~ U(u_lo, u_hi) in float32
+    (the decay is exp(-exp(w_raw))); kk ~ N(0, 1)^64, not normalised, in the config's dtype; a_lr as
+    for make_inputs; ln_w ~ U(0.2, 1) and ln_b ~ N(0, 0.05^2) per channel ([H * N] float32);
+    state_in ~ N(0, 0.1^2) float32 or None. Seeded from SeedSequence([seed, 1]) (per step:
+    [seed, 1, step]), a stream of its own.
+    """
+    B = cfg.B if B is None else B
+    T = cfg.T if T is None else T
+    H = cfg.H if H is None else H
+    N = cfg.N
+    seed = cfg.seed if seed is None else seed
+    with_state = cfg.state_in if with_state is None else with_state
+    root = np.random.SeedSequence([seed, 1] if step is None else [seed, 1, step])
+    kids = root.spawn(10)
+    shape = (B, T, H, N)
+    gen = [np.random.Generator(np.random.PCG64(k)) for k in kids]
+    out = {
+        "r": _cast(gen[0].standard_normal(shape), cfg.dtype),
+        "k": _cast(gen[1].standard_normal(shape) / 8.0, cfg.dtype),
+        "v": _cast(gen[2].standard_normal(shape), cfg.dtype),
+        "w_raw": f64_to_f32(gen[3].uniform(cfg.u_lo, cfg.u_hi, size=shape)),
+        "kk": _cast(gen[4].standard_normal(shape), cfg.dtype),
+    }
+    if cfg.a_uniform:
+        x = gen[5].uniform(0.0, 1.0, size=shape)
+        pick = gen[6].uniform(0.0, 1.0, size=shape)
+        x[pick < 0.01] = 0.0
+        x[(pick >= 0.01) & (pick < 0.02)] = 1.0
+    else:
+        x = 1.0 / (1.0 + np.exp(-gen[5].standard_normal(shape)))
+    out["a_lr"] = _cast(x, cfg.dtype)
+    out["ln_w"] = f64_to_f32(gen[7].uniform(0.2, 1.0, size=H * N))
+    out["ln_b"] = f64_to_f32(gen[8].standard_normal(H * N) * 0.05)
+    out["state_in"] = (gen[9].standard_normal((B, H, N, N)) * 0.1).astype(np.float32) if with_state else None
+    return out

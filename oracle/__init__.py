@@ -18,6 +18,11 @@ decayed by w, plus state*a*b, plus v k^T, then read out with r) and section
 Pins (tests/test_oracle_pins.py, all CPU): brute-force matrix products on tiny
 T, the closed forms for a = 0 and for w = 1 with a = 0, an exact rational run,
 delta-rule retrieval, the memoryless case, linearity and row equivariance.
+
+``tmix`` adds the operator's prologue (decay exp(-exp(w_raw)), normalised removal
+key, kernel slots) and epilogue (ln_x GroupNorm) around the recurrence, in numpy
+float64; tests/test_oracle_tmix.py pins those pieces to closed forms and to
+torch's normalize and group_norm.
 """
 from __future__ import annotations
 
@@ -159,3 +164,66 @@ def step_q(r, w, k, v, a, b, state_bits, fmt: str, nthreads: int | None = None):
     Returns (y float64, new state bits uint16)."""
     y, s = wkv7(r, w, k, v, a, b, state_in=state_bits, nthreads=nthreads, state_format=fmt)
     return y, round16(s, fmt)
+
+
+# ---------------------------------------------------------------------------------------------
+# The time-mix operator with its prologue and epilogue (RWKV-7 G0 7.2B notes, lshu.cn/news/198401,
+# section 7.1, "x070 architecture, the two core operators"): the decay enters as w = exp(-exp(w_raw));
+# the removal key kk is L2-normalised per head (F.normalize); the kernel slots are a = -kk and
+# b = kk * a_lr (a_lr the in-context learning rate); the recurrence output goes through ln_x, a
+# GroupNorm with one group per head and eps = 64e-5.
+
+GROUP_NORM_EPS = 64e-5
+NORMALIZE_EPS = 1e-12  # F.normalize divides by max(|x|_2, eps)
+
+
+def _widen_any(x) -> np.ndarray:
+    """Exact float64 value of float32, float64 or raw bfloat16 (uint16) inputs."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if x.dtype in (np.float32, np.float64):
+        return x.astype(np.float64)
+    raise TypeError("inputs must be float32, float64 or uint16 (bfloat16 bits), got %s" % x.dtype)
+
+
+def tmix_prologue(w_raw, kk, a_lr):
+    """Float64 decay and kernel slots from the raw inputs (arrays [..., N]).
+
+    w = exp(-exp(w_raw)); kk_hat = kk / max(|kk|_2, 1e-12) over the last (head) axis;
+    a = -kk_hat; b = kk_hat * a_lr. Returns (w, a, b).
+    """
+    u = _widen_any(w_raw)
+    w = np.exp(-np.exp(u))
+    kk64 = _widen_any(kk)
+    nrm = np.sqrt(np.sum(kk64 * kk64, axis=-1, keepdims=True))
+    kk_hat = kk64 / np.maximum(nrm, NORMALIZE_EPS)
+    return w, -kk_hat, kk_hat * _widen_any(a_lr)
+
+
+def group_norm(y, ln_w=None, ln_b=None, eps: float = GROUP_NORM_EPS):
+    """ln_x on y [B, T, H, N]: per (b, t, h), subtract the mean over N, divide by the square root of
+    the (population) variance plus eps, then scale by ln_w and shift by ln_b (per channel, [H*N];
+    None means 1 and 0)."""
+    y = np.asarray(y, dtype=np.float64)
+    H, N = y.shape[-2:]
+    mu = np.mean(y, axis=-1, keepdims=True)
+    d = y - mu
+    var = np.mean(d * d, axis=-1, keepdims=True)
+    out = d / np.sqrt(var + eps)
+    if ln_w is not None:
+        out = out * _widen_any(ln_w).reshape(H, N)
+    if ln_b is not None:
+        out = out + _widen_any(ln_b).reshape(H, N)
+    return out
+
+
+def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, nthreads: int | None = None):
+    """The fused operator in float64: prologue, recurrence, ln_x.
+
+    r, k, v, kk, a_lr: [B, T, H, N] float32 or bfloat16 bits; w_raw: [B, T, H, N] float32;
+    ln_w, ln_b: [H * N] float32 or None. Returns (out [B,T,H,N] float64, state_out float64).
+    """
+    w, a, b = tmix_prologue(w_raw, kk, a_lr)
+    y, s = wkv7(_widen_any(r), w, _widen_any(k), _widen_any(v), a, b, state_in=state_in, nthreads=nthreads)
+    return group_norm(y, ln_w, ln_b), s
