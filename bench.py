@@ -108,6 +108,7 @@ def main(argv=None):
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-16bit", action="store_true", help="skip the bf16 / f16 stored-state decode legs")
+    ap.add_argument("--no-decode-fused", action="store_true", help="skip the fused time-mix decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked (fused), 3 chunked (split)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -190,6 +191,9 @@ def main(argv=None):
             for fmt in ("bf16", "f16"):
                 out["decode_state_" + fmt] = bench_decode(torch, wkv, make_inputs, CONFIGS[3], args, fmt)
 
+    if not args.no_decode and not args.no_decode_fused:
+        out["decode_fused"] = bench_decode_fused(torch, wkv, CONFIGS[3], args)
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         bcopy = torch.empty_like(a)
@@ -243,6 +247,54 @@ def bench_decode(torch, wkv, make_inputs, cfg, args, fmt="f32"):
                      "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": measured_traffic(key, src),
                      "kernel": "%s (%s state)" % (kern, fmt), "algorithmic_bytes": nbytes},
+    }
+
+
+def bench_decode_fused(torch, wkv, cfg, args, distinct=32):
+    """Consecutive in-place steps of the fused time-mix operator (prologue, recurrence, ln_x) at the
+    decode shape. `distinct` seeded input sets are resident and cycled over the steps."""
+    import numpy as np
+    from linear_rnn_amd.inputs import make_tmix_inputs
+    B, H, S = cfg.B, cfg.H, args.decode_steps
+    names = ("r", "w_raw", "k", "v", "kk", "a_lr")
+    sets = []
+    for s in range(min(distinct, S)):
+        x = make_tmix_inputs(cfg, step=s, with_state=(s == 0))
+        if s == 0:
+            state = torch.from_numpy(x["state_in"]).cuda()
+            ln_w = torch.from_numpy(x["ln_w"]).cuda()
+            ln_b = torch.from_numpy(x["ln_b"]).cuda()
+        d = {}
+        for n in names:
+            a = x[n]
+            d[n] = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16 \
+                else torch.from_numpy(a).cuda()
+        sets.append(d)
+    o = torch.empty((B, 1, H, N), dtype=torch.float32, device="cuda")
+
+    def run_all():
+        for i in range(S):
+            d = sets[i % len(sets)]
+            wkv.rwkv7_tmix_step(*(d[n] for n in names), ln_w, ln_b, state, o, state)
+
+    run_all()
+    torch.cuda.synchronize()
+    per_step = [time_region(torch, run_all, 1) / S for _ in range(args.decode_reps)]
+    ms = float(sorted(per_step)[len(per_step) // 2])
+    # per (b, h): state in and out (fp32), five bf16 inputs and fp32 w_raw, fp32 output; ln_w / ln_b once
+    nbytes = B * H * (2 * N * N * 4 + N * (5 * 2 + 4) + N * 4) + 2 * H * N * 4
+    src = ["linear_rnn_amd/csrc/wkv7_tmix.hip", "linear_rnn_amd/csrc/wkv7_device.hpp"]
+    return {
+        "value": B * H / (ms * 1e-3), "unit": UNIT, "ms_per_step": ms, "steps_per_rep": S,
+        "reps": args.decode_reps, "ms_per_step_all_reps": per_step,
+        "config": {"workload": "%s: B=%d H=%d N=%d, %d consecutive in-place fused steps (decay, normalised "
+                               "removal key, slots, recurrence, ln_x), bf16 inputs, fp32 w_raw and state"
+                               % (cfg.name, B, H, N, S), "B": B, "H": H, "N": N, "state": "f32",
+                   "distinct_input_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("wkv7_tmix_kernel:" + cfg.name, src),
+                     "kernel": "wkv7_tmix_kernel (TB=1)", "algorithmic_bytes": nbytes},
     }
 
 

@@ -179,6 +179,53 @@ int rwkv7_wkv_prefill_ex(const void *r, const void *w, const void *k, const void
                          const void *b, const float *state_in, float *y, float *state_out, int64_t B,
                          int64_t T, int64_t H, int64_t N, int dtype, int algo, void *stream);
 
+/*
+ * The time-mix operator with its prologue and epilogue fused around the
+ * recurrence (RWKV-7 G0 7.2B notes, section 7.1, "x070 architecture, the two
+ * core operators": the decay is exp(-exp(w)) of a soft-clamped w; the removal
+ * key kk is L2-normalised per head with F.normalize; the kernel slots are
+ * a = -kk and b = kk * a_lr, a_lr being the in-context learning rate; the
+ * output goes through ln_x, a GroupNorm whose eps is 64e-5). Per (b, t, h):
+ *
+ *     w      = exp(-exp(w_raw))                    (float32)
+ *     kk_hat = kk / max(|kk|_2, 1e-12)             (over the head's 64 channels)
+ *     a      = -kk_hat,  b = kk_hat * a_lr
+ *     S_t    = S_{t-1} (diag(w) + a b^T) + v k^T,  y = S_t r
+ *     out    = (y - mean(y)) / sqrt(var(y) + 64e-5) * ln_w + ln_b
+ *              (mean and population variance over the head's 64 channels;
+ *               ln_w and ln_b are per channel, [H * 64])
+ *
+ * This saves the passes that would otherwise compute w, a and b into HBM
+ * before the recurrence and normalise y after it.
+ *
+ *   r, k, v, kk, a_lr  [B,T,H,N] in `dtype` (RWKV7_DTYPE_F32 or _BF16)
+ *   w_raw              [B,T,H,N] float32 (kept float32 for every dtype: decays
+ *                      close to 1 need it, RWKV-LM README, fp32 note)
+ *   ln_w, ln_b         [H*N] float32, or NULL for weight 1 / bias 0
+ *   state_in           [B,H,N,N] float32, or NULL for zeros
+ *   out                [B,T,H,N] float32, the normalised output
+ *   state_out          [B,H,N,N] float32, or NULL; may equal state_in
+ *   B, T, H, N         as for rwkv7_wkv_prefill (N must be 64)
+ *
+ * Layouts, ownership, alignment, aliasing and error codes are as for
+ * rwkv7_wkv_prefill (every pointer 16-byte aligned; out and state_out may not
+ * overlap any input; T == 0 copies the state). One workgroup per head runs the
+ * token-by-token recurrence with float32 state; results match the float64
+ * definition above to float32 rounding (bfloat16 inputs are widened exactly).
+ */
+int rwkv7_tmix_prefill(const void *r, const float *w_raw, const void *k, const void *v, const void *kk,
+                       const void *a_lr, const float *ln_w, const float *ln_b, const float *state_in, float *out,
+                       float *state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * Single-token step of the fused time-mix operator (RNN mode, G0 notes section
+ * 3.2): rwkv7_tmix_prefill with T == 1 (else RWKV7_ERR_SHAPE). T consecutive
+ * steps give the same bits as one rwkv7_tmix_prefill over the T tokens.
+ */
+int rwkv7_tmix_step(const void *r, const float *w_raw, const void *k, const void *v, const void *kk,
+                    const void *a_lr, const float *ln_w, const float *ln_b, const float *state_in, float *out,
+                    float *state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rwkv7_wkv_strerror(int status);
 

@@ -93,9 +93,77 @@ int run(const void* r, const void* w, const void* k, const void* v, const void* 
   return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 
+int validate_tmix(const void* const in[5], const float* w_raw, const float* ln_w, const float* ln_b,
+                  const float* s_in, const float* out, const float* s_out, int64_t B, int64_t T, int64_t H, int64_t N,
+                  int dtype) {
+  if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
+  if (N != RWKV7_HEAD_SIZE) return RWKV7_ERR_HEAD_SIZE;
+  int64_t units = 0, tok_heads = 0, elems = 0;
+  if (__builtin_mul_overflow(B, H, &units) || units > (int64_t(1) << 26)) return RWKV7_ERR_SHAPE;
+  if (__builtin_mul_overflow(units, T, &tok_heads) || __builtin_mul_overflow(tok_heads, int64_t(64), &elems) ||
+      elems > (int64_t(1) << 58))
+    return RWKV7_ERR_SHAPE;
+  const int64_t in_bytes = elems * (dtype == RWKV7_DTYPE_BF16 ? 2 : 4);
+  const int64_t f32_bytes = elems * 4;
+  const int64_t st_bytes = units * 64 * 64 * 4;
+  const int64_t ln_bytes = H * 64 * 4;
+  if (elems > 0) {
+    for (int i = 0; i < 5; ++i)
+      if (!in[i]) return RWKV7_ERR_NULL;
+    if (!w_raw || !out) return RWKV7_ERR_NULL;
+  }
+  const void* ptrs[11] = {in[0], in[1], in[2], in[3], in[4], w_raw, ln_w, ln_b, s_in, out, s_out};
+  for (const void* q : ptrs)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return RWKV7_ERR_ALIGN;
+  const Range ro = range_of(out, f32_bytes);
+  const Range rso = range_of(s_out, st_bytes);
+  const Range rsi = range_of(s_in, st_bytes);
+  const Range srcs[8] = {range_of(in[0], in_bytes), range_of(in[1], in_bytes), range_of(in[2], in_bytes),
+                         range_of(in[3], in_bytes), range_of(in[4], in_bytes), range_of(w_raw, f32_bytes),
+                         range_of(ln_w, ln_bytes), range_of(ln_b, ln_bytes)};
+  for (const Range& ri : srcs)
+    if (overlap(ro, ri) || overlap(rso, ri)) return RWKV7_ERR_ALIAS;
+  if (overlap(ro, rsi) || overlap(ro, rso)) return RWKV7_ERR_ALIAS;
+  if (s_out && s_in && s_out != s_in && overlap(rso, rsi)) return RWKV7_ERR_ALIAS;
+  return RWKV7_OK;
+}
+
+int run_tmix(const void* r, const float* w_raw, const void* k, const void* v, const void* kk, const void* a_lr,
+             const float* ln_w, const float* ln_b, const float* state_in, float* out, float* state_out, int64_t B,
+             int64_t T, int64_t H, int64_t N, int dtype, bool step, void* stream) {
+  const void* in[5] = {r, k, v, kk, a_lr};
+  const int st = validate_tmix(in, w_raw, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype);
+  if (st != RWKV7_OK) return st;
+  if (step && T != 1) return RWKV7_ERR_SHAPE;
+  if (B * H == 0) return RWKV7_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (state_out && state_out != state_in) e = rwkv7::launch_state_copy(state_in, state_out, B * H, s);
+    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+  }
+  rwkv7::TmixCall c{{r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, T, (int32_t)H}, B, H, dtype, s};
+  e = rwkv7::launch_tmix(c);
+  return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int rwkv7_tmix_prefill(const void* r, const float* w_raw, const void* k, const void* v, const void* kk,
+                       const void* a_lr, const float* ln_w, const float* ln_b, const float* state_in, float* out,
+                       float* state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void* stream) {
+  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, false, stream);
+}
+
+int rwkv7_tmix_step(const void* r, const float* w_raw, const void* k, const void* v, const void* kk,
+                    const void* a_lr, const float* ln_w, const float* ln_b, const float* state_in, float* out,
+                    float* state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void* stream) {
+  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, true, stream);
+}
+
 
 int rwkv7_wkv_prefill(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
                       const float* state_in, float* y, float* state_out, int64_t B, int64_t T, int64_t H,

@@ -31,6 +31,31 @@ hipError_t launch_chunked(const WkvCall& c);
 // kernel, with a record buffer cached per (device, stream).
 hipError_t launch_chunked_split(const WkvCall& c);
 
+// The time-mix operator with its prologue (decay, normalised removal key, the
+// a and b slots) and epilogue (ln_x GroupNorm) fused around the recurrence.
+struct TmixParams {
+  const void* r;
+  const float* w_raw;
+  const void* k;
+  const void* v;
+  const void* kk;
+  const void* a_lr;
+  const float* ln_w;  // may be null (weight 1)
+  const float* ln_b;  // may be null (bias 0)
+  const float* s_in;  // may be null (zero state)
+  float* out;
+  float* s_out;  // may be null
+  int64_t T;
+  int32_t H;
+};
+struct TmixCall {
+  TmixParams p;
+  int64_t B, H;
+  int dtype;  // RWKV7_DTYPE_* of r, k, v, kk, a_lr
+  hipStream_t stream;
+};
+hipError_t launch_tmix(const TmixCall& c);
+
 // state_out <- state_in (zeros when state_in is null) for B*H heads.
 hipError_t launch_state_copy(const float* s_in, float* s_out, int64_t units, hipStream_t stream);
 

@@ -118,37 +118,6 @@ struct StateIO<kStF16> {
   }
 };
 
-// One token for the MR rows a lane holds (4 columns each): sa = S a (4 in-lane
-// terms, then the 16-lane butterfly), S <- S diag(w) + sa b^T + v k^T, y = S r.
-// Returns y of row 4c + ri when c < MR (the lane's output slot); both kernels
-// call this, which keeps prefill and step bit-identical.
-template <int MR>
-__device__ __forceinline__ float token_update(float4 (&S)[MR], const float4 r4, const float4 w4, const float4 k4,
-                                              const float4 a4, const float4 b4, const float (&vm)[MR], int c) {
-  float sa[MR], yp[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-    sa[m] = fmaf(S[m].w, a4.w, fmaf(S[m].z, a4.z, fmaf(S[m].y, a4.y, S[m].x * a4.x)));
-#pragma unroll
-  for (int m = 0; m < MR; ++m) sa[m] = row16_sum(sa[m]);
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    S[m].x = fmaf(S[m].x, w4.x, fmaf(sa[m], b4.x, vm[m] * k4.x));
-    S[m].y = fmaf(S[m].y, w4.y, fmaf(sa[m], b4.y, vm[m] * k4.y));
-    S[m].z = fmaf(S[m].z, w4.z, fmaf(sa[m], b4.z, vm[m] * k4.z));
-    S[m].w = fmaf(S[m].w, w4.w, fmaf(sa[m], b4.w, vm[m] * k4.w));
-  }
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-    yp[m] = fmaf(S[m].w, r4.w, fmaf(S[m].z, r4.z, fmaf(S[m].y, r4.y, S[m].x * r4.x)));
-#pragma unroll
-  for (int m = 0; m < MR; ++m) yp[m] = row16_sum(yp[m]);
-  float yo = yp[0];
-#pragma unroll
-  for (int m = 1; m < MR; ++m) yo = (c == m) ? yp[m] : yo;
-  return yo;
-}
-
 template <bool BF16, int WAVES, int RPW, int TB, int SQ>
 __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
   using Tr = InTraits<BF16>;

@@ -95,8 +95,8 @@ __device__ __forceinline__ half4 to_h4(f32x4 x) {
 __device__ __forceinline__ half8 cat8(half4 lo, half4 hi) {
   return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-__device__ __forceinline__ half4 lo4(half8 x) { return half4{x[0], x[1], x[2], x[3]}; }
-__device__ __forceinline__ half4 hi4(half8 x) { return half4{x[4], x[5], x[6], x[7]}; }
+
+
 // bfloat16 bits (low 16 bits of the argument) widened to float32, exactly
 __device__ __forceinline__ float bfw(uint32_t raw16) { return __uint_as_float(raw16 << 16); }
 // element e (0..3) of four bfloat16 packed in a uint2

@@ -1,0 +1,224 @@
+// The WKV-7 time-mix operator with its prologue and epilogue fused around the
+// recurrence (RWKV-7 G0 7.2B notes, lshu.cn/news/198401, section 7.1, "x070
+// architecture, the two core operators"):
+//
+//   prologue  w = exp(-exp(w_raw))                       (decay, from float32 w_raw)
+//             kk_hat = kk / max(|kk|_2, 1e-12)           (per head, as F.normalize)
+//             a = -kk_hat,  b = kk_hat * a_lr            (the kernel's two slots)
+//   recurrence S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T,  y_t = S_t r_t
+//   epilogue  out = (y - mean) / sqrt(var + 64e-5) * ln_w + ln_b
+//             (ln_x: a GroupNorm with one group per head; mean and population
+//              variance over the head's 64 channels of one token)
+//
+// One workgroup owns one head (four waves of 16 value rows, the lane layout and
+// the per-token update of the sequential kernel), so a head's 64 outputs of a
+// token are all in the workgroup and the GroupNorm never leaves LDS. Blocks of
+// TB tokens are staged through LDS: the raw inputs of block n+1 are in flight in
+// registers while block n runs three passes, each wave taking every fourth token:
+//   1. prologue, lane = key column: decay, the row's squared norm by a wave
+//      reduction, the two slots, written back over the raw values;
+//   2. the recurrence, token by token, y into LDS;
+//   3. epilogue, lane = channel: mean and variance by wave reductions, affine,
+//      one coalesced 256-byte store per token.
+// The float32 decay is rounded once per element, as the pages keep it; prefill
+// and the single-token step run the same code, so T steps reproduce a prefill
+// over T tokens bit for bit.
+#include "wkv7_device.hpp"
+#include "wkv7_internal.hpp"
+
+namespace rwkv7 {
+namespace {
+
+constexpr float kGroupNormEps = 64e-5f;
+constexpr float kNormalizeEps = 1e-12f;
+constexpr int kWaves = 4;
+constexpr int kRpw = 16;            // value rows per wave
+constexpr int kMr = kRpw / 4;       // rows per lane
+constexpr int kThreads = kWave * kWaves;
+
+// Sum over the 64 lanes of a wave; every lane ends with the same bits (each
+// step adds a pair of partial sums that both partners hold).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  x = x + __shfl_xor(x, 16);
+  x = x + __shfl_xor(x, 32);
+  return x;
+}
+
+template <bool BF16>
+struct TmixIn {
+  static constexpr int kEpv = BF16 ? 8 : 4;  // elements per 16-byte load
+  static constexpr int kEsz = BF16 ? 2 : 4;
+  __device__ static void store(float* dst, const uint4 q) {
+    if constexpr (BF16) {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+      reinterpret_cast<float4*>(dst)[1] = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+    } else {
+      *reinterpret_cast<uint4*>(dst) = q;
+    }
+  }
+};
+
+template <bool BF16, int TB>
+__global__ __launch_bounds__(kThreads) void wkv7_tmix_kernel(TmixParams p) {
+  using In = TmixIn<BF16>;
+  constexpr int kEpv = In::kEpv;
+  constexpr int kSeg = kN / kEpv;       // 16-byte loads per token row of an input
+  constexpr int kSegW = kN / 4;         // 16-byte loads per token row of float32 w_raw
+  // staged tensors, in LDS slot order: r, w_raw -> w, k, kk -> a, a_lr -> b, then v
+  constexpr int kNq = (TB * kSeg + kThreads - 1) / kThreads;
+  constexpr int kNqW = (TB * kSegW + kThreads - 1) / kThreads;
+
+  __shared__ __align__(16) float kv_lds[TB][5][kN];
+  __shared__ __align__(16) float v_lds[TB][kN];
+  __shared__ __align__(16) float y_lds[TB][kN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int c = lane & 15;
+  const int ri = lane >> 4;
+
+  const int64_t unit = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int64_t bb = unit / p.H;
+  const int64_t hh = unit % p.H;
+  const int64_t T = p.T;
+  const int64_t tok_stride = (int64_t)p.H * kN;
+  const int64_t seq_base = (bb * T * p.H + hh) * kN;  // element offset of token 0
+  const int row0 = wave * kRpw;
+
+  // inputs in dtype, by staging slot (slot 1 is w_raw, float32 for every dtype)
+  const char* src[6] = {static_cast<const char*>(p.r), nullptr, static_cast<const char*>(p.k),
+                        static_cast<const char*>(p.kk), static_cast<const char*>(p.a_lr),
+                        static_cast<const char*>(p.v)};
+  const char* wsrc = reinterpret_cast<const char*>(p.w_raw);
+
+  float4 S[kMr];
+#pragma unroll
+  for (int m = 0; m < kMr; ++m) {
+    const int row = row0 + 4 * m + ri;
+    S[m] = p.s_in ? *reinterpret_cast<const float4*>(p.s_in + (unit * kN + row) * kN + 4 * c)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  uint4 stg[6][kNq];
+  uint4 stw[kNqW];
+  auto issue = [&](int64_t t0) {
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      if (x == 1) continue;
+#pragma unroll
+      for (int q = 0; q < kNq; ++q) {
+        const int e = tid + kThreads * q;
+        const int tok = e / kSeg, seg = e % kSeg;
+        if (e < TB * kSeg && t0 + tok < T)
+          stg[x][q] = *reinterpret_cast<const uint4*>(
+              src[x] + (seq_base + (t0 + tok) * tok_stride + seg * kEpv) * In::kEsz);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kNqW; ++q) {
+      const int e = tid + kThreads * q;
+      const int tok = e / kSegW, seg = e % kSegW;
+      if (e < TB * kSegW && t0 + tok < T)
+        stw[q] = *reinterpret_cast<const uint4*>(wsrc + (seq_base + (t0 + tok) * tok_stride + seg * 4) * 4);
+    }
+  };
+  auto commit = [&](int64_t t0) {
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      if (x == 1) continue;
+#pragma unroll
+      for (int q = 0; q < kNq; ++q) {
+        const int e = tid + kThreads * q;
+        const int tok = e / kSeg, seg = e % kSeg;
+        if (e < TB * kSeg && t0 + tok < T)
+          In::store(x < 5 ? &kv_lds[tok][x][seg * kEpv] : &v_lds[tok][seg * kEpv], stg[x][q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kNqW; ++q) {
+      const int e = tid + kThreads * q;
+      const int tok = e / kSegW, seg = e % kSegW;
+      if (e < TB * kSegW && t0 + tok < T) *reinterpret_cast<uint4*>(&kv_lds[tok][1][seg * 4]) = stw[q];
+    }
+  };
+
+  const float* lnw = p.ln_w ? p.ln_w + hh * kN : nullptr;
+  const float* lnb = p.ln_b ? p.ln_b + hh * kN : nullptr;
+  const float gw = lnw ? lnw[lane] : 1.f;  // lane = channel in the epilogue
+  const float gb = lnb ? lnb[lane] : 0.f;
+
+  if (T > 0) issue(0);
+  for (int64_t t0 = 0; t0 < T; t0 += TB) {
+    const int ntok = (T - t0 < TB) ? (int)(T - t0) : TB;
+    __syncthreads();  // every wave is done with the previous block's LDS
+    commit(t0);
+    __syncthreads();
+    if (t0 + TB < T) issue(t0 + TB);  // in flight while this block is computed
+
+    // ---- 1. prologue (lane = key column j)
+    for (int tt = wave; tt < ntok; tt += kWaves) {
+      const float u = kv_lds[tt][1][lane];
+      const float kk = kv_lds[tt][3][lane];
+      const float alr = kv_lds[tt][4][lane];
+      const float n2 = wave_sum(kk * kk);
+      const float kh = kk * (1.f / fmaxf(sqrtf(n2), kNormalizeEps));
+      kv_lds[tt][1][lane] = expf(-expf(u));
+      kv_lds[tt][3][lane] = -kh;
+      kv_lds[tt][4][lane] = kh * alr;
+    }
+    __syncthreads();
+
+    // ---- 2. recurrence
+    for (int tt = 0; tt < ntok; ++tt) {
+      const float4 r4 = *reinterpret_cast<const float4*>(&kv_lds[tt][0][4 * c]);
+      const float4 w4 = *reinterpret_cast<const float4*>(&kv_lds[tt][1][4 * c]);
+      const float4 k4 = *reinterpret_cast<const float4*>(&kv_lds[tt][2][4 * c]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&kv_lds[tt][3][4 * c]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&kv_lds[tt][4][4 * c]);
+      float vm[kMr];
+#pragma unroll
+      for (int m = 0; m < kMr; ++m) vm[m] = v_lds[tt][row0 + 4 * m + ri];
+      const float yo = token_update<kMr>(S, r4, w4, k4, a4, b4, vm, c);
+      if (c < kMr) y_lds[tt][row0 + 4 * c + ri] = yo;
+    }
+    __syncthreads();
+
+    // ---- 3. epilogue (lane = channel i)
+    for (int tt = wave; tt < ntok; tt += kWaves) {
+      const float y = y_lds[tt][lane];
+      const float mu = wave_sum(y) * (1.f / kN);
+      const float d = y - mu;
+      const float var = wave_sum(d * d) * (1.f / kN);
+      const float o = d * (1.f / sqrtf(var + kGroupNormEps));
+      p.out[seq_base + (t0 + tt) * tok_stride + lane] = fmaf(o, gw, gb);
+    }
+  }
+
+  if (p.s_out) {
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      const int row = row0 + 4 * m + ri;
+      *reinterpret_cast<float4*>(p.s_out + (unit * kN + row) * kN + 4 * c) = S[m];
+    }
+  }
+}
+
+template <bool BF16, int TB>
+hipError_t launch_cfg(const TmixCall& c) {
+  TmixParams p = c.p;
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_tmix_kernel<BF16, TB>), dim3((uint32_t)(c.B * c.H)),
+                         dim3(kThreads), args, 0, c.stream);
+}
+
+}  // namespace
+
+hipError_t launch_tmix(const TmixCall& c) {
+  // one token per block for the single-token step, sixteen for a prefill
+  if (c.dtype == 1) return c.p.T == 1 ? launch_cfg<true, 1>(c) : launch_cfg<true, 16>(c);
+  return c.p.T == 1 ? launch_cfg<false, 1>(c) : launch_cfg<false, 16>(c);
+}
+
+}  // namespace rwkv7

@@ -28,7 +28,7 @@ RWKV7_ALGO_CHUNKED = 2
 RWKV7_ALGO_CHUNKED_SPLIT = 3
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
-            "rwkv7_wkv_strerror")
+            "rwkv7_tmix_prefill", "rwkv7_tmix_step", "rwkv7_wkv_strerror")
 
 _lib = None
 _lock = threading.Lock()
@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
             L.rwkv7_wkv_step_q.argtypes = sig + [ci, vp]
             L.rwkv7_wkv_prefill_ex.restype = ci
             L.rwkv7_wkv_prefill_ex.argtypes = sig + [ci, vp]
+            for name in ("rwkv7_tmix_prefill", "rwkv7_tmix_step"):
+                f = getattr(L, name)
+                f.restype = ci
+                f.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp]
             L.rwkv7_wkv_strerror.restype = ctypes.c_char_p
             L.rwkv7_wkv_strerror.argtypes = [ci]
             _lib = L
@@ -146,3 +150,31 @@ def wkv7(r, w, k, v, a, b, state_in=None, algo=RWKV7_ALGO_AUTO, want_state=True,
     s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device) if want_state else None
     rwkv7_wkv_prefill_ex(r, w, k, v, a, b, state_in, y, s_out, algo=algo, stream=stream)
     return y, s_out
+
+
+def _tmix_args(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out):
+    B, T, H, N = r.shape
+    return [_ptr(x) for x in (r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out)] + \
+        [B, T, H, N, _dtype_code(r)]
+
+
+def rwkv7_tmix_prefill(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, stream=None):
+    """Fused time-mix prefill: prologue (decay, normalised removal key, slots), recurrence, ln_x."""
+    _check(lib().rwkv7_tmix_prefill(*_tmix_args(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out),
+                                    _stream(stream)))
+
+
+def rwkv7_tmix_step(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, stream=None):
+    """Fused time-mix single-token step (T == 1); state_out may be state_in."""
+    _check(lib().rwkv7_tmix_step(*_tmix_args(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out),
+                                 _stream(stream)))
+
+
+def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, want_state=True, stream=None):
+    """Allocate out ([B,T,H,64] float32) and the final state, run the fused prefill, return (out, state_out)."""
+    import torch
+    B, T, H, N = r.shape
+    out = torch.empty((B, T, H, N), dtype=torch.float32, device=r.device)
+    s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device) if want_state else None
+    rwkv7_tmix_prefill(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, s_out, stream=stream)
+    return out, s_out

@@ -177,3 +177,47 @@ def test_step_q_alias_uses_16_bit_state_size(L):
 def test_chunked_refuses_f32_inputs_before_any_launch(L):
     assert call(L, fn="rwkv7_wkv_prefill_ex", dtype=F32, algo=wkv.RWKV7_ALGO_CHUNKED) == E_ALGO
     assert call(L, fn="rwkv7_wkv_prefill_ex", dtype=F32, algo=wkv.RWKV7_ALGO_CHUNKED_SPLIT) == E_ALGO
+
+
+# ---- the fused time-mix entry points: r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out
+
+def tcall(L, fn="rwkv7_tmix_prefill", p=None, B=2, T=3, H=4, N=64, dtype=BF16):
+    p = ptrs(11) if p is None else p
+    return getattr(L, fn)(*(list(p) + [B, T, H, N, dtype, None]))
+
+
+def test_tmix_validation(L):
+    assert tcall(L, dtype=5) == E_DTYPE
+    assert tcall(L, N=32) == E_HEAD
+    assert tcall(L, B=-1) == E_SHAPE
+    assert tcall(L, fn="rwkv7_tmix_step", T=2) == E_SHAPE
+    for i in (0, 1, 2, 3, 4, 5, 9):  # r, w_raw, k, v, kk, a_lr, out are required
+        p = ptrs(11)
+        p[i] = None
+        assert tcall(L, p=p) == E_NULL, i
+    for i in range(11):
+        p = ptrs(11)
+        p[i] += 4
+        assert tcall(L, p=p) == E_ALIGN, i
+
+
+def test_tmix_aliasing(L):
+    p = ptrs(11)
+    p[9] = p[4]  # out over kk
+    assert tcall(L, p=p) == E_ALIAS
+    p = ptrs(11)
+    p[10] = p[1]  # state_out over w_raw
+    assert tcall(L, p=p) == E_ALIAS
+    p = ptrs(11)
+    p[9] = p[6]  # out over ln_w
+    assert tcall(L, p=p) == E_ALIAS
+    p = ptrs(11)
+    p[10] = p[8]  # state_out == state_in is allowed; with no work nothing launches
+    assert tcall(L, p=p, B=0) == OK
+
+
+def test_tmix_empty(L):
+    assert tcall(L, B=0) == OK and tcall(L, H=0) == OK
+    p = ptrs(11)
+    p[6] = p[7] = None  # ln_w / ln_b optional
+    assert tcall(L, p=p, B=0) == OK
