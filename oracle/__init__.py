@@ -23,6 +23,11 @@ delta-rule retrieval, the memoryless case, linearity and row equivariance.
 key, kernel slots) and epilogue (ln_x GroupNorm) around the recurrence, in numpy
 float64; tests/test_oracle_tmix.py pins those pieces to closed forms and to
 torch's normalize and group_norm.
+
+``wkv7_backward`` runs the C reverse-mode derivatives of the recurrence (every
+forward state kept, tokens walked backwards); tests/test_oracle_backward.py pins
+it to torch float64 autograd of a plain token loop, to finite differences and
+to a closed form, and plants mistakes that the pins must catch.
 """
 from __future__ import annotations
 
@@ -67,6 +72,9 @@ def _load():
             f = lib.wkv7_oracle_f64
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int] * 3
+            fb = lib.wkv7_oracle_bwd_f64
+            fb.restype = ctypes.c_int
+            fb.argtypes = [ctypes.c_void_p] * 16 + [ctypes.c_int64] * 4 + [ctypes.c_int] * 3
             for name in ("wkv7_oracle_round16", "wkv7_oracle_widen16"):
                 g = getattr(lib, name)
                 g.restype = ctypes.c_int
@@ -227,3 +235,36 @@ def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, nthreads
     w, a, b = tmix_prologue(w_raw, kk, a_lr)
     y, s = wkv7(_widen_any(r), w, _widen_any(k), _widen_any(v), a, b, state_in=state_in, nthreads=nthreads)
     return group_norm(y, ln_w, ln_b), s
+
+
+def wkv7_backward(r, w, k, v, a, b, dy, state_in=None, dstate_out=None, nthreads: int | None = None):
+    """Reverse-mode derivatives of the recurrence in float64 (training, G0 notes section 7.2).
+
+    Inputs as for wkv7 (one dtype for r..b; state_in float32/float64 or None); dy [B,T,H,N] and
+    dstate_out [B,H,N,N] (or None: zero) are the gradients of a loss with respect to y and the final
+    state. Returns dict with dr, dw, dk, dv, da, db ([B,T,H,N] float64) and dstate_in ([B,H,N,N]).
+    """
+    lib = _load()
+    ins = [np.ascontiguousarray(x) for x in (r, w, k, v, a, b)]
+    shape = ins[0].shape
+    if len(shape) != 4 or any(x.shape != shape for x in ins):
+        raise ValueError("r,w,k,v,a,b must share one [B,T,H,N] shape")
+    dt = _in_dtype(ins[0])
+    if any(_in_dtype(x) != dt for x in ins):
+        raise TypeError("r,w,k,v,a,b must share one dtype")
+    B, T, H, N = shape
+    s_in, st_dt = None, IN_F64
+    if state_in is not None:
+        s_in = np.ascontiguousarray(state_in)
+        st_dt = {np.dtype(np.float32): IN_F32, np.dtype(np.float64): IN_F64}[s_in.dtype]
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    dso = None if dstate_out is None else np.ascontiguousarray(dstate_out, dtype=np.float64)
+    out = {n: np.empty(shape, dtype=np.float64) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    out["dstate_in"] = np.empty((B, H, N, N), dtype=np.float64)
+    p = lambda x: None if x is None else x.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    rc = lib.wkv7_oracle_bwd_f64(*(p(x) for x in ins), p(s_in), p(dy), p(dso),
+                                 *(p(out[n]) for n in ("dr", "dw", "dk", "dv", "da", "db", "dstate_in")),
+                                 B, T, H, N, dt, st_dt, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle backward failed with status %d" % rc)
+    return out

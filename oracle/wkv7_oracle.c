@@ -286,3 +286,198 @@ int wkv7_oracle_widen16(const uint16_t *bits, double *out, int64_t n, int fmt)
         out[i] = widen(bits, fmt, (size_t)i);
     return 0;
 }
+
+/*
+ * Backward of the recurrence (reverse-mode derivatives, float64), for training
+ * (RWKV-7 G0 7.2B notes, section 7.2: the training code runs the same WKV-7
+ * operator forward and backward). Given dy = dL/dy_t for every token and
+ * dS_T = dL/dS_T for the final state (NULL: zero), it returns dL/dr, dL/dw,
+ * dL/dk, dL/dv, dL/da, dL/db ([B,T,H,N]) and dL/dS_0 ([B,H,N,N]).
+ *
+ * It keeps every state S_t of the forward pass and walks the tokens backwards
+ * with G = dL/dS_t. With M_t = diag(w_t) + a_t b_t^T:
+ *   y_t = S_t r_t                 ->  G += dy_t r_t^T,       dr_t = S_t^T dy_t
+ *   S_t = S_{t-1} M_t + v_t k_t^T ->  dv_t = G k_t,          dk_t = G^T v_t,
+ *                                     dM_t = S_{t-1}^T G,    dw_t = diag(dM_t),
+ *                                     da_t = dM_t b_t = S_{t-1}^T (G b_t),
+ *                                     db_t = dM_t^T a_t = G^T (S_{t-1} a_t),
+ *                                     G <- G M_t^T = G diag(w_t) + (G b_t) a_t^T
+ * and dL/dS_0 is G after the first token.
+ */
+typedef struct {
+    const void *r, *w, *k, *v, *a, *b; /* [B,T,H,N], dtype in_dtype */
+    const void *state_in;              /* [B,H,N,N] or NULL, dtype st_dtype */
+    const double *dy;                  /* [B,T,H,N] */
+    const double *dstate_out;          /* [B,H,N,N] or NULL */
+    double *dr, *dw, *dk, *dv, *da, *db; /* [B,T,H,N] */
+    double *dstate_in;                 /* [B,H,N,N] or NULL */
+    int64_t B, T, H, N;
+    int in_dtype, st_dtype;
+    int64_t next_unit;
+    pthread_mutex_t lock;
+} bjob_t;
+
+static int run_bwd_unit(bjob_t *J, int64_t unit)
+{
+    const int64_t N = J->N, T = J->T, H = J->H;
+    const int64_t bb = unit / H, hh = unit % H;
+    const size_t NN = (size_t)(N * N);
+    double *Sall = (double *)malloc(sizeof(double) * NN * (size_t)(T + 1));
+    double *G = (double *)malloc(sizeof(double) * NN);
+    double *vec = (double *)malloc(sizeof(double) * (size_t)(9 * N));
+    if (!Sall || !G || !vec) {
+        free(Sall);
+        free(G);
+        free(vec);
+        return -2;
+    }
+    double *r = vec, *w = vec + N, *k = vec + 2 * N, *v = vec + 3 * N, *a = vec + 4 * N, *b = vec + 5 * N;
+    double *dyv = vec + 6 * N, *gb = vec + 7 * N, *sa = vec + 8 * N;
+
+    for (size_t e = 0; e < NN; ++e)
+        Sall[e] = J->state_in ? widen(J->state_in, J->st_dtype, (size_t)unit * NN + e) : 0.0;
+    for (int64_t t = 0; t < T; ++t) { /* forward, keeping S_t in Sall[t + 1] */
+        const size_t base = (size_t)(((bb * T + t) * H + hh) * N);
+        for (int64_t j = 0; j < N; ++j) {
+            w[j] = widen(J->w, J->in_dtype, base + j);
+            k[j] = widen(J->k, J->in_dtype, base + j);
+            v[j] = widen(J->v, J->in_dtype, base + j);
+            a[j] = widen(J->a, J->in_dtype, base + j);
+            b[j] = widen(J->b, J->in_dtype, base + j);
+        }
+        const double *Sp = Sall + (size_t)t * NN;
+        double *Sc = Sall + (size_t)(t + 1) * NN;
+        for (int64_t i = 0; i < N; ++i) {
+            double s = 0.0;
+            for (int64_t j = 0; j < N; ++j)
+                s += Sp[i * N + j] * a[j];
+            for (int64_t j = 0; j < N; ++j)
+                Sc[i * N + j] = Sp[i * N + j] * w[j] + s * b[j] + v[i] * k[j];
+        }
+    }
+
+    for (size_t e = 0; e < NN; ++e)
+        G[e] = J->dstate_out ? J->dstate_out[(size_t)unit * NN + e] : 0.0;
+    for (int64_t t = T - 1; t >= 0; --t) {
+        const size_t base = (size_t)(((bb * T + t) * H + hh) * N);
+        for (int64_t j = 0; j < N; ++j) {
+            r[j] = widen(J->r, J->in_dtype, base + j);
+            w[j] = widen(J->w, J->in_dtype, base + j);
+            k[j] = widen(J->k, J->in_dtype, base + j);
+            v[j] = widen(J->v, J->in_dtype, base + j);
+            a[j] = widen(J->a, J->in_dtype, base + j);
+            b[j] = widen(J->b, J->in_dtype, base + j);
+            dyv[j] = J->dy[base + j];
+        }
+        const double *Sp = Sall + (size_t)t * NN;       /* S_{t-1} */
+        const double *Sc = Sall + (size_t)(t + 1) * NN; /* S_t */
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = 0; j < N; ++j)
+                G[i * N + j] += dyv[i] * r[j];
+        for (int64_t j = 0; j < N; ++j) {
+            double s_dr = 0.0, s_dk = 0.0, s_dw = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                s_dr += Sc[i * N + j] * dyv[i];
+                s_dk += G[i * N + j] * v[i];
+                s_dw += Sp[i * N + j] * G[i * N + j];
+            }
+            J->dr[base + j] = s_dr;
+            J->dk[base + j] = s_dk;
+            J->dw[base + j] = s_dw;
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            double s_dv = 0.0, s_gb = 0.0, s_sa = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                s_dv += G[i * N + j] * k[j];
+                s_gb += G[i * N + j] * b[j];
+                s_sa += Sp[i * N + j] * a[j];
+            }
+            J->dv[base + i] = s_dv;
+            gb[i] = s_gb;
+            sa[i] = s_sa;
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double s_da = 0.0, s_db = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                s_da += Sp[i * N + j] * gb[i];
+                s_db += G[i * N + j] * sa[i];
+            }
+            J->da[base + j] = s_da;
+            J->db[base + j] = s_db;
+        }
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = 0; j < N; ++j)
+                G[i * N + j] = G[i * N + j] * w[j] + gb[i] * a[j];
+    }
+    if (J->dstate_in)
+        memcpy(J->dstate_in + (size_t)unit * NN, G, sizeof(double) * NN);
+    free(Sall);
+    free(G);
+    free(vec);
+    return 0;
+}
+
+static void *bworker(void *arg)
+{
+    bjob_t *J = (bjob_t *)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t unit = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (unit >= J->B * J->H)
+            break;
+        if (run_bwd_unit(J, unit) != 0)
+            return (void *)1;
+    }
+    return NULL;
+}
+
+/* Backward over all B*H units with `nthreads` threads. Returns 0, -1 on bad arguments, -2 on allocation failure. */
+int wkv7_oracle_bwd_f64(const void *r, const void *w, const void *k, const void *v, const void *a,
+                        const void *b, const void *state_in, const double *dy, const double *dstate_out,
+                        double *dr, double *dw, double *dk, double *dv, double *da, double *db,
+                        double *dstate_in, int64_t B, int64_t T, int64_t H, int64_t N, int in_dtype,
+                        int st_dtype, int nthreads)
+{
+    if (!r || !w || !k || !v || !a || !b || !dy || !dr || !dw || !dk || !dv || !da || !db)
+        return -1;
+    if (B < 0 || T < 0 || H < 0 || N <= 0 || in_dtype < ORC_F32 || in_dtype > ORC_F64 || st_dtype < ORC_F32 ||
+        st_dtype > ORC_F16)
+        return -1;
+    bjob_t J;
+    J.r = r; J.w = w; J.k = k; J.v = v; J.a = a; J.b = b;
+    J.state_in = state_in; J.dy = dy; J.dstate_out = dstate_out;
+    J.dr = dr; J.dw = dw; J.dk = dk; J.dv = dv; J.da = da; J.db = db; J.dstate_in = dstate_in;
+    J.B = B; J.T = T; J.H = H; J.N = N;
+    J.in_dtype = in_dtype; J.st_dtype = st_dtype;
+    J.next_unit = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (B * H < nthreads)
+        nthreads = (int)(B * H > 0 ? B * H : 1);
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int status = 0, started = 0;
+    if (!tid) {
+        pthread_mutex_destroy(&J.lock);
+        return -2;
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, bworker, &J) != 0) {
+            status = -2;
+            break;
+        }
+        ++started;
+    }
+    if (started == 0 && status == 0)
+        status = -2;
+    for (int i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(tid[i], &ret);
+        if (ret)
+            status = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return status;
+}
