@@ -226,6 +226,42 @@ int rwkv7_tmix_step(const void *r, const float *w_raw, const void *k, const void
                     const void *a_lr, const float *ln_w, const float *ln_b, const float *state_in, float *out,
                     float *state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
 
+/*
+ * Gradients of the recurrence (training). The model is trained with the same
+ * wkv7 operator (RWKV-7 G0 7.2B notes, section 7.2, the training scripts), which
+ * needs its derivatives; the pages give only the forward formula (section 7.1),
+ * so these are its reverse-mode derivatives. Given dy = dL/dy and
+ * dstate_out = dL/dS_T, with G = dL/dS_t accumulated from the last token back:
+ *
+ *     G += dy_t r_t^T
+ *     dr_t = S_t^T dy_t          dk_t = G^T v_t          dv_t = G k_t
+ *     dw_t[j] = sum_i S_{t-1}[i,j] G[i,j]
+ *     da_t = S_{t-1}^T (G b_t)   db_t = G^T (S_{t-1} a_t)
+ *     G <- G diag(w_t) + (G b_t) a_t^T          and finally dstate_in = G.
+ *
+ *   r, w, k, v, a, b  [B,T,H,N] in `dtype` (the forward call's inputs)
+ *   state_in          [B,H,N,N] float32, or NULL (zeros): the forward's S_0
+ *   dy                [B,T,H,N] float32
+ *   dstate_out        [B,H,N,N] float32, or NULL (zero: the final state unused)
+ *   dr..db            [B,T,H,N] float32 outputs, all six required
+ *   dstate_in         [B,H,N,N] float32 output, or NULL; may equal dstate_out
+ *
+ * Every pointer 16-byte aligned; outputs may not overlap any input or each
+ * other (dstate_in == dstate_out exactly is allowed); T == 0 copies dstate_out
+ * to dstate_in (zeros when NULL). The forward pass is recomputed inside: a
+ * first kernel stores the state every 16 tokens, a second walks the sequence
+ * backwards, rebuilding each 8-token stretch of states from its checkpoint.
+ * The checkpoints (B*H*ceil(T/16) * 16 KiB) live in the per-(device, stream)
+ * workspace described for rwkv7_wkv_prefill_ex, grown as needed (growing
+ * synchronises the stream; an allocation failure returns RWKV7_ERR_HIP before
+ * any launch). Arithmetic is float32 throughout (bfloat16 inputs widened
+ * exactly); results match the float64 derivatives to float32 rounding.
+ */
+int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
+                       const float *state_in, const float *dy, const float *dstate_out, float *dr, float *dw,
+                       float *dk, float *dv, float *da, float *db, float *dstate_in, int64_t B, int64_t T,
+                       int64_t H, int64_t N, int dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rwkv7_wkv_strerror(int status);
 

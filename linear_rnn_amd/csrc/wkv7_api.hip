@@ -148,9 +148,73 @@ int run_tmix(const void* r, const float* w_raw, const void* k, const void* v, co
   return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 
+int validate_backward(const void* const in[6], const float* s_in, const float* dy, const float* ds_out,
+                      float* const grad[6], const float* ds_in, int64_t B, int64_t T, int64_t H, int64_t N,
+                      int dtype) {
+  if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
+  if (N != RWKV7_HEAD_SIZE) return RWKV7_ERR_HEAD_SIZE;
+  int64_t units = 0, tok_heads = 0, elems = 0;
+  if (__builtin_mul_overflow(B, H, &units) || units > (int64_t(1) << 26)) return RWKV7_ERR_SHAPE;
+  if (__builtin_mul_overflow(units, T, &tok_heads) || __builtin_mul_overflow(tok_heads, int64_t(64), &elems) ||
+      elems > (int64_t(1) << 58))
+    return RWKV7_ERR_SHAPE;
+  const int64_t in_bytes = elems * (dtype == RWKV7_DTYPE_BF16 ? 2 : 4);
+  const int64_t f32_bytes = elems * 4;
+  const int64_t st_bytes = units * 64 * 64 * 4;
+  if (elems > 0) {
+    for (int i = 0; i < 6; ++i)
+      if (!in[i] || !grad[i]) return RWKV7_ERR_NULL;
+    if (!dy) return RWKV7_ERR_NULL;
+  }
+  const void* ptrs[16] = {in[0],   in[1],   in[2],   in[3],   in[4],   in[5],   s_in,    dy,
+                          ds_out,  grad[0], grad[1], grad[2], grad[3], grad[4], grad[5], ds_in};
+  for (const void* q : ptrs)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return RWKV7_ERR_ALIGN;
+  Range src[9];
+  for (int i = 0; i < 6; ++i) src[i] = range_of(in[i], in_bytes);
+  src[6] = range_of(s_in, st_bytes);
+  src[7] = range_of(dy, f32_bytes);
+  src[8] = range_of(ds_out, st_bytes);
+  Range dst[7];
+  for (int i = 0; i < 6; ++i) dst[i] = range_of(grad[i], f32_bytes);
+  dst[6] = range_of(ds_in, st_bytes);
+  for (int d = 0; d < 7; ++d) {
+    for (int i = 0; i < 9; ++i) {
+      if (d == 6 && i == 8 && ds_in == ds_out) continue;  // dstate in place
+      if (overlap(dst[d], src[i])) return RWKV7_ERR_ALIAS;
+    }
+    for (int e = d + 1; e < 7; ++e)
+      if (overlap(dst[d], dst[e])) return RWKV7_ERR_ALIAS;
+  }
+  return RWKV7_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int rwkv7_wkv_backward(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
+                       const float* state_in, const float* dy, const float* dstate_out, float* dr, float* dw,
+                       float* dk, float* dv, float* da, float* db, float* dstate_in, int64_t B, int64_t T,
+                       int64_t H, int64_t N, int dtype, void* stream) {
+  const void* in[6] = {r, w, k, v, a, b};
+  float* const grad[6] = {dr, dw, dk, dv, da, db};
+  const int st = validate_backward(in, state_in, dy, dstate_out, grad, dstate_in, B, T, H, N, dtype);
+  if (st != RWKV7_OK) return st;
+  if (B * H == 0) return RWKV7_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (T == 0) {  // no tokens: the state gradient passes through
+    if (dstate_in && dstate_in != dstate_out) e = rwkv7::launch_state_copy(dstate_out, dstate_in, B * H, s);
+    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+  }
+  rwkv7::BwdCall c{{r, w, k, v, a, b}, state_in, dy, dstate_out, {dr, dw, dk, dv, da, db}, dstate_in, B, T, H,
+                   dtype, s};
+  e = rwkv7::launch_backward(c);
+  if (e == hipErrorNotSupported) return RWKV7_ERR_SHAPE;
+  return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
 
 int rwkv7_tmix_prefill(const void* r, const float* w_raw, const void* k, const void* v, const void* kk,
                        const void* a_lr, const float* ln_w, const float* ln_b, const float* state_in, float* out,

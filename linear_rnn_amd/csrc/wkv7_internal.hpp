@@ -56,6 +56,26 @@ struct TmixCall {
 };
 hipError_t launch_tmix(const TmixCall& c);
 
+// Reverse-mode derivatives of the recurrence: a checkpointing forward pass and
+// a reverse pass over the checkpoints, all gradients float32.
+struct BwdCall {
+  const void* in[6];     // r, w, k, v, a, b in dtype
+  const float* s_in;     // may be null (zero state)
+  const float* dy;
+  const float* ds_out;   // may be null (zero)
+  float* grad[6];        // dr, dw, dk, dv, da, db
+  float* ds_in;          // may be null
+  int64_t B, T, H;
+  int dtype;
+  hipStream_t stream;
+};
+hipError_t launch_backward(const BwdCall& c);
+
+// Device memory cached per (device, stream), shared by the launchers that need
+// scratch: calls on one stream run in order, so they can share it. Grown on
+// demand (synchronising the stream first), never shrunk.
+hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out);
+
 // state_out <- state_in (zeros when state_in is null) for B*H heads.
 hipError_t launch_state_copy(const float* s_in, float* s_out, int64_t units, hipStream_t stream);
 

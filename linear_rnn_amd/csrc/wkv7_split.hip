@@ -570,7 +570,8 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
 
 // ============================================================================ host side
 
-// Record buffer (and, if needed, a carried-state buffer) cached per (device, stream):
+// Device workspace (records of the chunked split prefill, checkpoints of the
+// backward) cached per (device, stream):
 // calls on one stream run in order, so they can share it; calls on different
 // streams get different buffers. Grown on demand, never shrunk.
 struct Workspace {
@@ -580,7 +581,22 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
-hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
+
+// Record-buffer budget per slab: the scan of a slab reads what its prep wrote
+// just before, so a slab that fits the 256 MB last-level (MALL) cache with room
+// to spare is read back without a second HBM round trip.
+size_t slab_budget_bytes() {
+  static const size_t mb = [] {
+    const char* s = std::getenv("RWKV7_SPLIT_SLAB_MB");
+    const long v = s ? std::atol(s) : 0;
+    return v > 0 ? (size_t)v : (size_t)96;
+  }();
+  return mb << 20;
+}
+
+}  // namespace
+
+hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -607,19 +623,6 @@ hipError_t workspace(hipStream_t stream, size_t bytes, void** out) {
   return hipSuccess;
 }
 
-// Record-buffer budget per slab: the scan of a slab reads what its prep wrote
-// just before, so a slab that fits the 256 MB last-level (MALL) cache with room
-// to spare is read back without a second HBM round trip.
-size_t slab_budget_bytes() {
-  static const size_t mb = [] {
-    const char* s = std::getenv("RWKV7_SPLIT_SLAB_MB");
-    const long v = s ? std::atol(s) : 0;
-    return v > 0 ? (size_t)v : (size_t)96;
-  }();
-  return mb << 20;
-}
-
-}  // namespace
 
 hipError_t launch_chunked_split(const WkvCall& c) {
   if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
@@ -637,7 +640,7 @@ hipError_t launch_chunked_split(const WkvCall& c) {
   const size_t rec_bytes = (size_t)(units * slab * kRecBytes);
   const size_t bytes = rec_bytes + (tmp_state ? (size_t)units * kN * kN * 4 : 0);
   void* ws = nullptr;
-  hipError_t e = workspace(c.stream, bytes, &ws);
+  hipError_t e = device_workspace(c.stream, bytes, &ws);
   if (e != hipSuccess) return e;
   unsigned char* rec = static_cast<unsigned char*>(ws);
   float* carry = tmp_state ? reinterpret_cast<float*>(rec + rec_bytes) : static_cast<float*>(c.s_out);

@@ -244,3 +244,12 @@ def make_tmix_inputs(cfg: WkvConfig, step: int | None = None, B: int | None = No
     out["ln_b"] = f64_to_f32(gen[8].standard_normal(H * N) * 0.05)
     out["state_in"] = (gen[9].standard_normal((B, H, N, N)) * 0.1).astype(np.float32) if with_state else None
     return out
+
+
+def make_cotangents(B: int, T: int, H: int, seed: int, with_dstate: bool = True, N: int = HEAD_SIZE) -> dict:
+    """Seeded gradients flowing into the backward: dy ~ N(0, 1) [B, T, H, N] float32 and
+    dstate_out ~ N(0, 0.1^2) [B, H, N, N] float32 (or None). Seeded from SeedSequence([seed, 2])."""
+    g_dy, g_ds = (np.random.Generator(np.random.PCG64(k)) for k in np.random.SeedSequence([seed, 2]).spawn(2))
+    dy = g_dy.standard_normal((B, T, H, N)).astype(np.float32)
+    ds = (g_ds.standard_normal((B, H, N, N)) * 0.1).astype(np.float32) if with_dstate else None
+    return {"dy": dy, "dstate_out": ds}

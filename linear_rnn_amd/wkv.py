@@ -28,7 +28,7 @@ RWKV7_ALGO_CHUNKED = 2
 RWKV7_ALGO_CHUNKED_SPLIT = 3
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
-            "rwkv7_tmix_prefill", "rwkv7_tmix_step", "rwkv7_wkv_strerror")
+            "rwkv7_tmix_prefill", "rwkv7_tmix_step", "rwkv7_wkv_backward", "rwkv7_wkv_strerror")
 
 _lib = None
 _lock = threading.Lock()
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
                 f = getattr(L, name)
                 f.restype = ci
                 f.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp]
+            L.rwkv7_wkv_backward.restype = ci
+            L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [i64] * 4 + [ci, vp]
             L.rwkv7_wkv_strerror.restype = ctypes.c_char_p
             L.rwkv7_wkv_strerror.argtypes = [ci]
             _lib = L
@@ -178,3 +180,23 @@ def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, want_sta
     s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device) if want_state else None
     rwkv7_tmix_prefill(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, s_out, stream=stream)
     return out, s_out
+
+
+def rwkv7_wkv_backward(r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in,
+                       stream=None):
+    """Gradients of the recurrence: dr..db ([B,T,H,64] float32) and dstate_in ([B,H,64,64] float32 or None)."""
+    B, T, H, N = r.shape
+    args = [_ptr(x) for x in (r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in)]
+    _check(lib().rwkv7_wkv_backward(*args, B, T, H, N, _dtype_code(r), _stream(stream)))
+
+
+def wkv7_backward(r, w, k, v, a, b, dy, state_in=None, dstate_out=None, want_dstate=True, stream=None):
+    """Allocate the gradients, run the backward, return dict dr, dw, dk, dv, da, db, dstate_in."""
+    import torch
+    B, T, H, N = r.shape
+    out = {n: torch.empty((B, T, H, N), dtype=torch.float32, device=r.device)
+           for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    out["dstate_in"] = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device) if want_dstate else None
+    rwkv7_wkv_backward(r, w, k, v, a, b, state_in, dy, dstate_out, *(out[n] for n in
+                       ("dr", "dw", "dk", "dv", "da", "db", "dstate_in")), stream=stream)
+    return out

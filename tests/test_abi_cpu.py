@@ -221,3 +221,51 @@ def test_tmix_empty(L):
     p = ptrs(11)
     p[6] = p[7] = None  # ln_w / ln_b optional
     assert tcall(L, p=p, B=0) == OK
+
+
+# ---- the backward: r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in
+
+def bcall(L, p=None, B=2, T=3, H=4, N=64, dtype=BF16):
+    p = ptrs(16) if p is None else p
+    return L.rwkv7_wkv_backward(*(list(p) + [B, T, H, N, dtype, None]))
+
+
+def test_backward_validation(L):
+    assert bcall(L, dtype=3) == E_DTYPE
+    assert bcall(L, N=128) == E_HEAD
+    assert bcall(L, T=-2) == E_SHAPE
+    for i in (0, 1, 2, 3, 4, 5, 7, 9, 10, 11, 12, 13, 14):  # inputs, dy and the six gradients are required
+        p = ptrs(16)
+        p[i] = None
+        assert bcall(L, p=p) == E_NULL, i
+    for i in range(16):
+        p = ptrs(16)
+        p[i] += 8
+        assert bcall(L, p=p) == E_ALIGN, i
+
+
+def test_backward_aliasing(L):
+    for d in range(9, 16):  # each output over each input
+        for s in range(9):
+            p = ptrs(16)
+            p[d] = p[s]
+            if d == 15 and s == 8:
+                continue  # dstate_in == dstate_out is allowed
+            assert bcall(L, p=p) == E_ALIAS, (d, s)
+    p = ptrs(16)
+    p[12] = p[10] + 256  # dv inside dw
+    assert bcall(L, p=p) == E_ALIAS
+    p = ptrs(16)
+    p[15] = p[8] + 1024  # partial overlap of dstate_in and dstate_out
+    assert bcall(L, p=p) == E_ALIAS
+    p = ptrs(16)
+    p[15] = p[8]
+    assert bcall(L, p=p, B=0) == OK
+
+
+def test_backward_empty(L):
+    assert bcall(L, B=0) == OK and bcall(L, H=0) == OK
+    p = ptrs(16)
+    p[6] = p[8] = p[15] = None  # optional states, T == 0: nothing to copy
+    assert bcall(L, p=p, T=0) == OK
+    assert bcall(L, p=[None] * 16, B=0) == OK

@@ -1,0 +1,136 @@
+"""GPU parity of the backward (reverse-mode derivatives of the recurrence) against the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_rnn_amd import wkv
+from linear_rnn_amd.inputs import CONFIGS, f32_to_bf16_bits, make_cotangents, make_inputs
+from tests.gpu_util import TOL_BF16, TOL_F32, rel, sample_units, say, to_dev
+
+pytestmark = pytest.mark.gpu
+GRADS = ("dr", "dw", "dk", "dv", "da", "db")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    wkv.lib()
+    oracle.build(force=False)
+    return t
+
+
+def run(torch, x, ct, state=True, dstate=True):
+    d = to_dev(x)
+    dy = torch.from_numpy(ct["dy"]).cuda()
+    ds = torch.from_numpy(ct["dstate_out"]).cuda() if dstate and ct["dstate_out"] is not None else None
+    g = wkv.wkv7_backward(*(d[n] for n in "rwkvab"), dy, d["state_in"] if state else None, ds)
+    torch.cuda.synchronize()
+    return {n: v.cpu().numpy() for n, v in g.items()}
+
+
+def ref(x, ct, state=True, dstate=True):
+    return oracle.wkv7_backward(*(x[n] for n in "rwkvab"), ct["dy"], state_in=x["state_in"] if state else None,
+                                dstate_out=ct["dstate_out"] if dstate else None)
+
+
+def errors(g, r):
+    return {n: rel(g[n], r[n]) for n in GRADS + ("dstate_in",)}
+
+
+def test_f32_tiny(torch):
+    say("backward f32 tiny")
+    x = make_inputs(CONFIGS[0])
+    ct = make_cotangents(1, 64, 2, seed=1, with_dstate=False)
+    e = errors(run(torch, x, ct, dstate=False), ref(x, ct, dstate=False))
+    say("backward f32 tiny errors", e)
+    assert max(e.values()) <= TOL_F32, e
+
+
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 15, 16, 17, 33, 100])
+def test_f32_ragged_with_states(torch, T):
+    """Every segment and sub-block tail, with state_in and dstate_out."""
+    say("backward f32 T", T)
+    x = make_inputs(CONFIGS[0], B=2, T=T, H=3, seed=500 + T, with_state=True)
+    ct = make_cotangents(2, T, 3, seed=T)
+    e = errors(run(torch, x, ct), ref(x, ct))
+    assert max(e.values()) <= TOL_F32, e
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 5, 1), (2, 64, 3), (3, 250, 4)])
+def test_bf16(torch, B, T, H):
+    say("backward bf16", B, T, H)
+    x = make_inputs(CONFIGS[1], B=B, T=T, H=H, seed=600 + T)
+    ct = make_cotangents(B, T, H, seed=T + 1)
+    e = errors(run(torch, x, ct), ref(x, ct))
+    say("backward bf16 errors", e)
+    assert max(e.values()) <= TOL_BF16, e
+
+
+def test_zero_token_passes_state_gradient(torch):
+    say("backward T == 0")
+    x = make_inputs(CONFIGS[0], B=2, T=0, H=2, seed=3, with_state=True)
+    ct = make_cotangents(2, 0, 2, seed=3)
+    g = run(torch, x, ct)
+    assert np.array_equal(g["dstate_in"], ct["dstate_out"])
+    assert all(g[n].shape == (2, 0, 2, 64) for n in GRADS)
+    g = run(torch, x, ct, dstate=False)
+    assert not np.any(g["dstate_in"])
+
+
+def test_dstate_in_place(torch):
+    """dstate_in may be the dstate_out buffer itself."""
+    say("backward dstate in place")
+    x = make_inputs(CONFIGS[0], B=1, T=40, H=2, seed=8, with_state=True)
+    ct = make_cotangents(1, 40, 2, seed=8)
+    d = to_dev(x)
+    dy = torch.from_numpy(ct["dy"]).cuda()
+    ds = torch.from_numpy(ct["dstate_out"]).cuda()
+    outs = [torch.empty((1, 40, 2, 64), dtype=torch.float32, device="cuda") for _ in GRADS]
+    wkv.rwkv7_wkv_backward(*(d[n] for n in "rwkvab"), d["state_in"], dy, ds, *outs, ds)
+    torch.cuda.synchronize()
+    r = ref(x, ct)
+    assert rel(ds.cpu().numpy(), r["dstate_in"]) <= TOL_F32
+    assert max(rel(o.cpu().numpy(), r[n]) for o, n in zip(outs, GRADS)) <= TOL_F32
+
+
+def test_extreme_decays_and_slots(torch):
+    """w in {0, tiny, 1}, exact zero a/b rows and a_lr of exactly 0 or 1."""
+    say("backward extreme decays")
+    x = make_inputs(CONFIGS[4], B=1, T=70, H=3, seed=21)
+    rng = np.random.default_rng(21)
+    choices = np.array([0.0, 1e-6, 0.5, 1.0], dtype=np.float32)
+    x["w"] = f32_to_bf16_bits(choices[rng.integers(0, 4, size=x["w"].shape)])
+    x["a"][0, 10:14] = 0
+    x["b"][0, 30:33] = 0
+    ct = make_cotangents(1, 70, 3, seed=21)
+    e = errors(run(torch, x, ct), ref(x, ct))
+    assert max(e.values()) <= TOL_BF16, e
+
+
+def test_repeat_is_deterministic(torch):
+    say("backward determinism")
+    x = make_inputs(CONFIGS[1], B=2, T=90, H=4, seed=31)
+    ct = make_cotangents(2, 90, 4, seed=31)
+    g1, g2 = run(torch, x, ct), run(torch, x, ct)
+    assert all(np.array_equal(g1[n], g2[n]) for n in g1)
+
+
+def test_full_size_sampled(torch):
+    """The 0.1B-model prefill shape (B=8, T=4096, H=12, bfloat16) against the oracle on sampled heads."""
+    cfg = CONFIGS[1]
+    say("backward full size", cfg.name)
+    x = make_inputs(cfg)
+    ct = make_cotangents(cfg.B, cfg.T, cfg.H, seed=cfg.seed)
+    g = run(torch, x, ct)
+    units = sample_units(cfg.B, cfg.H, 6, seed=5)
+    worst = {}
+    for (b, h) in units:
+        sl = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in "rwkvab"}
+        s_in = np.ascontiguousarray(x["state_in"][b:b + 1, h:h + 1])
+        r = oracle.wkv7_backward(*(sl[n] for n in "rwkvab"), np.ascontiguousarray(ct["dy"][b:b + 1, :, h:h + 1]),
+                                 state_in=s_in, dstate_out=np.ascontiguousarray(ct["dstate_out"][b:b + 1, h:h + 1]))
+        for n in GRADS:
+            worst[n] = max(worst.get(n, 0.0), rel(g[n][b:b + 1, :, h:h + 1], r[n]))
+        worst["dstate_in"] = max(worst.get("dstate_in", 0.0), rel(g["dstate_in"][b:b + 1, h:h + 1], r["dstate_in"]))
+    say("backward full size errors", worst)
+    assert max(worst.values()) <= TOL_BF16, worst
