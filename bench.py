@@ -7,8 +7,10 @@ One timed step = one whole-sequence prefill of the L12-D768 layer workload
 through the C ABI with the library's default algorithm. The batched decode
 step (D2048 shape: B=512, H=32, 256 consecutive in-place steps) is timed in the
 same run and reported under "decode", and again with the state stored as
-bfloat16 and as float16 ("decode_state_bf16", "decode_state_f16"). Inputs are
-seeded synthetic tensors, resident in HBM before timing starts.
+bfloat16 and as float16 ("decode_state_bf16", "decode_state_f16"); the fused
+time-mix step under "decode_fused"; and the backward (gradients of the
+recurrence) at the prefill shape under "backward". Inputs are seeded synthetic
+tensors, resident in HBM before timing starts.
 
 Prints one JSON line. "value" is prefill tokens*heads per second. "roofline"
 relates the dominant kernel's algorithmic bytes (or flops) per launch to its
@@ -34,6 +36,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense
 PEAK_FP32_VECTOR_TFLOPS = 157.3
 FLOP_REC = 9 * N * N  # per token*head: S a (2N^2), update (5N^2), S r (2N^2)
+# backward per token*head: the forward state rebuilt (S a 2N^2, update 6N^2) and the
+# reverse step (G += dy r^T, dr, dk, dw, dv, G b, da, db: 2N^2 each; G update 4N^2)
+FLOP_BWD = 26 * N * N
 METRIC = "WKV7 tokens*heads/sec (prefill & decode step) + % of HBM/MFMA roofline"
 UNIT = "tokens*heads/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -109,6 +114,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-decode-16bit", action="store_true", help="skip the bf16 / f16 stored-state decode legs")
     ap.add_argument("--no-decode-fused", action="store_true", help="skip the fused time-mix decode leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--backward-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked (fused), 3 chunked (split)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -193,6 +200,9 @@ def main(argv=None):
 
     if not args.no_decode and not args.no_decode_fused:
         out["decode_fused"] = bench_decode_fused(torch, wkv, CONFIGS[3], args)
+
+    if not args.no_backward:
+        out["backward"] = bench_backward(torch, wkv, x, d, s_in, cfg, args)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -295,6 +305,39 @@ def bench_decode_fused(torch, wkv, cfg, args, distinct=32):
                      "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": measured_traffic("wkv7_tmix_kernel:" + cfg.name, src),
                      "kernel": "wkv7_tmix_kernel (TB=1)", "algorithmic_bytes": nbytes},
+    }
+
+
+def bench_backward(torch, wkv, x, d, s_in, cfg, args):
+    """Gradients of the recurrence (dr, dw, dk, dv, da, db, dstate_in) at the prefill shape, from seeded
+    dy and dstate_out; one call = checkpoint forward, reverse pass and (two row blocks) column-sum add."""
+    from linear_rnn_amd.inputs import make_cotangents
+    B, T, H = cfg.B, cfg.T, cfg.H
+    ct = make_cotangents(B, T, H, seed=cfg.seed)
+    dy = torch.from_numpy(ct["dy"]).cuda()
+    ds = torch.from_numpy(ct["dstate_out"]).cuda()
+    grads = [torch.empty((B, T, H, N), dtype=torch.float32, device="cuda") for _ in range(6)]
+    dsi = torch.empty_like(ds)
+
+    def bwd():
+        wkv.rwkv7_wkv_backward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], s_in, dy, ds, *grads, dsi)
+
+    for _ in range(2):
+        bwd()
+    ms = time_region(torch, bwd, args.backward_reps)
+    tok_heads = B * T * H
+    flops = FLOP_BWD * tok_heads
+    # inputs (bf16) and dy read, six float32 gradients written, states in and out
+    nbytes = tok_heads * N * (6 * 2 + 4 + 6 * 4) + 3 * B * H * N * N * 4
+    return {
+        "value": tok_heads / (ms * 1e-3), "unit": UNIT, "ms_per_call": ms, "reps": args.backward_reps,
+        "config": {"workload": "%s: B=%d T=%d H=%d N=%d bf16 inputs, fp32 state_in, dy, dstate_out; fp32 "
+                               "gradients" % (cfg.name, B, T, H, N), "B": B, "T": T, "H": H, "N": N},
+        "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VECTOR_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,
+                     "traffic": None, "kernel": "wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel",
+                     "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                     "hbm_frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
 
 

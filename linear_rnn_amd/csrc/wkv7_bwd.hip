@@ -13,9 +13,14 @@
 //   db_j = sum_i G[i,j] sa_i              G   <- G diag(w) + gb a^T
 // and after token 0, G is dL/dS_0.
 //
-// Two kernels, each one workgroup per head, WAVES waves of 64/WAVES value rows,
-// with the lane layout of the sequential forward (lane = 16*ri + c holds columns
-// 4c..4c+3 of rows {4m + ri} of its wave):
+// The value rows of S (and of G) evolve independently: row i of the update needs
+// only its own row, v_i, dy_i and the key-space vectors. So a head's 64 rows are
+// split over NRB workgroups of WAVES waves, with the lane layout of the
+// sequential forward (lane = 16*ri + c holds columns 4c..4c+3 of rows {4m + ri}
+// of its wave). Only the column gradients couple rows; with two row blocks per
+// head, block 0 writes its column sums to the gradients and block 1 to a
+// workspace copy that a third kernel adds in (a sum of two terms, whatever the
+// order, so results stay deterministic). Splitting pays when heads are few.
 //   1. wkv7_ckpt_kernel runs the recurrence forward and stores the state at the
 //      start of every kSeg-token segment (a float32 checkpoint per segment in
 //      the workspace), with the forward kernels' arithmetic, bit for bit.
@@ -23,6 +28,7 @@
 //      kSub-token sub-block (the last one first) it rebuilds, from the
 //      segment's checkpoint, the kSub + 1 states the sub-block touches into
 //      registers, then takes the sub-block's tokens in reverse.
+//   3. wkv7_colsum_kernel (two row blocks only) adds block 1's column sums.
 // Row sums (dv, gb, and sa in the rebuild) are in-lane partials plus the 16-lane
 // DPP butterfly. Column sums (dr, dk, dw, da, db) are in-lane over the lane's
 // rows, then reduce-scattered over the wave's four lane rows with two
@@ -32,6 +38,8 @@
 // on scheduling. Inputs of a segment are staged through LDS, widened to float32,
 // while the next (earlier) segment's inputs and checkpoint are in flight in
 // registers. Gradients are float32.
+#include <type_traits>
+
 #include "wkv7_device.hpp"
 #include "wkv7_internal.hpp"
 
@@ -39,7 +47,7 @@ namespace rwkv7 {
 namespace {
 
 constexpr int kSub = 8;              // tokens whose states sit in registers at once
-constexpr int kSubs = 2;             // sub-blocks per checkpoint segment
+constexpr int kSubs = 1;             // sub-blocks per checkpoint segment
 constexpr int kSeg = kSub * kSubs;   // tokens between stored checkpoints
 constexpr int kSlots = 7;            // staged per token: r, w, k, v, a, b (dtype), dy (float32)
 constexpr int kDy = 6;
@@ -55,25 +63,26 @@ struct BwdParams {
   float* grad[6];       // dr, dw, dk, dv, da, db: [B, T, H, 64]
   float* ds_in;         // [B, H, 64, 64] or null
   float* ck;            // checkpoints [B*H][nseg][64][64]
+  float* col1;          // column sums of row block 1: [5][B, T, H, 64] (dr, dw, dk, da, db), or null
+  int64_t elems;        // B * T * H * 64
   int64_t T;
   int32_t H;
   int32_t nseg;
 };
 
-// Stages tokens [t0, t0 + kSeg) of the tensors selected by MASK (bits over
+// Stages tokens [t0, t0 + TOK) of the tensors selected by MASK (bits over
 // r, w, k, v, a, b, dy) into lds[token][slot][64] as float32: issue() starts the
 // 16-byte global loads into registers, commit() widens and stores them.
-// Tokens at or past T are neither loaded nor stored.
-template <bool BF16, int THREADS, unsigned MASK>
+template <bool BF16, int THREADS, unsigned MASK, int TOK = kSeg>
 struct SegLoader {
   static constexpr int kEpv = BF16 ? 8 : 4;  // dtype elements per 16-byte load
   static constexpr int kEsz = BF16 ? 2 : 4;
   static constexpr int kPin = kN / kEpv;     // 16-byte pieces per token row of an input
   static constexpr int kNin = __builtin_popcount(MASK & 0x3f);
-  static constexpr int kPer = kSeg * kPin;   // pieces per input tensor and segment
+  static constexpr int kPer = TOK * kPin;    // pieces per input tensor and batch
   static constexpr int kQin = (kNin * kPer + THREADS - 1) / THREADS;
   static constexpr bool kWithDy = (MASK >> kDy) & 1;
-  static constexpr int kQdy = kWithDy ? (kSeg * 16 + THREADS - 1) / THREADS : 0;
+  static constexpr int kQdy = kWithDy ? (TOK * 16 + THREADS - 1) / THREADS : 0;
 
   uint4 qin[kQin];
   uint4 qdy[kQdy > 0 ? kQdy : 1];
@@ -90,55 +99,62 @@ struct SegLoader {
     return s;
   }
 
+  // Every lane loads and stores unconditionally: pieces past the end repeat the
+  // last piece and tokens at or past T repeat token T-1 (T >= 1), so the code
+  // has no divergent branches around the loads, which would make the compiler
+  // serialise them with waits.
   __device__ void issue(const BwdParams& p, int64_t seq_base, int64_t tok_stride, int64_t t0, int tid) {
 #pragma unroll
     for (int q = 0; q < kQin; ++q) {
-      const int e = tid + THREADS * q;
+      const int e = min(tid + THREADS * q, kNin * kPer - 1);
       const int n = e / kPer, rem = e % kPer;
       const int tok = rem / kPin, piece = rem % kPin;
-      if (e < kNin * kPer && t0 + tok < p.T) {
-        const int slot = slot_of(n);
-        const char* src = nullptr;
+      const int64_t t = min(t0 + tok, p.T - 1);
+      const int slot = slot_of(n);
+      const char* src = static_cast<const char*>(p.in[0]);
 #pragma unroll
-        for (int x = 0; x < 6; ++x)
-          if (slot == x) src = static_cast<const char*>(p.in[x]);  // constant indices keep p in SGPRs
-        qin[q] = *reinterpret_cast<const uint4*>(src + (seq_base + (t0 + tok) * tok_stride + piece * kEpv) * kEsz);
-      }
+      for (int x = 1; x < 6; ++x)
+        if (slot == x) src = static_cast<const char*>(p.in[x]);  // constant indices keep p in SGPRs
+      qin[q] = *reinterpret_cast<const uint4*>(src + (seq_base + t * tok_stride + piece * kEpv) * kEsz);
     }
 #pragma unroll
     for (int q = 0; q < kQdy; ++q) {
-      const int e = tid + THREADS * q;
+      const int e = min(tid + THREADS * q, TOK * 16 - 1);
       const int tok = e / 16, piece = e % 16;
-      if (e < kSeg * 16 && t0 + tok < p.T)
-        qdy[q] = *reinterpret_cast<const uint4*>(p.dy + seq_base + (t0 + tok) * tok_stride + piece * 4);
+      const int64_t t = min(t0 + tok, p.T - 1);
+      qdy[q] = *reinterpret_cast<const uint4*>(p.dy + seq_base + t * tok_stride + piece * 4);
     }
   }
 
-  __device__ void commit(float (*lds)[kSlots][kN], int64_t T, int64_t t0, int tid) const {
+  __device__ void commit(float (*lds)[kSlots][kN], int tid) const {
 #pragma unroll
     for (int q = 0; q < kQin; ++q) {
-      const int e = tid + THREADS * q;
+      const int e = min(tid + THREADS * q, kNin * kPer - 1);
       const int n = e / kPer, rem = e % kPer;
       const int tok = rem / kPin, piece = rem % kPin;
-      if (e < kNin * kPer && t0 + tok < T) {
-        float* dst = &lds[tok][slot_of(n)][piece * kEpv];
-        const uint4 v = qin[q];
-        if constexpr (BF16) {
-          reinterpret_cast<float4*>(dst)[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-          reinterpret_cast<float4*>(dst)[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
-        } else {
-          *reinterpret_cast<uint4*>(dst) = v;
-        }
+      float* dst = &lds[tok][slot_of(n)][piece * kEpv];
+      const uint4 v = qin[q];
+      if constexpr (BF16) {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+        reinterpret_cast<float4*>(dst)[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+      } else {
+        *reinterpret_cast<uint4*>(dst) = v;
       }
     }
 #pragma unroll
     for (int q = 0; q < kQdy; ++q) {
-      const int e = tid + THREADS * q;
+      const int e = min(tid + THREADS * q, TOK * 16 - 1);
       const int tok = e / 16, piece = e % 16;
-      if (e < kSeg * 16 && t0 + tok < T) *reinterpret_cast<uint4*>(&lds[tok][kDy][piece * 4]) = qdy[q];
+      *reinterpret_cast<uint4*>(&lds[tok][kDy][piece * 4]) = qdy[q];
     }
   }
 };
+
+// Wait for every outstanding global load of this wave (s_waitcnt vmcnt(0)).
+// Placed after a loop's initial state load: otherwise the loop-carried state
+// looks possibly in flight at the loop header, and the compiler waits for all
+// loads (the prefetch of the next batch included) at every iteration.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 __device__ __forceinline__ float dot4(const float4 s, const float4 x) {
   return fmaf(s.w, x.w, fmaf(s.z, x.z, fmaf(s.y, x.y, s.x * x.x)));
@@ -187,93 +203,158 @@ __device__ __forceinline__ void column_reduce(const float (&X)[kNcol][4], float 
   }
 }
 
+// The key-space vectors at the lane's four columns, and v and dy at its rows.
+template <int MR>
+struct TokIn {
+  float4 r4, w4, k4, a4, b4;
+  float vm[MR], dym[MR];
+};
+
+// Read token j of the staged segment; rowl = the lane's first row (row0 + ri).
+// BWD adds r and dy, which only the reverse step reads.
+template <int MR, bool BWD>
+__device__ __forceinline__ void load_tok(const float (*lds)[kSlots][kN], int j, int c, int rowl, TokIn<MR>& t) {
+  if constexpr (BWD) t.r4 = *reinterpret_cast<const float4*>(&lds[j][kR][4 * c]);
+  t.w4 = *reinterpret_cast<const float4*>(&lds[j][kW][4 * c]);
+  t.k4 = *reinterpret_cast<const float4*>(&lds[j][kK][4 * c]);
+  t.a4 = *reinterpret_cast<const float4*>(&lds[j][kA][4 * c]);
+  t.b4 = *reinterpret_cast<const float4*>(&lds[j][kB][4 * c]);
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    t.vm[m] = lds[j][kV][rowl + 4 * m];
+    if constexpr (BWD) t.dym[m] = lds[j][kDy][rowl + 4 * m];
+  }
+}
+
 // ---------------------------------------------------------------- checkpoint forward
 
-template <bool BF16, int WAVES>
+// Inputs are staged kCkBatch tokens at a time (several checkpoint segments), so
+// that the global loads for the next batch have a whole batch of compute to
+// arrive in.
+constexpr int kCkBatch = 4 * kSeg;
+
+template <bool BF16, int WAVES, int NRB>
 __global__ __launch_bounds__(kWave* WAVES) void wkv7_ckpt_kernel(BwdParams p) {
   constexpr int kThreads = kWave * WAVES;
-  constexpr int kRpw = kN / WAVES;
+  constexpr int kRpw = kN / (NRB * WAVES);
   constexpr int kMr = kRpw / 4;
-  using Ld = SegLoader<BF16, kThreads, (1u << kW) | (1u << kK) | (1u << kV) | (1u << kA) | (1u << kB)>;
-  __shared__ __align__(16) float lds[kSeg][kSlots][kN];
+  static_assert(kRpw % 4 == 0, "bad tiling");
+  using Ld = SegLoader<BF16, kThreads, (1u << kW) | (1u << kK) | (1u << kV) | (1u << kA) | (1u << kB), kCkBatch>;
+  __shared__ __align__(16) float lds[kCkBatch][kSlots][kN];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int c = lane & 15;
   const int ri = lane >> 4;
-  const int64_t unit = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t logical = xcd_swizzle(blockIdx.x, gridDim.x);  // a head's row blocks share an XCD
+  const int64_t unit = logical / NRB;
+  const int rb = logical % NRB;
   const int64_t bb = unit / p.H, hh = unit % p.H;
   const int64_t T = p.T;
   const int64_t tok_stride = (int64_t)p.H * kN;
   const int64_t seq_base = (bb * T * p.H + hh) * kN;
-  const int row0 = wave * kRpw;
+  const int row0 = (rb * WAVES + wave) * kRpw;
+  const int rowl = row0 + ri;
 
   float4 S[kMr];
 #pragma unroll
-  for (int m = 0; m < kMr; ++m) {
-    const int row = row0 + 4 * m + ri;
-    S[m] = p.s_in ? *reinterpret_cast<const float4*>(p.s_in + (unit * kN + row) * kN + 4 * c)
+  for (int m = 0; m < kMr; ++m)
+    S[m] = p.s_in ? *reinterpret_cast<const float4*>(p.s_in + (unit * kN + rowl + 4 * m) * kN + 4 * c)
                   : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  vm_wait_all();
 
   Ld ld;
   ld.issue(p, seq_base, tok_stride, 0, tid);
-  for (int seg = 0; seg < p.nseg; ++seg) {
-    const int64_t t0 = (int64_t)seg * kSeg;
-    const int n = (T - t0 < kSeg) ? (int)(T - t0) : kSeg;
-    float* ck = p.ck + (unit * p.nseg + seg) * (int64_t)(kN * kN);
-#pragma unroll
-    for (int m = 0; m < kMr; ++m)
-      *reinterpret_cast<float4*>(ck + (row0 + 4 * m + ri) * kN + 4 * c) = S[m];
-    __syncthreads();  // every wave is done with the previous segment's LDS
-    ld.commit(lds, T, t0, tid);
+  for (int64_t tb = 0; tb < T; tb += kCkBatch) {
+    __syncthreads();  // every wave is done with the previous batch's LDS
+    ld.commit(lds, tid);
     __syncthreads();
-    if (seg + 1 < p.nseg) ld.issue(p, seq_base, tok_stride, t0 + kSeg, tid);
-    for (int j = 0; j < n; ++j) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&lds[j][kW][4 * c]);
-      const float4 k4 = *reinterpret_cast<const float4*>(&lds[j][kK][4 * c]);
-      const float4 a4 = *reinterpret_cast<const float4*>(&lds[j][kA][4 * c]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&lds[j][kB][4 * c]);
-      float vm[kMr], sa[kMr];
+    if (tb + kCkBatch < T) ld.issue(p, seq_base, tok_stride, tb + kCkBatch, tid);
+    // The batch's checkpoints are kept in registers and stored after its last
+    // token, so the token loop holds no global stores (a store in it makes the
+    // compiler wait for the in-flight input loads before entering it).
+    float4 ckr[kCkBatch / kSeg][kMr];
 #pragma unroll
-      for (int m = 0; m < kMr; ++m) vm[m] = lds[j][kV][row0 + 4 * m + ri];
-      fwd_token<kMr>(S, sa, w4, k4, a4, b4, vm);
+    for (int q = 0; q < kCkBatch / kSeg; ++q) {
+      const int js = q * kSeg;
+      if (tb + js < T) {
+        const int n = (T - tb - js < kSeg) ? (int)(T - tb - js) : kSeg;
+#pragma unroll
+        for (int m = 0; m < kMr; ++m) ckr[q][m] = S[m];
+        float sa[kMr];
+        if (n == kSeg) {  // whole segment: the next token's reads are in flight during this one
+          TokIn<kMr> cur, nxt;
+          load_tok<kMr, false>(lds, js, c, rowl, cur);
+#pragma unroll
+          for (int j = 0; j < kSeg; ++j) {
+            if (j + 1 < kSeg) load_tok<kMr, false>(lds, js + j + 1, c, rowl, nxt);
+            fwd_token<kMr>(S, sa, cur.w4, cur.k4, cur.a4, cur.b4, cur.vm);
+            if (j + 1 < kSeg) cur = nxt;
+          }
+        } else {
+          for (int j = 0; j < n; ++j) {
+            TokIn<kMr> cur;
+            load_tok<kMr, false>(lds, js + j, c, rowl, cur);
+            fwd_token<kMr>(S, sa, cur.w4, cur.k4, cur.a4, cur.b4, cur.vm);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kCkBatch / kSeg; ++q) {
+      if (tb + q * kSeg < T) {
+        float* ck = p.ck + (unit * p.nseg + (tb + q * kSeg) / kSeg) * (int64_t)(kN * kN);
+#pragma unroll
+        for (int m = 0; m < kMr; ++m) *reinterpret_cast<float4*>(ck + (rowl + 4 * m) * kN + 4 * c) = ckr[q][m];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- reverse pass
 
-template <bool BF16, int WAVES>
+template <bool BF16, int WAVES, int NRB>
 __global__ __launch_bounds__(kWave* WAVES) void wkv7_bwd_kernel(BwdParams p) {
   constexpr int kThreads = kWave * WAVES;
-  constexpr int kRpw = kN / WAVES;
+  constexpr int kRpb = kN / NRB;  // rows per workgroup
+  constexpr int kRpw = kRpb / WAVES;
   constexpr int kMr = kRpw / 4;
+  static_assert(kRpw % 4 == 0, "bad tiling");
   using Ld = SegLoader<BF16, kThreads, 0x7fu>;
   __shared__ __align__(16) float lds[kSeg][kSlots][kN];
   __shared__ __align__(16) float part[kSub][kNcol][WAVES][kN];  // per-wave column sums
-  __shared__ __align__(16) float dv_lds[kSub][kN];
+  __shared__ __align__(16) float dv_lds[kSub][kRpb];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int c = lane & 15;
   const int ri = lane >> 4;
-  const int64_t unit = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int64_t unit = logical / NRB;
+  const int rb = logical % NRB;
   const int64_t bb = unit / p.H, hh = unit % p.H;
   const int64_t T = p.T;
   const int64_t tok_stride = (int64_t)p.H * kN;
   const int64_t seq_base = (bb * T * p.H + hh) * kN;
-  const int row0 = wave * kRpw;
+  const int rbase = rb * kRpb;             // first row of this workgroup
+  const int row0 = rbase + wave * kRpw;    // first row of this wave
+  const int rowl = row0 + ri;              // the lane's first row
+  // column sums of this row block go to the gradients (block 0) or to the workspace copy (block 1)
+  float* colout[kNcol];
+  colout[kGr] = rb == 0 ? p.grad[0] : p.col1 + 0 * p.elems;
+  colout[kGw] = rb == 0 ? p.grad[1] : p.col1 + 1 * p.elems;
+  colout[kGk] = rb == 0 ? p.grad[2] : p.col1 + 2 * p.elems;
+  colout[kGa] = rb == 0 ? p.grad[4] : p.col1 + 3 * p.elems;
+  colout[kGb] = rb == 0 ? p.grad[5] : p.col1 + 4 * p.elems;
 
   float4 G[kMr];
 #pragma unroll
-  for (int m = 0; m < kMr; ++m) {
-    const int row = row0 + 4 * m + ri;
-    G[m] = p.ds_out ? *reinterpret_cast<const float4*>(p.ds_out + (unit * kN + row) * kN + 4 * c)
+  for (int m = 0; m < kMr; ++m)
+    G[m] = p.ds_out ? *reinterpret_cast<const float4*>(p.ds_out + (unit * kN + rowl + 4 * m) * kN + 4 * c)
                     : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  vm_wait_all();
 
   const float* ck_base = p.ck + unit * p.nseg * (int64_t)(kN * kN);
   Ld ld;
@@ -282,7 +363,97 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_bwd_kernel(BwdParams p) {
     ld.issue(p, seq_base, tok_stride, (int64_t)seg * kSeg, tid);
     const float* ck = ck_base + (int64_t)seg * (kN * kN);
 #pragma unroll
-    for (int m = 0; m < kMr; ++m) ckq[m] = *reinterpret_cast<const float4*>(ck + (row0 + 4 * m + ri) * kN + 4 * c);
+    for (int m = 0; m < kMr; ++m) ckq[m] = *reinterpret_cast<const float4*>(ck + (rowl + 4 * m) * kN + 4 * c);
+  };
+
+  // One token in reverse: G (dL/dS_t from later tokens) takes y's contribution,
+  // the token's gradients are formed, and G moves to dL/dS_{t-1}.
+  auto bwd_token = [&](int u, const TokIn<kMr>& t, const float4(&Sp)[kMr], const float4(&Sc)[kMr],
+                       const float(&sa)[kMr]) {
+    // G += dy r^T
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      G[m].x = fmaf(t.dym[m], t.r4.x, G[m].x);
+      G[m].y = fmaf(t.dym[m], t.r4.y, G[m].y);
+      G[m].z = fmaf(t.dym[m], t.r4.z, G[m].z);
+      G[m].w = fmaf(t.dym[m], t.r4.w, G[m].w);
+    }
+    // row sums: dv = G k, gb = G b
+    float dvr[kMr], gb[kMr];
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      dvr[m] = dot4(G[m], t.k4);
+      gb[m] = dot4(G[m], t.b4);
+    }
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      dvr[m] = row16_sum(dvr[m]);
+      gb[m] = row16_sum(gb[m]);
+    }
+    // column partials over the lane's rows
+    float X[kNcol][4];
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      const float sc[4] = {Sc[m].x, Sc[m].y, Sc[m].z, Sc[m].w};
+      const float sp[4] = {Sp[m].x, Sp[m].y, Sp[m].z, Sp[m].w};
+      const float gg[4] = {G[m].x, G[m].y, G[m].z, G[m].w};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        X[kGr][cc] = m == 0 ? sc[cc] * t.dym[m] : fmaf(sc[cc], t.dym[m], X[kGr][cc]);
+        X[kGk][cc] = m == 0 ? gg[cc] * t.vm[m] : fmaf(gg[cc], t.vm[m], X[kGk][cc]);
+        X[kGw][cc] = m == 0 ? sp[cc] * gg[cc] : fmaf(sp[cc], gg[cc], X[kGw][cc]);
+        X[kGa][cc] = m == 0 ? sp[cc] * gb[m] : fmaf(sp[cc], gb[m], X[kGa][cc]);
+        X[kGb][cc] = m == 0 ? gg[cc] * sa[m] : fmaf(gg[cc], sa[m], X[kGb][cc]);
+      }
+    }
+    float colsum[kNcol];
+    column_reduce(X, colsum);
+#pragma unroll
+    for (int x = 0; x < kNcol; ++x) part[u][x][wave][4 * c + ri] = colsum[x];
+    float dvo = dvr[0];
+#pragma unroll
+    for (int m = 1; m < kMr; ++m) dvo = (c == m) ? dvr[m] : dvo;
+    if (c < kMr) dv_lds[u][row0 - rbase + 4 * c + ri] = dvo;
+    // G <- G diag(w) + gb a^T
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) {
+      G[m].x = fmaf(G[m].x, t.w4.x, gb[m] * t.a4.x);
+      G[m].y = fmaf(G[m].y, t.w4.y, gb[m] * t.a4.y);
+      G[m].z = fmaf(G[m].z, t.w4.z, gb[m] * t.a4.z);
+      G[m].w = fmaf(G[m].w, t.w4.w, gb[m] * t.a4.w);
+    }
+  };
+
+  // Tokens j0 .. j0+cnt-1 of the staged segment, whose first state is S0. A
+  // whole sub-block (FULL) runs without per-token guards, with each token's LDS
+  // reads issued during the previous token.
+  auto sub_block = [&](auto full, int j0, int cnt, const float4(&S0)[kMr]) {
+    constexpr bool kFull = decltype(full)::value;
+    float4 Sv[kSub + 1][kMr];  // Sv[u] = the state before token j0 + u
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) Sv[0][m] = S0[m];
+    float sav[kSub][kMr];
+    TokIn<kMr> cur, nxt;
+    load_tok<kMr, false>(lds, j0, c, rowl, cur);
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      if (kFull || u < cnt) {
+        if (u + 1 < kSub && (kFull || u + 1 < cnt)) load_tok<kMr, false>(lds, j0 + u + 1, c, rowl, nxt);
+#pragma unroll
+        for (int m = 0; m < kMr; ++m) Sv[u + 1][m] = Sv[u][m];
+        fwd_token<kMr>(Sv[u + 1], sav[u], cur.w4, cur.k4, cur.a4, cur.b4, cur.vm);
+        if (u + 1 < kSub) cur = nxt;
+      }
+    }
+    load_tok<kMr, true>(lds, j0 + (kFull ? kSub : cnt) - 1, c, rowl, cur);
+#pragma unroll
+    for (int u = kSub - 1; u >= 0; --u) {
+      if (kFull || u < cnt) {
+        if (u > 0) load_tok<kMr, true>(lds, j0 + u - 1, c, rowl, nxt);
+        bwd_token(u, cur, Sv[u], Sv[u + 1], sav[u]);
+        if (u > 0) cur = nxt;
+      }
+    }
   };
 
   issue(p.nseg - 1);
@@ -290,7 +461,7 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_bwd_kernel(BwdParams p) {
     const int64_t t0 = (int64_t)seg * kSeg;
     const int n = (T - t0 < kSeg) ? (int)(T - t0) : kSeg;
     __syncthreads();  // every wave is done with the previous segment's inputs
-    ld.commit(lds, T, t0, tid);
+    ld.commit(lds, tid);
     float4 Sck[kMr];
 #pragma unroll
     for (int m = 0; m < kMr; ++m) Sck[m] = ckq[m];
@@ -298,117 +469,22 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_bwd_kernel(BwdParams p) {
     if (seg > 0) issue(seg - 1);
 
     for (int sb = (n - 1) / kSub; sb >= 0; --sb) {
-      const int j0 = sb * kSub;                             // first token of the sub-block in the segment
-      const int cnt = (n - j0 < kSub) ? n - j0 : kSub;      // its tokens
+      const int j0 = sb * kSub;                          // first token of the sub-block in the segment
+      const int cnt = (n - j0 < kSub) ? n - j0 : kSub;   // its tokens
       // the state before token j0 of the segment
-      float4 Sv[kSub + 1][kMr];
+      float4 S0[kMr];
 #pragma unroll
-      for (int m = 0; m < kMr; ++m) Sv[0][m] = Sck[m];
+      for (int m = 0; m < kMr; ++m) S0[m] = Sck[m];
       for (int j = 0; j < j0; ++j) {
-        const float4 w4 = *reinterpret_cast<const float4*>(&lds[j][kW][4 * c]);
-        const float4 k4 = *reinterpret_cast<const float4*>(&lds[j][kK][4 * c]);
-        const float4 a4 = *reinterpret_cast<const float4*>(&lds[j][kA][4 * c]);
-        const float4 b4 = *reinterpret_cast<const float4*>(&lds[j][kB][4 * c]);
-        float vm[kMr], sa[kMr];
-#pragma unroll
-        for (int m = 0; m < kMr; ++m) vm[m] = lds[j][kV][row0 + 4 * m + ri];
-        fwd_token<kMr>(Sv[0], sa, w4, k4, a4, b4, vm);
+        TokIn<kMr> t;
+        load_tok<kMr, false>(lds, j, c, rowl, t);
+        float sa[kMr];
+        fwd_token<kMr>(S0, sa, t.w4, t.k4, t.a4, t.b4, t.vm);
       }
-      // rebuild the sub-block's states: Sv[u] is the state before token j0 + u
-      float sav[kSub][kMr];
-#pragma unroll
-      for (int u = 0; u < kSub; ++u) {
-        if (u < cnt) {
-          const int j = j0 + u;
-          const float4 w4 = *reinterpret_cast<const float4*>(&lds[j][kW][4 * c]);
-          const float4 k4 = *reinterpret_cast<const float4*>(&lds[j][kK][4 * c]);
-          const float4 a4 = *reinterpret_cast<const float4*>(&lds[j][kA][4 * c]);
-          const float4 b4 = *reinterpret_cast<const float4*>(&lds[j][kB][4 * c]);
-          float vm[kMr];
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) vm[m] = lds[j][kV][row0 + 4 * m + ri];
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) Sv[u + 1][m] = Sv[u][m];
-          fwd_token<kMr>(Sv[u + 1], sav[u], w4, k4, a4, b4, vm);
-        }
-      }
-      // the sub-block's tokens in reverse
-#pragma unroll
-      for (int u = kSub - 1; u >= 0; --u) {
-        if (u < cnt) {
-          const int j = j0 + u;
-          const float4 r4 = *reinterpret_cast<const float4*>(&lds[j][kR][4 * c]);
-          const float4 w4 = *reinterpret_cast<const float4*>(&lds[j][kW][4 * c]);
-          const float4 k4 = *reinterpret_cast<const float4*>(&lds[j][kK][4 * c]);
-          const float4 a4 = *reinterpret_cast<const float4*>(&lds[j][kA][4 * c]);
-          const float4 b4 = *reinterpret_cast<const float4*>(&lds[j][kB][4 * c]);
-          float vm[kMr], dym[kMr];
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) {
-            vm[m] = lds[j][kV][row0 + 4 * m + ri];
-            dym[m] = lds[j][kDy][row0 + 4 * m + ri];
-          }
-          const float4(&Sp)[kMr] = Sv[u];
-          const float4(&Sc)[kMr] = Sv[u + 1];
-          // G += dy r^T
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) {
-            G[m].x = fmaf(dym[m], r4.x, G[m].x);
-            G[m].y = fmaf(dym[m], r4.y, G[m].y);
-            G[m].z = fmaf(dym[m], r4.z, G[m].z);
-            G[m].w = fmaf(dym[m], r4.w, G[m].w);
-          }
-          // row sums: dv = G k, gb = G b
-          float dvr[kMr], gb[kMr];
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) {
-            dvr[m] = dot4(G[m], k4);
-            gb[m] = dot4(G[m], b4);
-          }
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) {
-            dvr[m] = row16_sum(dvr[m]);
-            gb[m] = row16_sum(gb[m]);
-          }
-          // column partials over the lane's rows
-          float X[kNcol][4];
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-            for (int x = 0; x < kNcol; ++x) X[x][cc] = 0.f;
-          }
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) {
-            const float sc[4] = {Sc[m].x, Sc[m].y, Sc[m].z, Sc[m].w};
-            const float sp[4] = {Sp[m].x, Sp[m].y, Sp[m].z, Sp[m].w};
-            const float gg[4] = {G[m].x, G[m].y, G[m].z, G[m].w};
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-              X[kGr][cc] = fmaf(sc[cc], dym[m], X[kGr][cc]);
-              X[kGk][cc] = fmaf(gg[cc], vm[m], X[kGk][cc]);
-              X[kGw][cc] = fmaf(sp[cc], gg[cc], X[kGw][cc]);
-              X[kGa][cc] = fmaf(sp[cc], gb[m], X[kGa][cc]);
-              X[kGb][cc] = fmaf(gg[cc], sav[u][m], X[kGb][cc]);
-            }
-          }
-          float colsum[kNcol];
-          column_reduce(X, colsum);
-#pragma unroll
-          for (int x = 0; x < kNcol; ++x) part[u][x][wave][4 * c + ri] = colsum[x];
-          float dvo = dvr[0];
-#pragma unroll
-          for (int m = 1; m < kMr; ++m) dvo = (c == m) ? dvr[m] : dvo;
-          if (c < kMr) dv_lds[u][row0 + 4 * c + ri] = dvo;
-          // G <- G diag(w) + gb a^T
-#pragma unroll
-          for (int m = 0; m < kMr; ++m) {
-            G[m].x = fmaf(G[m].x, w4.x, gb[m] * a4.x);
-            G[m].y = fmaf(G[m].y, w4.y, gb[m] * a4.y);
-            G[m].z = fmaf(G[m].z, w4.z, gb[m] * a4.z);
-            G[m].w = fmaf(G[m].w, w4.w, gb[m] * a4.w);
-          }
-        }
-      }
+      if (cnt == kSub)
+        sub_block(std::true_type{}, j0, kSub, S0);
+      else
+        sub_block(std::false_type{}, j0, cnt, S0);
       __syncthreads();
       // sum the waves' partials in wave order and write the sub-block's gradients
       const int64_t tbase = seq_base + (t0 + j0) * tok_stride;
@@ -417,13 +493,14 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_bwd_kernel(BwdParams p) {
         float s = part[u][x][0][col];
 #pragma unroll
         for (int wv = 1; wv < WAVES; ++wv) s += part[u][x][wv][col];
-        // partial slots -> gradient tensors dr, dk, dw, da, db
-        float* dst = x == kGr ? p.grad[0] : x == kGk ? p.grad[2] : x == kGw ? p.grad[1] : x == kGa ? p.grad[4] : p.grad[5];
+        float* dst = colout[0];
+#pragma unroll
+        for (int y = 1; y < kNcol; ++y) dst = x == y ? colout[y] : dst;
         dst[tbase + u * tok_stride + col] = s;
       }
-      for (int e = tid; e < cnt * kN; e += kThreads) {
-        const int u = e / kN, col = e % kN;
-        p.grad[3][tbase + u * tok_stride + col] = dv_lds[u][col];
+      for (int e = tid; e < cnt * kRpb; e += kThreads) {
+        const int u = e / kRpb, row = e % kRpb;
+        p.grad[3][tbase + u * tok_stride + rbase + row] = dv_lds[u][row];
       }
       __syncthreads();  // the partial buffers are free again
     }
@@ -431,21 +508,41 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_bwd_kernel(BwdParams p) {
 
   if (p.ds_in) {
 #pragma unroll
-    for (int m = 0; m < kMr; ++m) {
-      const int row = row0 + 4 * m + ri;
-      *reinterpret_cast<float4*>(p.ds_in + (unit * kN + row) * kN + 4 * c) = G[m];
+    for (int m = 0; m < kMr; ++m)
+      *reinterpret_cast<float4*>(p.ds_in + (unit * kN + rowl + 4 * m) * kN + 4 * c) = G[m];
+  }
+}
+
+// grad[0,1,2,4,5] += the five column sums of row block 1 (float4 per thread).
+__global__ __launch_bounds__(256) void wkv7_colsum_kernel(BwdParams p) {
+  const int64_t n4 = p.elems / 4;
+  const float4* src = reinterpret_cast<const float4*>(p.col1);
+  float4* dst[kNcol] = {reinterpret_cast<float4*>(p.grad[0]), reinterpret_cast<float4*>(p.grad[1]),
+                        reinterpret_cast<float4*>(p.grad[2]), reinterpret_cast<float4*>(p.grad[4]),
+                        reinterpret_cast<float4*>(p.grad[5])};
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+#pragma unroll
+    for (int x = 0; x < kNcol; ++x) {
+      const float4 a = dst[x][i], b = src[x * n4 + i];
+      dst[x][i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
     }
   }
 }
 
-template <bool BF16, int WAVES>
+template <bool BF16, int CK_WAVES, int CK_NRB, int WAVES, int NRB>
 hipError_t launch_cfg(BwdParams p, int64_t units, hipStream_t stream) {
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_ckpt_kernel<BF16, WAVES>),
-                                 dim3((uint32_t)units), dim3(kWave * WAVES), args, 0, stream);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_ckpt_kernel<BF16, CK_WAVES, CK_NRB>),
+                                 dim3((uint32_t)(units * CK_NRB)), dim3(kWave * CK_WAVES), args, 0, stream);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_bwd_kernel<BF16, WAVES>), dim3((uint32_t)units),
-                         dim3(kWave * WAVES), args, 0, stream);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_bwd_kernel<BF16, WAVES, NRB>),
+                      dim3((uint32_t)(units * NRB)), dim3(kWave * WAVES), args, 0, stream);
+  if (e != hipSuccess || NRB == 1) return e;
+  const int64_t n4 = p.elems / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  blocks = blocks > 8192 ? 8192 : blocks;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_colsum_kernel), dim3((uint32_t)blocks), dim3(256),
+                         args, 0, stream);
 }
 
 }  // namespace
@@ -454,8 +551,13 @@ hipError_t launch_backward(const BwdCall& c) {
   const int64_t units = c.B * c.H;
   const int64_t nseg = (c.T + kSeg - 1) / kSeg;
   if (nseg > INT32_MAX) return hipErrorNotSupported;
+  // Two row blocks per head while that still fits the chip's 256 compute units.
+  const bool split = units <= 128;
+  const int64_t elems = units * c.T * kN;
+  const size_t ck_bytes = (size_t)(units * nseg) * kN * kN * sizeof(float);
+  const size_t col_bytes = split ? (size_t)elems * kNcol * sizeof(float) : 0;
   void* ws = nullptr;
-  hipError_t e = device_workspace(c.stream, (size_t)(units * nseg) * kN * kN * sizeof(float), &ws);
+  hipError_t e = device_workspace(c.stream, ck_bytes + col_bytes, &ws);
   if (e != hipSuccess) return e;
   BwdParams p{};
   for (int i = 0; i < 6; ++i) p.in[i] = c.in[i];
@@ -465,10 +567,16 @@ hipError_t launch_backward(const BwdCall& c) {
   for (int i = 0; i < 6; ++i) p.grad[i] = c.grad[i];
   p.ds_in = c.ds_in;
   p.ck = static_cast<float*>(ws);
+  p.col1 = split ? reinterpret_cast<float*>(static_cast<char*>(ws) + ck_bytes) : nullptr;
+  p.elems = elems;
   p.T = c.T;
   p.H = (int32_t)c.H;
   p.nseg = (int32_t)nseg;
-  return c.dtype == 1 ? launch_cfg<true, 8>(p, units, c.stream) : launch_cfg<false, 8>(p, units, c.stream);
+  // checkpoint forward: 8 waves of 4 rows, two row blocks per head; reverse pass:
+  // 8 waves of 4 rows (two row blocks) or of 8 rows (one row block)
+  if (c.dtype == 1)
+    return split ? launch_cfg<true, 8, 2, 8, 2>(p, units, c.stream) : launch_cfg<true, 8, 2, 8, 1>(p, units, c.stream);
+  return split ? launch_cfg<false, 8, 2, 8, 2>(p, units, c.stream) : launch_cfg<false, 8, 2, 8, 1>(p, units, c.stream);
 }
 
 }  // namespace rwkv7

@@ -66,6 +66,19 @@ def test_bf16(torch, B, T, H):
     assert max(e.values()) <= TOL_BF16, e
 
 
+def test_many_heads_single_row_block(torch):
+    """More than 128 heads: one workgroup per head (no row split), all rows' column sums in LDS."""
+    say("backward 140 heads")
+    x = make_inputs(CONFIGS[1], B=2, T=21, H=70, seed=77)
+    ct = make_cotangents(2, 21, 70, seed=77)
+    e = errors(run(torch, x, ct), ref(x, ct))
+    assert max(e.values()) <= TOL_BF16, e
+    x = make_inputs(CONFIGS[0], B=2, T=13, H=70, seed=78, with_state=True)
+    ct = make_cotangents(2, 13, 70, seed=78)
+    e = errors(run(torch, x, ct), ref(x, ct))
+    assert max(e.values()) <= TOL_F32, e
+
+
 def test_zero_token_passes_state_gradient(torch):
     say("backward T == 0")
     x = make_inputs(CONFIGS[0], B=2, T=0, H=2, seed=3, with_state=True)
