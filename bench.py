@@ -335,7 +335,10 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args):
                                "gradients" % (cfg.name, B, T, H, N), "B": B, "T": T, "H": H, "N": N},
         "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VECTOR_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,
-                     "traffic": None, "kernel": "wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel",
+                     "traffic": measured_traffic("wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel:" + cfg.name,
+                                                 ["linear_rnn_amd/csrc/wkv7_bwd.hip",
+                                                  "linear_rnn_amd/csrc/wkv7_device.hpp"]),
+                     "kernel": "wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel",
                      "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                      "hbm_frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
