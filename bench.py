@@ -115,6 +115,8 @@ def main(argv=None):
     ap.add_argument("--no-decode-16bit", action="store_true", help="skip the bf16 / f16 stored-state decode legs")
     ap.add_argument("--no-decode-fused", action="store_true", help="skip the fused time-mix decode leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer prompt-then-steps leg")
+    ap.add_argument("--stack-steps", type=int, default=32)
     ap.add_argument("--backward-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 sequential, 2 chunked (fused), 3 chunked (split)")
@@ -203,6 +205,9 @@ def main(argv=None):
 
     if not args.no_backward:
         out["backward"] = bench_backward(torch, wkv, x, d, s_in, cfg, args)
+
+    if not args.no_stack:
+        out["stack"] = bench_stack(torch, wkv, args)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -341,6 +346,66 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args):
                      "kernel": "wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel",
                      "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                      "hbm_frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+
+
+def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
+    """The hybrid mode end to end on a 12-layer stack at the 0.1B width (D=768): a T-token prompt
+    through every layer in one call, then single-token calls with the per-layer states carried.
+    Synthetic bfloat16 weights. The fused time-mix prefill (one workgroup per head) is also timed
+    alone at the prompt shape, since it dominates the prompt."""
+    import numpy as np
+    from linear_rnn_amd.inputs import make_stack_inputs
+    z = make_stack_inputs(L, B, T, H, "bf16", seed=7100, with_state=False)
+    d = {}
+    for n, a in z.items():
+        d[n] = torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    D = H * N
+    x = torch.empty_like(d["x"])
+    st = torch.empty_like(d["states"])
+    xs = torch.randn((B, 1, D), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+
+    def prompt():
+        x.copy_(d["x"])
+        st.zero_()
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], x, st)
+
+    def step():
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], xs, st)
+
+    prompt()
+    ms_prompt = time_region(torch, prompt, 3)
+    prompt()
+    step()
+    ms_step = time_region(torch, step, args.stack_steps)
+    # the fused operator alone at the prompt shape (inputs from the first layer's projection scale)
+    from linear_rnn_amd.inputs import CONFIGS, make_tmix_inputs
+    xt = make_tmix_inputs(CONFIGS[1], B=B, T=T, H=H, seed=7101)
+    dt = {n: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16
+              else torch.from_numpy(a).cuda()) for n, a in xt.items() if a is not None}
+    o = torch.empty((B, T, H, N), dtype=torch.float32, device="cuda")
+    so = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
+    names = ("r", "w_raw", "k", "v", "kk", "a_lr")
+
+    def tm():
+        wkv.rwkv7_tmix_prefill(*(dt[n] for n in names), dt["ln_w"], dt["ln_b"], dt["state_in"], o, so)
+
+    tm()
+    ms_tmix = time_region(torch, tm, 5)
+    flops = FLOP_REC * B * T * H
+    return {
+        "prompt_tokens_per_s": B * T / (ms_prompt * 1e-3), "ms_per_prompt": ms_prompt,
+        "step_tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": args.stack_steps,
+        "config": {"workload": "12-layer stack, D=768 (H=12), B=%d, %d-token prompt then single-token calls, "
+                               "synthetic bf16 weights, fp32 residual stream and states" % (B, T),
+                   "L": L, "B": B, "T": T, "H": H, "N": N},
+        "tmix_prefill_alone": {
+            "ms": ms_tmix, "share_of_prompt": ms_tmix * L / ms_prompt,
+            "roofline": {"bound": "alu", "achieved": flops / (ms_tmix * 1e-3) / 1e12,
+                         "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                         "frac": flops / (ms_tmix * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,
+                         "kernel": "wkv7_tmix_kernel (TB=16)", "traffic": None}},
     }
 
 

@@ -262,6 +262,42 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
                        float *dk, float *dv, float *da, float *db, float *dstate_in, int64_t B, int64_t T,
                        int64_t H, int64_t N, int dtype, void *stream);
 
+/*
+ * A stack of L time-mix layers over a residual stream: the hybrid ("fast")
+ * inference mode of RWKV-7 G0 7.2B notes section 3.2, where a prompt goes
+ * through every layer in one parallel call and generation then advances one
+ * token at a time with a fixed-size state per layer (section 3.3). Call with the
+ * prompt's T tokens, then with T == 1 per generated token; the per-layer states
+ * carry everything between calls. With D = H * N and, per layer l (section 7.1
+ * parameterisation: softplus soft clamp of the decay, sigmoid in-context
+ * learning rate, per-channel scaled key that the operator L2-normalises, ln_x):
+ *
+ *     P     = x W_in[l]                          [B*T, 5D], blocks r | k | v | w | a
+ *     w_raw = -softplus(-(w0 + P_w)) - 0.5       (float32)
+ *     kk    = P_k * k_k,  a_lr = sigmoid(a0 + P_a)
+ *     o     = rwkv7_tmix_prefill(r = P_r, w_raw, k = P_k, v = P_v, kk, a_lr,
+ *                                ln_w, ln_b, states[l])   (state updated in place)
+ *     x    += o W_out[l]
+ *
+ *   w_in    [L, D, 5D] in `dtype` (row-major: x[M, D] times w_in[l] gives [M, 5D])
+ *   w_out   [L, D, D]  in `dtype`
+ *   vecs    [L, 5, D]  float32: w0, a0, k_k, ln_w, ln_b of each layer
+ *   x       [B, T, D]  float32, read and overwritten with the stack's output
+ *   states  [L, B, H, N, N] float32, read and overwritten (zeros for a fresh sequence)
+ *
+ * With bfloat16 weights, x and o are rounded to bfloat16 for the projections and
+ * r, k, v, kk, a_lr are bfloat16 operator inputs; projections accumulate in
+ * float32. Token shift, the channel mix, the output gate and the low-rank
+ * projections of the full model are not included. Every pointer is 16-byte
+ * aligned; x and states may not overlap each other or the weights. B*T must be
+ * below 2^31. L == 0 or an empty x does nothing. The projections run on rocBLAS
+ * (one handle per device and stream); the intermediates (about 42 bytes per
+ * element of x with bfloat16 weights, 56 with float32) live in the workspace
+ * described for rwkv7_wkv_prefill_ex.
+ */
+int rwkv7_stack_forward(const void *w_in, const void *w_out, const float *vecs, float *x, float *states, int64_t L,
+                        int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rwkv7_wkv_strerror(int status);
 

@@ -40,7 +40,7 @@ def flags() -> list:
 def build(verbose: bool = False) -> str:
     """Compile every source under csrc/ into one shared library (always recompiles)."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + ["-shared", "-o", tmp] + sources()
+    cmd = [hipcc()] + flags() + ["-shared", "-o", tmp] + sources() + ["-lrocblas"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -190,9 +190,49 @@ int validate_backward(const void* const in[6], const float* s_in, const float* d
   return RWKV7_OK;
 }
 
+int validate_stack(const void* w_in, const void* w_out, const float* vecs, const float* x, const float* states,
+                   int64_t L, int64_t B, int64_t T, int64_t H, int64_t N, int dtype) {
+  if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
+  if (L < 0 || B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
+  if (N != RWKV7_HEAD_SIZE) return RWKV7_ERR_HEAD_SIZE;
+  // The projections' sizes must fit the GEMM library's 32-bit arguments: rows B*T and
+  // columns 5*D below 2^31; the tensors' byte sizes must fit int64 with room.
+  int64_t units = 0, M = 0, MD = 0, st = 0;
+  if (__builtin_mul_overflow(B, H, &units) || units > (int64_t(1) << 26)) return RWKV7_ERR_SHAPE;
+  if (H > (int64_t(1) << 20) || L > (int64_t(1) << 20)) return RWKV7_ERR_SHAPE;
+  if (__builtin_mul_overflow(B, T, &M) || M >= (int64_t(1) << 31)) return RWKV7_ERR_SHAPE;
+  const int64_t D = H * 64;
+  if (__builtin_mul_overflow(M, D, &MD) || MD > (int64_t(1) << 40)) return RWKV7_ERR_SHAPE;
+  if (__builtin_mul_overflow(units * 64 * 64, L, &st) || st > (int64_t(1) << 40)) return RWKV7_ERR_SHAPE;
+  const int64_t esz = dtype == RWKV7_DTYPE_BF16 ? 2 : 4;
+  if (L * D * D * 5 * esz > (int64_t(1) << 50)) return RWKV7_ERR_SHAPE;
+  const bool work = L > 0 && MD > 0;
+  if (work && (!w_in || !w_out || !vecs || !x || !states)) return RWKV7_ERR_NULL;
+  const void* ptrs[5] = {w_in, w_out, vecs, x, states};
+  for (const void* q : ptrs)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return RWKV7_ERR_ALIGN;
+  const Range rx = range_of(x, MD * 4), rs = range_of(states, st * 4);
+  const Range srcs[3] = {range_of(w_in, L * D * 5 * D * esz), range_of(w_out, L * D * D * esz),
+                         range_of(vecs, L * 5 * D * 4)};
+  for (const Range& r : srcs)
+    if (overlap(rx, r) || overlap(rs, r)) return RWKV7_ERR_ALIAS;
+  if (overlap(rx, rs)) return RWKV7_ERR_ALIAS;
+  return RWKV7_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int rwkv7_stack_forward(const void* w_in, const void* w_out, const float* vecs, float* x, float* states, int64_t L,
+                        int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void* stream) {
+  const int st = validate_stack(w_in, w_out, vecs, x, states, L, B, T, H, N, dtype);
+  if (st != RWKV7_OK) return st;
+  if (L == 0 || B * T * H == 0) return RWKV7_OK;
+  rwkv7::StackCall c{w_in, w_out, vecs, x, states, L, B, T, H, dtype, static_cast<hipStream_t>(stream)};
+  const hipError_t e = rwkv7::launch_stack(c);
+  return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
 
 int rwkv7_wkv_backward(const void* r, const void* w, const void* k, const void* v, const void* a, const void* b,
                        const float* state_in, const float* dy, const float* dstate_out, float* dr, float* dw,

@@ -71,6 +71,20 @@ struct BwdCall {
 };
 hipError_t launch_backward(const BwdCall& c);
 
+// L time-mix layers over a float32 residual stream x [B*T, H*64], in place, with
+// the per-layer states [L, B, H, 64, 64] updated in place.
+struct StackCall {
+  const void* w_in;   // [L, D, 5D] in dtype
+  const void* w_out;  // [L, D, D] in dtype
+  const float* vecs;  // [L, 5, D]: w0, a0, k_k, ln_w, ln_b
+  float* x;
+  float* states;
+  int64_t L, B, T, H;
+  int dtype;
+  hipStream_t stream;
+};
+hipError_t launch_stack(const StackCall& c);
+
 // Device memory cached per (device, stream), shared by the launchers that need
 // scratch: calls on one stream run in order, so they can share it. Grown on
 // demand (synchronising the stream first), never shrunk.

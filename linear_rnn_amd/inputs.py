@@ -253,3 +253,33 @@ def make_cotangents(B: int, T: int, H: int, seed: int, with_dstate: bool = True,
     dy = g_dy.standard_normal((B, T, H, N)).astype(np.float32)
     ds = (g_ds.standard_normal((B, H, N, N)) * 0.1).astype(np.float32) if with_dstate else None
     return {"dy": dy, "dstate_out": ds}
+
+
+def make_stack_inputs(L: int, B: int, T: int, H: int, dtype: str, seed: int, with_state: bool = True,
+                      N: int = HEAD_SIZE) -> dict:
+    """Synthetic weights and activations for a stack of L time-mix layers (D = H * N).
+
+    x ~ N(0, 1) [B, T, D] float32 (the residual stream); w_in ~ N(0, 1/D) [L, D, 5D] and
+    w_out ~ N(0, 0.25/D) [L, D, D] in `dtype` ("f32", or "bf16" as raw uint16 bits); vecs [L, 5, D]
+    float32: w0 ~ U(-5, -1) (decay bias: with unit projections the decays fall mostly in
+    0.9-0.999), a0 ~ N(0, 1) (in-context learning rate bias), k_k ~ U(0.5, 1.5) (removal-key scale),
+    ln_w ~ U(0.2, 1), ln_b ~ N(0, 0.05^2); states ~ N(0, 0.1^2) [L, B, H, N, N] float32, or zeros.
+    Seeded from SeedSequence([seed, 3]).
+    """
+    D = H * N
+    g = [np.random.Generator(np.random.PCG64(k)) for k in np.random.SeedSequence([seed, 3]).spawn(9)]
+    vecs = np.empty((L, 5, D), dtype=np.float64)
+    vecs[:, 0] = g[3].uniform(-5.0, -1.0, size=(L, D))
+    vecs[:, 1] = g[4].standard_normal((L, D))
+    vecs[:, 2] = g[5].uniform(0.5, 1.5, size=(L, D))
+    vecs[:, 3] = g[6].uniform(0.2, 1.0, size=(L, D))
+    vecs[:, 4] = g[7].standard_normal((L, D)) * 0.05
+    states = (g[8].standard_normal((L, B, H, N, N)) * 0.1).astype(np.float32) if with_state \
+        else np.zeros((L, B, H, N, N), dtype=np.float32)
+    return {
+        "x": f64_to_f32(g[0].standard_normal((B, T, D))),
+        "w_in": _cast(g[1].standard_normal((L, D, 5 * D)) / np.sqrt(D), dtype),
+        "w_out": _cast(g[2].standard_normal((L, D, D)) * (0.5 / np.sqrt(D)), dtype),
+        "vecs": f64_to_f32(vecs),
+        "states": states,
+    }

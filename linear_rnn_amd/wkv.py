@@ -28,7 +28,7 @@ RWKV7_ALGO_CHUNKED = 2
 RWKV7_ALGO_CHUNKED_SPLIT = 3
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
-            "rwkv7_tmix_prefill", "rwkv7_tmix_step", "rwkv7_wkv_backward", "rwkv7_wkv_strerror")
+            "rwkv7_tmix_prefill", "rwkv7_tmix_step", "rwkv7_wkv_backward", "rwkv7_stack_forward", "rwkv7_wkv_strerror")
 
 _lib = None
 _lock = threading.Lock()
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
                 f.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp]
             L.rwkv7_wkv_backward.restype = ci
             L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [i64] * 4 + [ci, vp]
+            L.rwkv7_stack_forward.restype = ci
+            L.rwkv7_stack_forward.argtypes = [vp] * 5 + [i64] * 5 + [ci, vp]
             L.rwkv7_wkv_strerror.restype = ctypes.c_char_p
             L.rwkv7_wkv_strerror.argtypes = [ci]
             _lib = L
@@ -200,3 +202,12 @@ def wkv7_backward(r, w, k, v, a, b, dy, state_in=None, dstate_out=None, want_dst
     rwkv7_wkv_backward(r, w, k, v, a, b, state_in, dy, dstate_out, *(out[n] for n in
                        ("dr", "dw", "dk", "dv", "da", "db", "dstate_in")), stream=stream)
     return out
+
+
+def rwkv7_stack_forward(w_in, w_out, vecs, x, states, stream=None):
+    """L time-mix layers over the residual stream x ([B,T,D] float32, in place) with per-layer states
+    ([L,B,H,64,64] float32, in place). w_in [L,D,5D] and w_out [L,D,D] in float32 or bfloat16."""
+    L, B, H, N = states.shape[0], states.shape[1], states.shape[2], states.shape[3]
+    T = x.shape[1]
+    _check(lib().rwkv7_stack_forward(_ptr(w_in), _ptr(w_out), _ptr(vecs), _ptr(x), _ptr(states), L, B, T, H, N,
+                                     _dtype_code(w_in), _stream(stream)))

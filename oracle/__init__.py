@@ -24,6 +24,11 @@ key, kernel slots) and epilogue (ln_x GroupNorm) around the recurrence, in numpy
 float64; tests/test_oracle_tmix.py pins those pieces to closed forms and to
 torch's normalize and group_norm.
 
+``stack_forward`` runs L time-mix layers over a residual stream (projections in numpy float64,
+the operator above), rounding to the weights' dtype at the points where the GPU rounds;
+tests/test_oracle_stack.py pins it to the GPT/RNN-mode equivalence and to a composition of torch's
+own softplus, sigmoid and matmul.
+
 ``wkv7_backward`` runs the C reverse-mode derivatives of the recurrence (every
 forward state kept, tokens walked backwards); tests/test_oracle_backward.py pins
 it to torch float64 autograd of a plain token loop, to finite differences and
@@ -268,3 +273,55 @@ def wkv7_backward(r, w, k, v, a, b, dy, state_in=None, dstate_out=None, nthreads
     if rc != 0:
         raise RuntimeError("oracle backward failed with status %d" % rc)
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# A stack of L time-mix layers over a residual stream (RWKV-7 G0 7.2B notes, section 3.2: the hybrid
+# mode takes the prompt through the model in parallel, then steps token by token with per-layer
+# state; section 7.1 for the parameterisation: the decay is soft-clamped by a softplus to at most
+# -0.5 before exp(-exp(.)), the in-context learning rate is a sigmoid, the removal key is the key
+# scaled per channel, normalised inside the operator).
+
+
+def _as_dtype(x64, dtype: str):
+    """float64 values -> the array the GPU hands on: float32 (round to nearest even), or for "bf16"
+    float32 then bfloat16 (each round to nearest even) as raw uint16 bits."""
+    x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return x32
+    return round16(x32.astype(np.float64), "bf16")
+
+
+def _softplus(z):
+    return np.logaddexp(0.0, z)
+
+
+def stack_forward(w_in, w_out, vecs, x, states, dtype: str = "f32", nthreads: int | None = None):
+    """L layers in float64. x [B, T, D] float32, states [L, B, H, N, N] (float32 or float64),
+    w_in [L, D, 5D] / w_out [L, D, D] float32 or bfloat16 bits (`dtype` names which), vecs [L, 5, D]
+    float32 (w0, a0, k_k, ln_w, ln_b). Per layer: P = q(x) W_in (blocks r|k|v|w|a, each rounded to
+    float32 as the projection's output); w_raw = -softplus(-(w0 + P_w)) - 0.5 (float32);
+    kk = P_k * k_k; a_lr = sigmoid(a0 + P_a); r, k, v, kk, a_lr rounded to `dtype`; the operator
+    with ln_x; x += q(o) W_out. q() rounds to bfloat16 for "bf16" and is the identity for "f32"
+    (float32 activations feed the float32 projections unrounded). Returns (x float64, states float64).
+    """
+    x = np.asarray(x, dtype=np.float64).copy()
+    st = np.asarray(states, dtype=np.float64).copy()
+    L, B, H, N = st.shape[:4]
+    T, D = x.shape[1], x.shape[2]
+    M = B * T
+    Wi, Wo, V = _widen_any(w_in), _widen_any(w_out), _widen_any(vecs)
+    q = (lambda a: _widen_any(_as_dtype(a, "bf16"))) if dtype == "bf16" else (lambda a: a)
+    for l in range(L):
+        P = (q(x).reshape(M, D) @ Wi[l]).astype(np.float32).astype(np.float64)
+        pr, pk, pv, pw, pa = (P[:, i * D:(i + 1) * D] for i in range(5))
+        w_raw = (-_softplus(-(V[l, 0] + pw)) - 0.5).astype(np.float32)
+        kk = pk * V[l, 2]
+        a_lr = 1.0 / (1.0 + np.exp(-(V[l, 1] + pa)))
+        shp = (B, T, H, N)
+        ops = [_as_dtype(t, dtype).reshape(shp) for t in (pr, pk, pv, kk, a_lr)]
+        out, s = tmix(ops[0], w_raw.reshape(shp), ops[1], ops[2], ops[3], ops[4], vecs[l, 3], vecs[l, 4],
+                      state_in=st[l], nthreads=nthreads)
+        st[l] = s
+        x = x + (q(out.reshape(M, D)) @ Wo[l]).reshape(B, T, D)
+    return x, st

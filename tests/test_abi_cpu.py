@@ -269,3 +269,31 @@ def test_backward_empty(L):
     p[6] = p[8] = p[15] = None  # optional states, T == 0: nothing to copy
     assert bcall(L, p=p, T=0) == OK
     assert bcall(L, p=[None] * 16, B=0) == OK
+
+
+# ---- the layer stack: w_in, w_out, vecs, x, states
+
+def scall(L_, p=None, n_layers=2, B=2, T=3, H=4, N=64, dtype=BF16):
+    p = ptrs(5) if p is None else p
+    return L_.rwkv7_stack_forward(*(list(p) + [n_layers, B, T, H, N, dtype, None]))
+
+
+def test_stack_validation(L):
+    assert scall(L, dtype=9) == E_DTYPE
+    assert scall(L, N=16) == E_HEAD
+    assert scall(L, n_layers=-1) == E_SHAPE
+    assert scall(L, B=1 << 16, T=1 << 16) == E_SHAPE  # B*T rows beyond the GEMM library's 32-bit sizes
+    for i in range(5):
+        p = ptrs(5)
+        p[i] = None
+        assert scall(L, p=p) == E_NULL, i
+        p = ptrs(5)
+        p[i] += 4
+        assert scall(L, p=p) == E_ALIGN, i
+    p = ptrs(5)
+    p[3] = p[0]  # x over w_in
+    assert scall(L, p=p) == E_ALIAS
+    p = ptrs(5)
+    p[4] = p[3] + 64  # states inside x
+    assert scall(L, p=p) == E_ALIAS
+    assert scall(L, n_layers=0) == OK and scall(L, T=0) == OK and scall(L, p=[None] * 5, B=0) == OK
