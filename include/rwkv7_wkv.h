@@ -171,9 +171,10 @@ int rwkv7_wkv_step_q(const void *r, const void *w, const void *k, const void *v,
  * bfloat16 inputs): the chunk records that pass from its first kernel to its
  * second live in a device buffer that the library allocates on the first call
  * that needs it and keeps for later calls, one buffer per (device, stream),
- * grown when a call needs more (about 96 MiB for long sequences: the sequence
- * is processed in slabs of chunks that fit it). Growing it synchronises that
- * stream; an allocation failure returns RWKV7_ERR_HIP before any launch.
+ * grown when a call needs more (at most about 256 MiB plus one state copy: a
+ * longer sequence is processed in slabs of chunks that fit; the environment
+ * variable RWKV7_SPLIT_SLAB_MB overrides the budget). Growing it synchronises
+ * that stream; an allocation failure returns RWKV7_ERR_HIP before any launch.
  */
 int rwkv7_wkv_prefill_ex(const void *r, const void *w, const void *k, const void *v, const void *a,
                          const void *b, const float *state_in, float *y, float *state_out, int64_t B,

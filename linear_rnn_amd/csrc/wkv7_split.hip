@@ -583,13 +583,15 @@ std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
 
 // Record-buffer budget per slab: the scan of a slab reads what its prep wrote
-// just before, so a slab that fits the 256 MB last-level (MALL) cache with room
-// to spare is read back without a second HBM round trip.
+// just before, so a slab about the size of the 256 MB last-level (MALL) cache
+// is mostly read back from it; fewer, larger slabs also spend less on launches
+// and on the prep's last, partly filled round of waves (measured: one 233 MB
+// slab beats three of 78 MB for the 96-head, 4096-token workload).
 size_t slab_budget_bytes() {
   static const size_t mb = [] {
     const char* s = std::getenv("RWKV7_SPLIT_SLAB_MB");
     const long v = s ? std::atol(s) : 0;
-    return v > 0 ? (size_t)v : (size_t)96;
+    return v > 0 ? (size_t)v : (size_t)256;
   }();
   return mb << 20;
 }
@@ -624,6 +626,20 @@ hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out) {
 }
 
 
+namespace {
+
+// Resident prep waves on this device: two waves per SIMD (the prep's register
+// footprint) times four SIMDs per compute unit.
+int64_t prep_waves_resident() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    cus = 256;
+  return (int64_t)cus * 8;
+}
+
+}  // namespace
+
 hipError_t launch_chunked_split(const WkvCall& c) {
   if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
   const int64_t units = c.B * c.H;
@@ -632,9 +648,17 @@ hipError_t launch_chunked_split(const WkvCall& c) {
   if (c.T * c.H * kN >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int64_t per_chunk = units * kRecBytes;
   int64_t slab = (int64_t)(slab_budget_bytes() / (size_t)per_chunk);
-  slab = slab < 1 ? 1 : (slab > nch ? nch : slab);
+  slab = slab < 1 ? 1 : slab;
+  if (slab < nch) {
+    // Every prep item takes about the same time, so a slab whose items fill
+    // whole rounds of resident waves leaves no round running nearly empty.
+    const int64_t W = prep_waves_resident();
+    const int64_t rounds = units * slab / W;
+    if (rounds >= 1) slab = rounds * W / units > 0 ? rounds * W / units : 1;
+  } else {
+    slab = nch;
+  }
   const int64_t nslab = (nch + slab - 1) / slab;
-  slab = (nch + nslab - 1) / nslab;  // balance the slabs
   if (units * slab > (int64_t(1) << 30)) return hipErrorNotSupported;
   const bool tmp_state = nslab > 1 && c.s_out == nullptr;
   const size_t rec_bytes = (size_t)(units * slab * kRecBytes);
