@@ -136,7 +136,7 @@ struct In<true> {
 template <>
 struct In<false> {
   using T = float;
-  static constexpr int kRow = kN + 4;  // (the float32 path is not launched)
+  [[maybe_unused]] static constexpr int kRow = kN + 4;  // (the float32 path is not launched)
   __device__ static float get(const T* p) { return *p; }
   __device__ static float widen(uint32_t raw) { return __uint_as_float(raw); }
   __device__ static void get8(const T* p, float* out) {

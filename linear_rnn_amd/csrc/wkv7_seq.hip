@@ -246,98 +246,138 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
   }
 }
 
-// Single-token step with a 16-bit stored state, persistent and software-
-// pipelined (the float32 step uses the prefill kernel above). A workgroup is four
-// independent waves; wave q owns value rows 16q..16q+15 of one head, lane
-// 16*ri + c holds columns 4c..4c+3 of rows 4m + ri (m = 0..3), as in the
-// prefill kernel, so the per-token arithmetic is the same function. Workgroup g
-// walks heads g, g + G, g + 2G, ...: while it computes one head, the raw bits
-// of the next (its state rows, the four columns of r, w, k, a, b it needs, v at
-// its four rows) are already in flight into a second register set, so a wave
-// always has a head's worth of loads outstanding. The two sets alternate
-// (ping-pong), so no loop-carried register copy forces an early wait. The four
-// waves of a workgroup read the same key-space vectors, which the CU's cache
-// serves once. No LDS, no barriers.
+// Single-token step with a 16-bit stored state (the float32 step uses the
+// prefill kernel above), persistent and software-pipelined. A workgroup is four
+// independent waves; wave q owns value rows 16q..16q+15 of one head, and lane
+// 8*r8 + c8 holds columns 8c8..8c8+7 of rows 16q + r8 and 16q + r8 + 8, so every
+// state and input access of a lane is one 16-byte load or store (with the
+// prefill kernel's layout a 16-bit state row piece is only 8 bytes). Row sums
+// are an 8-term in-lane chain and an 8-lane DPP butterfly (lane i with 7 - i,
+// then i ^ 2, then i ^ 1), which leaves the same bits in every lane of the
+// group; the operation order differs from the float32 kernels, so the float32
+// intermediate state can differ from theirs by rounding before it is rounded to
+// 16 bits. Workgroup g walks heads g, g + G, g + 2G, ...: while it computes one
+// head, the raw bits of the next (state rows, the eight columns of r, w, k, a, b,
+// v at its two rows) are already in flight into a second register set, and the
+// two sets alternate, so no loop-carried copy forces an early wait. No LDS, no
+// barriers.
+__device__ __forceinline__ float row8_sum(float x) {
+  x = x + dpp_f32<0x141>(x);  // row_half_mirror: lane i <-> 7 - i in each group of 8
+  x = x + dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = x + dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+
+template <int SQ>
+__device__ __forceinline__ float widen16(uint32_t h) {
+  if constexpr (SQ == kStBF16) return __uint_as_float(h << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
 template <bool BF16, int SQ>
 struct StepRaw {
-  using SV = typename std::conditional<SQ == kStF32, uint4, uint2>::type;  // 4 state elements
-  using IV = typename std::conditional<BF16, uint2, uint4>::type;          // 4 input elements
-  using IS = typename std::conditional<BF16, uint16_t, uint32_t>::type;    // 1 input element
-  SV s[4];
-  IV r, w, k, a, b;
-  IS v[4];
+  uint4 s[2];                                                       // 8 state elements of two rows
+  typename std::conditional<BF16, uint4, float4>::type r[BF16 ? 1 : 2], w[BF16 ? 1 : 2], k[BF16 ? 1 : 2],
+      a[BF16 ? 1 : 2], b[BF16 ? 1 : 2];
+  typename std::conditional<BF16, uint16_t, float>::type v[2];
 };
-
-template <bool BF16>
-__device__ __forceinline__ float4 widen_in4(uint2 q) {
-  return make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-}
-template <bool BF16>
-__device__ __forceinline__ float4 widen_in4(uint4 q) {
-  return make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
-}
-__device__ __forceinline__ float widen_in1(uint16_t q) { return __uint_as_float((uint32_t)q << 16); }
-__device__ __forceinline__ float widen_in1(uint32_t q) { return __uint_as_float(q); }
-
-template <int SQ>
-__device__ __forceinline__ float4 widen_state4(uint4 q) {
-  return make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
-}
-template <int SQ>
-__device__ __forceinline__ float4 widen_state4(uint2 q) {
-  if constexpr (SQ == kStBF16) {
-    return make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-  } else {
-    return make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(q.x & 0xffffu)),
-                       (float)__builtin_bit_cast(_Float16, (uint16_t)(q.x >> 16)),
-                       (float)__builtin_bit_cast(_Float16, (uint16_t)(q.y & 0xffffu)),
-                       (float)__builtin_bit_cast(_Float16, (uint16_t)(q.y >> 16)));
-  }
-}
 
 template <bool BF16, int SQ>
 __global__ __launch_bounds__(4 * kWave) void wkv7_step_kernel(SeqParams p, int64_t units) {
-  using Raw = StepRaw<BF16, SQ>;
   using St = StateIO<SQ>;
-  constexpr int kMr = 4;
+  using Raw = StepRaw<BF16, SQ>;
+  constexpr int kNv = BF16 ? 1 : 2;
   const int lane = threadIdx.x & (kWave - 1);
-  const int row0 = (threadIdx.x >> 6) * 16;  // first of this wave's 16 rows
-  const int c = lane & 15;
-  const int ri = lane >> 4;
+  const int q = threadIdx.x >> 6;
+  const int c8 = lane & 7;
+  const int r8 = lane >> 3;
+  const int row_a = 16 * q + r8;  // rows row_a and row_a + 8
   const int64_t G = gridDim.x;
   const int64_t g = xcd_swizzle(blockIdx.x, gridDim.x);
+  using IV = typename std::conditional<BF16, uint4, float4>::type;
+  using IS = typename std::conditional<BF16, uint16_t, float>::type;
 
   auto load = [&](Raw& x, int64_t u) {
-    const int64_t srow = (u * kN + row0 + ri) * kN + 4 * c;  // state element of row 4m + ri at m = 0
 #pragma unroll
-    for (int m = 0; m < kMr; ++m)
-      x.s[m] = p.s_in ? *reinterpret_cast<const typename Raw::SV*>(static_cast<const char*>(p.s_in) +
-                                                                    (srow + 4 * m * kN) * sizeof(typename Raw::SV) / 4)
-                      : typename Raw::SV{};
-    const int64_t ib = u * kN + 4 * c;  // T == 1: token row of unit u starts at u * N
-    using IV = typename Raw::IV;
-    using IS = typename Raw::IS;
-    x.r = *reinterpret_cast<const IV*>(static_cast<const IS*>(p.r) + ib);
-    x.w = *reinterpret_cast<const IV*>(static_cast<const IS*>(p.w) + ib);
-    x.k = *reinterpret_cast<const IV*>(static_cast<const IS*>(p.k) + ib);
-    x.a = *reinterpret_cast<const IV*>(static_cast<const IS*>(p.a) + ib);
-    x.b = *reinterpret_cast<const IV*>(static_cast<const IS*>(p.b) + ib);
+    for (int m = 0; m < 2; ++m)
+      x.s[m] = p.s_in ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.s_in) +
+                                                        (u * kN + row_a + 8 * m) * kN + 8 * c8)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    const int64_t ib = u * kN + 8 * c8;
 #pragma unroll
-    for (int m = 0; m < kMr; ++m) x.v[m] = static_cast<const IS*>(p.v)[u * kN + row0 + 4 * m + ri];
+    for (int h = 0; h < kNv; ++h) {
+      x.r[h] = reinterpret_cast<const IV*>(static_cast<const IS*>(p.r) + ib)[h];
+      x.w[h] = reinterpret_cast<const IV*>(static_cast<const IS*>(p.w) + ib)[h];
+      x.k[h] = reinterpret_cast<const IV*>(static_cast<const IS*>(p.k) + ib)[h];
+      x.a[h] = reinterpret_cast<const IV*>(static_cast<const IS*>(p.a) + ib)[h];
+      x.b[h] = reinterpret_cast<const IV*>(static_cast<const IS*>(p.b) + ib)[h];
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) x.v[m] = static_cast<const IS*>(p.v)[u * kN + row_a + 8 * m];
+  };
+  auto widen8 = [&](const IV* src, float (&o)[8]) {
+    if constexpr (BF16) {
+      const uint4 qv = src[0];
+      o[0] = bf16_lo(qv.x), o[1] = bf16_hi(qv.x), o[2] = bf16_lo(qv.y), o[3] = bf16_hi(qv.y);
+      o[4] = bf16_lo(qv.z), o[5] = bf16_hi(qv.z), o[6] = bf16_lo(qv.w), o[7] = bf16_hi(qv.w);
+    } else {
+      o[0] = src[0].x, o[1] = src[0].y, o[2] = src[0].z, o[3] = src[0].w;
+      o[4] = src[1].x, o[5] = src[1].y, o[6] = src[1].z, o[7] = src[1].w;
+    }
   };
   auto compute = [&](const Raw& x, int64_t u) {
-    float4 S[kMr];
+    float S[2][8];
 #pragma unroll
-    for (int m = 0; m < kMr; ++m) S[m] = widen_state4<SQ>(x.s[m]);
-    float vm[kMr];
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t wds[4] = {x.s[m].x, x.s[m].y, x.s[m].z, x.s[m].w};
 #pragma unroll
-    for (int m = 0; m < kMr; ++m) vm[m] = widen_in1(x.v[m]);
-    const float yo = token_update<kMr>(S, widen_in4<BF16>(x.r), widen_in4<BF16>(x.w), widen_in4<BF16>(x.k),
-                                       widen_in4<BF16>(x.a), widen_in4<BF16>(x.b), vm, c);
-    if (c < kMr) p.y[u * kN + row0 + 4 * c + ri] = yo;
+      for (int e = 0; e < 4; ++e) {
+        S[m][2 * e] = widen16<SQ>(wds[e] & 0xffffu);
+        S[m][2 * e + 1] = widen16<SQ>(wds[e] >> 16);
+      }
+    }
+    float r[8], w[8], k[8], a[8], b[8];
+    widen8(x.r, r), widen8(x.w, w), widen8(x.k, k), widen8(x.a, a), widen8(x.b, b);
+    float vm[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if constexpr (BF16) vm[m] = __uint_as_float((uint32_t)x.v[m] << 16);
+      else vm[m] = x.v[m];
+    }
+    float sa[2], yp[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float t = S[m][0] * a[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) t = fmaf(S[m][j], a[j], t);
+      sa[m] = t;
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) sa[m] = row8_sum(sa[m]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) S[m][j] = fmaf(S[m][j], w[j], fmaf(sa[m], b[j], vm[m] * k[j]));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float t = S[m][0] * r[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) t = fmaf(S[m][j], r[j], t);
+      yp[m] = t;
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) yp[m] = row8_sum(yp[m]);
+    if (c8 < 2) p.y[u * kN + row_a + 8 * c8] = c8 == 0 ? yp[0] : yp[1];
     if (p.s_out) {
 #pragma unroll
-      for (int m = 0; m < kMr; ++m) St::store4(p.s_out, (u * kN + row0 + 4 * m + ri) * kN + 4 * c, S[m]);
+      for (int m = 0; m < 2; ++m) {
+        uint4 o;
+        o.x = St::pack(S[m][0], S[m][1]);
+        o.y = St::pack(S[m][2], S[m][3]);
+        o.z = St::pack(S[m][4], S[m][5]);
+        o.w = St::pack(S[m][6], S[m][7]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.s_out) + (u * kN + row_a + 8 * m) * kN + 8 * c8) = o;
+      }
     }
   };
 
