@@ -379,6 +379,17 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
     prompt()
     step()
     ms_step = time_region(torch, step, args.stack_steps)
+    # the same single-token call captured once in a HIP graph (after the warm-up calls above, so
+    # the workspace and the library handles exist) and replayed: launch latency mostly removed
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        step()  # the workspace and the rocBLAS handle are per stream: create them before capture
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.synchronize()
+    ms_graph = time_region(torch, g.replay, args.stack_steps)
     # the fused operator alone at the prompt shape (inputs from the first layer's projection scale)
     from linear_rnn_amd.inputs import CONFIGS, make_tmix_inputs
     xt = make_tmix_inputs(CONFIGS[1], B=B, T=T, H=H, seed=7101)
@@ -397,6 +408,7 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
     return {
         "prompt_tokens_per_s": B * T / (ms_prompt * 1e-3), "ms_per_prompt": ms_prompt,
         "step_tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": args.stack_steps,
+        "graph_step_tokens_per_s": B / (ms_graph * 1e-3), "ms_per_graph_step": ms_graph,
         "config": {"workload": "12-layer stack, D=768 (H=12), B=%d, %d-token prompt then single-token calls, "
                                "synthetic bf16 weights, fp32 residual stream and states" % (B, T),
                    "L": L, "B": B, "T": T, "H": H, "N": N},

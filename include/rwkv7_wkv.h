@@ -295,6 +295,11 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  * (one handle per device and stream); the intermediates (about 42 bytes per
  * element of x with bfloat16 weights, 56 with float32) live in the workspace
  * described for rwkv7_wkv_prefill_ex.
+ *
+ * HIP graphs: a call can be captured in a graph on a stream once one call of at
+ * least the same size has run on that stream (it creates the workspace and the
+ * rocBLAS handle, which capture cannot); replays then launch the same kernels
+ * on the same buffers. The same holds for every entry point of this header.
  */
 int rwkv7_stack_forward(const void *w_in, const void *w_out, const float *vecs, float *x, float *states, int64_t L,
                         int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);

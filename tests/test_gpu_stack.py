@@ -89,3 +89,46 @@ def test_empty_and_zero_layers(torch):
     d = dev(torch, z)
     x, s = gpu_run(torch, d)
     assert np.array_equal(s.cpu().numpy(), z["states"])
+
+
+def test_step_in_a_hip_graph(torch):
+    """A 3-layer single-token step captured in a HIP graph (after a warm-up call, so the workspace and
+    the rocBLAS handle exist) and replayed several times, with eager calls in between, equals the
+    same steps run eagerly."""
+    say("stack step graph")
+    z = make_stack_inputs(3, 4, 1, 2, "bf16", seed=21)
+    d = dev(torch, z)
+    xs = [torch.randn((4, 1, 128), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(i))
+          for i in range(4)]
+    # eager reference: four consecutive steps
+    s_ref = d["states"].clone()
+    outs_ref = []
+    for x in xs:
+        xx = x.clone()
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], xx, s_ref)
+        outs_ref.append(xx)
+    torch.cuda.synchronize()
+    # graph: static input / state buffers
+    x_buf = torch.zeros((4, 1, 128), dtype=torch.float32, device="cuda")
+    s_buf = d["states"].clone()
+    s_warm = d["states"].clone()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        # warm-up on the capture stream: the workspace and the rocBLAS handle are per stream
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], x_buf.clone(), s_warm)
+        st.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], x_buf, s_buf)
+    torch.cuda.synchronize()
+    s_buf.copy_(d["states"])
+    for i, x in enumerate(xs):
+        x_buf.copy_(x)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x_buf, outs_ref[i]), i
+        # unrelated eager work between replays
+        tmp = torch.empty_like(x_buf)
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], tmp.copy_(x), s_warm)
+        torch.cuda.synchronize()
+    assert torch.equal(s_buf, s_ref)
