@@ -173,25 +173,34 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
 
   uint4 stk[5][kNqk];
   uint4 stv[kNqv];
+  // A prefill (TB > 1) loads and stores unconditionally: pieces past the end
+  // repeat the last piece and tokens at or past T repeat token T-1, so no
+  // divergent branch surrounds the loads (such branches make the compiler wait
+  // for each new prefetch before it issues the next). The single-token step
+  // (TB = 1, one block) loads only the pieces that exist.
   auto issue = [&](int64_t t0) {
 #pragma unroll
     for (int x = 0; x < 5; ++x) {
 #pragma unroll
       for (int q = 0; q < kNqk; ++q) {
-        const int e = tid + kThreads * q;
+        const int e0 = tid + kThreads * q;
+        const int e = TB > 1 ? min(e0, TB * kKseg - 1) : e0;
         const int tok = e / kKseg, seg = e % kKseg;
-        if (e < TB * kKseg && t0 + tok < T) {
-          const int64_t off = seq_base + (t0 + tok) * tok_stride + seg * kEpv;
+        const int64_t t = TB > 1 ? min(t0 + tok, T - 1) : t0 + tok;
+        if (TB > 1 || (e < TB * kKseg && t < T)) {
+          const int64_t off = seq_base + t * tok_stride + seg * kEpv;
           stk[x][q] = *reinterpret_cast<const uint4*>(src[x] + off * kEsz);
         }
       }
     }
 #pragma unroll
     for (int q = 0; q < kNqv; ++q) {
-      const int e = tid + kThreads * q;
+      const int e0 = tid + kThreads * q;
+      const int e = TB > 1 ? min(e0, TB * kVseg - 1) : e0;
       const int tok = e / kVseg, seg = e % kVseg;
-      if (e < TB * kVseg && t0 + tok < T) {
-        const int64_t off = seq_base + (t0 + tok) * tok_stride + row_wg + seg * kEpv;
+      const int64_t t = TB > 1 ? min(t0 + tok, T - 1) : t0 + tok;
+      if (TB > 1 || (e < TB * kVseg && t < T)) {
+        const int64_t off = seq_base + t * tok_stride + row_wg + seg * kEpv;
         stv[q] = *reinterpret_cast<const uint4*>(vsrc + off * kEsz);
       }
     }
@@ -201,38 +210,65 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
     for (int x = 0; x < 5; ++x) {
 #pragma unroll
       for (int q = 0; q < kNqk; ++q) {
-        const int e = tid + kThreads * q;
+        const int e0 = tid + kThreads * q;
+        const int e = TB > 1 ? min(e0, TB * kKseg - 1) : e0;
         const int tok = e / kKseg, seg = e % kKseg;
-        if (e < TB * kKseg && t0 + tok < T) Tr::store(&kv_lds[tok][x][seg * kEpv], stk[x][q]);
+        if (TB > 1 || (e < TB * kKseg && t0 + tok < T)) Tr::store(&kv_lds[tok][x][seg * kEpv], stk[x][q]);
       }
     }
 #pragma unroll
     for (int q = 0; q < kNqv; ++q) {
-      const int e = tid + kThreads * q;
+      const int e0 = tid + kThreads * q;
+      const int e = TB > 1 ? min(e0, TB * kVseg - 1) : e0;
       const int tok = e / kVseg, seg = e % kVseg;
-      if (e < TB * kVseg && t0 + tok < T) Tr::store(&v_lds[tok][seg * kEpv], stv[q]);
+      if (TB > 1 || (e < TB * kVseg && t0 + tok < T)) Tr::store(&v_lds[tok][seg * kEpv], stv[q]);
     }
+  };
+  auto load_tok = [&](int tt, float4& r4, float4& w4, float4& k4, float4& a4, float4& b4, float (&vm)[kMr]) {
+    r4 = *reinterpret_cast<const float4*>(&kv_lds[tt][0][4 * c]);
+    w4 = *reinterpret_cast<const float4*>(&kv_lds[tt][1][4 * c]);
+    k4 = *reinterpret_cast<const float4*>(&kv_lds[tt][2][4 * c]);
+    a4 = *reinterpret_cast<const float4*>(&kv_lds[tt][3][4 * c]);
+    b4 = *reinterpret_cast<const float4*>(&kv_lds[tt][4][4 * c]);
+#pragma unroll
+    for (int m = 0; m < kMr; ++m) vm[m] = v_lds[tt][wave * RPW + 4 * m + ri];
   };
 
   if (T > 0) issue(0);
+  // A prefill's state and first block complete here, together, so the block loop
+  // never waits for them (a loop-carried value that may still be in flight makes
+  // the compiler wait for every outstanding load, prefetches included).
+  if constexpr (TB > 1) __builtin_amdgcn_s_waitcnt(0x0f70);
   for (int64_t t0 = 0; t0 < T; t0 += TB) {
     __syncthreads();  // every wave is done reading the previous block
     commit(t0);
     __syncthreads();
     if (t0 + TB < T) issue(t0 + TB);  // in flight while this block is computed
     const int ntok = (T - t0 < TB) ? (int)(T - t0) : TB;
-    for (int tt = 0; tt < ntok; ++tt) {
-      const float4 r4 = *reinterpret_cast<const float4*>(&kv_lds[tt][0][4 * c]);
-      const float4 w4 = *reinterpret_cast<const float4*>(&kv_lds[tt][1][4 * c]);
-      const float4 k4 = *reinterpret_cast<const float4*>(&kv_lds[tt][2][4 * c]);
-      const float4 a4 = *reinterpret_cast<const float4*>(&kv_lds[tt][3][4 * c]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&kv_lds[tt][4][4 * c]);
-      float vm[kMr];
+    if (TB > 1 && ntok == TB) {  // a whole block: the next token's LDS reads are in flight during this one
+      float4 r4, w4, k4, a4, b4, r4n, w4n, k4n, a4n, b4n;
+      float vm[kMr], vmn[kMr];
+      load_tok(0, r4, w4, k4, a4, b4, vm);
 #pragma unroll
-      for (int m = 0; m < kMr; ++m) vm[m] = v_lds[tt][wave * RPW + 4 * m + ri];
-      const float yo = token_update<kMr>(S, r4, w4, k4, a4, b4, vm, c);
-      // lane c < RPW/4 writes row 4c + ri: the wave's RPW rows are contiguous.
-      if (c < kMr) p.y[seq_base + (t0 + tt) * tok_stride + row0 + 4 * c + ri] = yo;
+      for (int tt = 0; tt < TB; ++tt) {
+        if (tt + 1 < TB) load_tok(tt + 1, r4n, w4n, k4n, a4n, b4n, vmn);
+        const float yo = token_update<kMr>(S, r4, w4, k4, a4, b4, vm, c);
+        // lane c < RPW/4 writes row 4c + ri: the wave's RPW rows are contiguous.
+        if (c < kMr) p.y[seq_base + (t0 + tt) * tok_stride + row0 + 4 * c + ri] = yo;
+        if (tt + 1 < TB) {
+          r4 = r4n, w4 = w4n, k4 = k4n, a4 = a4n, b4 = b4n;
+#pragma unroll
+          for (int m = 0; m < kMr; ++m) vm[m] = vmn[m];
+        }
+      }
+    } else {
+      for (int tt = 0; tt < ntok; ++tt) {
+        float4 r4, w4, k4, a4, b4;
+        float vm[kMr];
+        load_tok(tt, r4, w4, k4, a4, b4, vm);
+        const float yo = token_update<kMr>(S, r4, w4, k4, a4, b4, vm, c);
+        if (c < kMr) p.y[seq_base + (t0 + tt) * tok_stride + row0 + 4 * c + ri] = yo;
+      }
     }
   }
 
