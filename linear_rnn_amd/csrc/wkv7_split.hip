@@ -409,59 +409,73 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // compute waves' temporaries the same physical registers, and its wait-count
   // insertion would then make the compute waves wait for their own y stores.
   if (wave >= kCompute) {
-    // ---- loader m serves chunks x = m (mod 4) with two register buffers (buffer
-    // (x / 4) % 2): it issues chunk x's loads at iteration x - 12 and commits them
-    // to the ring at iteration x - 4, so each load has eight chunk periods to arrive.
+    // ---- loader m moves a quarter of every chunk: each iteration it commits its
+    // part of chunk c + 4 to the ring and issues its loads for chunk c + 12 into
+    // the register buffer just freed (eight buffers, chunk x in buffer x % 8), so
+    // each load has eight chunk periods to arrive and every loader does the same
+    // small amount of work per iteration. Loads and stores are unconditional
+    // (indices clamped: past the last piece or chunk they repeat one), so no
+    // divergent branch surrounds them.
     const int m = wave - kCompute;
-    uint4 buf[2][kLoadsPerLane];
-    auto issue = [&](int x, uint4* bf) {
-      const int nt = min(kC, p.T - (p.c0 + x) * kC);
+    // each loader: a quarter of the record (kRecPer pieces, kQr loads per lane) and
+    // a quarter of v (kVPer pieces, one load per lane); every load has one type
+    constexpr int kRecPer = kRecPieces / kLoaders;         // 148
+    constexpr int kQr = (kRecPer + 63) / 64;               // 3
+    constexpr int kVPer = (kPieces - kRecPieces) / kLoaders;  // 16
+    static_assert(kRecPieces % kLoaders == 0 && (kPieces - kRecPieces) % kLoaders == 0 && kVPer <= 64, "split");
+    constexpr int kQ = kQr + 1;
+    constexpr int kBufs = 8;  // chunk x in buffer x % kBufs: loads are issued kBufs iterations before use
+    uint4 buf[kBufs][kQ];
+    const int vi = kVPer * m + min(lane, kVPer - 1);  // this lane's v piece: token vi / kVSegs
+    auto issue = [&](int x, uint4 (&bf)[kQ]) {
+      const int xc = min(x, nc - 1);
+      const int nt = min(kC, p.T - (p.c0 + xc) * kC);
 #pragma unroll
-      for (int q = 0; q < kLoadsPerLane; ++q) {
-        const int piece = lane + 64 * q;
-        if (piece < kRecPieces) {
-          bf[q] = ld_off<uint4>(recs, (uint32_t)(x * kRecBytes + piece * 16));
-        } else if (piece < kPieces) {
-          const int vi = piece - kRecPieces;  // token vi / kVSegs, 16-byte piece vi % kVSegs of its row
-          const int tok = min(vi / kVSegs, nt - 1);
-          bf[q] = ld_off<uint4>(vbase, (uint32_t)(((x * kC + tok) * tstride + (vi % kVSegs) * 8) * 2u));
-        }
+      for (int q = 0; q < kQr; ++q) {
+        const int piece = kRecPer * m + min(lane + 64 * q, kRecPer - 1);
+        bf[q] = ld_off<uint4>(recs, (uint32_t)(xc * kRecBytes + piece * 16));
       }
+      const int tok = min(vi / kVSegs, nt - 1);
+      bf[kQr] = ld_off<uint4>(vbase, (uint32_t)(((xc * kC + tok) * tstride + (vi % kVSegs) * 8) * 2u));
     };
-    auto commit = [&](int x, const uint4* bf) {
+    auto commit = [&](int x, const uint4 (&bf)[kQ]) {
       const int nt = min(kC, p.T - (p.c0 + x) * kC);
       unsigned char* slot = ring + (x % kRing) * kSlotBytes;
 #pragma unroll
-      for (int q = 0; q < kLoadsPerLane; ++q) {
-        const int piece = lane + 64 * q;
-        if (piece < kPieces) {
-          uint4 val = bf[q];
-          if (piece >= kRecPieces && (piece - kRecPieces) / kVSegs >= nt) val = make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(slot + piece * 16) = val;
-        }
+      for (int q = 0; q < kQr; ++q) {
+        const int piece = kRecPer * m + min(lane + 64 * q, kRecPer - 1);
+        *reinterpret_cast<uint4*>(slot + piece * 16) = bf[q];
       }
+      const bool dead = vi / kVSegs >= nt;  // v past the end of the sequence: zero
+      *reinterpret_cast<uint4*>(slot + (kRecPieces + vi) * 16) = dead ? make_uint4(0u, 0u, 0u, 0u) : bf[kQr];
     };
-    if (m < nc) {
-      issue(m, buf[0]);
-      commit(m, buf[0]);
-    }
-    if (m + 4 < nc) issue(m + 4, buf[1]);
-    if (m + 8 < nc) issue(m + 8, buf[0]);
-    lds_sync();
-    // unrolled by eight iterations so that the buffer of every commit is static
-    for (int c0 = 0; c0 < nc; c0 += 8) {
+    // chunks 0..3 straight into the ring, chunks 4..11 in flight
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = c0 + j;
-        if (c < nc) {
-          if (((j + kAhead) & 3) == m) {  // chunk x = c + 4 is this loader's, buffer ((j + 4) / 4) % 2
-            const int x = c + kAhead;
-            uint4* bf = buf[((j + kAhead) >> 2) & 1];
-            if (x < nc) commit(x, bf);
-            if (x + 8 < nc) issue(x + 8, bf);
-          }
-          lds_sync();
-        }
+    for (int x = 0; x < 4; ++x) issue(x, buf[x]);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (x < nc) commit(x, buf[x]);
+#pragma unroll
+    for (int x = 4; x < 4 + kBufs; ++x) issue(x, buf[x % kBufs]);
+    lds_sync();
+    // groups of kBufs iterations (every buffer index static, no guard around the
+    // loads, so the compiler's wait counts stay exact), then the remainder
+    int c0 = 0;
+    for (; c0 + kBufs <= nc; c0 += kBufs) {
+#pragma unroll
+      for (int j = 0; j < kBufs; ++j) {
+        const int x = c0 + j + kAhead;  // buffer x % kBufs == (j + kAhead) % kBufs
+        if (x < nc) commit(x, buf[(j + kAhead) % kBufs]);
+        issue(x + kBufs, buf[(j + kAhead) % kBufs]);
+        lds_sync();
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBufs - 1; ++j) {
+      if (c0 + j < nc) {
+        const int x = c0 + j + kAhead;
+        if (x < nc) commit(x, buf[(j + kAhead) % kBufs]);
+        lds_sync();
       }
     }
     return;
@@ -507,7 +521,25 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     for (int e = 0; e < 4; ++e) f.v[e] = vr[(4 * g + e) * kVCols + 16 * wave + li];
   };
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-  auto step = [&](int c, const Frag& f) {
+  // y[t = 4g + e][i = 16 rb + li] of chunk c; a whole chunk stores without per-lane guards
+  auto store_y = [&](int c, const f32x4& yv) {
+    const int nt = min(kC, p.T - (p.c0 + c) * kC);
+    if (nt == kC) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        st_off<float>(ybase, (uint32_t)(((c * kC + 4 * g + e) * tstride + 16 * wave + li) * 4u), yv[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * g + e;
+        if (t < nt) st_off<float>(ybase, (uint32_t)(((c * kC + t) * tstride + 16 * wave + li) * 4u), yv[e]);
+      }
+    }
+  };
+  // One chunk: returns its y. The previous chunk's y (prev_c >= 0) is stored once
+  // this chunk's first products are issued: a store right after the MFMA that
+  // produced its value would wait for that MFMA to finish.
+  auto step = [&](int c, const Frag& f, int prev_c, const f32x4& prev_y) {
     half4 vB;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
@@ -524,6 +556,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     yv = mfma32(f.r1, sB1, yv);
     u = mfma32(f.gl, cat8(vB, hz), u);
     yv = mfma32(f.gl, cat8(hz, vB), yv);
+    if (prev_c >= 0) store_y(prev_c, prev_y);
     const half8 uv = cat8(to_h4(u), vB);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -533,32 +566,28 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
       St[kt][3] *= f.dv[kt].w;
       St[kt] = mfma32(f.bk[kt], uv, St[kt]);
     }
-    // y[t = 4g + e][i = 16 rb + li]
-    const int nt = min(kC, p.T - (p.c0 + c) * kC);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 4 * g + e;
-      if (t < nt) st_off<float>(ybase, (uint32_t)(((c * kC + t) * tstride + 16 * wave + li) * 4u), yv[e]);
-    }
+    return yv;
   };
 
   // Two register sets alternate (the loop is unrolled by two), so the next
   // chunk's LDS reads are in flight while this chunk's MFMAs run.
   Frag fa, fb;
+  f32x4 ya = zero4(), yb = zero4();
   if (nc > 0) read(0, fa);
   // nothing is in flight from LDS when the loop starts: the wait-count pass then
   // never holds this chunk's operands back behind the next chunk's reads
   __builtin_amdgcn_s_waitcnt(0xc07f);
   for (int c = 0; c < nc; c += 2) {
     if (c + 1 < nc) read(c + 1, fb);
-    step(c, fa);
+    ya = step(c, fa, c - 1, yb);
     lds_sync();
     if (c + 1 < nc) {
       if (c + 2 < nc) read(c + 2, fa);
-      step(c + 1, fb);
+      yb = step(c + 1, fb, c, ya);
       lds_sync();
     }
   }
+  if (nc > 0) store_y(nc - 1, (nc - 1) % 2 == 0 ? ya : yb);
 
   if (p.s_dst) {
 #pragma unroll
