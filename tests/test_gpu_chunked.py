@@ -95,6 +95,10 @@ def test_config2_full_and_resume(torch, CH):
     assert max(e) <= TOL_BF16, e
     # segments are chunk-aligned, so the resumed run repeats the one-pass arithmetic exactly
     assert np.array_equal(y4, y1) and np.array_equal(s4, s1)
+    # no state_out: a sequence of several slabs carries its state through a workspace copy instead
+    yn, _ = wkv.wkv7(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state_in"], algo=CH, want_state=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(yn.cpu().numpy(), y1)
 
 
 def test_unaligned_resume(torch, CH):
