@@ -34,6 +34,9 @@ def sources() -> list:
 def flags() -> list:
     return ["-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC", "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in ordinary VGPRs: no copies out of the accumulation registers
+            # (only the chunk-prep kernel's code changes; the others already use this form)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-lambda-capture"]
 
 

@@ -83,9 +83,6 @@ constexpr int kRecD = kRecBlocks * 1024;
 constexpr int kRecBytes = kRecD + kN * 4;  // 9472
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma16(half4 a, half4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
@@ -139,15 +136,31 @@ struct PrepParams {
 };
 
 constexpr int kPrepWaves = 4;
-constexpr int kFacRow = kN + 4;  // padded float row
-// Factor rows (float32, [row][key]): E row t+1 = e^{gamma_t} (row 0 = 1), Suf row s =
-// e^{gamma_15 - gamma_s}, Gq row t+1 = e^{gamma_t - gamma_7} (row 0 for t = -1),
-// Fk row s = e^{gamma_7 - gamma_s}.
-constexpr int kRowE = 0, kRowS = 17, kRowG = 33, kRowF = 50, kFacRows = 66;
-constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 17,952 bytes
+constexpr int kFacRow = kN + 4;  // padded float row: token-layout reads of one row spread over the banks
+// Factor rows (float32, [row][key]), written in the key layout (lane = key j):
+//   E  row t     = e^{gamma_t},            t = 0..15
+//   Gq row t + 1 = e^{gamma_t - gamma_7},  t = -1..15
+//   Fk row t     = e^{gamma_7 - gamma_t},  t = 0..15
+// and e^{gamma_15 - gamma_t} = Gq_15 Fk_t is formed where it is used.
+constexpr int kRowE = 0, kRowG = 16, kRowF = 33, kFacRows = 49;
+constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 13,328 bytes: three 4-wave workgroups per CU
 // After the factors are consumed the same wave area holds L_ab and L_rb ([t][s],
 // float32) and the rows of T and M_r (float16).
 constexpr int kLabOff = 0, kLrbOff = 16 * 16, kTmOffBytes = 2 * 16 * 16 * 4;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// An ordering point for the values in x and for memory: the compiler computes x
+// before it and issues no later memory access ahead of it.
+__device__ __forceinline__ void pin16(float (&x)[16]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+               "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
+               :
+               : "memory");
+}
+__device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
 __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -170,8 +183,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   const uint32_t tstride = (uint32_t)p.H * kN;                                // elements between tokens
   unsigned char* rec = p.rec + ((int64_t)unit * p.nc + cl) * kRecBytes;
 
-  // ---- raw r, a, b, k in the token layout: lane (t = li, g) holds columns 16kt + 4g .. 4g+3.
-  // Past-the-end tokens read token nt-1 and are zeroed below (identity tokens).
+  // ---- raw r, a, b, k in the token layout: lane (t = li, g) holds keys 16kt + 4g .. 4g+3.
+  // Past-the-end tokens read token nt-1 and become identity tokens (r = k = a = b = 0, w = 1).
   const int tl = min(li, nt - 1);
   const bool live = li < nt;
   uint2 rr[4], ar[4], br[4], kr[4];
@@ -183,43 +196,37 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
     br[kt] = ld_off<uint2>(p.b + base, off);
     kr[kt] = ld_off<uint2>(p.k + base, off);
   }
-  // ---- w in the key layout: lane = key column j, all 16 tokens (past the end: w = 1)
-  float wc[kC], rc[kC];
+  // ---- w in the key layout: lane = key j, all 16 tokens
+  float wc[kC];
 #pragma unroll
   for (int t = 0; t < kC; ++t) {
     const int tt = min(t, nt - 1);
     float x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
     x = x < kWMin ? kWMin : x;  // clamp (a NaN passes through)
     wc[t] = t < nt ? x : 1.f;
-    rc[t] = __builtin_amdgcn_rcpf(wc[t]);
   }
 
-  // ---- decay factors (lane = j): running products, advanced together
+  // ---- decay factors (lane = j): running products from token 0 (E) and outward from
+  // token 7 (Gq, Fk), so no factor exceeds w_min^-8
   {
     const int j = lane;
-    float e = 1.f, sf = 1.f, gu = 1.f, gd = 1.f, fd = 1.f, fu = 1.f;
-    fac[kRowE * kFacRow + j] = 1.f;
-    fac[(kRowS + kC - 1) * kFacRow + j] = 1.f;
+    float e = 1.f, gu = 1.f, gd = 1.f, fu = 1.f, fd = 1.f;
     fac[(kRowG + 8) * kFacRow + j] = 1.f;  // Gq_7
     fac[(kRowF + 7) * kFacRow + j] = 1.f;  // Fk_7
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
       e *= wc[q];
-      fac[(kRowE + q + 1) * kFacRow + j] = e;  // E_q
-      if (q < kC - 1) {                        // Suf_s, s = 14 - q: times w_{s+1}
-        sf *= wc[kC - 1 - q];
-        fac[(kRowS + kC - 2 - q) * kFacRow + j] = sf;
-      }
-      if (q < 8) {  // Gq_t, t = 8 + q: times w_t
-        gu *= wc[8 + q];
+      fac[(kRowE + q) * kFacRow + j] = e;  // E_q
+      if (q < 8) {
+        gu *= wc[8 + q];  // Gq_t, t = 8 + q: times w_t
         fac[(kRowG + 9 + q) * kFacRow + j] = gu;
-        gd *= rc[7 - q];  // Gq_t, t = 6 - q: divided by w_{t+1}
+        gd *= __builtin_amdgcn_rcpf(wc[7 - q]);  // Gq_t, t = 6 - q: divided by w_{t+1}
         fac[(kRowG + 7 - q) * kFacRow + j] = gd;
-        fu *= rc[8 + q];  // Fk_s, s = 8 + q: divided by w_s
+        fu *= __builtin_amdgcn_rcpf(wc[8 + q]);  // Fk_t, t = 8 + q: divided by w_t
         fac[(kRowF + 8 + q) * kFacRow + j] = fu;
       }
-      if (q < 7) {  // Fk_s, s = 6 - q: times w_{s+1}
-        fd *= wc[7 - q];
+      if (q < 7) {
+        fd *= wc[7 - q];  // Fk_t, t = 6 - q: times w_{t+1}
         fac[(kRowF + 6 - q) * kFacRow + j] = fd;
       }
     }
@@ -228,66 +235,64 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS before other lanes read them
   __builtin_amdgcn_wave_barrier();
 
-  // ---- token layout: factors and operands. q = 4kt + e indexes key 16kt + 4g + e.
-  float ah[16], rh[16], bh[16], kh[16];  // Gram operands
-  half4 Ahat[4], Bbar[4], Kbar[4];
+  // ---- token layout: operands, the four Grams (float32 MFMA) and B-, K- (stored at once).
+  // q = 4kt + e indexes key 16kt + 4g + e. The Grams land in the D layout: lane (s = li, g)
+  // holds t = 4g + e; L_rk is formed transposed (operands swapped).
+  // Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
+  half4 eye;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
+  const uint32_t lo = (uint32_t)lane * 16u;  // record blocks: 16 bytes per lane
+  half4 Ahat[4];
   f32x4 Rhat[4];
+  f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
+  const uint2 z2 = make_uint2(0u, 0u);
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int col = 16 * kt + 4 * g;
-    const float4 gqm1 = *reinterpret_cast<const float4*>(&fac[(kRowG + li) * kFacRow + col]);
-    const float4 gq = *reinterpret_cast<const float4*>(&fac[(kRowG + li + 1) * kFacRow + col]);
-    const float4 fk = *reinterpret_cast<const float4*>(&fac[(kRowF + li) * kFacRow + col]);
-    const float4 em1 = *reinterpret_cast<const float4*>(&fac[(kRowE + li) * kFacRow + col]);
-    const float4 e0 = *reinterpret_cast<const float4*>(&fac[(kRowE + li + 1) * kFacRow + col]);
-    const float4 sf = *reinterpret_cast<const float4*>(&fac[(kRowS + li) * kFacRow + col]);
-    const float fgqm1[4] = {gqm1.x, gqm1.y, gqm1.z, gqm1.w}, fgq[4] = {gq.x, gq.y, gq.z, gq.w};
-    const float ffk[4] = {fk.x, fk.y, fk.z, fk.w}, fem1[4] = {em1.x, em1.y, em1.z, em1.w};
-    const float fe0[4] = {e0.x, e0.y, e0.z, e0.w}, fsf[4] = {sf.x, sf.y, sf.z, sf.w};
+    const float4 em1 = li == 0 ? make_float4(1.f, 1.f, 1.f, 1.f) : lds4(&fac[(kRowE + max(li - 1, 0)) * kFacRow + col]);
+    const float4 e0 = lds4(&fac[(kRowE + li) * kFacRow + col]);
+    const float4 gqm1 = lds4(&fac[(kRowG + li) * kFacRow + col]);
+    const float4 gq = lds4(&fac[(kRowG + li + 1) * kFacRow + col]);
+    const float4 fk = lds4(&fac[(kRowF + li) * kFacRow + col]);
+    const float4 g15 = lds4(&fac[(kRowG + 16) * kFacRow + col]);
+    const uint2 ra = live ? ar[kt] : z2, rv2 = live ? rr[kt] : z2, rb = live ? br[kt] : z2, rk = live ? kr[kt] : z2;
+    half4 bbar, kbar;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float av = live ? bf4(ar[kt], e) : 0.f;
-      const float rv = live ? bf4(rr[kt], e) : 0.f;
-      const float bv = live ? bf4(br[kt], e) : 0.f;
-      const float kv = live ? bf4(kr[kt], e) : 0.f;
-      const int q = 4 * kt + e;
-      ah[q] = av * fgqm1[e];
-      rh[q] = rv * fgq[e];
-      bh[q] = bv * ffk[e];
-      kh[q] = kv * ffk[e];
-      Ahat[kt][e] = (_Float16)(av * fem1[e]);
-      Rhat[kt][e] = rv * fe0[e];
-      Bbar[kt][e] = (_Float16)(bv * fsf[e]);
-      Kbar[kt][e] = (_Float16)(kv * fsf[e]);
+      const float av = bf4(ra, e), rv = bf4(rv2, e), bv = bf4(rb, e), kv = bf4(rk, e);
+      const float f = el(fk, e);
+      const float suf = el(g15, e) * f;  // e^{gamma_15 - gamma_t}
+      const float ah = av * el(gqm1, e), rh = rv * el(gq, e), bh = bv * f, kh = kv * f;
+      Lab = mfma4(ah, bh, Lab);
+      Lak = mfma4(ah, kh, Lak);
+      Lrb = mfma4(rh, bh, Lrb);
+      LrkT = mfma4(kh, rh, LrkT);
+      Ahat[kt][e] = (_Float16)(av * el(em1, e));
+      Rhat[kt][e] = rv * el(e0, e);
+      bbar[e] = (_Float16)(bv * suf);
+      kbar[e] = (_Float16)(kv * suf);
     }
-  }
-
-  // ---- Grams on float32 MFMA: L[t][s] in D layout (lane (s = li, g) holds t = 4g + e);
-  // L_rk is formed transposed (operands swapped) because it is needed as a D-layout seed.
-  f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    Lab = mfma4(ah[q], bh[q], Lab);
-    Lak = mfma4(ah[q], kh[q], Lak);
-    Lrb = mfma4(rh[q], bh[q], Lrb);
-    LrkT = mfma4(kh[q], rh[q], LrkT);
+    const half4 BT = to_h4(mfma16(bbar, eye, zero4()));  // lane (j = li, g): B-[4g+e][16kt + li]
+    const half4 KT = to_h4(mfma16(kbar, eye, zero4()));
+    st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT, KT));
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g + e;                 // row of Lab, Lak, Lrb; column li is s
-    Lab[e] = li < t ? Lab[e] : 0.f;          // strictly lower
+    const int t = 4 * g + e;            // row of Lab, Lak, Lrb; column li is s
+    Lab[e] = li < t ? Lab[e] : 0.f;     // strictly lower
     Lak[e] = li < t ? Lak[e] : 0.f;
-    Lrb[e] = li <= t ? Lrb[e] : 0.f;         // lower with the diagonal
-    LrkT[e] = t <= li ? LrkT[e] : 0.f;       // element (s = 4g+e, t = li) of L_rk^T
+    Lrb[e] = li <= t ? Lrb[e] : 0.f;    // lower with the diagonal
+    LrkT[e] = t <= li ? LrkT[e] : 0.f;  // element (s = 4g+e, t = li) of L_rk^T
   }
 
   // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
   // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
-  // every x[s], s < s2. The factor rows are no longer read, so their area is reused.
+  // every x[s], s < s2. The factor rows are no longer read, so their area is reused;
+  // the row of L_ab for the next step is read while the current one is applied.
   float* lab = fac + kLabOff;
   float* lrb = fac + kLrbOff;
-  // every factor read of this wave has completed before the area is overwritten
-  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // every factor read of this wave has completed
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -300,19 +305,25 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   float x[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float4 v = *reinterpret_cast<const float4*>(&lrb[row * 16 + 4 * q]);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
+    float4 v = lds4(&lrb[row * 16 + 4 * q]);
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));  // read by every lane, no branch
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * q + e] = g == 0 ? (4 * q + e == row ? 1.f : 0.f) : vv[e];
+    for (int e = 0; e < 4; ++e) x[4 * q + e] = g == 0 ? (4 * q + e == row ? 1.f : 0.f) : el(v, e);
   }
+  float4 cur[4], nxt[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cur[q] = lds4(&lab[(kC - 1) * 16 + 4 * q]);
 #pragma unroll
   for (int s2 = kC - 1; s2 >= 1; --s2) {
-    float lrow[16];
+    if (s2 > 1) {
 #pragma unroll
-    for (int q = 0; q < (s2 + 3) / 4; ++q)
-      *reinterpret_cast<float4*>(&lrow[4 * q]) = *reinterpret_cast<const float4*>(&lab[s2 * 16 + 4 * q]);
+      for (int q = 0; q < (s2 + 2) / 4; ++q) nxt[q] = lds4(&lab[(s2 - 1) * 16 + 4 * q]);
+    }
 #pragma unroll
-    for (int s = 0; s < s2; ++s) x[s] = fmaf(x[s2], lrow[s], x[s]);
+    for (int s = 0; s < s2; ++s) x[s] = fmaf(x[s2], el(cur[s / 4], s % 4), x[s]);
+    pin16(x);  // this step's updates before the next row's reads: one row in flight, not all
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
   }
   _Float16* tm = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(fac) + kTmOffBytes);
   if (g < 2) {
@@ -326,32 +337,24 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   const half4 tB = *reinterpret_cast<const half4*>(&tm[li * 16 + 4 * g]);         // T[t = li][4g..]: T^T as B
   const half4 mB = *reinterpret_cast<const half4*>(&tm[(16 + li) * 16 + 4 * g]);  // M_r^T as B
 
-  // ---- products. Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
-  half4 eye;
+  // ---- products, stored per block. L_rk^T is added on the vector unit.
 #pragma unroll
-  for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
-  half4 ApT[4], RpT[4], BT[4], KT[4];
+  for (int kp = 0; kp < 2; ++kp) {
+    half4 ApT[2], RpT[2];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const half4 AT = to_h4(mfma16(Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
-    ApT[kt] = to_h4(mfma16(AT, tB, zero4()));                // lane (t = li, g): A'[t][16kt + 4g + e]
-    RpT[kt] = to_h4(mfma16(AT, mB, Rhat[kt]));               // R'[t][16kt + 4g + e]
-    BT[kt] = to_h4(mfma16(Bbar[kt], eye, zero4()));          // lane (j = li, g): B-[4g+e][16kt + li]
-    KT[kt] = to_h4(mfma16(Kbar[kt], eye, zero4()));
+    for (int u = 0; u < 2; ++u) {
+      const int kt = 2 * kp + u;
+      const half4 AT = to_h4(mfma16(Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
+      ApT[u] = to_h4(mfma16(AT, tB, zero4()));                 // lane (t = li, g): A'[t][16kt + 4g + e]
+      RpT[u] = to_h4(mfma16(AT, mB, Rhat[kt]));                // R'[t][16kt + 4g + e]
+    }
+    st_off<half8>(rec, (kRecA0 + kp) * 1024 + lo, cat8(ApT[0], ApT[1]));
+    st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
   }
   const half4 LakH = to_h4(Lak);  // as an A operand: L_ak^T (M = s', K = s)
-  const half4 GuT = to_h4(mfma16(LakH, tB, zero4()));  // lane (t = li, g): G_u[t][4g + e]
-  const half4 GyT = to_h4(mfma16(LakH, mB, LrkT));     // G_y[t][4g + e]
-
-  // ---- record: 16 bytes per lane per block
-  const uint32_t lo = (uint32_t)lane * 16u;
-  st_off<half8>(rec, kRecA0 * 1024 + lo, cat8(ApT[0], ApT[1]));
-  st_off<half8>(rec, kRecA1 * 1024 + lo, cat8(ApT[2], ApT[3]));
-  st_off<half8>(rec, kRecR0 * 1024 + lo, cat8(RpT[0], RpT[1]));
-  st_off<half8>(rec, kRecR1 * 1024 + lo, cat8(RpT[2], RpT[3]));
+  const half4 GuT = to_h4(mfma16(LakH, tB, zero4()));         // lane (t = li, g): G_u[t][4g + e]
+  const half4 GyT = to_h4(mfma16(LakH, mB, zero4()) + LrkT);  // G_y[t][4g + e]
   st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT[kt], KT[kt]));
 }
 
 // ============================================================================ kernel 2: scan
@@ -380,7 +383,6 @@ constexpr int kSlotBytes = kRecBytes + kVBytes;    // 10,496
 constexpr int kRecPieces = kRecBytes / 16;         // 592
 constexpr int kVSegs = kVCols * 2 / 16;            // 16-byte pieces per token row of v
 constexpr int kPieces = kSlotBytes / 16;           // 656
-constexpr int kLoadsPerLane = (kPieces + 63) / 64;  // 11
 constexpr int kScanThreads = 64 * (kCompute + kLoaders);
 
 __device__ __forceinline__ f32x4 mfma32(half8 a, half8 b, f32x4 c) {
@@ -657,14 +659,18 @@ hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out) {
 
 namespace {
 
-// Resident prep waves on this device: two waves per SIMD (the prep's register
-// footprint) times four SIMDs per compute unit.
+// Resident prep waves on this device: workgroups per compute unit (the prep's
+// register footprint decides) times its waves times the compute units.
 int64_t prep_waves_resident() {
-  int dev = 0, cus = 0;
+  int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess || cus <= 0)
     cus = 256;
-  return (int64_t)cus * 8;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&wkv7_prep_kernel),
+                                                   64 * kPrepWaves, kPrepWaves * kPrepLdsPerWave) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 2;
+  return (int64_t)cus * per_cu * kPrepWaves;
 }
 
 }  // namespace
