@@ -102,15 +102,6 @@ __device__ __forceinline__ float bf4(uint2 q, int e) {
   return (e & 1) ? __uint_as_float(u & 0xffff0000u) : __uint_as_float(u << 16);
 }
 
-// Workgroup barrier for data exchanged through LDS: an explicit lgkmcnt(0) that
-// the compiler's wait-count pass sees (so it knows every earlier LDS read has
-// completed and does not wait on them again after the barrier), then s_barrier
-// as inline assembly, which adds no wait on outstanding global loads or stores.
-__device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-}
-
 template <class V>
 __device__ __forceinline__ V ld_off(const void* base, uint32_t byte_off) {
   return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
@@ -369,24 +360,47 @@ struct ScanParams {
   int32_t c0, nc;
 };
 
-// A head's 64 value rows are independent; they are split over kWgPerHead
-// workgroups of kCompute compute waves (16 rows each) and kLoaders loader waves.
-// One workgroup per CU leaves every compute wave a SIMD of its own.
-constexpr int kCompute = 2;
-constexpr int kWgPerHead = 4 / kCompute;
-constexpr int kLoaders = 4;
-constexpr int kAhead = 4;                          // chunks committed ahead of the compute waves
-constexpr int kRing = kAhead + 1;                  // LDS slots
-constexpr int kVCols = 16 * kCompute;              // value columns of v this workgroup needs
-constexpr int kVBytes = kC * kVCols * 2;           // bfloat16, [token][kVCols]
-constexpr int kSlotBytes = kRecBytes + kVBytes;    // 10,496
-constexpr int kRecPieces = kRecBytes / 16;         // 592
-constexpr int kVSegs = kVCols * 2 / 16;            // 16-byte pieces per token row of v
-constexpr int kPieces = kSlotBytes / 16;           // 656
-constexpr int kScanThreads = 64 * (kCompute + kLoaders);
+// A head's 64 value rows are independent: four compute waves of 16 rows each, two
+// per workgroup (one workgroup per CU keeps every compute wave on a SIMD of its
+// own). A third wave streams the workgroup's chunks straight into an LDS ring with
+// global-to-LDS loads (no register staging), kDist chunks ahead of the reads; the
+// compute waves issue no global loads, so nothing they wait on is behind a load.
+// One barrier per chunk.
+constexpr int kScanWaves = 2;  // compute waves per workgroup
+constexpr int kWgPerHead = 4 / kScanWaves;
+constexpr int kDist = 5;                          // chunks in flight ahead of the one read next
+constexpr int kSlots = kDist + 1;                 // ring slots
+constexpr int kVCols = 16 * kScanWaves;           // value columns of v this workgroup needs
+constexpr int kVBytes = kC * kVCols * 2;          // bfloat16, [token][kVCols]: 1 KiB
+constexpr int kSlotBytes = kRecBytes + kVBytes;   // 10,496
+constexpr int kScanLds = kSlots * kSlotBytes;     // 62,976
+constexpr int kLoads = kRecBlocks + 2;  // loads per lane per chunk: record blocks, e^gamma, v
+constexpr int kScanThreads = 64 * (kScanWaves + 1);
+static_assert(kVBytes == 64 * 16 && kRecBlocks == 9, "one 16-byte piece of v per lane");
 
 __device__ __forceinline__ f32x4 mfma32(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Global-to-LDS load: lane l's BYTES land at LDS address lds + BYTES * l (lds
+// wave-uniform, in M0). Written as assembly so that the compiler, which cannot
+// tell which later LDS reads these loads feed, inserts no wait of its own; every
+// wait on them is an explicit vm_wait.
+template <int BYTES>
+__device__ __forceinline__ void to_lds(const void* g, uint32_t lds) {
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// Waits until at most N of this wave's vector-memory operations are outstanding
+// (they complete in issue order), and orders every later memory access after it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
@@ -400,92 +414,48 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   const int bb = unit / p.H, hh = unit % p.H;
   const int nc = p.nc;
   const uint32_t tstride = (uint32_t)p.H * kN;
+  const int rb = kScanWaves * part + wave;  // a compute wave's value rows: 16 rb .. 16 rb + 15
   const unsigned char* recs = p.rec + (int64_t)unit * nc * kRecBytes;
   const int64_t seq_base =
       ((int64_t)bb * p.T + (int64_t)p.c0 * kC) * p.H * kN + (int64_t)hh * kN + kVCols * part;
   const uint16_t* vbase = p.v + seq_base;  // this workgroup's value columns
-  float* ybase = p.y + seq_base;
+  float* ybase = p.y + seq_base + 16 * wave;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
 
-  // The two roles run separate loops with the same number of barriers. One shared
-  // loop would let the compiler give the loaders' in-flight load registers and the
-  // compute waves' temporaries the same physical registers, and its wait-count
-  // insertion would then make the compute waves wait for their own y stores.
-  if (wave >= kCompute) {
-    // ---- loader m moves a quarter of every chunk: each iteration it commits its
-    // part of chunk c + 4 to the ring and issues its loads for chunk c + 12 into
-    // the register buffer just freed (eight buffers, chunk x in buffer x % 8), so
-    // each load has eight chunk periods to arrive and every loader does the same
-    // small amount of work per iteration. Loads and stores are unconditional
-    // (indices clamped: past the last piece or chunk they repeat one), so no
-    // divergent branch surrounds them.
-    const int m = wave - kCompute;
-    // each loader: a quarter of the record (kRecPer pieces, kQr loads per lane) and
-    // a quarter of v (kVPer pieces, one load per lane); every load has one type
-    constexpr int kRecPer = kRecPieces / kLoaders;         // 148
-    constexpr int kQr = (kRecPer + 63) / 64;               // 3
-    constexpr int kVPer = (kPieces - kRecPieces) / kLoaders;  // 16
-    static_assert(kRecPieces % kLoaders == 0 && (kPieces - kRecPieces) % kLoaders == 0 && kVPer <= 64, "split");
-    constexpr int kQ = kQr + 1;
-    constexpr int kBufs = 8;  // chunk x in buffer x % kBufs: loads are issued kBufs iterations before use
-    uint4 buf[kBufs][kQ];
-    const int vi = kVPer * m + min(lane, kVPer - 1);  // this lane's v piece: token vi / kVSegs
-    auto issue = [&](int x, uint4 (&bf)[kQ]) {
+  // ---- loader wave: chunk x (clamped to the last one: past the end the loads repeat it)
+  // into slot x % kSlots: the record as it is (nine 1 KiB blocks, then e^{gamma_15}),
+  // then v [token][kVCols] (lane l: token l / 4, eight columns). Tokens past the end of
+  // the sequence repeat the last one; their coefficients in the record are zero.
+  // Chunk x + kDist reuses the slot of chunk x - 1, which the compute waves read
+  // (and waited for: lgkmcnt(0)) before the barrier that precedes its loads.
+  if (wave == kScanWaves) {
+    auto issue = [&](int x) {
       const int xc = min(x, nc - 1);
+      const uint32_t slot = ring_lds + (uint32_t)((x % kSlots) * kSlotBytes);
+      const unsigned char* src = recs + (int64_t)xc * kRecBytes;
+#pragma unroll
+      for (int b = 0; b < kRecBlocks; ++b) to_lds<16>(src + b * 1024 + lane * 16, slot + b * 1024);
+      to_lds<4>(src + kRecD + lane * 4, slot + kRecD);
       const int nt = min(kC, p.T - (p.c0 + xc) * kC);
-#pragma unroll
-      for (int q = 0; q < kQr; ++q) {
-        const int piece = kRecPer * m + min(lane + 64 * q, kRecPer - 1);
-        bf[q] = ld_off<uint4>(recs, (uint32_t)(xc * kRecBytes + piece * 16));
-      }
-      const int tok = min(vi / kVSegs, nt - 1);
-      bf[kQr] = ld_off<uint4>(vbase, (uint32_t)(((xc * kC + tok) * tstride + (vi % kVSegs) * 8) * 2u));
+      const int t = min(lane >> 2, nt - 1);
+      to_lds<16>(vbase + ((int64_t)(xc * kC + t) * tstride + 8 * (lane & 3)), slot + kRecBytes);
     };
-    auto commit = [&](int x, const uint4 (&bf)[kQ]) {
-      const int nt = min(kC, p.T - (p.c0 + x) * kC);
-      unsigned char* slot = ring + (x % kRing) * kSlotBytes;
+    // once chunk c + kDist is issued, chunk c + 1 has landed when at most the loads of
+    // kDist - 1 chunks are outstanding (they complete in issue order)
 #pragma unroll
-      for (int q = 0; q < kQr; ++q) {
-        const int piece = kRecPer * m + min(lane + 64 * q, kRecPer - 1);
-        *reinterpret_cast<uint4*>(slot + piece * 16) = bf[q];
-      }
-      const bool dead = vi / kVSegs >= nt;  // v past the end of the sequence: zero
-      *reinterpret_cast<uint4*>(slot + (kRecPieces + vi) * 16) = dead ? make_uint4(0u, 0u, 0u, 0u) : bf[kQr];
-    };
-    // chunks 0..3 straight into the ring, chunks 4..11 in flight
-#pragma unroll
-    for (int x = 0; x < 4; ++x) issue(x, buf[x]);
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      if (x < nc) commit(x, buf[x]);
-#pragma unroll
-    for (int x = 4; x < 4 + kBufs; ++x) issue(x, buf[x % kBufs]);
-    lds_sync();
-    // groups of kBufs iterations (every buffer index static, no guard around the
-    // loads, so the compiler's wait counts stay exact), then the remainder
-    int c0 = 0;
-    for (; c0 + kBufs <= nc; c0 += kBufs) {
-#pragma unroll
-      for (int j = 0; j < kBufs; ++j) {
-        const int x = c0 + j + kAhead;  // buffer x % kBufs == (j + kAhead) % kBufs
-        if (x < nc) commit(x, buf[(j + kAhead) % kBufs]);
-        issue(x + kBufs, buf[(j + kAhead) % kBufs]);
-        lds_sync();
-      }
+    for (int x = 0; x < kDist; ++x) issue(x);
+    vm_wait<(kDist - 1) * kLoads>();
+    asm volatile("s_barrier" ::: "memory");  // chunk 0
+    for (int c = 0; c < nc; ++c) {
+      issue(c + kDist);
+      vm_wait<(kDist - 1) * kLoads>();
+      asm volatile("s_barrier" ::: "memory");  // chunk c + 1
     }
-#pragma unroll
-    for (int j = 0; j < kBufs - 1; ++j) {
-      if (c0 + j < nc) {
-        const int x = c0 + j + kAhead;
-        if (x < nc) commit(x, buf[(j + kAhead) % kBufs]);
-        lds_sync();
-      }
-    }
+    vm_wait<0>();  // every load has landed before the wave ends
     return;
   }
 
-  // ---- compute wave: value rows 16 rb .. 16 rb + 15 of the head,
   // element e of St[kt] = S[i = 16 rb + li][j = 16kt + 4g + e]
-  const int rb = kCompute * part + wave;
   f32x4 St[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) St[kt] = zero4();
@@ -497,7 +467,9 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
       St[kt] = f32x4{s.x, s.y, s.z, s.w};
     }
   }
-  lds_sync();
+  // vmcnt(0) as a builtin, so the compiler's own wait counting knows the state has landed
+  // (it would otherwise wait for it at the first use, behind the first chunks' loads)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 
   // fragments of one chunk, read from its ring slot one iteration ahead
   struct Frag {
@@ -507,7 +479,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   };
   const uint32_t lo = (uint32_t)lane * 16u;
   auto read = [&](int c, Frag& f) {
-    const unsigned char* slot = ring + (c % kRing) * kSlotBytes;
+    const unsigned char* slot = ring + (c % kSlots) * kSlotBytes;
     f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
     f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
     f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
@@ -529,19 +501,18 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     if (nt == kC) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        st_off<float>(ybase, (uint32_t)(((c * kC + 4 * g + e) * tstride + 16 * wave + li) * 4u), yv[e]);
+        st_off<float>(ybase, (uint32_t)(((c * kC + 4 * g + e) * tstride + li) * 4u), yv[e]);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 4 * g + e;
-        if (t < nt) st_off<float>(ybase, (uint32_t)(((c * kC + t) * tstride + 16 * wave + li) * 4u), yv[e]);
+        if (t < nt) st_off<float>(ybase, (uint32_t)(((c * kC + t) * tstride + li) * 4u), yv[e]);
       }
     }
   };
-  // One chunk: returns its y. The previous chunk's y (prev_c >= 0) is stored once
-  // this chunk's first products are issued: a store right after the MFMA that
-  // produced its value would wait for that MFMA to finish.
-  auto step = [&](int c, const Frag& f, int prev_c, const f32x4& prev_y) {
+  // One chunk. Its y is stored at the end, after the state update is issued, when the
+  // products that made it have long completed.
+  auto step = [&](int c, const Frag& f) {
     half4 vB;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
@@ -558,7 +529,6 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     yv = mfma32(f.r1, sB1, yv);
     u = mfma32(f.gl, cat8(vB, hz), u);
     yv = mfma32(f.gl, cat8(hz, vB), yv);
-    if (prev_c >= 0) store_y(prev_c, prev_y);
     const half8 uv = cat8(to_h4(u), vB);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -568,28 +538,31 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
       St[kt][3] *= f.dv[kt].w;
       St[kt] = mfma32(f.bk[kt], uv, St[kt]);
     }
-    return yv;
+    store_y(c, yv);
   };
 
-  // Two register sets alternate (the loop is unrolled by two), so the next
-  // chunk's LDS reads are in flight while this chunk's MFMAs run.
+  // ---- compute waves. The loop body has no branch around the reads: a read past the
+  // last chunk reads a slot that holds a repeat of it and is never used. (A read on one
+  // side of a branch only would make the compiler's wait at the join cover the next
+  // chunk's reads too.) Before each barrier every LDS read issued so far has completed.
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
   Frag fa, fb;
-  f32x4 ya = zero4(), yb = zero4();
-  if (nc > 0) read(0, fa);
-  // nothing is in flight from LDS when the loop starts: the wait-count pass then
-  // never holds this chunk's operands back behind the next chunk's reads
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  for (int c = 0; c < nc; c += 2) {
-    if (c + 1 < nc) read(c + 1, fb);
-    ya = step(c, fa, c - 1, yb);
-    lds_sync();
-    if (c + 1 < nc) {
-      if (c + 2 < nc) read(c + 2, fa);
-      yb = step(c + 1, fb, c, ya);
-      lds_sync();
-    }
+  sync();  // chunk 0
+  read(0, fa);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): nothing from LDS in flight when the loop starts
+  for (int c = 0;; c += 2) {
+    sync();  // chunk c + 1
+    read(c + 1, fb);
+    step(c, fa);
+    if (c + 1 >= nc) break;
+    sync();  // chunk c + 2
+    read(c + 2, fa);
+    step(c + 1, fb);
+    if (c + 2 >= nc) break;
   }
-  if (nc > 0) store_y(nc - 1, (nc - 1) % 2 == 0 ? ya : yb);
 
   if (p.s_dst) {
 #pragma unroll
@@ -707,7 +680,7 @@ hipError_t launch_chunked_split(const WkvCall& c) {
   const void* prep_fn = reinterpret_cast<const void*>(&wkv7_prep_kernel);
   const void* scan_fn = reinterpret_cast<const void*>(&wkv7_scan_kernel);
   const int prep_lds = kPrepWaves * kPrepLdsPerWave;
-  const int scan_lds = kRing * kSlotBytes;
+  const int scan_lds = kScanLds;
   static const hipError_t a1 = hipFuncSetAttribute(prep_fn, hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
   static const hipError_t a2 = hipFuncSetAttribute(scan_fn, hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
   if (a1 != hipSuccess) return a1;
