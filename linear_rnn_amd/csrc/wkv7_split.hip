@@ -376,6 +376,8 @@ constexpr int kSlotBytes = kRecBytes + kVBytes;   // 10,496
 constexpr int kScanLds = kSlots * kSlotBytes;     // 62,976
 constexpr int kLoads = kRecBlocks + 2;  // loads per lane per chunk: record blocks, e^gamma, v
 constexpr int kScanThreads = 64 * (kScanWaves + 1);
+// the load counter holds at most 63 outstanding operations: never more are in flight
+static_assert(kDist * kLoads < 64, "load counter");
 static_assert(kVBytes == 64 * 16 && kRecBlocks == 9, "one 16-byte piece of v per lane");
 
 __device__ __forceinline__ f32x4 mfma32(half8 a, half8 b, f32x4 c) {
@@ -521,14 +523,16 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     //   G V term (the record's G block holds G_u | G_y, so a B operand of V | 0
     //   or 0 | V selects one of them);
     //   S^T <- diag(e^{gamma_15}) S^T + [B- | K-] [U ; V] per key tile.
+    // the G V terms first: they do not depend on the state, so they need not wait for
+    // the previous chunk's update
+    f32x4 u = mfma32(f.gl, cat8(vB, hz), zero4());
+    f32x4 yv = mfma32(f.gl, cat8(hz, vB), zero4());
     const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
     const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
-    f32x4 u = mfma32(f.a0, sB0, zero4());
-    f32x4 yv = mfma32(f.r0, sB0, zero4());
+    u = mfma32(f.a0, sB0, u);
+    yv = mfma32(f.r0, sB0, yv);
     u = mfma32(f.a1, sB1, u);
     yv = mfma32(f.r1, sB1, yv);
-    u = mfma32(f.gl, cat8(vB, hz), u);
-    yv = mfma32(f.gl, cat8(hz, vB), yv);
     const half8 uv = cat8(to_h4(u), vB);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
