@@ -27,9 +27,9 @@
 // Kernel 2 (scan) carries the float32 state through the chunks. A head's 64
 // value rows are independent, so it is split over two workgroups; each has two
 // compute waves (16 value rows each, one SIMD each) that advance the state with
-// ten 16x16x32 MFMAs per chunk, and four loader waves that stream the records
-// and the needed v columns into a five-slot LDS ring, each load issued eight
-// chunk periods before it is needed. One LDS barrier per chunk.
+// ten 16x16x32 MFMAs per chunk, and one loader wave that streams the records and
+// the needed v columns straight into a six-slot LDS ring (global-to-LDS loads),
+// five chunks ahead. One LDS barrier per chunk.
 //
 // Every dependent MFMA chain keeps one instruction shape: chains that mixed
 // 16x16x32 and 16x16x16 f16 products gave wrong results on gfx950 (in whichever
