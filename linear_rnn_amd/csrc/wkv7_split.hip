@@ -131,10 +131,10 @@ constexpr int kFacRow = kN + 4;  // padded float row: token-layout reads of one 
 // Factor rows (float32, [row][key]), written in the key layout (lane = key j):
 //   E  row t     = e^{gamma_t},            t = 0..15
 //   Gq row t + 1 = e^{gamma_t - gamma_7},  t = -1..15
-//   Fk row t     = e^{gamma_7 - gamma_t},  t = 0..15
-// and e^{gamma_15 - gamma_t} = Gq_15 Fk_t is formed where it is used.
-constexpr int kRowE = 0, kRowG = 16, kRowF = 33, kFacRows = 49;
-constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 13,328 bytes: three 4-wave workgroups per CU
+// Fk_t = e^{gamma_7 - gamma_t} = 1 / Gq_t and e^{gamma_15 - gamma_t} = Gq_15 Fk_t are
+// formed where they are used.
+constexpr int kRowE = 0, kRowG = 16, kFacRows = 33;
+constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 8,976 bytes: four 4-wave workgroups per CU
 // After the factors are consumed the same wave area holds L_ab and L_rb ([t][s],
 // float32) and the rows of T and M_r (float16).
 constexpr int kLabOff = 0, kLrbOff = 16 * 16, kTmOffBytes = 2 * 16 * 16 * 4;
@@ -198,12 +198,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   }
 
   // ---- decay factors (lane = j): running products from token 0 (E) and outward from
-  // token 7 (Gq, Fk), so no factor exceeds w_min^-8
+  // token 7 (Gq), so no factor exceeds w_min^-8
   {
     const int j = lane;
-    float e = 1.f, gu = 1.f, gd = 1.f, fu = 1.f, fd = 1.f;
+    float e = 1.f, gu = 1.f, gd = 1.f;
     fac[(kRowG + 8) * kFacRow + j] = 1.f;  // Gq_7
-    fac[(kRowF + 7) * kFacRow + j] = 1.f;  // Fk_7
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
       e *= wc[q];
@@ -213,12 +212,6 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
         fac[(kRowG + 9 + q) * kFacRow + j] = gu;
         gd *= __builtin_amdgcn_rcpf(wc[7 - q]);  // Gq_t, t = 6 - q: divided by w_{t+1}
         fac[(kRowG + 7 - q) * kFacRow + j] = gd;
-        fu *= __builtin_amdgcn_rcpf(wc[8 + q]);  // Fk_t, t = 8 + q: divided by w_t
-        fac[(kRowF + 8 + q) * kFacRow + j] = fu;
-      }
-      if (q < 7) {
-        fd *= wc[7 - q];  // Fk_t, t = 6 - q: times w_{t+1}
-        fac[(kRowF + 6 - q) * kFacRow + j] = fd;
       }
     }
     st_off<float>(rec, (uint32_t)(kRecD + 4 * j), e);  // e^{gamma_15}
@@ -245,14 +238,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
     const float4 e0 = lds4(&fac[(kRowE + li) * kFacRow + col]);
     const float4 gqm1 = lds4(&fac[(kRowG + li) * kFacRow + col]);
     const float4 gq = lds4(&fac[(kRowG + li + 1) * kFacRow + col]);
-    const float4 fk = lds4(&fac[(kRowF + li) * kFacRow + col]);
     const float4 g15 = lds4(&fac[(kRowG + 16) * kFacRow + col]);
     const uint2 ra = live ? ar[kt] : z2, rv2 = live ? rr[kt] : z2, rb = live ? br[kt] : z2, rk = live ? kr[kt] : z2;
     half4 bbar, kbar;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float av = bf4(ra, e), rv = bf4(rv2, e), bv = bf4(rb, e), kv = bf4(rk, e);
-      const float f = el(fk, e);
+      const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
       const float suf = el(g15, e) * f;  // e^{gamma_15 - gamma_t}
       const float ah = av * el(gqm1, e), rh = rv * el(gq, e), bh = bv * f, kh = kv * f;
       Lab = mfma4(ah, bh, Lab);
