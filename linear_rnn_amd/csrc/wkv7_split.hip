@@ -129,15 +129,17 @@ struct PrepParams {
 constexpr int kPrepWaves = 4;
 constexpr int kFacRow = kN + 4;  // padded float row: token-layout reads of one row spread over the banks
 // Factor rows (float32, [row][key]), written in the key layout (lane = key j):
-//   E  row t     = e^{gamma_t},            t = 0..15
+//   E  row t + 1 = e^{gamma_t},            t = -1..15
 //   Gq row t + 1 = e^{gamma_t - gamma_7},  t = -1..15
 // Fk_t = e^{gamma_7 - gamma_t} = 1 / Gq_t and e^{gamma_15 - gamma_t} = Gq_15 Fk_t are
 // formed where they are used.
-constexpr int kRowE = 0, kRowG = 16, kFacRows = 33;
-constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 8,976 bytes: four 4-wave workgroups per CU
-// After the factors are consumed the same wave area holds L_ab and L_rb ([t][s],
-// float32) and the rows of T and M_r (float16).
-constexpr int kLabOff = 0, kLrbOff = 16 * 16, kTmOffBytes = 2 * 16 * 16 * 4;
+constexpr int kRowE = 0, kRowG = 17, kFacRows = 34;
+constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 9,248 bytes: four 4-wave workgroups per CU
+// After the factors are consumed the same wave area holds L_ab ([t][s], float32), the
+// right-hand sides of the solve (the identity, then L_rb, [32][16] float32) and the
+// rows of T and M_r (float16).
+constexpr int kLabOff = 0, kRhsOff = 16 * 16, kTmOffBytes = 3 * 16 * 16 * 4;
+static_assert(kTmOffBytes + 2 * 16 * 16 * 2 <= kPrepLdsPerWave, "solve area");
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -153,7 +155,7 @@ __device__ __forceinline__ void pin16(float (&x)[16]) {
 }
 __device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
-__global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu(4))) void wkv7_prep_kernel(PrepParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -192,9 +194,22 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
 #pragma unroll
   for (int t = 0; t < kC; ++t) {
     const int tt = min(t, nt - 1);
-    float x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
-    x = x < kWMin ? kWMin : x;  // clamp (a NaN passes through)
-    wc[t] = t < nt ? x : 1.f;
+    const float x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
+    wc[t] = x < kWMin ? kWMin : x;  // clamp (a NaN passes through)
+  }
+  // The last chunk of a sequence may run past its end: its tokens t >= nt become
+  // identity tokens (w = 1, r = k = a = b = 0). The branch is the same for the whole wave.
+  if (nt < kC) {
+    const uint2 z2 = make_uint2(0u, 0u);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      rr[kt] = live ? rr[kt] : z2;
+      ar[kt] = live ? ar[kt] : z2;
+      br[kt] = live ? br[kt] : z2;
+      kr[kt] = live ? kr[kt] : z2;
+    }
+#pragma unroll
+    for (int t = 0; t < kC; ++t) wc[t] = t < nt ? wc[t] : 1.f;
   }
 
   // ---- decay factors (lane = j): running products from token 0 (E) and outward from
@@ -202,11 +217,12 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   {
     const int j = lane;
     float e = 1.f, gu = 1.f, gd = 1.f;
+    fac[kRowE * kFacRow + j] = 1.f;        // E_{-1}
     fac[(kRowG + 8) * kFacRow + j] = 1.f;  // Gq_7
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
       e *= wc[q];
-      fac[(kRowE + q) * kFacRow + j] = e;  // E_q
+      fac[(kRowE + q + 1) * kFacRow + j] = e;  // E_q
       if (q < 8) {
         gu *= wc[8 + q];  // Gq_t, t = 8 + q: times w_t
         fac[(kRowG + 9 + q) * kFacRow + j] = gu;
@@ -230,16 +246,15 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   half4 Ahat[4];
   f32x4 Rhat[4];
   f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
-  const uint2 z2 = make_uint2(0u, 0u);
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int col = 16 * kt + 4 * g;
-    const float4 em1 = li == 0 ? make_float4(1.f, 1.f, 1.f, 1.f) : lds4(&fac[(kRowE + max(li - 1, 0)) * kFacRow + col]);
-    const float4 e0 = lds4(&fac[(kRowE + li) * kFacRow + col]);
+    const float4 em1 = lds4(&fac[(kRowE + li) * kFacRow + col]);
+    const float4 e0 = lds4(&fac[(kRowE + li + 1) * kFacRow + col]);
     const float4 gqm1 = lds4(&fac[(kRowG + li) * kFacRow + col]);
     const float4 gq = lds4(&fac[(kRowG + li + 1) * kFacRow + col]);
     const float4 g15 = lds4(&fac[(kRowG + 16) * kFacRow + col]);
-    const uint2 ra = live ? ar[kt] : z2, rv2 = live ? rr[kt] : z2, rb = live ? br[kt] : z2, rk = live ? kr[kt] : z2;
+    const uint2 ra = ar[kt], rv2 = rr[kt], rb = br[kt], rk = kr[kt];
     half4 bbar, kbar;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -274,13 +289,14 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   // every x[s], s < s2. The factor rows are no longer read, so their area is reused;
   // the row of L_ab for the next step is read while the current one is applied.
   float* lab = fac + kLabOff;
-  float* lrb = fac + kLrbOff;
+  float* rhs = fac + kRhsOff;
   __builtin_amdgcn_s_waitcnt(0xc07f);  // every factor read of this wave has completed
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     lab[(4 * g + e) * 16 + li] = Lab[e];
-    lrb[(4 * g + e) * 16 + li] = Lrb[e];
+    rhs[(4 * g + e) * 16 + li] = 4 * g + e == li ? 1.f : 0.f;  // identity: the rows of T
+    rhs[(16 + 4 * g + e) * 16 + li] = Lrb[e];                 // L_rb: the rows of M_r
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
@@ -288,10 +304,9 @@ __global__ __launch_bounds__(64 * kPrepWaves) void wkv7_prep_kernel(PrepParams p
   float x[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float4 v = lds4(&lrb[row * 16 + 4 * q]);
-    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));  // read by every lane, no branch
+    const float4 v = lds4(&rhs[((g & 1) * 16 + row) * 16 + 4 * q]);  // lanes 32-63 repeat lanes 0-31
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * q + e] = g == 0 ? (4 * q + e == row ? 1.f : 0.f) : el(v, e);
+    for (int e = 0; e < 4; ++e) x[4 * q + e] = el(v, e);
   }
   float4 cur[4], nxt[4];
 #pragma unroll
