@@ -352,8 +352,8 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args):
 def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
     """The hybrid mode end to end on a 12-layer stack at the 0.1B width (D=768): a T-token prompt
     through every layer in one call, then single-token calls with the per-layer states carried.
-    Synthetic bfloat16 weights. The fused time-mix prefill (one workgroup per head) is also timed
-    alone at the prompt shape, since it dominates the prompt."""
+    Synthetic bfloat16 weights. The fused time-mix prefill is also timed alone at the prompt shape,
+    both as the chunked prefill (what the stack's prompt runs) and token by token."""
     import numpy as np
     from linear_rnn_amd.inputs import make_stack_inputs
     z = make_stack_inputs(L, B, T, H, "bf16", seed=7100, with_state=False)
@@ -404,6 +404,15 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
 
     tm()
     ms_tmix = time_region(torch, tm, 5)
+
+    def tmc():
+        wkv.rwkv7_tmix_prefill_ex(*(dt[n] for n in names), dt["ln_w"], dt["ln_b"], dt["state_in"], o, so,
+                                  algo=wkv.RWKV7_ALGO_CHUNKED_SPLIT)
+
+    tmc()
+    ms_tmix_ch = time_region(torch, tmc, 5)
+    # algorithmic bytes: r, k, v, kk, a_lr (bf16), w_raw and out (float32) per element, the state in and out
+    tm_bytes = B * T * H * N * (5 * 2 + 4 + 4) + 2 * B * H * N * N * 4
     flops = FLOP_REC * B * T * H
     return {
         "prompt_tokens_per_s": B * T / (ms_prompt * 1e-3), "ms_per_prompt": ms_prompt,
@@ -412,8 +421,14 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
         "config": {"workload": "12-layer stack, D=768 (H=12), B=%d, %d-token prompt then single-token calls, "
                                "synthetic bf16 weights, fp32 residual stream and states" % (B, T),
                    "L": L, "B": B, "T": T, "H": H, "N": N},
-        "tmix_prefill_alone": {
-            "ms": ms_tmix, "share_of_prompt": ms_tmix * L / ms_prompt,
+        "tmix_prefill_chunked": {
+            "ms": ms_tmix_ch, "share_of_prompt": ms_tmix_ch * L / ms_prompt,
+            "roofline": {"bound": "hbm", "achieved": tm_bytes / (ms_tmix_ch * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": tm_bytes / (ms_tmix_ch * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "kernel": "wkv7_prep_kernel<time-mix> + wkv7_scan_kernel + tmix_ln_kernel",
+                         "algorithmic_bytes": tm_bytes, "traffic": None}},
+        "tmix_prefill_sequential": {
+            "ms": ms_tmix,
             "roofline": {"bound": "alu", "achieved": flops / (ms_tmix * 1e-3) / 1e12,
                          "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                          "frac": flops / (ms_tmix * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,

@@ -219,6 +219,24 @@ int rwkv7_tmix_prefill(const void *r, const float *w_raw, const void *k, const v
                        float *state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
 
 /*
+ * rwkv7_tmix_prefill with a choice of algorithm:
+ *   RWKV7_ALGO_AUTO, RWKV7_ALGO_SEQUENTIAL  the token-by-token kernel (what
+ *                      rwkv7_tmix_prefill runs; bit-identical to T single steps)
+ *   RWKV7_ALGO_CHUNKED_SPLIT  bfloat16 inputs only: the chunked prefill of
+ *                      rwkv7_wkv_prefill_ex (prep and scan kernels, its cached device
+ *                      workspace), with the decay exp(-exp(w_raw)), the unit key and
+ *                      the two slots formed inside the prep, y written to out and
+ *                      ln_x applied to out in place. Decays below 2^-15 are clamped
+ *                      there (as in that prefill); results match the definition to the
+ *                      chunked tolerance, not bit for bit with the steps.
+ * Any other algo, or CHUNKED_SPLIT with float32 inputs: RWKV7_ERR_ALGO.
+ */
+int rwkv7_tmix_prefill_ex(const void *r, const float *w_raw, const void *k, const void *v, const void *kk,
+                          const void *a_lr, const float *ln_w, const float *ln_b, const float *state_in, float *out,
+                          float *state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, int algo,
+                          void *stream);
+
+/*
  * Single-token step of the fused time-mix operator (RNN mode, G0 notes section
  * 3.2): rwkv7_tmix_prefill with T == 1 (else RWKV7_ERR_SHAPE). T consecutive
  * steps give the same bits as one rwkv7_tmix_prefill over the T tokens.
@@ -288,7 +306,9 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  *
  * With bfloat16 weights, x and o are rounded to bfloat16 for the projections and
  * r, k, v, kk, a_lr are bfloat16 operator inputs; projections accumulate in
- * float32. Token shift, the channel mix, the output gate and the low-rank
+ * float32. A bfloat16 call of T >= 32 tokens runs the operator as
+ * rwkv7_tmix_prefill_ex with RWKV7_ALGO_CHUNKED_SPLIT (a prompt); other calls run
+ * it token by token. Token shift, the channel mix, the output gate and the low-rank
  * projections of the full model are not included. Every pointer is 16-byte
  * aligned; x and states may not overlap each other or the weights. B*T must be
  * below 2^31. L == 0 or an empty x does nothing. The projections run on rocBLAS

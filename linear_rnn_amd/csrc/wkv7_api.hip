@@ -131,11 +131,16 @@ int validate_tmix(const void* const in[5], const float* w_raw, const float* ln_w
 
 int run_tmix(const void* r, const float* w_raw, const void* k, const void* v, const void* kk, const void* a_lr,
              const float* ln_w, const float* ln_b, const float* state_in, float* out, float* state_out, int64_t B,
-             int64_t T, int64_t H, int64_t N, int dtype, bool step, void* stream) {
+             int64_t T, int64_t H, int64_t N, int dtype, int algo, bool step, void* stream) {
   const void* in[5] = {r, k, v, kk, a_lr};
   const int st = validate_tmix(in, w_raw, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype);
   if (st != RWKV7_OK) return st;
   if (step && T != 1) return RWKV7_ERR_SHAPE;
+  // the token-by-token kernel (AUTO keeps the bit-exact match with T single steps), or
+  // the chunked prefill for bfloat16 inputs
+  if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SEQUENTIAL && algo != RWKV7_ALGO_CHUNKED_SPLIT)
+    return RWKV7_ERR_ALGO;
+  if (algo == RWKV7_ALGO_CHUNKED_SPLIT && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_ALGO;
   if (B * H == 0) return RWKV7_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -144,7 +149,9 @@ int run_tmix(const void* r, const float* w_raw, const void* k, const void* v, co
     return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
   }
   rwkv7::TmixCall c{{r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, T, (int32_t)H}, B, H, dtype, s};
+  c.chunked = algo == RWKV7_ALGO_CHUNKED_SPLIT;
   e = rwkv7::launch_tmix(c);
+  if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;
   return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 
@@ -259,13 +266,23 @@ int rwkv7_wkv_backward(const void* r, const void* w, const void* k, const void* 
 int rwkv7_tmix_prefill(const void* r, const float* w_raw, const void* k, const void* v, const void* kk,
                        const void* a_lr, const float* ln_w, const float* ln_b, const float* state_in, float* out,
                        float* state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void* stream) {
-  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, false, stream);
+  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, RWKV7_ALGO_AUTO,
+                  false, stream);
+}
+
+int rwkv7_tmix_prefill_ex(const void* r, const float* w_raw, const void* k, const void* v, const void* kk,
+                          const void* a_lr, const float* ln_w, const float* ln_b, const float* state_in, float* out,
+                          float* state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, int algo,
+                          void* stream) {
+  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, algo, false,
+                  stream);
 }
 
 int rwkv7_tmix_step(const void* r, const float* w_raw, const void* k, const void* v, const void* kk,
                     const void* a_lr, const float* ln_w, const float* ln_b, const float* state_in, float* out,
                     float* state_out, int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void* stream) {
-  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, true, stream);
+  return run_tmix(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, B, T, H, N, dtype, RWKV7_ALGO_AUTO,
+                  true, stream);
 }
 
 

@@ -53,8 +53,14 @@ struct TmixCall {
   int64_t B, H;
   int dtype;  // RWKV7_DTYPE_* of r, k, v, kk, a_lr
   hipStream_t stream;
+  bool chunked = false;  // a prefill (T > 1, bfloat16) through the chunked prep and scan
 };
 hipError_t launch_tmix(const TmixCall& c);
+// The fused operator as a chunked prefill (bfloat16 inputs): the prep forms the
+// decay, the unit key and the two slots, the scan writes y into out, and ln_x
+// normalises it in place. Decays below 2^-15 are clamped, as in the chunked
+// prefill of the recurrence.
+hipError_t launch_tmix_chunked(const TmixCall& c);
 
 // Reverse-mode derivatives of the recurrence: a checkpointing forward pass and
 // a reverse pass over the checkpoints, all gradients float32.
@@ -88,7 +94,10 @@ hipError_t launch_stack(const StackCall& c);
 // Device memory cached per (device, stream), shared by the launchers that need
 // scratch: calls on one stream run in order, so they can share it. Grown on
 // demand (synchronising the stream first), never shrunk.
-hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out);
+// Two independent buffers per (device, stream): the chunked kernels' records use
+// their own, so a caller holding the general one (the layer stack) can run them.
+constexpr int kWorkspaceGeneral = 0, kWorkspaceChunks = 1;
+hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out, int slot = kWorkspaceGeneral);
 
 // state_out <- state_in (zeros when state_in is null) for B*H heads.
 hipError_t launch_state_copy(const float* s_in, float* s_out, int64_t units, hipStream_t stream);

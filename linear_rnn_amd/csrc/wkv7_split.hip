@@ -61,6 +61,7 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "wkv7_device.hpp"
@@ -113,12 +114,18 @@ __device__ __forceinline__ void st_off(void* base, uint32_t byte_off, V v) {
 
 // ============================================================================ kernel 1: prep
 
+// Inputs of the prep. The plain recurrence takes r, w, k, a, b (bfloat16). The fused
+// time-mix operator takes r, k (bfloat16), w_raw (float32) in place of w, and kk,
+// a_lr in place of a, b; the prep then forms w = exp(-exp(w_raw)), the unit key
+// kk^ = kk / max(|kk|, 1e-12) over the head's 64 channels, a = -kk^ and b = kk^ a_lr.
+constexpr int kPrepPlain = 0, kPrepTmix = 1;
 struct PrepParams {
   const uint16_t* r;
-  const uint16_t* w;
+  const uint16_t* w;   // plain: the decay
+  const float* w_raw;  // time-mix: the decay's log-log form
   const uint16_t* k;
-  const uint16_t* a;
-  const uint16_t* b;
+  const uint16_t* a;   // plain: a; time-mix: kk
+  const uint16_t* b;   // plain: b; time-mix: a_lr
   unsigned char* rec;  // [unit][chunk of slab][kRecBytes]
   int32_t T, H;
   int32_t c0;     // first chunk of the slab
@@ -155,6 +162,7 @@ __device__ __forceinline__ void pin16(float (&x)[16]) {
 }
 __device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
+template <int MODE>
 __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu(4))) void wkv7_prep_kernel(PrepParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int lane = threadIdx.x & 63;
@@ -194,7 +202,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int t = 0; t < kC; ++t) {
     const int tt = min(t, nt - 1);
-    const float x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
+    float x;
+    if constexpr (MODE == kPrepTmix)
+      x = expf(-expf(ld_off<float>(p.w_raw + base, (uint32_t)(tt * tstride + lane) * 4u)));
+    else
+      x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
     wc[t] = x < kWMin ? kWMin : x;  // clamp (a NaN passes through)
   }
   // The last chunk of a sequence may run past its end: its tokens t >= nt become
@@ -246,6 +258,22 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
   half4 Ahat[4];
   f32x4 Rhat[4];
   f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
+  // time-mix: 1 / max(|kk|, 1e-12) of this lane's token (its 64 channels are spread over
+  // the four lanes li, li + 16, li + 32, li + 48)
+  float inv = 1.f;
+  if constexpr (MODE == kPrepTmix) {
+    float n2 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = bf4(ar[kt], e);
+        n2 = fmaf(x, x, n2);
+      }
+    n2 += __shfl_xor(n2, 16);
+    n2 += __shfl_xor(n2, 32);
+    inv = 1.f / fmaxf(sqrtf(n2), 1e-12f);
+  }
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int col = 16 * kt + 4 * g;
@@ -258,7 +286,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
     half4 bbar, kbar;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float av = bf4(ra, e), rv = bf4(rv2, e), bv = bf4(rb, e), kv = bf4(rk, e);
+      float av = bf4(ra, e), bv = bf4(rb, e);
+      const float rv = bf4(rv2, e), kv = bf4(rk, e);
+      if constexpr (MODE == kPrepTmix) {  // a = -kk^, b = kk^ a_lr
+        const float kh1 = av * inv;
+        av = -kh1;
+        bv = kh1 * bv;
+      }
       const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
       const float suf = el(g15, e) * f;  // e^{gamma_15 - gamma_t}
       const float ah = av * el(gqm1, e), rh = rv * el(gq, e), bh = bv * f, kh = kv * f;
@@ -594,7 +628,7 @@ struct Workspace {
   size_t bytes = 0;
 };
 std::mutex g_ws_mu;
-std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+std::map<std::tuple<int, uintptr_t, int>, Workspace> g_ws;
 
 
 // Record-buffer budget per slab: the scan of a slab reads what its prep wrote
@@ -613,12 +647,12 @@ size_t slab_budget_bytes() {
 
 }  // namespace
 
-hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out) {
+hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out, int slot) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
+  Workspace& ws = g_ws[std::make_tuple(dev, reinterpret_cast<uintptr_t>(stream), slot)];
   if (ws.bytes < bytes) {
     if (ws.ptr) {
       // work already queued on this stream may still use the old buffer
@@ -650,7 +684,7 @@ int64_t prep_waves_resident() {
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&wkv7_prep_kernel),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>),
                                                    64 * kPrepWaves, kPrepWaves * kPrepLdsPerWave) != hipSuccess ||
       per_cu <= 0)
     per_cu = 2;
@@ -659,12 +693,25 @@ int64_t prep_waves_resident() {
 
 }  // namespace
 
-hipError_t launch_chunked_split(const WkvCall& c) {
-  if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
-  const int64_t units = c.B * c.H;
-  const int64_t nch = (c.T + kC - 1) / kC;
+namespace {
+
+// One chunked pass: the prep (in the given input mode) and the scan, slab by slab.
+struct SplitJob {
+  PrepParams in;  // input pointers (and T, H); the rest is filled per slab
+  int mode;
+  const uint16_t* v;
+  float* y;
+  const float* s_in;
+  float* s_out;
+  int64_t B, T, H;
+  hipStream_t stream;
+};
+
+hipError_t run_split(const SplitJob& j) {
+  const int64_t units = j.B * j.H;
+  const int64_t nch = (j.T + kC - 1) / kC;
   // In-sequence offsets are 32-bit: T * H * 64 elements must stay below 2^31.
-  if (c.T * c.H * kN >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  if (j.T * j.H * kN >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int64_t per_chunk = units * kRecBytes;
   int64_t slab = (int64_t)(slab_budget_bytes() / (size_t)per_chunk);
   slab = slab < 1 ? 1 : slab;
@@ -679,45 +726,126 @@ hipError_t launch_chunked_split(const WkvCall& c) {
   }
   const int64_t nslab = (nch + slab - 1) / slab;
   if (units * slab > (int64_t(1) << 30)) return hipErrorNotSupported;
-  const bool tmp_state = nslab > 1 && c.s_out == nullptr;
+  const bool tmp_state = nslab > 1 && j.s_out == nullptr;
   const size_t rec_bytes = (size_t)(units * slab * kRecBytes);
   const size_t bytes = rec_bytes + (tmp_state ? (size_t)units * kN * kN * 4 : 0);
   void* ws = nullptr;
-  hipError_t e = device_workspace(c.stream, bytes, &ws);
+  hipError_t e = device_workspace(j.stream, bytes, &ws, kWorkspaceChunks);
   if (e != hipSuccess) return e;
   unsigned char* rec = static_cast<unsigned char*>(ws);
-  float* carry = tmp_state ? reinterpret_cast<float*>(rec + rec_bytes) : static_cast<float*>(c.s_out);
+  float* carry = tmp_state ? reinterpret_cast<float*>(rec + rec_bytes) : j.s_out;
 
-  const void* prep_fn = reinterpret_cast<const void*>(&wkv7_prep_kernel);
+  const void* prep_fn = j.mode == kPrepTmix ? reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepTmix>)
+                                            : reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>);
   const void* scan_fn = reinterpret_cast<const void*>(&wkv7_scan_kernel);
   const int prep_lds = kPrepWaves * kPrepLdsPerWave;
   const int scan_lds = kScanLds;
-  static const hipError_t a1 = hipFuncSetAttribute(prep_fn, hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
+  static const hipError_t a0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
+  static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepTmix>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
   static const hipError_t a2 = hipFuncSetAttribute(scan_fn, hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
+  if (a0 != hipSuccess) return a0;
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
 
   for (int64_t s = 0; s < nslab; ++s) {
     const int64_t c0 = s * slab;
     const int64_t ncs = (nch - c0 < slab) ? nch - c0 : slab;
-    PrepParams pp{static_cast<const uint16_t*>(c.in[0]), static_cast<const uint16_t*>(c.in[1]),
-                  static_cast<const uint16_t*>(c.in[2]), static_cast<const uint16_t*>(c.in[4]),
-                  static_cast<const uint16_t*>(c.in[5]), rec, (int32_t)c.T, (int32_t)c.H, (int32_t)c0,
-                  (int32_t)ncs, (int32_t)(units * ncs)};
+    PrepParams pp = j.in;
+    pp.rec = rec;
+    pp.T = (int32_t)j.T;
+    pp.H = (int32_t)j.H;
+    pp.c0 = (int32_t)c0;
+    pp.nc = (int32_t)ncs;
+    pp.items = (int32_t)(units * ncs);
     void* pargs[] = {&pp};
     const uint32_t pblocks = (uint32_t)((units * ncs + kPrepWaves - 1) / kPrepWaves);
-    e = hipLaunchKernel(prep_fn, dim3(pblocks), dim3(64 * kPrepWaves), pargs, prep_lds, c.stream);
+    e = hipLaunchKernel(prep_fn, dim3(pblocks), dim3(64 * kPrepWaves), pargs, prep_lds, j.stream);
     if (e != hipSuccess) return e;
-    ScanParams sp{rec, static_cast<const uint16_t*>(c.in[3]), c.y,
-                  s == 0 ? static_cast<const float*>(c.s_in) : carry,
-                  s == nslab - 1 ? static_cast<float*>(c.s_out) : carry, (int32_t)c.T, (int32_t)c.H,
-                  (int32_t)c0, (int32_t)ncs};
+    ScanParams sp{rec,
+                  j.v,
+                  j.y,
+                  s == 0 ? j.s_in : carry,
+                  s == nslab - 1 ? j.s_out : carry,
+                  (int32_t)j.T,
+                  (int32_t)j.H,
+                  (int32_t)c0,
+                  (int32_t)ncs};
     void* sargs[] = {&sp};
     e = hipLaunchKernel(scan_fn, dim3((uint32_t)(units * kWgPerHead)), dim3(kScanThreads), sargs, scan_lds,
-                        c.stream);
+                        j.stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Sum over the 64 lanes of a wave (every lane ends with the same bits).
+__device__ __forceinline__ float wave_sum64(float x) {
+  x = row16_sum(x);
+  x = x + __shfl_xor(x, 16);
+  x = x + __shfl_xor(x, 32);
+  return x;
+}
+
+// ln_x in place on y [rows, 64] (a row is one token of one head): a GroupNorm with
+// one group per head, mean and population variance over the 64 channels, then the
+// per-channel affine. One wave per row, lane = channel.
+constexpr float kGroupNormEps = 64e-5f;
+__global__ __launch_bounds__(256) void tmix_ln_kernel(float* y, const float* ln_w, const float* ln_b, int64_t rows,
+                                                      int32_t H) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const int h = (int)(row % H);
+  float* yr = y + row * kN;
+  const float v = yr[lane];
+  const float mu = wave_sum64(v) * (1.f / kN);
+  const float d = v - mu;
+  const float var = wave_sum64(d * d) * (1.f / kN);
+  const float o = d * (1.f / sqrtf(var + kGroupNormEps));
+  const float gw = ln_w ? ln_w[h * kN + lane] : 1.f;
+  const float gb = ln_b ? ln_b[h * kN + lane] : 0.f;
+  yr[lane] = fmaf(o, gw, gb);
+}
+
+}  // namespace
+
+hipError_t launch_chunked_split(const WkvCall& c) {
+  if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
+  PrepParams in{};
+  in.r = static_cast<const uint16_t*>(c.in[0]);
+  in.w = static_cast<const uint16_t*>(c.in[1]);
+  in.k = static_cast<const uint16_t*>(c.in[2]);
+  in.a = static_cast<const uint16_t*>(c.in[4]);
+  in.b = static_cast<const uint16_t*>(c.in[5]);
+  SplitJob j{in, kPrepPlain, static_cast<const uint16_t*>(c.in[3]), c.y, static_cast<const float*>(c.s_in),
+             static_cast<float*>(c.s_out), c.B, c.T, c.H, c.stream};
+  return run_split(j);
+}
+
+hipError_t launch_tmix_chunked(const TmixCall& c) {
+  if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
+  const TmixParams& t = c.p;
+  PrepParams in{};
+  in.r = static_cast<const uint16_t*>(t.r);
+  in.w_raw = t.w_raw;
+  in.k = static_cast<const uint16_t*>(t.k);
+  in.a = static_cast<const uint16_t*>(t.kk);
+  in.b = static_cast<const uint16_t*>(t.a_lr);
+  // the scan writes y into out; ln_x then normalises it in place
+  SplitJob j{in, kPrepTmix, static_cast<const uint16_t*>(t.v), t.out, t.s_in, t.s_out, c.B, t.T, c.H, c.stream};
+  hipError_t e = run_split(j);
+  if (e != hipSuccess) return e;
+  const int64_t rows = c.B * t.T * c.H;
+  float* out = t.out;
+  const float* lw = t.ln_w;
+  const float* lb = t.ln_b;
+  int64_t nrows = rows;
+  int32_t h32 = (int32_t)c.H;
+  void* args[] = {&out, &lw, &lb, &nrows, &h32};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&tmix_ln_kernel), dim3((uint32_t)((rows + 3) / 4)),
+                         dim3(256), args, 0, c.stream);
 }
 
 }  // namespace rwkv7

@@ -21,7 +21,9 @@
 // input projection (rocBLAS GEMM, float32 accumulation and output), the
 // activation kernel below, the fused time-mix kernel (one workgroup per head),
 // a cast of o, and the output projection accumulated into x by the GEMM
-// (beta = 1). Intermediates live in the per-(device, stream) workspace.
+// (beta = 1). Intermediates live in the per-(device, stream) workspace. A
+// bfloat16 prompt of 32 tokens or more runs the time-mix operator as a chunked
+// prefill (its own workspace); shorter calls run it token by token.
 #include <rocblas/rocblas.h>
 
 #include <map>
@@ -125,6 +127,10 @@ hipError_t gemm(rocblas_handle h, bool bf16, const void* X, const void* W, float
   return st == rocblas_status_success ? hipSuccess : hipErrorUnknown;
 }
 
+// bfloat16 prompts of at least this many tokens run the time-mix operator as a
+// chunked prefill (shorter ones and single-token calls run it token by token)
+constexpr int64_t kChunkedPromptMin = 32;
+
 uint32_t grid_for(int64_t n) {
   int64_t b = (n + 255) / 256;
   return (uint32_t)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
@@ -186,6 +192,7 @@ hipError_t launch_stack(const StackCall& c) {
     TmixCall tc{{in[0], w_raw, in[1], in[2], in[3], in[4], vecs + 3 * D, vecs + 4 * D, state, o, state, c.T,
                  (int32_t)c.H},
                 c.B, c.H, c.dtype, c.stream};
+    tc.chunked = bf16 && c.T >= kChunkedPromptMin;
     e = launch_tmix(tc);
     if (e != hipSuccess) return e;
     const void* oin = o;

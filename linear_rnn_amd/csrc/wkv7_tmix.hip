@@ -258,6 +258,7 @@ hipError_t launch_cfg(const TmixCall& c) {
 }  // namespace
 
 hipError_t launch_tmix(const TmixCall& c) {
+  if (c.chunked && c.dtype == 1 && c.p.T > 1) return launch_tmix_chunked(c);
   // the single-token step: one token per block, four waves of 16 rows (bound by HBM);
   // a prefill: sixteen-token blocks, eight waves of 8 rows (two per SIMD, to hide the
   // per-token dependency chain)

@@ -28,7 +28,8 @@ RWKV7_ALGO_CHUNKED = 2
 RWKV7_ALGO_CHUNKED_SPLIT = 3
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
-            "rwkv7_tmix_prefill", "rwkv7_tmix_step", "rwkv7_wkv_backward", "rwkv7_stack_forward", "rwkv7_wkv_strerror")
+            "rwkv7_tmix_prefill", "rwkv7_tmix_prefill_ex", "rwkv7_tmix_step", "rwkv7_wkv_backward",
+            "rwkv7_stack_forward", "rwkv7_wkv_strerror")
 
 _lib = None
 _lock = threading.Lock()
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
                 f = getattr(L, name)
                 f.restype = ci
                 f.argtypes = [vp] * 11 + [i64] * 4 + [ci, vp]
+            L.rwkv7_tmix_prefill_ex.restype = ci
+            L.rwkv7_tmix_prefill_ex.argtypes = [vp] * 11 + [i64] * 4 + [ci, ci, vp]
             L.rwkv7_wkv_backward.restype = ci
             L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [i64] * 4 + [ci, vp]
             L.rwkv7_stack_forward.restype = ci
@@ -168,19 +171,27 @@ def rwkv7_tmix_prefill(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, stat
                                     _stream(stream)))
 
 
+def rwkv7_tmix_prefill_ex(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, algo=RWKV7_ALGO_AUTO,
+                          stream=None):
+    """Fused time-mix prefill with an explicit algorithm (RWKV7_ALGO_AUTO / _SEQUENTIAL / _CHUNKED_SPLIT)."""
+    _check(lib().rwkv7_tmix_prefill_ex(*_tmix_args(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out),
+                                       int(algo), _stream(stream)))
+
+
 def rwkv7_tmix_step(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, stream=None):
     """Fused time-mix single-token step (T == 1); state_out may be state_in."""
     _check(lib().rwkv7_tmix_step(*_tmix_args(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out),
                                  _stream(stream)))
 
 
-def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, want_state=True, stream=None):
+def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, want_state=True, algo=RWKV7_ALGO_AUTO,
+         stream=None):
     """Allocate out ([B,T,H,64] float32) and the final state, run the fused prefill, return (out, state_out)."""
     import torch
     B, T, H, N = r.shape
     out = torch.empty((B, T, H, N), dtype=torch.float32, device=r.device)
     s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device) if want_state else None
-    rwkv7_tmix_prefill(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, s_out, stream=stream)
+    rwkv7_tmix_prefill_ex(r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, s_out, algo=algo, stream=stream)
     return out, s_out
 
 

@@ -216,6 +216,18 @@ def test_tmix_aliasing(L):
     assert tcall(L, p=p, B=0) == OK
 
 
+def test_tmix_prefill_ex_algorithms(L):
+    """AUTO and SEQUENTIAL, or CHUNKED_SPLIT with bfloat16 inputs; everything else is refused before any launch."""
+    def xcall(algo, dtype=BF16, B=2):
+        return L.rwkv7_tmix_prefill_ex(*(list(ptrs(11)) + [B, 3, 4, 64, dtype, algo, None]))
+    assert xcall(wkv.RWKV7_ALGO_CHUNKED_SPLIT, dtype=F32) == E_ALGO
+    for algo in (wkv.RWKV7_ALGO_CHUNKED, 4, -1):
+        assert xcall(algo) == E_ALGO, algo
+    for algo in (wkv.RWKV7_ALGO_AUTO, wkv.RWKV7_ALGO_SEQUENTIAL, wkv.RWKV7_ALGO_CHUNKED_SPLIT):
+        assert xcall(algo, B=0) == OK, algo
+    assert xcall(wkv.RWKV7_ALGO_AUTO, dtype=7) == E_DTYPE
+
+
 def test_tmix_empty(L):
     assert tcall(L, B=0) == OK and tcall(L, H=0) == OK
     p = ptrs(11)

@@ -124,3 +124,79 @@ def test_decode_shape_sampled(torch):
         orf, srf = ref(xs)
         e = (rel(o[b, :, h], orf[0, :, 0]), rel(s[b, h], srf[0, 0]))
         assert max(e) <= TOL_BF16, ((b, h), e)
+
+
+# ---- the chunked prefill of the fused operator (RWKV7_ALGO_CHUNKED_SPLIT, bfloat16 inputs)
+
+CH = wkv.RWKV7_ALGO_CHUNKED_SPLIT
+
+
+def run_ch(torch, d, state=True, affine=True, algo=CH):
+    o, s = wkv.tmix(*(d[n] for n in NAMES), d["ln_w"] if affine else None, d["ln_b"] if affine else None,
+                    d["state_in"] if state else None, algo=algo)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 2, 1), (1, 17, 2), (2, 37, 3), (3, 100, 5), (1, 300, 12), (2, 1000, 4)])
+def test_chunked_vs_oracle(torch, B, T, H):
+    say("tmix chunked", B, T, H)
+    x = make_tmix_inputs(CONFIGS[1], B=B, T=T, H=H, seed=500 + T)
+    o, s = run_ch(torch, dev(torch, x))
+    orf, srf = ref(x)
+    e = (rel(o, orf), rel(s, srf))
+    say("tmix chunked errors", e)
+    assert max(e) <= TOL_BF16, e
+
+
+def test_chunked_zero_state_null_affine_zero_key(torch):
+    """state_in NULL, ln_w / ln_b NULL, and all-zero removal-key rows (a = b = 0) on the chunked path."""
+    say("tmix chunked, NULL state and affine, zero kk rows")
+    x = make_tmix_inputs(CONFIGS[1], B=2, T=70, H=3, seed=41)
+    x["kk"][1, 20:36] = 0
+    o, s = run_ch(torch, dev(torch, x), state=False, affine=False)
+    orf, srf = ref(x, state=False, affine=False)
+    assert np.all(np.isfinite(o))
+    assert max(rel(o, orf), rel(s, srf)) <= TOL_BF16
+
+
+def test_chunked_state_in_place_and_sequential_agree(torch):
+    """state_out == state_in on the chunked path; the chunked and the token-by-token prefill agree to the
+    bfloat16 tolerance."""
+    say("tmix chunked in place vs sequential")
+    x = make_tmix_inputs(CONFIGS[1], B=2, T=333, H=4, seed=43)
+    d = dev(torch, x)
+    st = d["state_in"].clone()
+    out = torch.empty((2, 333, 4, 64), dtype=torch.float32, device="cuda")
+    wkv.rwkv7_tmix_prefill_ex(*(d[n] for n in NAMES), d["ln_w"], d["ln_b"], st, out, st, algo=CH)
+    o_seq, s_seq = run_ch(torch, d, algo=wkv.RWKV7_ALGO_SEQUENTIAL)
+    torch.cuda.synchronize()
+    o_ch, s_ch = out.cpu().numpy(), st.cpu().numpy()
+    assert max(rel(o_ch, o_seq), rel(s_ch, s_seq)) <= TOL_BF16
+    orf, srf = ref(x)
+    assert max(rel(o_ch, orf), rel(s_ch, srf)) <= TOL_BF16
+
+
+def test_chunked_extreme_decays(torch):
+    """w_raw = -inf (w = 1), 30 (w = 0, which the chunked path clamps to 2^-15) and ordinary values."""
+    say("tmix chunked extreme decays")
+    x = make_tmix_inputs(CONFIGS[1], B=1, T=90, H=2, seed=45, with_state=True)
+    rng = np.random.default_rng(45)
+    pick = rng.integers(0, 4, size=x["w_raw"].shape)
+    x["w_raw"] = np.where(pick == 0, -np.inf, np.where(pick == 1, 30.0, x["w_raw"])).astype(np.float32)
+    o, s = run_ch(torch, dev(torch, x))
+    orf, srf = ref(x)
+    assert max(rel(o, orf), rel(s, srf)) <= TOL_BF16
+
+
+def test_chunked_refuses_f32_and_unknown_algos(torch):
+    x = make_tmix_inputs(CONFIGS[0], T=8, seed=2)
+    d = dev(torch, x)
+    with pytest.raises(wkv.Rwkv7Error) as ei:
+        run_ch(torch, d)
+    assert ei.value.status == -7
+    xb = make_tmix_inputs(CONFIGS[1], B=1, T=8, H=1, seed=2)
+    for algo in (wkv.RWKV7_ALGO_CHUNKED, 9, -1):
+        with pytest.raises(wkv.Rwkv7Error) as ei:
+            run_ch(torch, dev(torch, xb), algo=algo)
+        assert ei.value.status == -7
