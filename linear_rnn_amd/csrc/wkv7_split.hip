@@ -538,20 +538,12 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     for (int e = 0; e < 4; ++e) f.v[e] = vr[(4 * g + e) * kVCols + 16 * wave + li];
   };
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-  // y[t = 4g + e][i = 16 rb + li] of chunk c; a whole chunk stores without per-lane guards
+  // y[t = li][i = 16 rb + 4g + e] of chunk c: four consecutive values per lane, one
+  // 16-byte store (tokens past the end of the sequence are not stored)
   auto store_y = [&](int c, const f32x4& yv) {
     const int nt = min(kC, p.T - (p.c0 + c) * kC);
-    if (nt == kC) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        st_off<float>(ybase, (uint32_t)(((c * kC + 4 * g + e) * tstride + li) * 4u), yv[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * g + e;
-        if (t < nt) st_off<float>(ybase, (uint32_t)(((c * kC + t) * tstride + li) * 4u), yv[e]);
-      }
-    }
+    if (li < nt)
+      st_off<float4>(ybase, (uint32_t)(((c * kC + li) * tstride + 4 * g) * 4u), make_float4(yv[0], yv[1], yv[2], yv[3]));
   };
   // One chunk. Its y is stored at the end, after the state update is issued, when the
   // products that made it have long completed.
@@ -565,15 +557,17 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     //   or 0 | V selects one of them);
     //   S^T <- diag(e^{gamma_15}) S^T + [B- | K-] [U ; V] per key tile.
     // the G V terms first: they do not depend on the state, so they need not wait for
-    // the previous chunk's update
+    // the previous chunk's update. Y is formed transposed (operands swapped: the state
+    // and V fragments serve as A operands, R' and G as B operands, from the same
+    // registers), so a lane holds four consecutive value rows of one token for its store.
     f32x4 u = mfma32(f.gl, cat8(vB, hz), zero4());
-    f32x4 yv = mfma32(f.gl, cat8(hz, vB), zero4());
+    f32x4 yv = mfma32(cat8(hz, vB), f.gl, zero4());
     const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
     const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
     u = mfma32(f.a0, sB0, u);
-    yv = mfma32(f.r0, sB0, yv);
+    yv = mfma32(sB0, f.r0, yv);
     u = mfma32(f.a1, sB1, u);
-    yv = mfma32(f.r1, sB1, yv);
+    yv = mfma32(sB1, f.r1, yv);
     const half8 uv = cat8(to_h4(u), vB);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
