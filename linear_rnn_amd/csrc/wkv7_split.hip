@@ -62,6 +62,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "wkv7_device.hpp"
@@ -521,8 +522,10 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     uint32_t v[4];  // V[t = 4g + e][i = 16 rb + li], raw bfloat16 bits (widened when used)
   };
   const uint32_t lo = (uint32_t)lane * 16u;
-  auto read = [&](int c, Frag& f) {
-    const unsigned char* slot = ring + (c % kSlots) * kSlotBytes;
+  // the loop below is unrolled by the ring size, so every slot index is a constant and
+  // every LDS address a fixed offset from the lane's base
+  auto read = [&](auto slot_index, Frag& f) {
+    const unsigned char* slot = ring + decltype(slot_index)::value * kSlotBytes;
     f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
     f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
     f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
@@ -542,8 +545,11 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // 16-byte store (tokens past the end of the sequence are not stored)
   auto store_y = [&](int c, const f32x4& yv) {
     const int nt = min(kC, p.T - (p.c0 + c) * kC);
-    if (li < nt)
-      st_off<float4>(ybase, (uint32_t)(((c * kC + li) * tstride + 4 * g) * 4u), make_float4(yv[0], yv[1], yv[2], yv[3]));
+    const uint32_t off = (uint32_t)(((c * kC + li) * tstride + 4 * g) * 4u);
+    if (nt == kC)  // the same for the whole wave: a whole chunk stores with no lane masked
+      st_off<float4>(ybase, off, make_float4(yv[0], yv[1], yv[2], yv[3]));
+    else if (li < nt)
+      st_off<float4>(ybase, off, make_float4(yv[0], yv[1], yv[2], yv[3]));
   };
   // One chunk. Its y is stored at the end, after the state update is issued, when the
   // products that made it have long completed.
@@ -589,18 +595,42 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     asm volatile("s_barrier" ::: "memory");
   };
   Frag fa, fb;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using S4 = std::integral_constant<int, 4>;
+  using S5 = std::integral_constant<int, 5>;
+  static_assert(kSlots == 6, "the loop is unrolled by the ring size");
   sync();  // chunk 0
-  read(0, fa);
+  read(S0{}, fa);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): nothing from LDS in flight when the loop starts
-  for (int c = 0;; c += 2) {
+  // chunk c + j sits in slot j (c is a multiple of the ring size); the two register sets alternate
+  for (int c = 0;; c += kSlots) {
     sync();  // chunk c + 1
-    read(c + 1, fb);
+    read(S1{}, fb);
     step(c, fa);
     if (c + 1 >= nc) break;
-    sync();  // chunk c + 2
-    read(c + 2, fa);
+    sync();
+    read(S2{}, fa);
     step(c + 1, fb);
     if (c + 2 >= nc) break;
+    sync();
+    read(S3{}, fb);
+    step(c + 2, fa);
+    if (c + 3 >= nc) break;
+    sync();
+    read(S4{}, fa);
+    step(c + 3, fb);
+    if (c + 4 >= nc) break;
+    sync();
+    read(S5{}, fb);
+    step(c + 4, fa);
+    if (c + 5 >= nc) break;
+    sync();
+    read(S0{}, fa);
+    step(c + 5, fb);
+    if (c + 6 >= nc) break;
   }
 
   if (p.s_dst) {
