@@ -19,7 +19,7 @@
 // Everything except S0 and V is a function of the chunk's own r, w, k, a, b.
 //
 // Kernel 1 (prep) runs one wave per (head, chunk), all chunks in parallel. It
-// computes the decay factors, the four Grams (float32 MFMA), T and M_r (float32
+// computes the decay factors, the four Grams (bfloat16 hi/lo MFMA), T and M_r (float32
 // back substitution) and the products above, and writes a 9,472-byte record per
 // chunk: A', R', G_u, G_y, B-, K- as float16 MFMA fragments in the exact register
 // layout that kernel 2 consumes, plus e^{gamma_15} in float32.
@@ -42,16 +42,16 @@
 //
 // Numerics. Decay factors are running products of w (clamped below at 2^-15):
 // factors that multiply the state are <= 1, and the Gram factors pass through
-// the decay at token 7, so no factor exceeds w_min^-8. The Grams are float32
-// products with float32 accumulation; T and M_r are float32; A', R', G_u, G_y,
+// the decay at token 7, so no factor exceeds w_min^-8. The Grams are products of
+// bfloat16 hi/lo halves (hi*hi + hi*lo + lo*hi, about 2^-16 relative, with the
+// float32 range) with float32 accumulation; T and M_r are float32; A', R', G_u, G_y,
 // B-, K-, the state operand and U are rounded once to float16 as MFMA operands
 // (float32 accumulation), so magnitudes must stay below 2^15. The carried state
 // is float32 throughout.
 //
 // MFMA layouts (gfx950, wave64; l = lane, li = l % 16, g = l / 16):
-//   16x16x4  f32 : A[m=li][k=g],      B[k=g][n=li]
-//   16x16x16 f16 : A[m=li][k=4g+e],   B[k=4g+e][n=li]   (e = 0..3)
-//   16x16x32 f16 : A[m=li][k=8g+e],   B[k=8g+e][n=li]   (e = 0..7)
+//   16x16x16 f16      : A[m=li][k=4g+e],   B[k=4g+e][n=li]   (e = 0..3)
+//   16x16x32 f16/bf16 : A[m=li][k=8g+e],   B[k=8g+e][n=li]   (e = 0..7)
 //   all          : D[m=4g+e][n=li]
 // A D result is unchanged a B operand with K = 16, and a product with the
 // identity as B turns an A-layout tile into the D layout (a transpose).
@@ -142,15 +142,23 @@ constexpr int kFacRow = kN + 4;  // padded float row: token-layout reads of one 
 // Fk_t = e^{gamma_7 - gamma_t} = 1 / Gq_t and e^{gamma_15 - gamma_t} = Gq_15 Fk_t are
 // formed where they are used.
 constexpr int kRowE = 0, kRowG = 17, kFacRows = 34;
-constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 9,248 bytes: four 4-wave workgroups per CU
+constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 9,248 bytes
 // After the factors are consumed the same wave area holds L_ab ([t][s], float32), the
 // right-hand sides of the solve (the identity, then L_rb, [32][16] float32) and the
 // rows of T and M_r (float16).
 constexpr int kLabOff = 0, kRhsOff = 16 * 16, kTmOffBytes = 3 * 16 * 16 * 4;
 static_assert(kTmOffBytes + 2 * 16 * 16 * 2 <= kPrepLdsPerWave, "solve area");
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// x = hi + lo with both halves bfloat16 (round to nearest even): 16 significant bits and
+// the float32 exponent range, which the Gram operands need (factors up to w_min^-8).
+__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int i) {
+  const __bf16 h = (__bf16)x;
+  hi[i] = h;
+  lo[i] = (__bf16)(x - (float)h);
+}
+__device__ __forceinline__ f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 // An ordering point for the values in x and for memory: the compiler computes x
@@ -164,7 +172,8 @@ __device__ __forceinline__ void pin16(float (&x)[16]) {
 __device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
 template <int MODE>
-__global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu(4))) void wkv7_prep_kernel(PrepParams p) {
+// three waves per SIMD: the register budget of four spills
+__global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu(3))) void wkv7_prep_kernel(PrepParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -248,9 +257,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS before other lanes read them
   __builtin_amdgcn_wave_barrier();
 
-  // ---- token layout: operands, the four Grams (float32 MFMA) and B-, K- (stored at once).
-  // q = 4kt + e indexes key 16kt + 4g + e. The Grams land in the D layout: lane (s = li, g)
-  // holds t = 4g + e; L_rk is formed transposed (operands swapped).
+  // ---- token layout: operands, the four Grams and B-, K- (stored at once). Key 16kt + 4g + e
+  // of the lane's token. Each Gram contracts 64 keys on 16x16x32 bfloat16 MFMAs as
+  // hi*hi + hi*lo + lo*hi of the operands' bfloat16 halves (relative error about 2^-16),
+  // two key blocks per product: K index 8g + 4(kt % 2) + e. The Grams land in the D layout:
+  // lane (s = li, g) holds t = 4g + e; L_rk is formed transposed (operands swapped).
   // Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
   half4 eye;
 #pragma unroll
@@ -275,6 +286,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
     n2 += __shfl_xor(n2, 32);
     inv = 1.f / fmaxf(sqrtf(n2), 1e-12f);
   }
+  bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int col = 16 * kt + 4 * g;
@@ -296,11 +308,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
       }
       const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
       const float suf = el(g15, e) * f;  // e^{gamma_15 - gamma_t}
-      const float ah = av * el(gqm1, e), rh = rv * el(gq, e), bh = bv * f, kh = kv * f;
-      Lab = mfma4(ah, bh, Lab);
-      Lak = mfma4(ah, kh, Lak);
-      Lrb = mfma4(rh, bh, Lrb);
-      LrkT = mfma4(kh, rh, LrkT);
+      const int q8 = 4 * (kt & 1) + e;
+      split_bf16(av * el(gqm1, e), ahH, ahL, q8);
+      split_bf16(rv * el(gq, e), rhH, rhL, q8);
+      split_bf16(bv * f, bhH, bhL, q8);
+      split_bf16(kv * f, khH, khL, q8);
       Ahat[kt][e] = (_Float16)(av * el(em1, e));
       Rhat[kt][e] = rv * el(e0, e);
       bbar[e] = (_Float16)(bv * suf);
@@ -309,6 +321,20 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
     const half4 BT = to_h4(mfma16(bbar, eye, zero4()));  // lane (j = li, g): B-[4g+e][16kt + li]
     const half4 KT = to_h4(mfma16(kbar, eye, zero4()));
     st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT, KT));
+    if (kt & 1) {
+      Lab = mfma_bf(ahH, bhH, Lab);
+      Lak = mfma_bf(ahH, khH, Lak);
+      Lrb = mfma_bf(rhH, bhH, Lrb);
+      LrkT = mfma_bf(khH, rhH, LrkT);
+      Lab = mfma_bf(ahH, bhL, Lab);
+      Lak = mfma_bf(ahH, khL, Lak);
+      Lrb = mfma_bf(rhH, bhL, Lrb);
+      LrkT = mfma_bf(khH, rhL, LrkT);
+      Lab = mfma_bf(ahL, bhH, Lab);
+      Lak = mfma_bf(ahL, khH, Lak);
+      Lrb = mfma_bf(rhL, bhH, Lrb);
+      LrkT = mfma_bf(khL, rhH, LrkT);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
