@@ -465,6 +465,11 @@ __device__ __forceinline__ void to_lds(const void* g, uint32_t lds) {
   else
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
 }
+// Every lane of a row of 16 reads lane K of that row (DPP row broadcast).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xf, 0xf, false));
+}
 // Waits until at most N of this wave's vector-memory operations are outstanding
 // (they complete in issue order), and orders every later memory access after it.
 template <int N>
@@ -544,7 +549,8 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // fragments of one chunk, read from its ring slot one iteration ahead
   struct Frag {
     half8 a0, a1, r0, r1, gl, bk[4];
-    float4 dv[4];
+    float dv;  // e^{gamma_15} of key 16 (li / 4) + 4g + li % 4: lane 4kt + e of row g holds the
+               // decay that every lane of the row needs as its (kt, e) element
     uint32_t v[4];  // V[t = 4g + e][i = 16 rb + li], raw bfloat16 bits (widened when used)
   };
   const uint32_t lo = (uint32_t)lane * 16u;
@@ -558,10 +564,8 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     f.r1 = *reinterpret_cast<const half8*>(slot + kRecR1 * 1024 + lo);
     f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
-      f.dv[kt] = *reinterpret_cast<const float4*>(slot + kRecD + (16 * kt + 4 * g) * 4);
-    }
+    for (int kt = 0; kt < 4; ++kt) f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
+    f.dv = *reinterpret_cast<const float*>(slot + kRecD + (16 * (li >> 2) + 4 * g + (li & 3)) * 4);
     const uint16_t* vr = reinterpret_cast<const uint16_t*>(slot + kRecBytes);  // [token][kVCols]
 #pragma unroll
     for (int e = 0; e < 4; ++e) f.v[e] = vr[(4 * g + e) * kVCols + 16 * wave + li];
@@ -601,14 +605,27 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     u = mfma32(f.a1, sB1, u);
     yv = mfma32(sB1, f.r1, yv);
     const half8 uv = cat8(to_h4(u), vB);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      St[kt][0] *= f.dv[kt].x;
-      St[kt][1] *= f.dv[kt].y;
-      St[kt][2] *= f.dv[kt].z;
-      St[kt][3] *= f.dv[kt].w;
-      St[kt] = mfma32(f.bk[kt], uv, St[kt]);
-    }
+    // the decays by row broadcasts (one 4-byte LDS read per lane instead of four 16-byte ones)
+    St[0][0] *= row_bcast<0>(f.dv);
+    St[0][1] *= row_bcast<1>(f.dv);
+    St[0][2] *= row_bcast<2>(f.dv);
+    St[0][3] *= row_bcast<3>(f.dv);
+    St[0] = mfma32(f.bk[0], uv, St[0]);
+    St[1][0] *= row_bcast<4>(f.dv);
+    St[1][1] *= row_bcast<5>(f.dv);
+    St[1][2] *= row_bcast<6>(f.dv);
+    St[1][3] *= row_bcast<7>(f.dv);
+    St[1] = mfma32(f.bk[1], uv, St[1]);
+    St[2][0] *= row_bcast<8>(f.dv);
+    St[2][1] *= row_bcast<9>(f.dv);
+    St[2][2] *= row_bcast<10>(f.dv);
+    St[2][3] *= row_bcast<11>(f.dv);
+    St[2] = mfma32(f.bk[2], uv, St[2]);
+    St[3][0] *= row_bcast<12>(f.dv);
+    St[3][1] *= row_bcast<13>(f.dv);
+    St[3][2] *= row_bcast<14>(f.dv);
+    St[3][3] *= row_bcast<15>(f.dv);
+    St[3] = mfma32(f.bk[3], uv, St[3]);
     store_y(c, yv);
   };
 
