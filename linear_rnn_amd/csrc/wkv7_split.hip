@@ -437,11 +437,14 @@ struct ScanParams {
 constexpr int kScanWaves = 2;  // compute waves per workgroup
 constexpr int kWgPerHead = 4 / kScanWaves;
 constexpr int kDist = 5;                          // chunks in flight ahead of the one read next
-constexpr int kSlots = kDist + 1;                 // ring slots
+// ring slots: the chunk being read, the kDist in flight and one spare, so that a slot is
+// reloaded only once the compute waves have used what they read from it (no wait on
+// outstanding LDS reads at the barrier)
+constexpr int kSlots = kDist + 2;
 constexpr int kVCols = 16 * kScanWaves;           // value columns of v this workgroup needs
 constexpr int kVBytes = kC * kVCols * 2;          // bfloat16, [token][kVCols]: 1 KiB
 constexpr int kSlotBytes = kRecBytes + kVBytes;   // 10,496
-constexpr int kScanLds = kSlots * kSlotBytes;     // 62,976
+constexpr int kScanLds = kSlots * kSlotBytes;     // 73,472: two workgroups fit a compute unit
 constexpr int kLoads = kRecBlocks + 2;  // loads per lane per chunk: record blocks, e^gamma, v
 constexpr int kScanThreads = 64 * (kScanWaves + 1);
 // the load counter holds at most 63 outstanding operations: never more are in flight
@@ -501,8 +504,9 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // into slot x % kSlots: the record as it is (nine 1 KiB blocks, then e^{gamma_15}),
   // then v [token][kVCols] (lane l: token l / 4, eight columns). Tokens past the end of
   // the sequence repeat the last one; their coefficients in the record are zero.
-  // Chunk x + kDist reuses the slot of chunk x - 1, which the compute waves read
-  // (and waited for: lgkmcnt(0)) before the barrier that precedes its loads.
+  // Chunk x + kDist reuses the slot of chunk x + kDist - kSlots = x - 2: the compute
+  // waves used what they read from it in the step of chunk x - 2, before the barrier
+  // that precedes the loads of chunk x + kDist.
   if (wave == kScanWaves) {
     auto issue = [&](int x) {
       const int xc = min(x, nc - 1);
@@ -558,17 +562,18 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // every LDS address a fixed offset from the lane's base
   auto read = [&](auto slot_index, Frag& f) {
     const unsigned char* slot = ring + decltype(slot_index)::value * kSlotBytes;
-    f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
-    f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
-    f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
-    f.r1 = *reinterpret_cast<const half8*>(slot + kRecR1 * 1024 + lo);
-    f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
-    f.dv = *reinterpret_cast<const float*>(slot + kRecD + (16 * (li >> 2) + 4 * g + (li & 3)) * 4);
+    // in the order of use (the next chunk's first products take v and G)
     const uint16_t* vr = reinterpret_cast<const uint16_t*>(slot + kRecBytes);  // [token][kVCols]
 #pragma unroll
     for (int e = 0; e < 4; ++e) f.v[e] = vr[(4 * g + e) * kVCols + 16 * wave + li];
+    f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
+    f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
+    f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
+    f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
+    f.r1 = *reinterpret_cast<const half8*>(slot + kRecR1 * 1024 + lo);
+    f.dv = *reinterpret_cast<const float*>(slot + kRecD + (16 * (li >> 2) + 4 * g + (li & 3)) * 4);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
   };
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
   // y[t = li][i = 16 rb + 4g + e] of chunk c: four consecutive values per lane, one
@@ -629,52 +634,42 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     store_y(c, yv);
   };
 
-  // ---- compute waves. The loop body has no branch around the reads: a read past the
-  // last chunk reads a slot that holds a repeat of it and is never used. (A read on one
-  // side of a branch only would make the compiler's wait at the join cover the next
-  // chunk's reads too.) Before each barrier every LDS read issued so far has completed.
-  auto sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
+  // ---- compute waves. After barrier m they read chunk m and run the step of chunk
+  // m - 1, which uses the reads of the iteration before: by barrier m + 1 every read of
+  // chunk m - 1 has completed (its values were used), and the loader reloads that
+  // chunk's slot only after barrier m + 1 (the ring has a spare slot), so the barrier
+  // waits for no LDS read. The loop body has no branch around the reads: a read past
+  // the last chunk reads a slot that holds a repeat of it and is never used. (A read on
+  // one side of a branch only would make the compiler's wait at the join cover the
+  // next chunk's reads too.)
+  auto sync = [&]() { asm volatile("s_barrier" ::: "memory"); };
+  Frag fr[2];
+  // chunk c + j sits in slot j % kSlots (c is a multiple of the unroll, itself a multiple
+  // of the ring size); the two register sets alternate, so the unroll is also even
+  constexpr int kUnroll = kSlots % 2 == 0 ? kSlots : 2 * kSlots;
+  int c = 0;
+  // chunk c + J: barrier, read of the next chunk, step; true after the last chunk
+  auto chunk = [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    sync();
+    read(std::integral_constant<int, (j + 1) % kSlots>{}, fr[(j + 1) % 2]);
+    step(c + j, fr[j % 2]);
+    return c + j + 1 >= nc;
   };
-  Frag fa, fb;
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  using S4 = std::integral_constant<int, 4>;
-  using S5 = std::integral_constant<int, 5>;
-  static_assert(kSlots == 6, "the loop is unrolled by the ring size");
+  // chunks c .. c + kUnroll - 1, every slot index a constant; true after the last chunk
+  auto unrolled = [&](auto self, auto J) -> bool {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == kUnroll) {
+      return false;
+    } else {
+      if (chunk(J)) return true;
+      return self(self, std::integral_constant<int, j + 1>{});
+    }
+  };
   sync();  // chunk 0
-  read(S0{}, fa);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): nothing from LDS in flight when the loop starts
-  // chunk c + j sits in slot j (c is a multiple of the ring size); the two register sets alternate
-  for (int c = 0;; c += kSlots) {
-    sync();  // chunk c + 1
-    read(S1{}, fb);
-    step(c, fa);
-    if (c + 1 >= nc) break;
-    sync();
-    read(S2{}, fa);
-    step(c + 1, fb);
-    if (c + 2 >= nc) break;
-    sync();
-    read(S3{}, fb);
-    step(c + 2, fa);
-    if (c + 3 >= nc) break;
-    sync();
-    read(S4{}, fa);
-    step(c + 3, fb);
-    if (c + 4 >= nc) break;
-    sync();
-    read(S5{}, fb);
-    step(c + 4, fa);
-    if (c + 5 >= nc) break;
-    sync();
-    read(S0{}, fa);
-    step(c + 5, fb);
-    if (c + 6 >= nc) break;
-  }
+  read(std::integral_constant<int, 0>{}, fr[0]);
+  for (;; c += kUnroll)
+    if (unrolled(unrolled, std::integral_constant<int, 0>{})) break;
 
   if (p.s_dst) {
 #pragma unroll
