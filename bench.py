@@ -141,7 +141,7 @@ def main(argv=None):
     dev_name = torch.cuda.get_device_name(0)
 
     # ------------------------------------------------------------------ prefill
-    cfg = CONFIGS[1]
+    cfg = CONFIGS["L12-D768-prefill"]
     B, T, H = cfg.B, cfg.T, cfg.H
     x = make_inputs(cfg)
     d = to_dev(x, torch)
@@ -195,13 +195,13 @@ def main(argv=None):
 
     # ------------------------------------------------------------------ decode
     if not args.no_decode:
-        out["decode"] = bench_decode(torch, wkv, make_inputs, CONFIGS[3], args)
+        out["decode"] = bench_decode(torch, wkv, make_inputs, CONFIGS["D2048-decode"], args)
         if not args.no_decode_16bit:
             for fmt in ("bf16", "f16"):
-                out["decode_state_" + fmt] = bench_decode(torch, wkv, make_inputs, CONFIGS[3], args, fmt)
+                out["decode_state_" + fmt] = bench_decode(torch, wkv, make_inputs, CONFIGS["D2048-decode"], args, fmt)
 
     if not args.no_decode and not args.no_decode_fused:
-        out["decode_fused"] = bench_decode_fused(torch, wkv, CONFIGS[3], args)
+        out["decode_fused"] = bench_decode_fused(torch, wkv, CONFIGS["D2048-decode"], args)
 
     if not args.no_backward:
         out["backward"] = bench_backward(torch, wkv, x, d, s_in, cfg, args)
@@ -392,7 +392,7 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
     ms_graph = time_region(torch, g.replay, args.stack_steps)
     # the fused operator alone at the prompt shape (inputs from the first layer's projection scale)
     from linear_rnn_amd.inputs import CONFIGS, make_tmix_inputs
-    xt = make_tmix_inputs(CONFIGS[1], B=B, T=T, H=H, seed=7101)
+    xt = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=7101)
     dt = {n: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if a.dtype == np.uint16
               else torch.from_numpy(a).cuda()) for n, a in xt.items() if a is not None}
     o = torch.empty((B, T, H, N), dtype=torch.float32, device="cuda")

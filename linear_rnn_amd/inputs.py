@@ -64,12 +64,15 @@ class WkvConfig:
 # pages (0.1B L12-D768 -> H=12; L24-D1024 -> H=16; 1.5B D2048 -> H=32;
 # 7B-class D4096 -> H=64), each with head size 64.
 CONFIGS = {
-    0: WkvConfig("tiny-prefill-f32", B=1, T=64, H=2, dtype="f32", state_in=False, seed=7000),
-    1: WkvConfig("L12-D768-prefill", B=8, T=4096, H=12, dtype="bf16", state_in=True, seed=7001),
-    2: WkvConfig("L24-D1024-prefill-resume", B=16, T=4096, H=16, dtype="bf16", state_in=True, seed=7002),
-    3: WkvConfig("D2048-decode", B=512, T=1, H=32, dtype="bf16", state_in=True, steps=256, seed=7003),
-    4: WkvConfig("D4096-long-prefill", B=4, T=16384, H=64, dtype="bf16", state_in=True,
-                 u_lo=-8.0, u_hi=-0.1, a_uniform=True, seed=7004),
+    cfg.name: cfg
+    for cfg in (
+        WkvConfig("tiny-prefill-f32", B=1, T=64, H=2, dtype="f32", state_in=False, seed=7000),
+        WkvConfig("L12-D768-prefill", B=8, T=4096, H=12, dtype="bf16", state_in=True, seed=7001),
+        WkvConfig("L24-D1024-prefill-resume", B=16, T=4096, H=16, dtype="bf16", state_in=True, seed=7002),
+        WkvConfig("D2048-decode", B=512, T=1, H=32, dtype="bf16", state_in=True, steps=256, seed=7003),
+        WkvConfig("D4096-long-prefill", B=4, T=16384, H=64, dtype="bf16", state_in=True,
+                  u_lo=-8.0, u_hi=-0.1, a_uniform=True, seed=7004),
+    )
 }
 
 TENSORS = ("r", "w", "k", "v", "a", "b")

@@ -39,7 +39,7 @@ def errors(g, r):
 
 def test_f32_tiny(torch):
     say("backward f32 tiny")
-    x = make_inputs(CONFIGS[0])
+    x = make_inputs(CONFIGS["tiny-prefill-f32"])
     ct = make_cotangents(1, 64, 2, seed=1, with_dstate=False)
     e = errors(run(torch, x, ct, dstate=False), ref(x, ct, dstate=False))
     say("backward f32 tiny errors", e)
@@ -50,7 +50,7 @@ def test_f32_tiny(torch):
 def test_f32_ragged_with_states(torch, T):
     """Every segment and sub-block tail, with state_in and dstate_out."""
     say("backward f32 T", T)
-    x = make_inputs(CONFIGS[0], B=2, T=T, H=3, seed=500 + T, with_state=True)
+    x = make_inputs(CONFIGS["tiny-prefill-f32"], B=2, T=T, H=3, seed=500 + T, with_state=True)
     ct = make_cotangents(2, T, 3, seed=T)
     e = errors(run(torch, x, ct), ref(x, ct))
     assert max(e.values()) <= TOL_F32, e
@@ -59,7 +59,7 @@ def test_f32_ragged_with_states(torch, T):
 @pytest.mark.parametrize("B,T,H", [(1, 5, 1), (2, 64, 3), (3, 250, 4)])
 def test_bf16(torch, B, T, H):
     say("backward bf16", B, T, H)
-    x = make_inputs(CONFIGS[1], B=B, T=T, H=H, seed=600 + T)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=600 + T)
     ct = make_cotangents(B, T, H, seed=T + 1)
     e = errors(run(torch, x, ct), ref(x, ct))
     say("backward bf16 errors", e)
@@ -69,11 +69,11 @@ def test_bf16(torch, B, T, H):
 def test_many_heads_single_row_block(torch):
     """More than 128 heads: one workgroup per head (no row split), all rows' column sums in LDS."""
     say("backward 140 heads")
-    x = make_inputs(CONFIGS[1], B=2, T=21, H=70, seed=77)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=21, H=70, seed=77)
     ct = make_cotangents(2, 21, 70, seed=77)
     e = errors(run(torch, x, ct), ref(x, ct))
     assert max(e.values()) <= TOL_BF16, e
-    x = make_inputs(CONFIGS[0], B=2, T=13, H=70, seed=78, with_state=True)
+    x = make_inputs(CONFIGS["tiny-prefill-f32"], B=2, T=13, H=70, seed=78, with_state=True)
     ct = make_cotangents(2, 13, 70, seed=78)
     e = errors(run(torch, x, ct), ref(x, ct))
     assert max(e.values()) <= TOL_F32, e
@@ -81,7 +81,7 @@ def test_many_heads_single_row_block(torch):
 
 def test_zero_token_passes_state_gradient(torch):
     say("backward T == 0")
-    x = make_inputs(CONFIGS[0], B=2, T=0, H=2, seed=3, with_state=True)
+    x = make_inputs(CONFIGS["tiny-prefill-f32"], B=2, T=0, H=2, seed=3, with_state=True)
     ct = make_cotangents(2, 0, 2, seed=3)
     g = run(torch, x, ct)
     assert np.array_equal(g["dstate_in"], ct["dstate_out"])
@@ -93,7 +93,7 @@ def test_zero_token_passes_state_gradient(torch):
 def test_dstate_in_place(torch):
     """dstate_in may be the dstate_out buffer itself."""
     say("backward dstate in place")
-    x = make_inputs(CONFIGS[0], B=1, T=40, H=2, seed=8, with_state=True)
+    x = make_inputs(CONFIGS["tiny-prefill-f32"], B=1, T=40, H=2, seed=8, with_state=True)
     ct = make_cotangents(1, 40, 2, seed=8)
     d = to_dev(x)
     dy = torch.from_numpy(ct["dy"]).cuda()
@@ -109,7 +109,7 @@ def test_dstate_in_place(torch):
 def test_extreme_decays_and_slots(torch):
     """w in {0, tiny, 1}, exact zero a/b rows and a_lr of exactly 0 or 1."""
     say("backward extreme decays")
-    x = make_inputs(CONFIGS[4], B=1, T=70, H=3, seed=21)
+    x = make_inputs(CONFIGS["D4096-long-prefill"], B=1, T=70, H=3, seed=21)
     rng = np.random.default_rng(21)
     choices = np.array([0.0, 1e-6, 0.5, 1.0], dtype=np.float32)
     x["w"] = f32_to_bf16_bits(choices[rng.integers(0, 4, size=x["w"].shape)])
@@ -122,7 +122,7 @@ def test_extreme_decays_and_slots(torch):
 
 def test_repeat_is_deterministic(torch):
     say("backward determinism")
-    x = make_inputs(CONFIGS[1], B=2, T=90, H=4, seed=31)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=90, H=4, seed=31)
     ct = make_cotangents(2, 90, 4, seed=31)
     g1, g2 = run(torch, x, ct), run(torch, x, ct)
     assert all(np.array_equal(g1[n], g2[n]) for n in g1)
@@ -130,7 +130,7 @@ def test_repeat_is_deterministic(torch):
 
 def test_full_size_sampled(torch):
     """The 0.1B-model prefill shape (B=8, T=4096, H=12, bfloat16) against the oracle on sampled heads."""
-    cfg = CONFIGS[1]
+    cfg = CONFIGS["L12-D768-prefill"]
     say("backward full size", cfg.name)
     x = make_inputs(cfg)
     ct = make_cotangents(cfg.B, cfg.T, cfg.H, seed=cfg.seed)

@@ -38,7 +38,7 @@ def run(torch, d, algo, state=True):
                                    (2, 1000, 12)])
 def test_ragged_vs_oracle(torch, CH, B, T, H):
     say("algo", CH, "chunked ragged", B, T, H)
-    x = make_inputs(CONFIGS[1], B=B, T=T, H=H, seed=200 + T)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=200 + T)
     y, s = run(torch, to_dev(x), CH)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
@@ -46,7 +46,7 @@ def test_ragged_vs_oracle(torch, CH, B, T, H):
 
 def test_zero_initial_state(torch, CH):
     say("algo", CH, "chunked, state_in NULL")
-    x = make_inputs(CONFIGS[1], B=2, T=77, H=4, seed=3)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=77, H=4, seed=3)
     y, s = run(torch, to_dev(x), CH, state=False)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=None)
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16
@@ -55,14 +55,14 @@ def test_zero_initial_state(torch, CH):
 def test_f32_inputs_are_refused(torch, CH):
     """The chunked algorithm takes bfloat16 inputs only; float32 inputs stay on the sequential kernel."""
     say("algo", CH, "chunked, f32 inputs refused")
-    x = make_inputs(CONFIGS[0])
+    x = make_inputs(CONFIGS["tiny-prefill-f32"])
     with pytest.raises(wkv.Rwkv7Error) as ei:
         run(torch, to_dev(x), CH)
     assert ei.value.status == -7
 
 
 def test_config1_full(torch, CH):
-    cfg = CONFIGS[1]
+    cfg = CONFIGS["L12-D768-prefill"]
     say("algo", CH, "chunked config 1 full", cfg)
     x = make_inputs(cfg)
     y, s = run(torch, to_dev(x), CH)
@@ -74,7 +74,7 @@ def test_config1_full(torch, CH):
 
 def test_config2_full_and_resume(torch, CH):
     """One pass and 4 x 1024-token segments with the state carried, each against the oracle."""
-    cfg = CONFIGS[2]
+    cfg = CONFIGS["L24-D1024-prefill-resume"]
     say("algo", CH, "chunked config 2 full + resume", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
@@ -103,7 +103,7 @@ def test_config2_full_and_resume(torch, CH):
 
 def test_unaligned_resume(torch, CH):
     say("algo", CH, "chunked unaligned resume")
-    x = make_inputs(CONFIGS[1], B=2, T=300, H=3, seed=11)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=300, H=3, seed=11)
     d = to_dev(x)
     st = d["state_in"].clone()
     ys = []
@@ -119,7 +119,7 @@ def test_unaligned_resume(torch, CH):
 
 
 def test_config4_sampled_heads_and_vs_sequential(torch, CH):
-    cfg = CONFIGS[4]
+    cfg = CONFIGS["D4096-long-prefill"]
     say("algo", CH, "chunked config 4 full, 16 sampled heads + sequential comparison", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
@@ -146,7 +146,7 @@ def test_extreme_decays(torch, CH):
     """w in {0, 1e-6, 1e-2, 0.5, 1}: below 2^-15 the chunked form clamps, which moves a decayed
     term by at most 2^-15 of its size."""
     say("algo", CH, "chunked extreme decays")
-    x = make_inputs(CONFIGS[1], B=2, T=90, H=3, seed=17)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=90, H=3, seed=17)
     rng = np.random.default_rng(17)
     choices = np.array([0.0, 1e-6, 1e-2, 0.5, 1.0], dtype=np.float32)
     x["w"] = f32_to_bf16_bits(choices[rng.integers(0, 5, size=x["w"].shape)])
@@ -175,7 +175,7 @@ def test_delta_rule_retrieval(torch, CH):
 
 def test_deterministic(torch, CH):
     say("algo", CH, "chunked determinism")
-    x = make_inputs(CONFIGS[1], B=2, T=300, H=6, seed=8)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=300, H=6, seed=8)
     d = to_dev(x)
     y1, s1 = run(torch, d, CH)
     y2, s2 = run(torch, d, CH)
@@ -184,7 +184,7 @@ def test_deterministic(torch, CH):
 
 def test_auto_uses_chunked_for_bf16(torch):
     say("auto dispatch")
-    x = make_inputs(CONFIGS[1], B=1, T=40, H=2, seed=4)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=1, T=40, H=2, seed=4)
     d = to_dev(x)
     y_auto = torch.empty((1, 40, 2, 64), dtype=torch.float32, device="cuda")
     wkv.rwkv7_wkv_prefill(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state_in"], y_auto, None)

@@ -28,7 +28,7 @@ def run_prefill(torch, d, algo=SEQ):
 
 def test_tiny_f32(torch):
     say("tiny f32 prefill, sequential")
-    x = make_inputs(CONFIGS[0])
+    x = make_inputs(CONFIGS["tiny-prefill-f32"])
     y, s = run_prefill(torch, to_dev(x))
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= TOL_F32 and rel(s, sr) <= TOL_F32, (rel(y, yr), rel(s, sr))
@@ -60,7 +60,7 @@ def test_exact_dyadic_bit_for_bit(torch, dtype):
 @pytest.mark.parametrize("B,T,H", [(1, 1, 1), (2, 31, 3), (1, 33, 2), (3, 100, 5), (1, 1000, 12)])
 def test_ragged_bf16_sequential(torch, B, T, H):
     say("ragged bf16 sequential", B, T, H)
-    x = make_inputs(CONFIGS[1], B=B, T=T, H=H, seed=100 + T)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=100 + T)
     y, s = run_prefill(torch, to_dev(x))
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= 1e-5 and rel(s, sr) <= 1e-5, (rel(y, yr), rel(s, sr))
@@ -69,14 +69,14 @@ def test_ragged_bf16_sequential(torch, B, T, H):
 def test_many_heads_path(torch):
     """B*H >= 2048 selects the one-head-per-workgroup tiling."""
     say("many heads sequential")
-    x = make_inputs(CONFIGS[1], B=64, T=20, H=32, seed=5)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=64, T=20, H=32, seed=5)
     y, s = run_prefill(torch, to_dev(x))
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     assert rel(y, yr) <= 1e-5 and rel(s, sr) <= 1e-5
 
 
 def test_config1_full(torch):
-    cfg = CONFIGS[1]
+    cfg = CONFIGS["L12-D768-prefill"]
     say("config 1 full, sequential", cfg)
     x = make_inputs(cfg)
     y, s = run_prefill(torch, to_dev(x))
@@ -87,7 +87,7 @@ def test_config1_full(torch):
 
 def test_config2_split_resume_bit_identical(torch):
     """4 segments of 1024 tokens with the state carried equal one pass, bit for bit."""
-    cfg = CONFIGS[2]
+    cfg = CONFIGS["L24-D1024-prefill-resume"]
     say("config 2 split/resume, sequential", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
@@ -108,7 +108,7 @@ def test_config2_split_resume_bit_identical(torch):
 
 def test_config3_decode_steps(torch):
     """256 in-place steps at B=512, H=32; oracle on 64 sampled heads over all steps."""
-    cfg = CONFIGS[3]
+    cfg = CONFIGS["D2048-decode"]
     say("config 3 decode, 256 steps", cfg)
     units = sample_units(cfg.B, cfg.H, 64, seed=3)
     x0 = make_inputs(cfg, step=0)
@@ -140,7 +140,7 @@ def test_config3_decode_steps(torch):
 
 def test_prefill_equals_steps_bit_identical(torch):
     say("prefill vs steps")
-    x = make_inputs(CONFIGS[1], B=3, T=50, H=4, seed=9)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=3, T=50, H=4, seed=9)
     d = to_dev(x)
     y1, s1 = run_prefill(torch, d)
     st = d["state_in"].clone()
@@ -156,7 +156,7 @@ def test_prefill_equals_steps_bit_identical(torch):
 
 
 def test_config4_sampled_heads(torch):
-    cfg = CONFIGS[4]
+    cfg = CONFIGS["D4096-long-prefill"]
     say("config 4 full, sequential, 16 sampled heads", cfg)
     x = make_inputs(cfg)
     units = sample_units(cfg.B, cfg.H, 16, seed=4)
@@ -192,7 +192,7 @@ def test_invariants_on_gpu(torch):
 
 def test_null_state_in_and_out(torch):
     say("null state in/out")
-    x = make_inputs(CONFIGS[1], B=2, T=17, H=3, seed=3)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=17, H=3, seed=3)
     d = to_dev(x)
     y = torch.empty((2, 17, 3, 64), dtype=torch.float32, device="cuda")
     wkv.rwkv7_wkv_prefill_ex(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], None, y, None, algo=SEQ)
@@ -217,7 +217,7 @@ def test_empty_sequence_copies_state(torch):
 
 def test_deterministic(torch):
     say("determinism")
-    x = make_inputs(CONFIGS[1], B=2, T=300, H=6, seed=8)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=300, H=6, seed=8)
     d = to_dev(x)
     y1, s1 = run_prefill(torch, d)
     y2, s2 = run_prefill(torch, d)

@@ -79,7 +79,7 @@ def step_q(d, state_in, y, state_out):
 
 def test_f32_state_code_is_the_plain_step(torch):
     say("step_q with float32 state vs step")
-    x = make_inputs(CONFIGS[3], B=6, H=7, step=0)
+    x = make_inputs(CONFIGS["D2048-decode"], B=6, H=7, step=0)
     d = to_dev(x)
     y1 = torch.empty((6, 1, 7, 64), dtype=torch.float32, device="cuda")
     y2 = torch.empty_like(y1)
@@ -95,7 +95,7 @@ def test_f32_state_code_is_the_plain_step(torch):
 @pytest.mark.parametrize("B,H", [(512, 32), (3, 5), (1, 1)])
 def test_one_step_vs_oracle(torch, fmt, B, H):
     say("step_q one step", fmt, B, H)
-    x = make_inputs(CONFIGS[3], B=B, H=H, step=0)
+    x = make_inputs(CONFIGS["D2048-decode"], B=B, H=H, step=0)
     bits = oracle.round16(x["state_in"].astype(np.float64), fmt)
     d = to_dev(x)
     s_in = bits_to_dev(torch, bits, fmt)
@@ -113,7 +113,7 @@ def test_one_step_vs_oracle(torch, fmt, B, H):
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_null_state_in_and_in_place(torch, fmt):
     say("step_q NULL state_in, then in place", fmt)
-    x = make_inputs(CONFIGS[3], B=4, H=6, step=1, with_state=False)
+    x = make_inputs(CONFIGS["D2048-decode"], B=4, H=6, step=1, with_state=False)
     d = to_dev(x)
     st = torch.empty((4, 6, 64, 64), dtype=tdtype(torch, fmt), device="cuda")
     y = torch.empty((4, 1, 6, 64), dtype=torch.float32, device="cuda")
@@ -130,7 +130,7 @@ def test_null_state_in_and_in_place(torch, fmt):
 def test_config3_256_steps(torch, fmt):
     """256 in-place steps at B=512, H=32 against the oracle's own 16-bit trajectory on 64
     sampled heads, and against the float32-state kernel (drift of the reduced state)."""
-    cfg = CONFIGS[3]
+    cfg = CONFIGS["D2048-decode"]
     say("step_q config 3, 256 steps", fmt)
     code, ulp = FMTS[fmt]
     units = sample_units(cfg.B, cfg.H, 64, seed=5)

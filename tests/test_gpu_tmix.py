@@ -45,7 +45,7 @@ def ref(x, state=True, affine=True):
 
 def test_f32_tiny(torch):
     say("tmix f32 tiny")
-    x = make_tmix_inputs(CONFIGS[0])
+    x = make_tmix_inputs(CONFIGS["tiny-prefill-f32"])
     o, s = run(torch, dev(torch, x), state=False)
     orf, srf = ref(x, state=False)
     e = (rel(o, orf), rel(s, srf))
@@ -56,7 +56,7 @@ def test_f32_tiny(torch):
 @pytest.mark.parametrize("B,T,H", [(1, 1, 2), (2, 37, 3), (3, 100, 5), (1, 300, 12)])
 def test_bf16_ragged(torch, B, T, H):
     say("tmix bf16", B, T, H)
-    x = make_tmix_inputs(CONFIGS[1], B=B, T=T, H=H, seed=400 + T)
+    x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=400 + T)
     o, s = run(torch, dev(torch, x))
     orf, srf = ref(x)
     e = (rel(o, orf), rel(s, srf))
@@ -66,7 +66,7 @@ def test_bf16_ragged(torch, B, T, H):
 def test_identity_affine_and_zero_key(torch):
     """ln_w / ln_b NULL mean weight 1 and bias 0; an all-zero removal key row gives a = b = 0."""
     say("tmix NULL affine, zero kk rows")
-    x = make_tmix_inputs(CONFIGS[0], T=40, seed=9)
+    x = make_tmix_inputs(CONFIGS["tiny-prefill-f32"], T=40, seed=9)
     x["kk"][0, 5:9] = 0.0
     o, s = run(torch, dev(torch, x), affine=False)
     orf, srf = ref(x, affine=False)
@@ -77,7 +77,7 @@ def test_identity_affine_and_zero_key(torch):
 def test_extreme_decays(torch):
     """w_raw = -inf (w = 1), very large (w = 0) and ordinary values mixed."""
     say("tmix extreme decays")
-    x = make_tmix_inputs(CONFIGS[0], T=50, seed=12, with_state=True)
+    x = make_tmix_inputs(CONFIGS["tiny-prefill-f32"], T=50, seed=12, with_state=True)
     rng = np.random.default_rng(12)
     pick = rng.integers(0, 4, size=x["w_raw"].shape)
     x["w_raw"] = np.where(pick == 0, -np.inf, np.where(pick == 1, 30.0, x["w_raw"])).astype(np.float32)
@@ -89,7 +89,7 @@ def test_extreme_decays(torch):
 def test_steps_equal_prefill(torch):
     """T single-token steps reproduce a prefill over the T tokens bit for bit."""
     say("tmix steps == prefill")
-    x = make_tmix_inputs(CONFIGS[1], B=2, T=21, H=3, seed=31)
+    x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=2, T=21, H=3, seed=31)
     d = dev(torch, x)
     o1, s1 = run(torch, d)
     st = d["state_in"].clone()
@@ -106,7 +106,7 @@ def test_steps_equal_prefill(torch):
 
 def test_decode_shape_sampled(torch):
     """One fused step at the D2048 decode shape (B=512, H=32), sampled heads against the oracle."""
-    cfg = CONFIGS[3]
+    cfg = CONFIGS["D2048-decode"]
     say("tmix decode shape", cfg)
     x = make_tmix_inputs(cfg, step=0)
     d = dev(torch, x)
@@ -141,7 +141,7 @@ def run_ch(torch, d, state=True, affine=True, algo=CH):
 @pytest.mark.parametrize("B,T,H", [(1, 2, 1), (1, 17, 2), (2, 37, 3), (3, 100, 5), (1, 300, 12), (2, 1000, 4)])
 def test_chunked_vs_oracle(torch, B, T, H):
     say("tmix chunked", B, T, H)
-    x = make_tmix_inputs(CONFIGS[1], B=B, T=T, H=H, seed=500 + T)
+    x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=500 + T)
     o, s = run_ch(torch, dev(torch, x))
     orf, srf = ref(x)
     e = (rel(o, orf), rel(s, srf))
@@ -152,7 +152,7 @@ def test_chunked_vs_oracle(torch, B, T, H):
 def test_chunked_zero_state_null_affine_zero_key(torch):
     """state_in NULL, ln_w / ln_b NULL, and all-zero removal-key rows (a = b = 0) on the chunked path."""
     say("tmix chunked, NULL state and affine, zero kk rows")
-    x = make_tmix_inputs(CONFIGS[1], B=2, T=70, H=3, seed=41)
+    x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=2, T=70, H=3, seed=41)
     x["kk"][1, 20:36] = 0
     o, s = run_ch(torch, dev(torch, x), state=False, affine=False)
     orf, srf = ref(x, state=False, affine=False)
@@ -164,7 +164,7 @@ def test_chunked_state_in_place_and_sequential_agree(torch):
     """state_out == state_in on the chunked path; the chunked and the token-by-token prefill agree to the
     bfloat16 tolerance."""
     say("tmix chunked in place vs sequential")
-    x = make_tmix_inputs(CONFIGS[1], B=2, T=333, H=4, seed=43)
+    x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=2, T=333, H=4, seed=43)
     d = dev(torch, x)
     st = d["state_in"].clone()
     out = torch.empty((2, 333, 4, 64), dtype=torch.float32, device="cuda")
@@ -180,7 +180,7 @@ def test_chunked_state_in_place_and_sequential_agree(torch):
 def test_chunked_extreme_decays(torch):
     """w_raw = -inf (w = 1), 30 (w = 0, which the chunked path clamps to 2^-15) and ordinary values."""
     say("tmix chunked extreme decays")
-    x = make_tmix_inputs(CONFIGS[1], B=1, T=90, H=2, seed=45, with_state=True)
+    x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=1, T=90, H=2, seed=45, with_state=True)
     rng = np.random.default_rng(45)
     pick = rng.integers(0, 4, size=x["w_raw"].shape)
     x["w_raw"] = np.where(pick == 0, -np.inf, np.where(pick == 1, 30.0, x["w_raw"])).astype(np.float32)
@@ -190,12 +190,12 @@ def test_chunked_extreme_decays(torch):
 
 
 def test_chunked_refuses_f32_and_unknown_algos(torch):
-    x = make_tmix_inputs(CONFIGS[0], T=8, seed=2)
+    x = make_tmix_inputs(CONFIGS["tiny-prefill-f32"], T=8, seed=2)
     d = dev(torch, x)
     with pytest.raises(wkv.Rwkv7Error) as ei:
         run_ch(torch, d)
     assert ei.value.status == -7
-    xb = make_tmix_inputs(CONFIGS[1], B=1, T=8, H=1, seed=2)
+    xb = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=1, T=8, H=1, seed=2)
     for algo in (wkv.RWKV7_ALGO_CHUNKED, 9, -1):
         with pytest.raises(wkv.Rwkv7Error) as ei:
             run_ch(torch, dev(torch, xb), algo=algo)

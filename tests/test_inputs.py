@@ -11,25 +11,25 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def test_deterministic_and_seed_sensitive():
-    a = make_inputs(CONFIGS[0])
-    b = make_inputs(CONFIGS[0])
-    c = make_inputs(CONFIGS[0], seed=1)
+    a = make_inputs(CONFIGS["tiny-prefill-f32"])
+    b = make_inputs(CONFIGS["tiny-prefill-f32"])
+    c = make_inputs(CONFIGS["tiny-prefill-f32"], seed=1)
     for n in "rwkvab":
         assert np.array_equal(a[n], b[n])
         assert not np.array_equal(a[n], c[n])
 
 
 def test_shapes_and_dtypes():
-    x = make_inputs(CONFIGS[1], B=2, T=33, H=3)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=33, H=3)
     for n in "rwkvab":
         assert x[n].shape == (2, 33, 3, 64) and x[n].dtype == np.uint16
     assert x["state_in"].shape == (2, 3, 64, 64) and x["state_in"].dtype == np.float32
-    x0 = make_inputs(CONFIGS[0])
+    x0 = make_inputs(CONFIGS["tiny-prefill-f32"])
     assert x0["r"].dtype == np.float32 and x0["state_in"] is None
 
 
 def test_distributions():
-    x = make_inputs(CONFIGS[1], B=2, T=512, H=4)
+    x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=512, H=4)
     f = {n: bf16_bits_to_f32(x[n]).astype(np.float64) for n in "rwkvab"}
     assert abs(f["r"].std() - 1.0) < 0.02 and abs(f["k"].std() - 0.125) < 0.003
     assert f["w"].min() >= np.exp(-np.exp(-0.5)) - 1e-2 and f["w"].max() <= 1.0
@@ -41,7 +41,7 @@ def test_distributions():
 
 
 def test_long_context_decay_and_forced_learning_rates():
-    cfg = CONFIGS[4]
+    cfg = CONFIGS["D4096-long-prefill"]
     x = make_inputs(cfg, B=1, T=256, H=8)
     w = bf16_bits_to_f32(x["w"])
     assert w.min() >= np.float32(np.exp(-np.exp(-0.1))) - 1e-2

@@ -55,7 +55,7 @@ def test_identity_token_keeps_a_representable_state(orc, fmt):
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_step_q_is_f64_step_then_rounding(orc, fmt):
     """A stored-state step equals the float64 step from the widened state, rounded once."""
-    cfg = CONFIGS[3]
+    cfg = CONFIGS["D2048-decode"]
     x = make_inputs(cfg, B=2, H=3, step=0)
     bits = orc.round16(x["state_in"].astype(np.float64), fmt)
     y, out = orc.step_q(*(x[n] for n in "rwkvab"), bits, fmt)
