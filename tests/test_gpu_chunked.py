@@ -61,21 +61,21 @@ def test_f32_inputs_are_refused(torch, CH):
     assert ei.value.status == -7
 
 
-def test_config1_full(torch, CH):
+def test_l12_d768_full(torch, CH):
     cfg = CONFIGS["L12-D768-prefill"]
-    say("algo", CH, "chunked config 1 full", cfg)
+    say("algo", CH, "chunked L12-D768 full", cfg)
     x = make_inputs(cfg)
     y, s = run(torch, to_dev(x), CH)
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     e = (rel(y, yr), rel(s, sr))
-    say("config 1 chunked errors", e)
+    say("L12-D768 chunked errors", e)
     assert e[0] <= TOL_BF16 and e[1] <= TOL_BF16, e
 
 
-def test_config2_full_and_resume(torch, CH):
+def test_l24_d1024_full_and_resume(torch, CH):
     """One pass and 4 x 1024-token segments with the state carried, each against the oracle."""
     cfg = CONFIGS["L24-D1024-prefill-resume"]
-    say("algo", CH, "chunked config 2 full + resume", cfg)
+    say("algo", CH, "chunked L24-D1024 full + resume", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
     y1, s1 = run(torch, d, CH)
@@ -91,7 +91,7 @@ def test_config2_full_and_resume(torch, CH):
     s4 = st.cpu().numpy()
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
     e = (rel(y1, yr), rel(s1, sr), rel(y4, yr), rel(s4, sr))
-    say("config 2 chunked errors (one pass y, s; resumed y, s)", e)
+    say("L24-D1024 chunked errors (one pass y, s; resumed y, s)", e)
     assert max(e) <= TOL_BF16, e
     # segments are chunk-aligned, so the resumed run repeats the one-pass arithmetic exactly
     assert np.array_equal(y4, y1) and np.array_equal(s4, s1)
@@ -118,9 +118,9 @@ def test_unaligned_resume(torch, CH):
     assert max(e) <= TOL_BF16, e
 
 
-def test_config4_sampled_heads_and_vs_sequential(torch, CH):
+def test_d4096_long_sampled_heads_and_vs_sequential(torch, CH):
     cfg = CONFIGS["D4096-long-prefill"]
-    say("algo", CH, "chunked config 4 full, 16 sampled heads + sequential comparison", cfg)
+    say("algo", CH, "chunked D4096-long full, 16 sampled heads + sequential comparison", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
     y, s = wkv.wkv7(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], d["state_in"], algo=CH)
@@ -129,7 +129,7 @@ def test_config4_sampled_heads_and_vs_sequential(torch, CH):
     # whole-tensor agreement with the float32 sequential kernel (itself ~1e-6 from the oracle)
     dy = (torch.max(torch.abs(y - ys)) / torch.max(torch.abs(ys))).item()
     ds = (torch.max(torch.abs(s - ss)) / torch.max(torch.abs(ss))).item()
-    say("config 4 chunked vs sequential", dy, ds)
+    say("D4096-long chunked vs sequential", dy, ds)
     assert dy <= TOL_BF16 and ds <= TOL_BF16, (dy, ds)
     units = sample_units(cfg.B, cfg.H, 16, seed=4)
     ref = oracle_units(x, units)
@@ -138,7 +138,7 @@ def test_config4_sampled_heads_and_vs_sequential(torch, CH):
     yr = np.stack([ref[u][0] for u in units])
     sr = np.stack([ref[u][1] for u in units])
     e = (rel(yg, yr), rel(sg, sr))
-    say("config 4 chunked vs oracle (sampled)", e)
+    say("D4096-long chunked vs oracle (sampled)", e)
     assert max(e) <= TOL_BF16, e
 
 

@@ -75,9 +75,9 @@ def test_many_heads_path(torch):
     assert rel(y, yr) <= 1e-5 and rel(s, sr) <= 1e-5
 
 
-def test_config1_full(torch):
+def test_l12_d768_full(torch):
     cfg = CONFIGS["L12-D768-prefill"]
-    say("config 1 full, sequential", cfg)
+    say("L12-D768 full, sequential", cfg)
     x = make_inputs(cfg)
     y, s = run_prefill(torch, to_dev(x))
     yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
@@ -85,10 +85,10 @@ def test_config1_full(torch):
     assert rel(y, yr) <= 1e-5 and rel(s, sr) <= 1e-5  # what the fp32 recurrence actually achieves
 
 
-def test_config2_split_resume_bit_identical(torch):
+def test_l24_d1024_split_resume_bit_identical(torch):
     """4 segments of 1024 tokens with the state carried equal one pass, bit for bit."""
     cfg = CONFIGS["L24-D1024-prefill-resume"]
-    say("config 2 split/resume, sequential", cfg)
+    say("L24-D1024 split/resume, sequential", cfg)
     x = make_inputs(cfg)
     d = to_dev(x)
     y1, s1 = run_prefill(torch, d)
@@ -106,10 +106,10 @@ def test_config2_split_resume_bit_identical(torch):
     assert rel(y1, yr) <= TOL_BF16 and rel(s1, sr) <= TOL_BF16, (rel(y1, yr), rel(s1, sr))
 
 
-def test_config3_decode_steps(torch):
+def test_d2048_decode_steps(torch):
     """256 in-place steps at B=512, H=32; oracle on 64 sampled heads over all steps."""
     cfg = CONFIGS["D2048-decode"]
-    say("config 3 decode, 256 steps", cfg)
+    say("D2048-decode decode, 256 steps", cfg)
     units = sample_units(cfg.B, cfg.H, 64, seed=3)
     x0 = make_inputs(cfg, step=0)
     state = torch.from_numpy(x0["state_in"]).cuda()
@@ -155,9 +155,9 @@ def test_prefill_equals_steps_bit_identical(torch):
     assert np.array_equal(st.cpu().numpy(), s1)
 
 
-def test_config4_sampled_heads(torch):
+def test_d4096_long_sampled_heads(torch):
     cfg = CONFIGS["D4096-long-prefill"]
-    say("config 4 full, sequential, 16 sampled heads", cfg)
+    say("D4096-long full, sequential, 16 sampled heads", cfg)
     x = make_inputs(cfg)
     units = sample_units(cfg.B, cfg.H, 16, seed=4)
     d = to_dev(x)

@@ -127,11 +127,11 @@ def test_null_state_in_and_in_place(torch, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
-def test_config3_256_steps(torch, fmt):
+def test_d2048_decode_256_steps(torch, fmt):
     """256 in-place steps at B=512, H=32 against the oracle's own 16-bit trajectory on 64
     sampled heads, and against the float32-state kernel (drift of the reduced state)."""
     cfg = CONFIGS["D2048-decode"]
-    say("step_q config 3, 256 steps", fmt)
+    say("step_q D2048-decode, 256 steps", fmt)
     code, ulp = FMTS[fmt]
     units = sample_units(cfg.B, cfg.H, 64, seed=5)
     bs = np.array([u[0] for u in units])
