@@ -444,7 +444,10 @@ constexpr int kSlots = kDist + 2;
 constexpr int kVCols = 16 * kScanWaves;           // value columns of v this workgroup needs
 constexpr int kVBytes = kC * kVCols * 2;          // bfloat16, [token][kVCols]: 1 KiB
 constexpr int kSlotBytes = kRecBytes + kVBytes;   // 10,496
-constexpr int kScanLds = kSlots * kSlotBytes;     // 73,472: two workgroups fit a compute unit
+// y staging: two chunks (by parity) of [token][kVCols] float32, so that a workgroup's y rows
+// leave in whole 128-byte lines rather than one 64-byte half per compute wave
+constexpr int kYStageBytes = kC * kVCols * 4;  // 2 KiB
+constexpr int kScanLds = kSlots * kSlotBytes + 2 * kYStageBytes;  // 77,568: two workgroups fit a compute unit
 constexpr int kLoads = kRecBlocks + 2;  // loads per lane per chunk: record blocks, e^gamma, v
 constexpr int kScanThreads = 64 * (kScanWaves + 1);
 // the load counter holds at most 63 outstanding operations: never more are in flight
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   const int64_t seq_base =
       ((int64_t)bb * p.T + (int64_t)p.c0 * kC) * p.H * kN + (int64_t)hh * kN + kVCols * part;
   const uint16_t* vbase = p.v + seq_base;  // this workgroup's value columns
-  float* ybase = p.y + seq_base + 16 * wave;
+  float* ybase = p.y + seq_base;  // this workgroup's value columns of y
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
 
   // ---- loader wave: chunk x (clamped to the last one: past the end the loads repeat it)
@@ -530,6 +533,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
       vm_wait<(kDist - 1) * kLoads>();
       asm volatile("s_barrier" ::: "memory");  // chunk c + 1
     }
+    asm volatile("s_barrier" ::: "memory");  // the last chunk's y is staged
     vm_wait<0>();  // every load has landed before the wave ends
     return;
   }
@@ -576,19 +580,28 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     for (int kt = 0; kt < 4; ++kt) f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
   };
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-  // y[t = li][i = 16 rb + 4g + e] of chunk c: four consecutive values per lane, one
-  // 16-byte store (tokens past the end of the sequence are not stored)
-  auto store_y = [&](int c, const f32x4& yv) {
-    const int nt = min(kC, p.T - (p.c0 + c) * kC);
-    const uint32_t off = (uint32_t)(((c * kC + li) * tstride + 4 * g) * 4u);
-    if (nt == kC)  // the same for the whole wave: a whole chunk stores with no lane masked
-      st_off<float4>(ybase, off, make_float4(yv[0], yv[1], yv[2], yv[3]));
-    else if (li < nt)
-      st_off<float4>(ybase, off, make_float4(yv[0], yv[1], yv[2], yv[3]));
+  // y of chunk c goes through LDS: each compute wave stages its 16 columns (lane: token li,
+  // columns 16 wave + 4g .. + 3), and after the next barrier wave q stores tokens 8q .. 8q + 7
+  // of all kVCols columns, eight lanes (128 contiguous bytes) per token; tokens past the end
+  // of the sequence are not stored
+  unsigned char* ystage = ring + kSlots * kSlotBytes;
+  auto stage_y = [&](auto par, const f32x4& yv) {
+    *reinterpret_cast<f32x4*>(ystage + decltype(par)::value * kYStageBytes + (li * kVCols + 16 * wave + 4 * g) * 4) = yv;
   };
-  // One chunk. Its y is stored at the end, after the state update is issued, when the
+  auto flush_y = [&](auto par, int c) {
+    const int tt = 8 * wave + (lane >> 3), cc = 4 * (lane & 7);
+    const f32x4 v =
+        *reinterpret_cast<const f32x4*>(ystage + decltype(par)::value * kYStageBytes + (tt * kVCols + cc) * 4);
+    const int nt = min(kC, p.T - (p.c0 + c) * kC);
+    const uint32_t off = (uint32_t)(((c * kC + tt) * tstride + cc) * 4u);
+    if (nt == kC)  // the same for the whole wave: a whole chunk stores with no lane masked
+      st_off<float4>(ybase, off, make_float4(v[0], v[1], v[2], v[3]));
+    else if (tt < nt)
+      st_off<float4>(ybase, off, make_float4(v[0], v[1], v[2], v[3]));
+  };
+  // One chunk. Its y is staged at the end, after the state update is issued, when the
   // products that made it have long completed.
-  auto step = [&](int c, const Frag& f) {
+  auto step = [&](auto par, const Frag& f) {
     half4 vB;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
@@ -631,7 +644,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     St[3][2] *= row_bcast<14>(f.dv);
     St[3][3] *= row_bcast<15>(f.dv);
     St[3] = mfma32(f.bk[3], uv, St[3]);
-    store_y(c, yv);
+    stage_y(par, yv);
   };
 
   // ---- compute waves. After barrier m they read chunk m and run the step of chunk
@@ -642,18 +655,25 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // the last chunk reads a slot that holds a repeat of it and is never used. (A read on
   // one side of a branch only would make the compiler's wait at the join cover the
   // next chunk's reads too.)
-  auto sync = [&]() { asm volatile("s_barrier" ::: "memory"); };
+  // the staged y of the previous chunk must be in LDS before the barrier; this also waits for
+  // the next chunk's reads, issued a step earlier
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
   Frag fr[2];
   // chunk c + j sits in slot j % kSlots (c is a multiple of the unroll, itself a multiple
   // of the ring size); the two register sets alternate, so the unroll is also even
   constexpr int kUnroll = kSlots % 2 == 0 ? kSlots : 2 * kSlots;
   int c = 0;
-  // chunk c + J: barrier, read of the next chunk, step; true after the last chunk
+  // chunk c + J: barrier, read of the next chunk, y of the chunk before, step; true after
+  // the last chunk
   auto chunk = [&](auto J) {
     constexpr int j = decltype(J)::value;
     sync();
     read(std::integral_constant<int, (j + 1) % kSlots>{}, fr[(j + 1) % 2]);
-    step(c + j, fr[j % 2]);
+    if (c + j > 0) flush_y(std::integral_constant<int, (j + 1) % 2>{}, c + j - 1);
+    step(std::integral_constant<int, j % 2>{}, fr[j % 2]);
     return c + j + 1 >= nc;
   };
   // chunks c .. c + kUnroll - 1, every slot index a constant; true after the last chunk
@@ -670,6 +690,11 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   read(std::integral_constant<int, 0>{}, fr[0]);
   for (;; c += kUnroll)
     if (unrolled(unrolled, std::integral_constant<int, 0>{})) break;
+  sync();  // the last chunk's y is staged (the loader waits at this barrier too)
+  if ((nc - 1) % 2 == 0)
+    flush_y(std::integral_constant<int, 0>{}, nc - 1);
+  else
+    flush_y(std::integral_constant<int, 1>{}, nc - 1);
 
   if (p.s_dst) {
 #pragma unroll
