@@ -138,9 +138,9 @@ int run_tmix(const void* r, const float* w_raw, const void* k, const void* v, co
   if (step && T != 1) return RWKV7_ERR_SHAPE;
   // the token-by-token kernel (AUTO keeps the bit-exact match with T single steps), or
   // the chunked prefill for bfloat16 inputs
-  if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SEQUENTIAL && algo != RWKV7_ALGO_CHUNKED_SPLIT)
+  if (algo < RWKV7_ALGO_AUTO || algo > RWKV7_ALGO_CHUNKED_SPLIT) return RWKV7_ERR_ALGO;
+  if ((algo == RWKV7_ALGO_CHUNKED || algo == RWKV7_ALGO_CHUNKED_SPLIT) && dtype != RWKV7_DTYPE_BF16)
     return RWKV7_ERR_ALGO;
-  if (algo == RWKV7_ALGO_CHUNKED_SPLIT && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_ALGO;
   if (B * H == 0) return RWKV7_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -149,7 +149,7 @@ int run_tmix(const void* r, const float* w_raw, const void* k, const void* v, co
     return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
   }
   rwkv7::TmixCall c{{r, w_raw, k, v, kk, a_lr, ln_w, ln_b, state_in, out, state_out, T, (int32_t)H}, B, H, dtype, s};
-  c.chunked = algo == RWKV7_ALGO_CHUNKED_SPLIT;
+  c.algo = algo;
   e = rwkv7::launch_tmix(c);
   if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;
   return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;

@@ -1,0 +1,506 @@
+// Chunk algebra of the chunked WKV-7 prefill, shared by the split kernels
+// (prep and scan as two launches, records in device memory) and the fused kernel
+// (both roles in one workgroup per head, records in an LDS ring).
+//
+// Recurrence (RWKV-7 G0 7.2B notes, lshu.cn/news/198401, section 7.1), per head:
+//   S_t = S_{t-1} (diag(w_t) + a_t b_t^T) + v_t k_t^T,   y_t = S_t r_t.
+//
+// Chunk form (derived; WY / "DPLR" style). Tokens t = 0..15 of a chunk, state S0
+// at its start, gamma_t = sum_{u<=t} log w_u per key column j:
+//   U[t]  = S_{t-1} a_t                       (the "state*a" term, a row over values i)
+//   U     = A' S0^T + G_u V,   Y = R' S0^T + G_y V,
+//   S_C^T = diag(e^{gamma_15}) S0^T + B- U + K- V
+// with
+//   A^[t] = a_t e^{gamma_{t-1}},  R^[t] = r_t e^{gamma_t},
+//   B-[s] = b_s e^{gamma_15 - gamma_s},  K-[s] = k_s e^{gamma_15 - gamma_s},
+//   L_ab[t][s] = sum_j a_t,j b_s,j e^{gamma_{t-1} - gamma_s}  (s <  t), L_ak likewise with k,
+//   L_rb[t][s] = sum_j r_t,j b_s,j e^{gamma_t - gamma_s}      (s <= t), L_rk likewise with k,
+//   T = (I - L_ab)^{-1},  M_r = L_rb T,
+//   A' = T A^,  R' = R^ + M_r A^,  G_u = T L_ak,  G_y = M_r L_ak + L_rk.
+// Everything except S0 and V is a function of the chunk's own r, w, k, a, b: the
+// "prep" of a chunk forms it as one record; the "scan" carries the state through
+// the records in order.
+//
+// Numerics. Decay factors are running products of w (clamped below at 2^-15).
+// The Gram factors pass through the decay at token 7 (Gq_t = e^{gamma_t - gamma_7}),
+// so no factor exceeds w_min^-8; e^{gamma_t} = Gq_t e^{gamma_7} (e^{gamma_7} >= 2^-120
+// is a normal float). The Grams are products of bfloat16 hi/lo halves (hi*hi + hi*lo +
+// lo*hi, about 2^-16 relative, with the float32 range) with float32 accumulation; T and
+// M_r are float32; A', R', G_u, G_y, B-, K-, the state operand and U are rounded once to
+// float16 as MFMA operands (float32 accumulation), so magnitudes must stay below 2^15.
+// The carried state is float32 throughout.
+//
+// MFMA layouts (gfx950, wave64; l = lane, li = l % 16, g = l / 16):
+//   16x16x16 f16      : A[m=li][k=4g+e],   B[k=4g+e][n=li]   (e = 0..3)
+//   16x16x32 f16/bf16 : A[m=li][k=8g+e],   B[k=8g+e][n=li]   (e = 0..7)
+//   all          : D[m=4g+e][n=li]
+// A D result is unchanged a B operand with K = 16, and a product with the
+// identity as B turns an A-layout tile into the D layout (a transpose).
+// Contractions may permute their K index freely as long as both operands use
+// the same permutation: the 64-key contractions below take key 16kt + 4g + e for
+// (step, lane group, element), matching the state tiles' D layout.
+//
+// One MFMA shape per dependent chain. Chains that mixed 16x16x32 and 16x16x16 f16
+// products gave wrong values on gfx950 in whichever product the register
+// allocation placed last; the same chains in one shape are exact. The wrappers
+// below therefore come in two families that take distinct operand types: Mma16
+// (16x16x16 f16, half4 operands, used only for the prep's transposes and its
+// 16-token products) and Mma32 (16x16x32, half8 / bf16x8 operands). Each chain in
+// this file accumulates through exactly one of them, so a chain that passes a
+// 16x16x16 result as the accumulator of a 16x16x32 product (or back) must convert
+// through an explicit f32x4 temporary that the code names as such.
+#pragma once
+
+#include "wkv7_device.hpp"
+
+namespace rwkv7 {
+namespace chunk {
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kC = 16;  // tokens per chunk
+constexpr float kWMin = 0x1p-15f;
+
+// Record of one (head, chunk): nine 1 KiB fragment blocks (16 bytes per lane),
+// then e^{gamma_15} for the 64 key columns.
+enum { kRecA0 = 0, kRecA1 = 1, kRecR0 = 2, kRecR1 = 3, kRecG = 4, kRecBK = 5, kRecBlocks = 9 };
+constexpr int kRecD = kRecBlocks * 1024;
+constexpr int kRecBytes = kRecD + kN * 4;  // 9472
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// 16x16x16 f16 family (the prep's transposes and 16-token products)
+struct Mma16 {
+  __device__ static __forceinline__ f32x4 mma(half4 a, half4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+// 16x16x32 family (the Grams in bfloat16, the scan in float16)
+struct Mma32 {
+  __device__ static __forceinline__ f32x4 mma(half8 a, half8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+__device__ __forceinline__ half4 to_h4(f32x4 x) {
+  return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+__device__ __forceinline__ half8 cat8(half4 lo, half4 hi) {
+  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// bfloat16 bits (low 16 bits of the argument) widened to float32, exactly
+__device__ __forceinline__ float bfw(uint32_t raw16) { return __uint_as_float(raw16 << 16); }
+// element e (0..3) of four bfloat16 packed in a uint2
+__device__ __forceinline__ float bf4(uint2 q, int e) {
+  const uint32_t u = e < 2 ? q.x : q.y;
+  return (e & 1) ? __uint_as_float(u & 0xffff0000u) : __uint_as_float(u << 16);
+}
+
+template <class V>
+__device__ __forceinline__ V ld_off(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
+}
+template <class V>
+__device__ __forceinline__ void st_off(void* base, uint32_t byte_off, V v) {
+  *reinterpret_cast<V*>(static_cast<char*>(base) + byte_off) = v;
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
+// ============================================================================ prep
+
+// Inputs of the prep. The plain recurrence takes r, w, k, a, b (bfloat16). The fused
+// time-mix operator takes r, k (bfloat16), w_raw (float32) in place of w, and kk,
+// a_lr in place of a, b; the prep then forms w = exp(-exp(w_raw)), the unit key
+// kk^ = kk / max(|kk|, 1e-12) over the head's 64 channels, a = -kk^ and b = kk^ a_lr.
+constexpr int kPrepPlain = 0, kPrepTmix = 1;
+struct PrepIn {
+  const uint16_t* r;
+  const uint16_t* w;   // plain: the decay
+  const float* w_raw;  // time-mix: the decay's log-log form
+  const uint16_t* k;
+  const uint16_t* a;   // plain: a; time-mix: kk
+  const uint16_t* b;   // plain: b; time-mix: a_lr
+  int32_t T, H;
+};
+
+constexpr int kFacRow = kN + 4;  // padded float row: token-layout reads of one row spread over the banks
+// Factor rows (float32, [row][key]), written in the key layout (lane = key j):
+//   row t + 1 = Gq_t = e^{gamma_t - gamma_7},  t = -1..15;   row kRowE7 = e^{gamma_7}.
+// e^{gamma_t} = Gq_t e^{gamma_7}, e^{gamma_7 - gamma_t} = 1 / Gq_t and
+// e^{gamma_15 - gamma_t} = Gq_15 / Gq_t are formed where they are used.
+constexpr int kRowE7 = 17, kFacRows = 18;
+constexpr int kFacBytes = kFacRows * kFacRow * 4;  // 4,896 bytes
+// After the factors are consumed the same area holds L_ab ([t][s], float32), the
+// right-hand sides of the solve (the identity, then L_rb, [32][16] float32) and the
+// rows of T and M_r (float16).
+constexpr int kLabOff = 0, kRhsOff = 16 * 16, kTmOffBytes = 3 * 16 * 16 * 4;
+constexpr int kPrepScratch = kFacBytes > kTmOffBytes + 2 * 16 * 16 * 2 ? kFacBytes : kTmOffBytes + 2 * 16 * 16 * 2;
+// In the fused kernel the scratch sits at the start of the chunk's own record slot:
+// it must end before the first record block that the prep writes while the factors
+// are still read (B- and K-, and e^{gamma_15}), and the products that overwrite it
+// are written only after T and M_r have been read into registers.
+static_assert(kPrepScratch <= kRecBK * 1024, "prep scratch overlaps the B-/K- blocks");
+
+// x = hi + lo with both halves bfloat16 (round to nearest even): 16 significant bits and
+// the float32 exponent range, which the Gram operands need (factors up to w_min^-8).
+__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int i) {
+  const __bf16 h = (__bf16)x;
+  hi[i] = h;
+  lo[i] = (__bf16)(x - (float)h);
+}
+// An ordering point for the values in x and for memory: the compiler computes x
+// before it and issues no later memory access ahead of it.
+__device__ __forceinline__ void pin16(float (&x)[16]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+               "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
+               :
+               : "memory");
+}
+
+// Raw inputs of one (head, chunk) in registers. Token layout for r, a, b, k: lane
+// (t = li, g) holds keys 16kt + 4g .. + 3 of token t; key layout for w: lane = key j,
+// all 16 tokens. Past-the-end tokens read token nt - 1 (masked in prep_compute).
+struct PrepRaw {
+  uint2 rr[4], ar[4], br[4], kr[4];
+  uint32_t wr[kC];  // plain: bfloat16 bits; time-mix: float32 bits of w_raw
+  int nt;           // live tokens, 1..16
+};
+
+// Issues the loads of chunk (bb, h, first token t0). base: element offset of token t0.
+template <int MODE>
+__device__ __forceinline__ void prep_load(const PrepIn& p, int64_t base, int nt, PrepRaw& x) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const uint32_t tstride = (uint32_t)p.H * kN;  // elements between tokens
+  const int tl = min(li, nt - 1);
+  x.nt = nt;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const uint32_t off = (uint32_t)(tl * tstride + 16 * kt + 4 * g) * 2u;
+    x.rr[kt] = ld_off<uint2>(p.r + base, off);
+    x.ar[kt] = ld_off<uint2>(p.a + base, off);
+    x.br[kt] = ld_off<uint2>(p.b + base, off);
+    x.kr[kt] = ld_off<uint2>(p.k + base, off);
+  }
+#pragma unroll
+  for (int t = 0; t < kC; ++t) {
+    const int tt = min(t, nt - 1);
+    if constexpr (MODE == kPrepTmix)
+      x.wr[t] = __float_as_uint(ld_off<float>(p.w_raw + base, (uint32_t)(tt * tstride + lane) * 4u));
+    else
+      x.wr[t] = ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u);
+  }
+}
+
+// The prep of one chunk from its raw inputs. fac: kPrepScratch bytes of this wave's
+// LDS. rec: the chunk's record (device memory or LDS); written as nine 1 KiB blocks,
+// 16 bytes per lane, plus e^{gamma_15}. rec may hold fac at its start (see above).
+template <int MODE>
+__device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned char* rec) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const int nt = x.nt;
+  const bool live = li < nt;
+
+  float wc[kC];
+#pragma unroll
+  for (int t = 0; t < kC; ++t) {
+    float w;
+    if constexpr (MODE == kPrepTmix)
+      w = expf(-expf(__uint_as_float(x.wr[t])));
+    else
+      w = bfw(x.wr[t]);
+    wc[t] = w < kWMin ? kWMin : w;  // clamp (a NaN passes through)
+  }
+  // The last chunk of a sequence may run past its end: its tokens t >= nt become
+  // identity tokens (w = 1, r = k = a = b = 0). The branch is the same for the whole wave.
+  if (nt < kC) {
+    const uint2 z2 = make_uint2(0u, 0u);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      x.rr[kt] = live ? x.rr[kt] : z2;
+      x.ar[kt] = live ? x.ar[kt] : z2;
+      x.br[kt] = live ? x.br[kt] : z2;
+      x.kr[kt] = live ? x.kr[kt] : z2;
+    }
+#pragma unroll
+    for (int t = 0; t < kC; ++t) wc[t] = t < nt ? wc[t] : 1.f;
+  }
+
+  // ---- decay factors (lane = j): Gq outward from token 7, so no factor exceeds
+  // w_min^-8, and the plain running product for e^{gamma_7} and e^{gamma_15}
+  {
+    const int j = lane;
+    float e = 1.f, gu = 1.f, gd = 1.f;
+    fac[8 * kFacRow + j] = 1.f;  // Gq_7
+#pragma unroll
+    for (int q = 0; q < kC; ++q) {
+      e *= wc[q];
+      if (q == 7) fac[kRowE7 * kFacRow + j] = e;
+      if (q < 8) {
+        gu *= wc[8 + q];  // Gq_t, t = 8 + q: times w_t
+        fac[(9 + q) * kFacRow + j] = gu;
+        gd *= __builtin_amdgcn_rcpf(wc[7 - q]);  // Gq_t, t = 6 - q: divided by w_{t+1}
+        fac[(7 - q) * kFacRow + j] = gd;
+      }
+    }
+    st_off<float>(rec, (uint32_t)(kRecD + 4 * j), e);  // e^{gamma_15}
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS before other lanes read them
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- token layout: operands, the four Grams and B-, K- (stored at once). Key 16kt + 4g + e
+  // of the lane's token. Each Gram contracts 64 keys on 16x16x32 bfloat16 MFMAs as
+  // hi*hi + hi*lo + lo*hi of the operands' bfloat16 halves (relative error about 2^-16),
+  // two key blocks per product: K index 8g + 4(kt % 2) + e. The Grams land in the D layout:
+  // lane (s = li, g) holds t = 4g + e; L_rk is formed transposed (operands swapped).
+  // Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
+  half4 eye;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
+  const uint32_t lo = (uint32_t)lane * 16u;  // record blocks: 16 bytes per lane
+  half4 Ahat[4];
+  f32x4 Rhat[4];
+  f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
+  // time-mix: 1 / max(|kk|, 1e-12) of this lane's token (its 64 channels are spread over
+  // the four lanes li, li + 16, li + 32, li + 48)
+  float inv = 1.f;
+  if constexpr (MODE == kPrepTmix) {
+    float n2 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = bf4(x.ar[kt], e);
+        n2 = fmaf(v, v, n2);
+      }
+    n2 += __shfl_xor(n2, 16);
+    n2 += __shfl_xor(n2, 32);
+    inv = 1.f / fmaxf(sqrtf(n2), 1e-12f);
+  }
+  bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int col = 16 * kt + 4 * g;
+    const float4 gqm1 = lds4(&fac[li * kFacRow + col]);      // Gq_{t-1}
+    const float4 gq = lds4(&fac[(li + 1) * kFacRow + col]);  // Gq_t
+    const float4 g15 = lds4(&fac[16 * kFacRow + col]);       // Gq_15
+    const float4 e7 = lds4(&fac[kRowE7 * kFacRow + col]);    // e^{gamma_7}
+    const uint2 ra = x.ar[kt], rv2 = x.rr[kt], rb = x.br[kt], rk = x.kr[kt];
+    half4 bbar, kbar;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float av = bf4(ra, e), bv = bf4(rb, e);
+      const float rv = bf4(rv2, e), kv = bf4(rk, e);
+      if constexpr (MODE == kPrepTmix) {  // a = -kk^, b = kk^ a_lr
+        const float kh1 = av * inv;
+        av = -kh1;
+        bv = kh1 * bv;
+      }
+      const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
+      const float suf = el(g15, e) * f;                  // e^{gamma_15 - gamma_t}
+      const int q8 = 4 * (kt & 1) + e;
+      const float ag = av * el(gqm1, e), rg = rv * el(gq, e);  // Gram operands
+      split_bf16(ag, ahH, ahL, q8);
+      split_bf16(rg, rhH, rhL, q8);
+      split_bf16(bv * f, bhH, bhL, q8);
+      split_bf16(kv * f, khH, khL, q8);
+      Ahat[kt][e] = (_Float16)(ag * el(e7, e));  // a e^{gamma_{t-1}}
+      Rhat[kt][e] = rg * el(e7, e);              // r e^{gamma_t}
+      bbar[e] = (_Float16)(bv * suf);
+      kbar[e] = (_Float16)(kv * suf);
+    }
+    const half4 BT = to_h4(Mma16::mma(bbar, eye, zero4()));  // lane (j = li, g): B-[4g+e][16kt + li]
+    const half4 KT = to_h4(Mma16::mma(kbar, eye, zero4()));
+    st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT, KT));
+    if (kt & 1) {
+      Lab = Mma32::mma(ahH, bhH, Lab);
+      Lak = Mma32::mma(ahH, khH, Lak);
+      Lrb = Mma32::mma(rhH, bhH, Lrb);
+      LrkT = Mma32::mma(khH, rhH, LrkT);
+      Lab = Mma32::mma(ahH, bhL, Lab);
+      Lak = Mma32::mma(ahH, khL, Lak);
+      Lrb = Mma32::mma(rhH, bhL, Lrb);
+      LrkT = Mma32::mma(khH, rhL, LrkT);
+      Lab = Mma32::mma(ahL, bhH, Lab);
+      Lak = Mma32::mma(ahL, khH, Lak);
+      Lrb = Mma32::mma(rhL, bhH, Lrb);
+      LrkT = Mma32::mma(khL, rhH, LrkT);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = 4 * g + e;            // row of Lab, Lak, Lrb; column li is s
+    Lab[e] = li < t ? Lab[e] : 0.f;     // strictly lower
+    Lak[e] = li < t ? Lak[e] : 0.f;
+    Lrb[e] = li <= t ? Lrb[e] : 0.f;    // lower with the diagonal
+    LrkT[e] = t <= li ? LrkT[e] : 0.f;  // element (s = 4g+e, t = li) of L_rk^T
+  }
+
+  // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
+  // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
+  // every x[s], s < s2. The factor rows are no longer read, so their area is reused;
+  // the row of L_ab for the next step is read while the current one is applied.
+  float* lab = fac + kLabOff;
+  float* rhs = fac + kRhsOff;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // every factor read of this wave has completed
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lab[(4 * g + e) * 16 + li] = Lab[e];
+    rhs[(4 * g + e) * 16 + li] = 4 * g + e == li ? 1.f : 0.f;  // identity: the rows of T
+    rhs[(16 + 4 * g + e) * 16 + li] = Lrb[e];                 // L_rb: the rows of M_r
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const int row = li;
+  float xs[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = lds4(&rhs[((g & 1) * 16 + row) * 16 + 4 * q]);  // lanes 32-63 repeat lanes 0-31
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xs[4 * q + e] = el(v, e);
+  }
+  float4 cur[4], nxt[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cur[q] = lds4(&lab[(kC - 1) * 16 + 4 * q]);
+#pragma unroll
+  for (int s2 = kC - 1; s2 >= 1; --s2) {
+    if (s2 > 1) {
+#pragma unroll
+      for (int q = 0; q < (s2 + 2) / 4; ++q) nxt[q] = lds4(&lab[(s2 - 1) * 16 + 4 * q]);
+    }
+#pragma unroll
+    for (int s = 0; s < s2; ++s) xs[s] = fmaf(xs[s2], el(cur[s / 4], s % 4), xs[s]);
+    pin16(xs);  // this step's updates before the next row's reads: one row in flight, not all
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+  }
+  _Float16* tm = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(fac) + kTmOffBytes);
+  if (g < 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<half4*>(&tm[(g * 16 + row) * 16 + 4 * q]) =
+          half4{(_Float16)xs[4 * q], (_Float16)xs[4 * q + 1], (_Float16)xs[4 * q + 2], (_Float16)xs[4 * q + 3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const half4 tB = *reinterpret_cast<const half4*>(&tm[li * 16 + 4 * g]);         // T[t = li][4g..]: T^T as B
+  const half4 mB = *reinterpret_cast<const half4*>(&tm[(16 + li) * 16 + 4 * g]);  // M_r^T as B
+  // T and M_r are in registers before any product overwrites the scratch (when the
+  // scratch is the record's own start)
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
+
+  // ---- products, stored per block. L_rk^T is added on the vector unit (a 16x16x32
+  // Gram result is not fed to a 16x16x16 product as its accumulator).
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    half4 ApT[2], RpT[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kt = 2 * kp + u;
+      const half4 AT = to_h4(Mma16::mma(Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
+      ApT[u] = to_h4(Mma16::mma(AT, tB, zero4()));                 // lane (t = li, g): A'[t][16kt + 4g + e]
+      RpT[u] = to_h4(Mma16::mma(AT, mB, Rhat[kt]));                // R'[t][16kt + 4g + e]
+    }
+    st_off<half8>(rec, (kRecA0 + kp) * 1024 + lo, cat8(ApT[0], ApT[1]));
+    st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
+  }
+  const half4 LakH = to_h4(Lak);  // as an A operand: L_ak^T (M = s', K = s)
+  const half4 GuT = to_h4(Mma16::mma(LakH, tB, zero4()));     // lane (t = li, g): G_u[t][4g + e]
+  const half4 GyT = to_h4(Mma16::mma(LakH, mB, zero4()) + LrkT);  // G_y[t][4g + e]
+  st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
+}
+
+// ============================================================================ scan
+
+// Fragments of one chunk as a scan wave consumes them.
+struct Frag {
+  half8 a0, a1, r0, r1, gl, bk[4];
+  float dv;       // e^{gamma_15} of key 16 (li / 4) + 4g + li % 4: lane 4kt + e of row g holds the
+                  // decay that every lane of the row needs as its (kt, e) element
+  uint32_t v[4];  // V[t = 4g + e][i = the wave's row li], raw bfloat16 bits (widened when used)
+};
+
+// Reads a chunk's fragments from its record in LDS. vrow: the record's v for this
+// wave, [token][vcols] bfloat16, at this wave's first value column.
+__device__ __forceinline__ void read_frag(const unsigned char* slot, const uint16_t* vrow, int vcols, Frag& f) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const uint32_t lo = (uint32_t)lane * 16u;
+  // in the order of use (the next chunk's first products take v and G)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.v[e] = vrow[(4 * g + e) * vcols + li];
+  f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
+  f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
+  f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
+  f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
+  f.r1 = *reinterpret_cast<const half8*>(slot + kRecR1 * 1024 + lo);
+  f.dv = *reinterpret_cast<const float*>(slot + kRecD + (16 * (li >> 2) + 4 * g + (li & 3)) * 4);
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
+}
+
+// Every lane of a row of 16 reads lane K of that row (DPP row broadcast).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xf, 0xf, false));
+}
+
+// One chunk of the scan for 16 value rows. St: the state in the D layout, element e of
+// St[kt] = S[i = row li][j = 16kt + 4g + e]. Returns Y transposed: lane (t = li, g) holds
+// y[t][i = 4g + e] of the wave's 16 rows.
+//   U = A' S0^T + G_u V and Y = R' S0^T + G_y V: two key halves, then the G V term
+//   (the record's G block holds G_u | G_y, so a B operand of V | 0 or 0 | V selects one
+//   of them); S^T <- diag(e^{gamma_15}) S^T + [B- | K-] [U ; V] per key tile.
+// Every product is 16x16x32 f16 (one shape for the whole dependent chain). The G V terms
+// come first: they do not depend on the state, so they need not wait for the previous
+// chunk's update. Y is formed transposed (operands swapped: the state and V fragments
+// serve as A operands, R' and G as B operands, from the same registers).
+__device__ __forceinline__ f32x4 scan_step(f32x4 (&St)[4], const Frag& f) {
+  const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+  half4 vB;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
+  f32x4 u = Mma32::mma(f.gl, cat8(vB, hz), zero4());
+  f32x4 yv = Mma32::mma(cat8(hz, vB), f.gl, zero4());
+  const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
+  const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
+  u = Mma32::mma(f.a0, sB0, u);
+  yv = Mma32::mma(sB0, f.r0, yv);
+  u = Mma32::mma(f.a1, sB1, u);
+  yv = Mma32::mma(sB1, f.r1, yv);
+  const half8 uv = cat8(to_h4(u), vB);
+  // the decays by row broadcasts (one 4-byte LDS read per lane instead of four 16-byte ones)
+  St[0][0] *= row_bcast<0>(f.dv);
+  St[0][1] *= row_bcast<1>(f.dv);
+  St[0][2] *= row_bcast<2>(f.dv);
+  St[0][3] *= row_bcast<3>(f.dv);
+  St[0] = Mma32::mma(f.bk[0], uv, St[0]);
+  St[1][0] *= row_bcast<4>(f.dv);
+  St[1][1] *= row_bcast<5>(f.dv);
+  St[1][2] *= row_bcast<6>(f.dv);
+  St[1][3] *= row_bcast<7>(f.dv);
+  St[1] = Mma32::mma(f.bk[1], uv, St[1]);
+  St[2][0] *= row_bcast<8>(f.dv);
+  St[2][1] *= row_bcast<9>(f.dv);
+  St[2][2] *= row_bcast<10>(f.dv);
+  St[2][3] *= row_bcast<11>(f.dv);
+  St[2] = Mma32::mma(f.bk[2], uv, St[2]);
+  St[3][0] *= row_bcast<12>(f.dv);
+  St[3][1] *= row_bcast<13>(f.dv);
+  St[3][2] *= row_bcast<14>(f.dv);
+  St[3][3] *= row_bcast<15>(f.dv);
+  St[3] = Mma32::mma(f.bk[3], uv, St[3]);
+  return yv;
+}
+
+}  // namespace chunk
+}  // namespace rwkv7

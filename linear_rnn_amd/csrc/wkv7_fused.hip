@@ -1,0 +1,242 @@
+// Chunked WKV-7 prefill in one kernel: one workgroup per head, whose prep waves
+// form the chunk records (the chunk algebra of wkv7_chunk_ops.hpp) into an LDS
+// ring and whose scan waves carry the float32 state through them in order. No
+// record leaves the compute unit, so the kernel moves only the algorithmic bytes:
+// the six inputs once, y once, the state in and out.
+//
+// Roles (12 waves, three per SIMD):
+//   waves 0-3   scan: wave w owns value rows 16w .. 16w + 15 of the state (float32, in
+//               MFMA accumulators); per chunk ten 16x16x32 MFMAs and one 16-byte y
+//               store per lane (RWKV-7 G0 7.2B notes, lshu.cn/news/198401, section
+//               7.1: y is read out with r after the update).
+//   waves 4-11  prep: wave p takes chunks p, p + 8, p + 16, ...; it loads the chunk's
+//               r, w, k, a, b (and v for the scan), waits for its ring slot to be free,
+//               forms the record in the slot (its factor and solve scratch lives at the
+//               slot's start) and marks the slot ready.
+// Hand-off through LDS words, no workgroup barrier after the first: ready[slot] holds
+// the last chunk whose record is complete in that slot (written after the writer's
+// LDS stores have completed), consumed[w] the number of chunks whose fragments scan
+// wave w has read into registers. A prep wave reuses the slot of chunk c - kRing once
+// every consumed[w] > c - kRing. The smallest unfinished chunk never waits on a later
+// one, so the hand-off cannot deadlock; every wait is also bounded (kSpinMax polls),
+// so a wave never spins forever even if the protocol were broken.
+#include <cstdint>
+
+#include "wkv7_chunk_ops.hpp"
+#include "wkv7_internal.hpp"
+
+namespace rwkv7 {
+namespace {
+
+using namespace chunk;
+
+constexpr int kScanW = 4;                    // scan waves (16 value rows each)
+constexpr int kPrepW = 8;                    // prep waves (one chunk each at a time)
+constexpr int kRing = 10;                    // record slots
+constexpr int kVRow = kN + 4;                // v row in the slot, bfloat16 elements (136 bytes: rows
+                                             // 4 apart start 8 banks apart, so a scan wave's v reads
+                                             // hit 32 distinct banks)
+constexpr int kVSlot = kC * kVRow * 2;       // 2,176 bytes
+constexpr int kSlot = kRecBytes + kVSlot;    // 11,648 bytes
+constexpr int kCtrlOff = kRing * kSlot;      // ready[kRing], then consumed[kScanW]
+constexpr int kLds = kCtrlOff + 4 * (kRing + kScanW);
+constexpr int kThreads = 64 * (kScanW + kPrepW);
+constexpr int kSpinMax = 1 << 20;            // polls of 100-200 cycles: well over any legitimate wait
+static_assert(kRing >= 3, "the scan reads one chunk ahead");
+static_assert(kLds <= 160 * 1024, "LDS per compute unit");
+static_assert(kRecBytes % 16 == 0 && kSlot % 16 == 0, "16-byte record blocks");
+
+struct FusedParams {
+  PrepIn in;  // r, w (or w_raw), k, a (or kk), b (or a_lr), T, H
+  const uint16_t* v;
+  float* y;
+  const float* s_in;  // may be null (zero state)
+  float* s_out;       // may be null
+  int32_t nc;         // chunks per sequence
+};
+
+__device__ __forceinline__ int lds_peek(const int* p) {
+  return __builtin_amdgcn_readfirstlane(__atomic_load_n(p, __ATOMIC_RELAXED));
+}
+// Waits until *flag >= target, then orders every later memory access after the wait.
+__device__ __forceinline__ void wait_at_least(const int* flag, int target) {
+#pragma clang loop unroll(disable)
+  for (int n = 0; n < kSpinMax; ++n) {
+    if (lds_peek(flag) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+// Waits until every one of the kScanW words at flags is >= target.
+__device__ __forceinline__ void wait_all_at_least(const int* flags, int target) {
+#pragma clang loop unroll(disable)
+  for (int n = 0; n < kSpinMax; ++n) {
+    int m = lds_peek(flags);
+#pragma unroll
+    for (int w = 1; w < kScanW; ++w) m = min(m, lds_peek(flags + w));
+    if (m >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+// Publishes value once every earlier LDS access of this wave has completed.
+__device__ __forceinline__ void post(int* flag, int value) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __atomic_store_n(flag, value, __ATOMIC_RELAXED);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
+  extern __shared__ __align__(16) unsigned char ring[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int unit = blockIdx.x;
+  const int H = p.in.H, T = p.in.T, nc = p.nc;
+  const int bb = unit / H, hh = unit % H;
+  const uint32_t tstride = (uint32_t)H * kN;  // elements between tokens
+  const int64_t seq_base = (int64_t)bb * T * H * kN + (int64_t)hh * kN;  // element offset of (bb, 0, hh, 0)
+  int* ready = reinterpret_cast<int*>(ring + kCtrlOff);
+  int* consumed = ready + kRing;
+  if (threadIdx.x < kRing) ready[threadIdx.x] = -1;
+  if (threadIdx.x < kScanW) consumed[threadIdx.x] = 0;
+  __syncthreads();
+
+  if (wave >= kScanW) {
+    // ---------------------------------------------------------------- prep waves
+    for (int c = wave - kScanW; c < nc; c += kPrepW) {
+      const int slot = c % kRing;
+      unsigned char* rec = ring + slot * kSlot;
+      const int t0 = c * kC;
+      const int nt = min(kC, T - t0);
+      const int64_t base = seq_base + (int64_t)t0 * tstride;
+      PrepRaw x;
+      prep_load<MODE>(p.in, base, nt, x);
+      // v of the chunk for the scan: lane l holds token l / 8 (+ 8) columns 8 (l % 8) .. + 7;
+      // tokens past the end repeat the last one (their record coefficients are zero)
+      uint4 vq[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int tv = min((lane >> 3) + 8 * h2, nt - 1);
+        vq[h2] = ld_off<uint4>(p.v + base, (uint32_t)(tv * tstride + 8 * (lane & 7)) * 2u);
+      }
+      wait_all_at_least(consumed, c - kRing + 1);  // the slot's previous chunk has been read
+      prep_compute<MODE>(x, reinterpret_cast<float*>(rec), rec);
+      uint16_t* vs = reinterpret_cast<uint16_t*>(rec + kRecBytes);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        uint2* d = reinterpret_cast<uint2*>(vs + ((lane >> 3) + 8 * h2) * kVRow + 8 * (lane & 7));
+        d[0] = make_uint2(vq[h2].x, vq[h2].y);
+        d[1] = make_uint2(vq[h2].z, vq[h2].w);
+      }
+      post(&ready[slot], c);
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------------ scan waves
+  __builtin_amdgcn_s_setprio(2);  // the chain of the state, ahead of the prep's work on this SIMD
+  const int w = wave;
+  f32x4 St[4];  // element e of St[kt] = S[i = 16 w + li][j = 16 kt + 4 g + e]
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) St[kt] = zero4();
+  if (p.s_in) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const float4 s = *reinterpret_cast<const float4*>(p.s_in + ((int64_t)unit * kN + 16 * w + li) * kN +
+                                                        16 * kt + 4 * g);
+      St[kt] = f32x4{s.x, s.y, s.z, s.w};
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
+  float* ybase = p.y + seq_base + 16 * w + 4 * g;
+  auto slot_of = [&](int c) { return ring + (c % kRing) * kSlot; };
+  auto read = [&](int c, Frag& f) {
+    const unsigned char* s = slot_of(c);
+    read_frag(s, reinterpret_cast<const uint16_t*>(s + kRecBytes) + 16 * w, kVRow, f);
+  };
+  Frag fa, fb;
+  wait_at_least(&ready[0], 0);
+  read(0, fa);
+  int c = 0;
+  // One chunk: the next chunk's fragments are read (its slot waited for) before this
+  // chunk's products are issued. Past the last chunk the read repeats the last chunk's
+  // slot, so the reads are unconditional (a read inside a branch would make the
+  // compiler wait for it at the join). Returns false after the last chunk.
+  auto body = [&](Frag& cur, Frag& nxt) {
+    const int cn = min(c + 1, nc - 1);
+    wait_at_least(&ready[cn % kRing], cn);
+    read(cn, nxt);
+    const f32x4 yv = scan_step(St, cur);
+    const int t = c * kC + li;
+    if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    post(&consumed[w], cn + 1);  // every fragment up to chunk cn is in registers
+    ++c;
+    return c < nc;
+  };
+  while (body(fa, fb) && body(fb, fa)) {
+  }
+  if (p.s_out) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      *reinterpret_cast<float4*>(p.s_out + ((int64_t)unit * kN + 16 * w + li) * kN + 16 * kt + 4 * g) =
+          make_float4(St[kt][0], St[kt][1], St[kt][2], St[kt][3]);
+  }
+}
+
+template <int MODE>
+hipError_t launch_fused(const FusedParams& fp, int64_t units, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&wkv7_fused_kernel<MODE>);
+  static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (attr != hipSuccess) return attr;
+  FusedParams q = fp;
+  void* args[] = {&q};
+  return hipLaunchKernel(fn, dim3((uint32_t)units), dim3(kThreads), args, kLds, stream);
+}
+
+// Offsets inside a sequence are 32-bit element counts (T * H * 64 below 2^31).
+bool fused_domain(int64_t T, int64_t H) { return T * H * kN < (int64_t(1) << 31); }
+
+}  // namespace
+
+hipError_t launch_chunked(const WkvCall& c) {
+  // bfloat16 inputs only: float32 inputs keep float32 accuracy on the sequential kernel
+  if (c.dtype != 1 || !fused_domain(c.T, c.H)) return hipErrorNotSupported;
+  FusedParams fp{};
+  fp.in.r = static_cast<const uint16_t*>(c.in[0]);
+  fp.in.w = static_cast<const uint16_t*>(c.in[1]);
+  fp.in.k = static_cast<const uint16_t*>(c.in[2]);
+  fp.in.a = static_cast<const uint16_t*>(c.in[4]);
+  fp.in.b = static_cast<const uint16_t*>(c.in[5]);
+  fp.in.T = (int32_t)c.T;
+  fp.in.H = (int32_t)c.H;
+  fp.v = static_cast<const uint16_t*>(c.in[3]);
+  fp.y = c.y;
+  fp.s_in = static_cast<const float*>(c.s_in);
+  fp.s_out = static_cast<float*>(c.s_out);
+  fp.nc = (int32_t)((c.T + kC - 1) / kC);
+  return launch_fused<kPrepPlain>(fp, c.B * c.H, c.stream);
+}
+
+hipError_t launch_tmix_fused(const TmixCall& c) {
+  const TmixParams& t = c.p;
+  if (c.dtype != 1 || !fused_domain(t.T, c.H)) return hipErrorNotSupported;
+  FusedParams fp{};
+  fp.in.r = static_cast<const uint16_t*>(t.r);
+  fp.in.w_raw = t.w_raw;
+  fp.in.k = static_cast<const uint16_t*>(t.k);
+  fp.in.a = static_cast<const uint16_t*>(t.kk);
+  fp.in.b = static_cast<const uint16_t*>(t.a_lr);
+  fp.in.T = (int32_t)t.T;
+  fp.in.H = (int32_t)c.H;
+  fp.v = static_cast<const uint16_t*>(t.v);
+  fp.y = t.out;
+  fp.s_in = t.s_in;
+  fp.s_out = t.s_out;
+  fp.nc = (int32_t)((t.T + kC - 1) / kC);
+  const hipError_t e = launch_fused<kPrepTmix>(fp, c.B * c.H, c.stream);
+  if (e != hipSuccess) return e;
+  return launch_tmix_ln(t.out, t.ln_w, t.ln_b, c.B * t.T * c.H, (int32_t)c.H, c.stream);
+}
+
+}  // namespace rwkv7

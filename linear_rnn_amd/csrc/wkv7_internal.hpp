@@ -24,7 +24,9 @@ struct WkvCall {
 hipError_t launch_sequential(const WkvCall& c, bool decode_shape);
 
 // Chunked (WY / UT) prefill with the intra-chunk products on MFMA, one
-// workgroup per head doing every stage.
+// workgroup per head: prep waves form the chunk records in an LDS ring that the
+// head's scan waves consume (no workspace). hipErrorNotSupported outside its
+// domain (bfloat16 inputs, T * H * 64 below 2^31).
 hipError_t launch_chunked(const WkvCall& c);
 
 // Chunked prefill split into a chunk-parallel prep kernel and a per-head scan
@@ -53,7 +55,7 @@ struct TmixCall {
   int64_t B, H;
   int dtype;  // RWKV7_DTYPE_* of r, k, v, kk, a_lr
   hipStream_t stream;
-  bool chunked = false;  // a prefill (T > 1, bfloat16) through the chunked prep and scan
+  int algo = 0;  // RWKV7_ALGO_*: AUTO / SEQUENTIAL token by token; CHUNKED or CHUNKED_SPLIT (bfloat16, T > 1)
 };
 hipError_t launch_tmix(const TmixCall& c);
 // The fused operator as a chunked prefill (bfloat16 inputs): the prep forms the
@@ -61,6 +63,13 @@ hipError_t launch_tmix(const TmixCall& c);
 // normalises it in place. Decays below 2^-15 are clamped, as in the chunked
 // prefill of the recurrence.
 hipError_t launch_tmix_chunked(const TmixCall& c);
+// The same with the one-kernel chunked prefill (the prep's time-mix mode in the
+// fused kernel), then ln_x in place.
+hipError_t launch_tmix_fused(const TmixCall& c);
+// ln_x in place on rows of 64 (one token of one head each): GroupNorm per head with
+// eps 64e-5, then the per-channel affine (ln_w / ln_b may be null).
+hipError_t launch_tmix_ln(float* out, const float* ln_w, const float* ln_b, int64_t rows, int32_t H,
+                          hipStream_t stream);
 
 // Reverse-mode derivatives of the recurrence: a checkpointing forward pass and
 // a reverse pass over the checkpoints, all gradients float32.

@@ -65,355 +65,49 @@
 #include <type_traits>
 #include <utility>
 
-#include "wkv7_device.hpp"
+#include "wkv7_chunk_ops.hpp"
 #include "wkv7_internal.hpp"
 
 namespace rwkv7 {
 namespace {
 
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kC = 16;   // tokens per chunk
-constexpr float kWMin = 0x1p-15f;
-
-// Record of one (head, chunk): nine 1 KiB fragment blocks (16 bytes per lane),
-// then e^{gamma_15} for the 64 key columns.
-enum { kRecA0 = 0, kRecA1 = 1, kRecR0 = 2, kRecR1 = 3, kRecG = 4, kRecBK = 5, kRecBlocks = 9 };
-constexpr int kRecD = kRecBlocks * 1024;
-constexpr int kRecBytes = kRecD + kN * 4;  // 9472
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ f32x4 mfma16(half4 a, half4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ half4 to_h4(f32x4 x) {
-  return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-}
-__device__ __forceinline__ half8 cat8(half4 lo, half4 hi) {
-  return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-
-// bfloat16 bits (low 16 bits of the argument) widened to float32, exactly
-__device__ __forceinline__ float bfw(uint32_t raw16) { return __uint_as_float(raw16 << 16); }
-// element e (0..3) of four bfloat16 packed in a uint2
-__device__ __forceinline__ float bf4(uint2 q, int e) {
-  const uint32_t u = e < 2 ? q.x : q.y;
-  return (e & 1) ? __uint_as_float(u & 0xffff0000u) : __uint_as_float(u << 16);
-}
-
-template <class V>
-__device__ __forceinline__ V ld_off(const void* base, uint32_t byte_off) {
-  return *reinterpret_cast<const V*>(static_cast<const char*>(base) + byte_off);
-}
-template <class V>
-__device__ __forceinline__ void st_off(void* base, uint32_t byte_off, V v) {
-  *reinterpret_cast<V*>(static_cast<char*>(base) + byte_off) = v;
-}
+using namespace chunk;
 
 // ============================================================================ kernel 1: prep
 
-// Inputs of the prep. The plain recurrence takes r, w, k, a, b (bfloat16). The fused
-// time-mix operator takes r, k (bfloat16), w_raw (float32) in place of w, and kk,
-// a_lr in place of a, b; the prep then forms w = exp(-exp(w_raw)), the unit key
-// kk^ = kk / max(|kk|, 1e-12) over the head's 64 channels, a = -kk^ and b = kk^ a_lr.
-constexpr int kPrepPlain = 0, kPrepTmix = 1;
 struct PrepParams {
-  const uint16_t* r;
-  const uint16_t* w;   // plain: the decay
-  const float* w_raw;  // time-mix: the decay's log-log form
-  const uint16_t* k;
-  const uint16_t* a;   // plain: a; time-mix: kk
-  const uint16_t* b;   // plain: b; time-mix: a_lr
+  PrepIn in;
   unsigned char* rec;  // [unit][chunk of slab][kRecBytes]
-  int32_t T, H;
   int32_t c0;     // first chunk of the slab
   int32_t nc;     // chunks in the slab
   int32_t items;  // B * H * nc
 };
 
 constexpr int kPrepWaves = 4;
-constexpr int kFacRow = kN + 4;  // padded float row: token-layout reads of one row spread over the banks
-// Factor rows (float32, [row][key]), written in the key layout (lane = key j):
-//   E  row t + 1 = e^{gamma_t},            t = -1..15
-//   Gq row t + 1 = e^{gamma_t - gamma_7},  t = -1..15
-// Fk_t = e^{gamma_7 - gamma_t} = 1 / Gq_t and e^{gamma_15 - gamma_t} = Gq_15 Fk_t are
-// formed where they are used.
-constexpr int kRowE = 0, kRowG = 17, kFacRows = 34;
-constexpr int kPrepLdsPerWave = kFacRows * kFacRow * 4;  // 9,248 bytes
-// After the factors are consumed the same wave area holds L_ab ([t][s], float32), the
-// right-hand sides of the solve (the identity, then L_rb, [32][16] float32) and the
-// rows of T and M_r (float16).
-constexpr int kLabOff = 0, kRhsOff = 16 * 16, kTmOffBytes = 3 * 16 * 16 * 4;
-static_assert(kTmOffBytes + 2 * 16 * 16 * 2 <= kPrepLdsPerWave, "solve area");
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-// x = hi + lo with both halves bfloat16 (round to nearest even): 16 significant bits and
-// the float32 exponent range, which the Gram operands need (factors up to w_min^-8).
-__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int i) {
-  const __bf16 h = (__bf16)x;
-  hi[i] = h;
-  lo[i] = (__bf16)(x - (float)h);
-}
-__device__ __forceinline__ f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-// An ordering point for the values in x and for memory: the compiler computes x
-// before it and issues no later memory access ahead of it.
-__device__ __forceinline__ void pin16(float (&x)[16]) {
-  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
-               "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15])
-               :
-               : "memory");
-}
-__device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
 template <int MODE>
 // three waves per SIMD: the register budget of four spills
 __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu(3))) void wkv7_prep_kernel(PrepParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, g = lane >> 4;
   const int item = (int)blockIdx.x * kPrepWaves + wave;
   if (item >= p.items) return;  // wave-uniform; this kernel has no workgroup barrier
-  float* fac = reinterpret_cast<float*>(smem_raw + wave * kPrepLdsPerWave);
+  float* fac = reinterpret_cast<float*>(smem_raw + wave * kPrepScratch);
 
   // item = (b * nc + chunk) * H + h: neighbouring waves read neighbouring heads of one token block
-  const int h = item % p.H;
-  const int rest = item / p.H;
+  const int H = p.in.H;
+  const int h = item % H;
+  const int rest = item / H;
   const int cl = rest % p.nc;
   const int bb = rest / p.nc;
-  const int unit = bb * p.H + h;
+  const int unit = bb * H + h;
   const int t0 = (p.c0 + cl) * kC;
-  const int nt = min(kC, p.T - t0);  // live tokens, >= 1
-  const int64_t base = ((int64_t)bb * p.T + t0) * p.H * kN + (int64_t)h * kN;  // element offset of token t0
-  const uint32_t tstride = (uint32_t)p.H * kN;                                // elements between tokens
+  const int nt = min(kC, p.in.T - t0);  // live tokens, >= 1
+  const int64_t base = ((int64_t)bb * p.in.T + t0) * H * kN + (int64_t)h * kN;  // element offset of token t0
   unsigned char* rec = p.rec + ((int64_t)unit * p.nc + cl) * kRecBytes;
-
-  // ---- raw r, a, b, k in the token layout: lane (t = li, g) holds keys 16kt + 4g .. 4g+3.
-  // Past-the-end tokens read token nt-1 and become identity tokens (r = k = a = b = 0, w = 1).
-  const int tl = min(li, nt - 1);
-  const bool live = li < nt;
-  uint2 rr[4], ar[4], br[4], kr[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const uint32_t off = (uint32_t)(tl * tstride + 16 * kt + 4 * g) * 2u;
-    rr[kt] = ld_off<uint2>(p.r + base, off);
-    ar[kt] = ld_off<uint2>(p.a + base, off);
-    br[kt] = ld_off<uint2>(p.b + base, off);
-    kr[kt] = ld_off<uint2>(p.k + base, off);
-  }
-  // ---- w in the key layout: lane = key j, all 16 tokens
-  float wc[kC];
-#pragma unroll
-  for (int t = 0; t < kC; ++t) {
-    const int tt = min(t, nt - 1);
-    float x;
-    if constexpr (MODE == kPrepTmix)
-      x = expf(-expf(ld_off<float>(p.w_raw + base, (uint32_t)(tt * tstride + lane) * 4u)));
-    else
-      x = bfw(ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u));
-    wc[t] = x < kWMin ? kWMin : x;  // clamp (a NaN passes through)
-  }
-  // The last chunk of a sequence may run past its end: its tokens t >= nt become
-  // identity tokens (w = 1, r = k = a = b = 0). The branch is the same for the whole wave.
-  if (nt < kC) {
-    const uint2 z2 = make_uint2(0u, 0u);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      rr[kt] = live ? rr[kt] : z2;
-      ar[kt] = live ? ar[kt] : z2;
-      br[kt] = live ? br[kt] : z2;
-      kr[kt] = live ? kr[kt] : z2;
-    }
-#pragma unroll
-    for (int t = 0; t < kC; ++t) wc[t] = t < nt ? wc[t] : 1.f;
-  }
-
-  // ---- decay factors (lane = j): running products from token 0 (E) and outward from
-  // token 7 (Gq), so no factor exceeds w_min^-8
-  {
-    const int j = lane;
-    float e = 1.f, gu = 1.f, gd = 1.f;
-    fac[kRowE * kFacRow + j] = 1.f;        // E_{-1}
-    fac[(kRowG + 8) * kFacRow + j] = 1.f;  // Gq_7
-#pragma unroll
-    for (int q = 0; q < kC; ++q) {
-      e *= wc[q];
-      fac[(kRowE + q + 1) * kFacRow + j] = e;  // E_q
-      if (q < 8) {
-        gu *= wc[8 + q];  // Gq_t, t = 8 + q: times w_t
-        fac[(kRowG + 9 + q) * kFacRow + j] = gu;
-        gd *= __builtin_amdgcn_rcpf(wc[7 - q]);  // Gq_t, t = 6 - q: divided by w_{t+1}
-        fac[(kRowG + 7 - q) * kFacRow + j] = gd;
-      }
-    }
-    st_off<float>(rec, (uint32_t)(kRecD + 4 * j), e);  // e^{gamma_15}
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS before other lanes read them
-  __builtin_amdgcn_wave_barrier();
-
-  // ---- token layout: operands, the four Grams and B-, K- (stored at once). Key 16kt + 4g + e
-  // of the lane's token. Each Gram contracts 64 keys on 16x16x32 bfloat16 MFMAs as
-  // hi*hi + hi*lo + lo*hi of the operands' bfloat16 halves (relative error about 2^-16),
-  // two key blocks per product: K index 8g + 4(kt % 2) + e. The Grams land in the D layout:
-  // lane (s = li, g) holds t = 4g + e; L_rk is formed transposed (operands swapped).
-  // Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
-  half4 eye;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
-  const uint32_t lo = (uint32_t)lane * 16u;  // record blocks: 16 bytes per lane
-  half4 Ahat[4];
-  f32x4 Rhat[4];
-  f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
-  // time-mix: 1 / max(|kk|, 1e-12) of this lane's token (its 64 channels are spread over
-  // the four lanes li, li + 16, li + 32, li + 48)
-  float inv = 1.f;
-  if constexpr (MODE == kPrepTmix) {
-    float n2 = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = bf4(ar[kt], e);
-        n2 = fmaf(x, x, n2);
-      }
-    n2 += __shfl_xor(n2, 16);
-    n2 += __shfl_xor(n2, 32);
-    inv = 1.f / fmaxf(sqrtf(n2), 1e-12f);
-  }
-  bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int col = 16 * kt + 4 * g;
-    const float4 em1 = lds4(&fac[(kRowE + li) * kFacRow + col]);
-    const float4 e0 = lds4(&fac[(kRowE + li + 1) * kFacRow + col]);
-    const float4 gqm1 = lds4(&fac[(kRowG + li) * kFacRow + col]);
-    const float4 gq = lds4(&fac[(kRowG + li + 1) * kFacRow + col]);
-    const float4 g15 = lds4(&fac[(kRowG + 16) * kFacRow + col]);
-    const uint2 ra = ar[kt], rv2 = rr[kt], rb = br[kt], rk = kr[kt];
-    half4 bbar, kbar;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float av = bf4(ra, e), bv = bf4(rb, e);
-      const float rv = bf4(rv2, e), kv = bf4(rk, e);
-      if constexpr (MODE == kPrepTmix) {  // a = -kk^, b = kk^ a_lr
-        const float kh1 = av * inv;
-        av = -kh1;
-        bv = kh1 * bv;
-      }
-      const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
-      const float suf = el(g15, e) * f;  // e^{gamma_15 - gamma_t}
-      const int q8 = 4 * (kt & 1) + e;
-      split_bf16(av * el(gqm1, e), ahH, ahL, q8);
-      split_bf16(rv * el(gq, e), rhH, rhL, q8);
-      split_bf16(bv * f, bhH, bhL, q8);
-      split_bf16(kv * f, khH, khL, q8);
-      Ahat[kt][e] = (_Float16)(av * el(em1, e));
-      Rhat[kt][e] = rv * el(e0, e);
-      bbar[e] = (_Float16)(bv * suf);
-      kbar[e] = (_Float16)(kv * suf);
-    }
-    const half4 BT = to_h4(mfma16(bbar, eye, zero4()));  // lane (j = li, g): B-[4g+e][16kt + li]
-    const half4 KT = to_h4(mfma16(kbar, eye, zero4()));
-    st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT, KT));
-    if (kt & 1) {
-      Lab = mfma_bf(ahH, bhH, Lab);
-      Lak = mfma_bf(ahH, khH, Lak);
-      Lrb = mfma_bf(rhH, bhH, Lrb);
-      LrkT = mfma_bf(khH, rhH, LrkT);
-      Lab = mfma_bf(ahH, bhL, Lab);
-      Lak = mfma_bf(ahH, khL, Lak);
-      Lrb = mfma_bf(rhH, bhL, Lrb);
-      LrkT = mfma_bf(khH, rhL, LrkT);
-      Lab = mfma_bf(ahL, bhH, Lab);
-      Lak = mfma_bf(ahL, khH, Lak);
-      Lrb = mfma_bf(rhL, bhH, Lrb);
-      LrkT = mfma_bf(khL, rhH, LrkT);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g + e;            // row of Lab, Lak, Lrb; column li is s
-    Lab[e] = li < t ? Lab[e] : 0.f;     // strictly lower
-    Lak[e] = li < t ? Lak[e] : 0.f;
-    Lrb[e] = li <= t ? Lrb[e] : 0.f;    // lower with the diagonal
-    LrkT[e] = t <= li ? LrkT[e] : 0.f;  // element (s = 4g+e, t = li) of L_rk^T
-  }
-
-  // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
-  // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
-  // every x[s], s < s2. The factor rows are no longer read, so their area is reused;
-  // the row of L_ab for the next step is read while the current one is applied.
-  float* lab = fac + kLabOff;
-  float* rhs = fac + kRhsOff;
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // every factor read of this wave has completed
-  asm volatile("" ::: "memory");
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    lab[(4 * g + e) * 16 + li] = Lab[e];
-    rhs[(4 * g + e) * 16 + li] = 4 * g + e == li ? 1.f : 0.f;  // identity: the rows of T
-    rhs[(16 + 4 * g + e) * 16 + li] = Lrb[e];                 // L_rb: the rows of M_r
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  const int row = li;
-  float x[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 v = lds4(&rhs[((g & 1) * 16 + row) * 16 + 4 * q]);  // lanes 32-63 repeat lanes 0-31
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * q + e] = el(v, e);
-  }
-  float4 cur[4], nxt[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) cur[q] = lds4(&lab[(kC - 1) * 16 + 4 * q]);
-#pragma unroll
-  for (int s2 = kC - 1; s2 >= 1; --s2) {
-    if (s2 > 1) {
-#pragma unroll
-      for (int q = 0; q < (s2 + 2) / 4; ++q) nxt[q] = lds4(&lab[(s2 - 1) * 16 + 4 * q]);
-    }
-#pragma unroll
-    for (int s = 0; s < s2; ++s) x[s] = fmaf(x[s2], el(cur[s / 4], s % 4), x[s]);
-    pin16(x);  // this step's updates before the next row's reads: one row in flight, not all
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
-  }
-  _Float16* tm = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(fac) + kTmOffBytes);
-  if (g < 2) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<half4*>(&tm[(g * 16 + row) * 16 + 4 * q]) =
-          half4{(_Float16)x[4 * q], (_Float16)x[4 * q + 1], (_Float16)x[4 * q + 2], (_Float16)x[4 * q + 3]};
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  const half4 tB = *reinterpret_cast<const half4*>(&tm[li * 16 + 4 * g]);         // T[t = li][4g..]: T^T as B
-  const half4 mB = *reinterpret_cast<const half4*>(&tm[(16 + li) * 16 + 4 * g]);  // M_r^T as B
-
-  // ---- products, stored per block. L_rk^T is added on the vector unit.
-#pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    half4 ApT[2], RpT[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kt = 2 * kp + u;
-      const half4 AT = to_h4(mfma16(Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
-      ApT[u] = to_h4(mfma16(AT, tB, zero4()));                 // lane (t = li, g): A'[t][16kt + 4g + e]
-      RpT[u] = to_h4(mfma16(AT, mB, Rhat[kt]));                // R'[t][16kt + 4g + e]
-    }
-    st_off<half8>(rec, (kRecA0 + kp) * 1024 + lo, cat8(ApT[0], ApT[1]));
-    st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
-  }
-  const half4 LakH = to_h4(Lak);  // as an A operand: L_ak^T (M = s', K = s)
-  const half4 GuT = to_h4(mfma16(LakH, tB, zero4()));         // lane (t = li, g): G_u[t][4g + e]
-  const half4 GyT = to_h4(mfma16(LakH, mB, zero4()) + LrkT);  // G_y[t][4g + e]
-  st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
+  PrepRaw x;
+  prep_load<MODE>(p.in, base, nt, x);
+  prep_compute<MODE>(x, fac, rec);
 }
 
 // ============================================================================ kernel 2: scan
@@ -454,9 +148,6 @@ constexpr int kScanThreads = 64 * (kScanWaves + 1);
 static_assert(kDist * kLoads < 64, "load counter");
 static_assert(kVBytes == 64 * 16 && kRecBlocks == 9, "one 16-byte piece of v per lane");
 
-__device__ __forceinline__ f32x4 mfma32(half8 a, half8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -470,11 +161,6 @@ __device__ __forceinline__ void to_lds(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
   else
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
-}
-// Every lane of a row of 16 reads lane K of that row (DPP row broadcast).
-template <int K>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xf, 0xf, false));
 }
 // Waits until at most N of this wave's vector-memory operations are outstanding
 // (they complete in issue order), and orders every later memory access after it.
@@ -554,32 +240,13 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // (it would otherwise wait for it at the first use, behind the first chunks' loads)
   __builtin_amdgcn_s_waitcnt(0x0f70);
 
-  // fragments of one chunk, read from its ring slot one iteration ahead
-  struct Frag {
-    half8 a0, a1, r0, r1, gl, bk[4];
-    float dv;  // e^{gamma_15} of key 16 (li / 4) + 4g + li % 4: lane 4kt + e of row g holds the
-               // decay that every lane of the row needs as its (kt, e) element
-    uint32_t v[4];  // V[t = 4g + e][i = 16 rb + li], raw bfloat16 bits (widened when used)
-  };
-  const uint32_t lo = (uint32_t)lane * 16u;
-  // the loop below is unrolled by the ring size, so every slot index is a constant and
-  // every LDS address a fixed offset from the lane's base
+  // fragments of one chunk, read from its ring slot one iteration ahead. The loop below
+  // is unrolled by the ring size, so every slot index is a constant and every LDS
+  // address a fixed offset from the lane's base.
   auto read = [&](auto slot_index, Frag& f) {
     const unsigned char* slot = ring + decltype(slot_index)::value * kSlotBytes;
-    // in the order of use (the next chunk's first products take v and G)
-    const uint16_t* vr = reinterpret_cast<const uint16_t*>(slot + kRecBytes);  // [token][kVCols]
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.v[e] = vr[(4 * g + e) * kVCols + 16 * wave + li];
-    f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
-    f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
-    f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);
-    f.a1 = *reinterpret_cast<const half8*>(slot + kRecA1 * 1024 + lo);
-    f.r1 = *reinterpret_cast<const half8*>(slot + kRecR1 * 1024 + lo);
-    f.dv = *reinterpret_cast<const float*>(slot + kRecD + (16 * (li >> 2) + 4 * g + (li & 3)) * 4);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) f.bk[kt] = *reinterpret_cast<const half8*>(slot + (kRecBK + kt) * 1024 + lo);
+    read_frag(slot, reinterpret_cast<const uint16_t*>(slot + kRecBytes) + 16 * wave, kVCols, f);
   };
-  const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
   // y of chunk c goes through LDS: each compute wave stages its 16 columns (lane: token li,
   // columns 16 wave + 4g .. + 3), and after the next barrier wave q stores tokens 8q .. 8q + 7
   // of all kVCols columns, eight lanes (128 contiguous bytes) per token; tokens past the end
@@ -602,48 +269,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // One chunk. Its y is staged at the end, after the state update is issued, when the
   // products that made it have long completed.
   auto step = [&](auto par, const Frag& f) {
-    half4 vB;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
-    // K = 32 products (16x16x32 only: every dependent chain keeps one MFMA shape).
-    //   U = A' S0^T + G_u V and Y = R' S0^T + G_y V: two key halves, then the
-    //   G V term (the record's G block holds G_u | G_y, so a B operand of V | 0
-    //   or 0 | V selects one of them);
-    //   S^T <- diag(e^{gamma_15}) S^T + [B- | K-] [U ; V] per key tile.
-    // the G V terms first: they do not depend on the state, so they need not wait for
-    // the previous chunk's update. Y is formed transposed (operands swapped: the state
-    // and V fragments serve as A operands, R' and G as B operands, from the same
-    // registers), so a lane holds four consecutive value rows of one token for its store.
-    f32x4 u = mfma32(f.gl, cat8(vB, hz), zero4());
-    f32x4 yv = mfma32(cat8(hz, vB), f.gl, zero4());
-    const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
-    const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
-    u = mfma32(f.a0, sB0, u);
-    yv = mfma32(sB0, f.r0, yv);
-    u = mfma32(f.a1, sB1, u);
-    yv = mfma32(sB1, f.r1, yv);
-    const half8 uv = cat8(to_h4(u), vB);
-    // the decays by row broadcasts (one 4-byte LDS read per lane instead of four 16-byte ones)
-    St[0][0] *= row_bcast<0>(f.dv);
-    St[0][1] *= row_bcast<1>(f.dv);
-    St[0][2] *= row_bcast<2>(f.dv);
-    St[0][3] *= row_bcast<3>(f.dv);
-    St[0] = mfma32(f.bk[0], uv, St[0]);
-    St[1][0] *= row_bcast<4>(f.dv);
-    St[1][1] *= row_bcast<5>(f.dv);
-    St[1][2] *= row_bcast<6>(f.dv);
-    St[1][3] *= row_bcast<7>(f.dv);
-    St[1] = mfma32(f.bk[1], uv, St[1]);
-    St[2][0] *= row_bcast<8>(f.dv);
-    St[2][1] *= row_bcast<9>(f.dv);
-    St[2][2] *= row_bcast<10>(f.dv);
-    St[2][3] *= row_bcast<11>(f.dv);
-    St[2] = mfma32(f.bk[2], uv, St[2]);
-    St[3][0] *= row_bcast<12>(f.dv);
-    St[3][1] *= row_bcast<13>(f.dv);
-    St[3][2] *= row_bcast<14>(f.dv);
-    St[3][3] *= row_bcast<15>(f.dv);
-    St[3] = mfma32(f.bk[3], uv, St[3]);
+    const f32x4 yv = scan_step(St, f);
     stage_y(par, yv);
   };
 
@@ -772,7 +398,7 @@ int64_t prep_waves_resident() {
                                               hipSuccess || cus <= 0)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>),
-                                                   64 * kPrepWaves, kPrepWaves * kPrepLdsPerWave) != hipSuccess ||
+                                                   64 * kPrepWaves, kPrepWaves * kPrepScratch) != hipSuccess ||
       per_cu <= 0)
     per_cu = 2;
   return (int64_t)cus * per_cu * kPrepWaves;
@@ -784,7 +410,7 @@ namespace {
 
 // One chunked pass: the prep (in the given input mode) and the scan, slab by slab.
 struct SplitJob {
-  PrepParams in;  // input pointers (and T, H); the rest is filled per slab
+  PrepIn in;  // input pointers (T and H are filled in from the call)
   int mode;
   const uint16_t* v;
   float* y;
@@ -825,7 +451,7 @@ hipError_t run_split(const SplitJob& j) {
   const void* prep_fn = j.mode == kPrepTmix ? reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepTmix>)
                                             : reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>);
   const void* scan_fn = reinterpret_cast<const void*>(&wkv7_scan_kernel);
-  const int prep_lds = kPrepWaves * kPrepLdsPerWave;
+  const int prep_lds = kPrepWaves * kPrepScratch;
   const int scan_lds = kScanLds;
   static const hipError_t a0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
@@ -839,10 +465,11 @@ hipError_t run_split(const SplitJob& j) {
   for (int64_t s = 0; s < nslab; ++s) {
     const int64_t c0 = s * slab;
     const int64_t ncs = (nch - c0 < slab) ? nch - c0 : slab;
-    PrepParams pp = j.in;
+    PrepParams pp{};
+    pp.in = j.in;
+    pp.in.T = (int32_t)j.T;
+    pp.in.H = (int32_t)j.H;
     pp.rec = rec;
-    pp.T = (int32_t)j.T;
-    pp.H = (int32_t)j.H;
     pp.c0 = (int32_t)c0;
     pp.nc = (int32_t)ncs;
     pp.items = (int32_t)(units * ncs);
@@ -900,7 +527,7 @@ __global__ __launch_bounds__(256) void tmix_ln_kernel(float* y, const float* ln_
 
 hipError_t launch_chunked_split(const WkvCall& c) {
   if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
-  PrepParams in{};
+  PrepIn in{};
   in.r = static_cast<const uint16_t*>(c.in[0]);
   in.w = static_cast<const uint16_t*>(c.in[1]);
   in.k = static_cast<const uint16_t*>(c.in[2]);
@@ -914,7 +541,7 @@ hipError_t launch_chunked_split(const WkvCall& c) {
 hipError_t launch_tmix_chunked(const TmixCall& c) {
   if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
   const TmixParams& t = c.p;
-  PrepParams in{};
+  PrepIn in{};
   in.r = static_cast<const uint16_t*>(t.r);
   in.w_raw = t.w_raw;
   in.k = static_cast<const uint16_t*>(t.k);
@@ -924,15 +551,15 @@ hipError_t launch_tmix_chunked(const TmixCall& c) {
   SplitJob j{in, kPrepTmix, static_cast<const uint16_t*>(t.v), t.out, t.s_in, t.s_out, c.B, t.T, c.H, c.stream};
   hipError_t e = run_split(j);
   if (e != hipSuccess) return e;
-  const int64_t rows = c.B * t.T * c.H;
-  float* out = t.out;
-  const float* lw = t.ln_w;
-  const float* lb = t.ln_b;
-  int64_t nrows = rows;
-  int32_t h32 = (int32_t)c.H;
-  void* args[] = {&out, &lw, &lb, &nrows, &h32};
+  return launch_tmix_ln(t.out, t.ln_w, t.ln_b, c.B * t.T * c.H, (int32_t)c.H, c.stream);
+}
+
+hipError_t launch_tmix_ln(float* out, const float* ln_w, const float* ln_b, int64_t rows, int32_t H,
+                          hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  void* args[] = {&out, &ln_w, &ln_b, &rows, &H};
   return hipLaunchKernel(reinterpret_cast<const void*>(&tmix_ln_kernel), dim3((uint32_t)((rows + 3) / 4)),
-                         dim3(256), args, 0, c.stream);
+                         dim3(256), args, 0, stream);
 }
 
 }  // namespace rwkv7

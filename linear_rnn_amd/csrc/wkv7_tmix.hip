@@ -25,6 +25,7 @@
 // and the single-token step run the same per-row arithmetic (only the number of
 // rows a wave holds differs), so T steps reproduce a prefill over T tokens bit
 // for bit.
+#include "rwkv7_wkv.h"
 #include "wkv7_device.hpp"
 #include "wkv7_internal.hpp"
 
@@ -258,7 +259,10 @@ hipError_t launch_cfg(const TmixCall& c) {
 }  // namespace
 
 hipError_t launch_tmix(const TmixCall& c) {
-  if (c.chunked && c.dtype == 1 && c.p.T > 1) return launch_tmix_chunked(c);
+  if (c.dtype == 1 && c.p.T > 1) {
+    if (c.algo == RWKV7_ALGO_CHUNKED_SPLIT) return launch_tmix_chunked(c);
+    if (c.algo == RWKV7_ALGO_CHUNKED) return launch_tmix_fused(c);
+  }
   // the single-token step: one token per block, four waves of 16 rows (bound by HBM);
   // a prefill: sixteen-token blocks, eight waves of 8 rows (two per SIMD, to hide the
   // per-token dependency chain)

@@ -217,13 +217,16 @@ def test_tmix_aliasing(L):
 
 
 def test_tmix_prefill_ex_algorithms(L):
-    """AUTO and SEQUENTIAL, or CHUNKED_SPLIT with bfloat16 inputs; everything else is refused before any launch."""
+    """AUTO and SEQUENTIAL, or CHUNKED / CHUNKED_SPLIT with bfloat16 inputs; everything else is refused
+    before any launch."""
     def xcall(algo, dtype=BF16, B=2):
         return L.rwkv7_tmix_prefill_ex(*(list(ptrs(11)) + [B, 3, 4, 64, dtype, algo, None]))
     assert xcall(wkv.RWKV7_ALGO_CHUNKED_SPLIT, dtype=F32) == E_ALGO
-    for algo in (wkv.RWKV7_ALGO_CHUNKED, 4, -1):
+    assert xcall(wkv.RWKV7_ALGO_CHUNKED, dtype=F32) == E_ALGO
+    for algo in (4, -1):
         assert xcall(algo) == E_ALGO, algo
-    for algo in (wkv.RWKV7_ALGO_AUTO, wkv.RWKV7_ALGO_SEQUENTIAL, wkv.RWKV7_ALGO_CHUNKED_SPLIT):
+    for algo in (wkv.RWKV7_ALGO_AUTO, wkv.RWKV7_ALGO_SEQUENTIAL, wkv.RWKV7_ALGO_CHUNKED,
+                 wkv.RWKV7_ALGO_CHUNKED_SPLIT):
         assert xcall(algo, B=0) == OK, algo
     assert xcall(wkv.RWKV7_ALGO_AUTO, dtype=7) == E_DTYPE
 

@@ -34,9 +34,12 @@ def run(torch, d, algo, state=True):
     return y.cpu().numpy(), s.cpu().numpy()
 
 
-# 13, 14 and 15 chunks straddle the scan loop's unroll of 14 (twice its 7-slot ring)
+# 13, 14 and 15 chunks straddle the split scan loop's unroll of 14 (twice its 7-slot ring); 9, 10, 11,
+# 20 and 21 chunks straddle one and two turns of the fused kernel's 10-slot ring (161 and 321 tokens
+# end in a one-token chunk)
 @pytest.mark.parametrize("B,T,H", [(1, 1, 1), (1, 15, 2), (2, 16, 3), (1, 17, 2), (2, 33, 3), (3, 100, 5),
-                                   (1, 208, 2), (1, 224, 2), (1, 240, 2), (2, 1000, 12)])
+                                   (1, 144, 2), (1, 160, 3), (1, 161, 2), (1, 208, 2), (1, 224, 2),
+                                   (1, 240, 2), (1, 320, 2), (2, 321, 3), (2, 1000, 12)])
 def test_ragged_vs_oracle(torch, CH, B, T, H):
     say("algo", CH, "chunked ragged", B, T, H)
     x = make_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=200 + T)

@@ -126,12 +126,18 @@ def test_decode_shape_sampled(torch):
         assert max(e) <= TOL_BF16, ((b, h), e)
 
 
-# ---- the chunked prefill of the fused operator (RWKV7_ALGO_CHUNKED_SPLIT, bfloat16 inputs)
+# ---- the chunked prefill of the fused operator (bfloat16 inputs): one kernel per head
+# (RWKV7_ALGO_CHUNKED) and split prep / scan kernels (RWKV7_ALGO_CHUNKED_SPLIT)
 
-CH = wkv.RWKV7_ALGO_CHUNKED_SPLIT
+CH_VARIANTS = {"fused": wkv.RWKV7_ALGO_CHUNKED, "split": wkv.RWKV7_ALGO_CHUNKED_SPLIT}
 
 
-def run_ch(torch, d, state=True, affine=True, algo=CH):
+@pytest.fixture(params=sorted(CH_VARIANTS), scope="module")
+def CH(request):
+    return CH_VARIANTS[request.param]
+
+
+def run_ch(torch, d, state=True, affine=True, algo=None):
     o, s = wkv.tmix(*(d[n] for n in NAMES), d["ln_w"] if affine else None, d["ln_b"] if affine else None,
                     d["state_in"] if state else None, algo=algo)
     torch.cuda.synchronize()
@@ -139,31 +145,31 @@ def run_ch(torch, d, state=True, affine=True, algo=CH):
 
 
 @pytest.mark.parametrize("B,T,H", [(1, 2, 1), (1, 17, 2), (2, 37, 3), (3, 100, 5), (1, 300, 12), (2, 1000, 4)])
-def test_chunked_vs_oracle(torch, B, T, H):
-    say("tmix chunked", B, T, H)
+def test_chunked_vs_oracle(torch, CH, B, T, H):
+    say("tmix chunked", CH, B, T, H)
     x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=B, T=T, H=H, seed=500 + T)
-    o, s = run_ch(torch, dev(torch, x))
+    o, s = run_ch(torch, dev(torch, x), algo=CH)
     orf, srf = ref(x)
     e = (rel(o, orf), rel(s, srf))
     say("tmix chunked errors", e)
     assert max(e) <= TOL_BF16, e
 
 
-def test_chunked_zero_state_null_affine_zero_key(torch):
+def test_chunked_zero_state_null_affine_zero_key(torch, CH):
     """state_in NULL, ln_w / ln_b NULL, and all-zero removal-key rows (a = b = 0) on the chunked path."""
-    say("tmix chunked, NULL state and affine, zero kk rows")
+    say("tmix chunked, NULL state and affine, zero kk rows", CH)
     x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=2, T=70, H=3, seed=41)
     x["kk"][1, 20:36] = 0
-    o, s = run_ch(torch, dev(torch, x), state=False, affine=False)
+    o, s = run_ch(torch, dev(torch, x), state=False, affine=False, algo=CH)
     orf, srf = ref(x, state=False, affine=False)
     assert np.all(np.isfinite(o))
     assert max(rel(o, orf), rel(s, srf)) <= TOL_BF16
 
 
-def test_chunked_state_in_place_and_sequential_agree(torch):
+def test_chunked_state_in_place_and_sequential_agree(torch, CH):
     """state_out == state_in on the chunked path; the chunked and the token-by-token prefill agree to the
     bfloat16 tolerance."""
-    say("tmix chunked in place vs sequential")
+    say("tmix chunked in place vs sequential", CH)
     x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=2, T=333, H=4, seed=43)
     d = dev(torch, x)
     st = d["state_in"].clone()
@@ -177,14 +183,14 @@ def test_chunked_state_in_place_and_sequential_agree(torch):
     assert max(rel(o_ch, orf), rel(s_ch, srf)) <= TOL_BF16
 
 
-def test_chunked_extreme_decays(torch):
+def test_chunked_extreme_decays(torch, CH):
     """w_raw = -inf (w = 1), 30 (w = 0, which the chunked path clamps to 2^-15) and ordinary values."""
-    say("tmix chunked extreme decays")
+    say("tmix chunked extreme decays", CH)
     x = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=1, T=90, H=2, seed=45, with_state=True)
     rng = np.random.default_rng(45)
     pick = rng.integers(0, 4, size=x["w_raw"].shape)
     x["w_raw"] = np.where(pick == 0, -np.inf, np.where(pick == 1, 30.0, x["w_raw"])).astype(np.float32)
-    o, s = run_ch(torch, dev(torch, x))
+    o, s = run_ch(torch, dev(torch, x), algo=CH)
     orf, srf = ref(x)
     assert max(rel(o, orf), rel(s, srf)) <= TOL_BF16
 
@@ -192,11 +198,12 @@ def test_chunked_extreme_decays(torch):
 def test_chunked_refuses_f32_and_unknown_algos(torch):
     x = make_tmix_inputs(CONFIGS["tiny-prefill-f32"], T=8, seed=2)
     d = dev(torch, x)
-    with pytest.raises(wkv.Rwkv7Error) as ei:
-        run_ch(torch, d)
-    assert ei.value.status == -7
+    for algo in CH_VARIANTS.values():
+        with pytest.raises(wkv.Rwkv7Error) as ei:
+            run_ch(torch, d, algo=algo)
+        assert ei.value.status == -7
     xb = make_tmix_inputs(CONFIGS["L12-D768-prefill"], B=1, T=8, H=1, seed=2)
-    for algo in (wkv.RWKV7_ALGO_CHUNKED, 9, -1):
+    for algo in (9, -1):
         with pytest.raises(wkv.Rwkv7Error) as ei:
             run_ch(torch, dev(torch, xb), algo=algo)
         assert ei.value.status == -7
