@@ -80,7 +80,8 @@ extern "C" {
 /* Prefill algorithm (rwkv7_wkv_prefill_ex). */
 #define RWKV7_ALGO_AUTO 0       /* library's choice (what rwkv7_wkv_prefill does) */
 #define RWKV7_ALGO_SEQUENTIAL 1 /* token-by-token recurrence, state resident in registers */
-#define RWKV7_ALGO_CHUNKED 2    /* chunked (WY / UT) form, one workgroup per head doing every stage */
+#define RWKV7_ALGO_CHUNKED 2    /* chunked (WY / UT) form, one workgroup per head doing every stage
+                                   (chunk records pass from its prep waves to its scan waves in LDS) */
 #define RWKV7_ALGO_CHUNKED_SPLIT 3 /* chunked form split into a chunk-parallel prep kernel and a
                                       per-head scan kernel (uses a cached device workspace) */
 
@@ -101,8 +102,18 @@ extern "C" {
  *   dtype             RWKV7_DTYPE_F32 or RWKV7_DTYPE_BF16
  *   stream            hipStream_t to launch on (NULL = null stream)
  *
- * The automatic choice uses the sequential algorithm for float32 inputs and the
- * split chunked algorithm (RWKV7_ALGO_CHUNKED_SPLIT) for bfloat16 inputs.
+ * Algorithm (what RWKV7_ALGO_AUTO picks; rwkv7_wkv_prefill_algo reports it):
+ *   float32 inputs                      RWKV7_ALGO_SEQUENTIAL (float32 throughout);
+ *   bfloat16, T * H * 64 >= 2^31        RWKV7_ALGO_SEQUENTIAL (outside the chunked domain);
+ *   bfloat16, B * H >= 7/16 of the      RWKV7_ALGO_CHUNKED (one workgroup per head);
+ *     current device's compute units
+ *   bfloat16, fewer heads               RWKV7_ALGO_CHUNKED_SPLIT (prep spread over the chip).
+ * The chunked algorithms carry the state in float32 but round intra-chunk
+ * operands, the state operand of a chunk's products included, to float16: the
+ * domain described under rwkv7_wkv_prefill_ex applies (magnitudes below 2^15,
+ * decays below 2^-15 treated as 2^-15), and results agree with the float32
+ * recurrence to about 1e-3 relative. Callers outside that domain use
+ * rwkv7_wkv_prefill_ex with RWKV7_ALGO_SEQUENTIAL.
  */
 int rwkv7_wkv_prefill(const void *r, const void *w, const void *k, const void *v, const void *a,
                       const void *b, const float *state_in, float *y, float *state_out, int64_t B,
@@ -167,14 +178,21 @@ int rwkv7_wkv_step_q(const void *r, const void *w, const void *k, const void *v,
  * Results agree with the sequential algorithm to about 1e-3 relative (max-norm
  * over a tensor) rather than bit for bit.
  *
+ * RWKV7_ALGO_CHUNKED uses no workspace: its chunk records stay in the
+ * compute unit's LDS.
+ *
  * Workspace of RWKV7_ALGO_CHUNKED_SPLIT (also the automatic choice for
- * bfloat16 inputs): the chunk records that pass from its first kernel to its
- * second live in a device buffer that the library allocates on the first call
- * that needs it and keeps for later calls, one buffer per (device, stream),
- * grown when a call needs more (at most about 256 MiB plus one state copy: a
- * longer sequence is processed in slabs of chunks that fit; the environment
- * variable RWKV7_SPLIT_SLAB_MB overrides the budget). Growing it synchronises
- * that stream; an allocation failure returns RWKV7_ERR_HIP before any launch.
+ * bfloat16 inputs with few heads): the chunk records that pass from its first
+ * kernel to its second live in a device buffer that the library allocates on
+ * the first call that needs it and keeps for later calls, one buffer per
+ * (device, stream), grown when a call needs more (at most about 256 MiB plus
+ * one state copy: a longer sequence is processed in slabs of chunks that fit;
+ * the environment variable RWKV7_SPLIT_SLAB_MB overrides the budget). A buffer
+ * that growth replaces stays allocated until the process ends, because a HIP
+ * graph captured earlier on that stream may still use it; growth at least
+ * doubles the buffer, so that retired memory is bounded by the live buffer's
+ * size. An allocation failure returns RWKV7_ERR_HIP before any launch, and so
+ * does a call that would grow the buffer while its stream is being captured.
  */
 int rwkv7_wkv_prefill_ex(const void *r, const void *w, const void *k, const void *v, const void *a,
                          const void *b, const float *state_in, float *y, float *state_out, int64_t B,
@@ -271,9 +289,9 @@ int rwkv7_tmix_step(const void *r, const float *w_raw, const void *k, const void
  * first kernel stores the state every 16 tokens, a second walks the sequence
  * backwards, rebuilding each 8-token stretch of states from its checkpoint.
  * The checkpoints (B*H*ceil(T/16) * 16 KiB) live in the per-(device, stream)
- * workspace described for rwkv7_wkv_prefill_ex, grown as needed (growing
- * synchronises the stream; an allocation failure returns RWKV7_ERR_HIP before
- * any launch). Arithmetic is float32 throughout (bfloat16 inputs widened
+ * workspace described for rwkv7_wkv_prefill_ex, grown as needed (an
+ * allocation failure, or growth during graph capture, returns RWKV7_ERR_HIP
+ * before any launch). Arithmetic is float32 throughout (bfloat16 inputs widened
  * exactly); results match the float64 derivatives to float32 rounding.
  */
 int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
@@ -318,11 +336,25 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  *
  * HIP graphs: a call can be captured in a graph on a stream once one call of at
  * least the same size has run on that stream (it creates the workspace and the
- * rocBLAS handle, which capture cannot); replays then launch the same kernels
- * on the same buffers. The same holds for every entry point of this header.
+ * rocBLAS handle, which capture cannot; a call that would have to grow the
+ * workspace during capture fails with RWKV7_ERR_HIP); replays then launch the
+ * same kernels on the same buffers, and remain valid after later, larger eager
+ * calls have grown the workspace (the buffer a graph holds is never freed). The
+ * same holds for every entry point of this header.
  */
 int rwkv7_stack_forward(const void *w_in, const void *w_out, const float *vecs, float *x, float *states, int64_t L,
                         int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * The algorithm rwkv7_wkv_prefill would run for a bfloat16 or float32 prefill of
+ * this shape on the current device (RWKV7_ALGO_SEQUENTIAL, RWKV7_ALGO_CHUNKED or
+ * RWKV7_ALGO_CHUNKED_SPLIT; the rule is stated at rwkv7_wkv_prefill), or
+ * RWKV7_ERR_DTYPE / RWKV7_ERR_SHAPE / RWKV7_ERR_HEAD_SIZE for arguments that
+ * rwkv7_wkv_prefill would refuse. Launches nothing and allocates nothing; it may
+ * query the current device's compute-unit count (256 is assumed if none can be
+ * queried).
+ */
+int rwkv7_wkv_prefill_algo(int64_t B, int64_t T, int64_t H, int64_t N, int dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rwkv7_wkv_strerror(int status);

@@ -84,7 +84,7 @@ int run(const void* r, const void* w, const void* k, const void* v, const void* 
   if (step) {
     e = rwkv7::launch_sequential(c, /*decode_shape=*/true);
   } else {
-    if (algo == RWKV7_ALGO_AUTO) algo = dtype == RWKV7_DTYPE_BF16 ? RWKV7_ALGO_CHUNKED_SPLIT : RWKV7_ALGO_SEQUENTIAL;
+    if (algo == RWKV7_ALGO_AUTO) algo = rwkv7::auto_prefill_algo(B, T, H, dtype);
     e = algo == RWKV7_ALGO_CHUNKED         ? rwkv7::launch_chunked(c)
         : algo == RWKV7_ALGO_CHUNKED_SPLIT ? rwkv7::launch_chunked_split(c)
                                            : rwkv7::launch_sequential(c, false);
@@ -311,6 +311,18 @@ int rwkv7_wkv_prefill_ex(const void* r, const void* w, const void* k, const void
                          const void* b, const float* state_in, float* y, float* state_out, int64_t B, int64_t T,
                          int64_t H, int64_t N, int dtype, int algo, void* stream) {
   return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_STATE_F32, algo, false, stream);
+}
+
+int rwkv7_wkv_prefill_algo(int64_t B, int64_t T, int64_t H, int64_t N, int dtype) {
+  if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
+  if (N != RWKV7_HEAD_SIZE) return RWKV7_ERR_HEAD_SIZE;
+  int64_t units = 0, tok_heads = 0, elems = 0;
+  if (__builtin_mul_overflow(B, H, &units) || units > (int64_t(1) << 26)) return RWKV7_ERR_SHAPE;
+  if (__builtin_mul_overflow(units, T, &tok_heads) || __builtin_mul_overflow(tok_heads, int64_t(64), &elems) ||
+      elems > (int64_t(1) << 58))
+    return RWKV7_ERR_SHAPE;
+  return rwkv7::auto_prefill_algo(B, T, H, dtype);
 }
 
 const char* rwkv7_wkv_strerror(int status) {

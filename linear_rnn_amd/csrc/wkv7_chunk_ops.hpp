@@ -25,8 +25,9 @@
 // The Gram factors pass through the decay at token 7 (Gq_t = e^{gamma_t - gamma_7}),
 // so no factor exceeds w_min^-8; e^{gamma_t} = Gq_t e^{gamma_7} (e^{gamma_7} >= 2^-120
 // is a normal float). The Grams are products of bfloat16 hi/lo halves (hi*hi + hi*lo +
-// lo*hi, about 2^-16 relative, with the float32 range) with float32 accumulation; T and
-// M_r are float32; A', R', G_u, G_y, B-, K-, the state operand and U are rounded once to
+// lo*hi, about 2^-16 relative, with the float32 range) with float32 accumulation (float32
+// 16x16x4 products measured slower: the prep then holds the matrix pipe that its SIMD's
+// scan wave needs); T and M_r are float32; A', R', G_u, G_y, B-, K-, the state operand and U are rounded once to
 // float16 as MFMA operands (float32 accumulation), so magnitudes must stay below 2^15.
 // The carried state is float32 throughout.
 //
@@ -43,12 +44,12 @@
 // One MFMA shape per dependent chain. Chains that mixed 16x16x32 and 16x16x16 f16
 // products gave wrong values on gfx950 in whichever product the register
 // allocation placed last; the same chains in one shape are exact. The wrappers
-// below therefore come in two families that take distinct operand types: Mma16
-// (16x16x16 f16, half4 operands, used only for the prep's transposes and its
-// 16-token products) and Mma32 (16x16x32, half8 / bf16x8 operands). Each chain in
-// this file accumulates through exactly one of them, so a chain that passes a
-// 16x16x16 result as the accumulator of a 16x16x32 product (or back) must convert
-// through an explicit f32x4 temporary that the code names as such.
+// below therefore come in three families that take distinct operand types: Mma16
+// (16x16x16 f16, half4 operands: the prep's transposes and 16-token products), MmaBF
+// (16x16x32 bf16, bf16x8 operands: the prep's Grams) and Mma32 (16x16x32 f16, half8
+// operands: the scan). Each chain in this file accumulates through exactly one of
+// them; a result of one family reaches another only as a converted operand or through
+// a vector-unit addition, never as another family's accumulator.
 #pragma once
 
 #include "wkv7_device.hpp"
@@ -77,11 +78,14 @@ struct Mma16 {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
 };
-// 16x16x32 family (the Grams in bfloat16, the scan in float16)
+// 16x16x32 f16 family (the scan)
 struct Mma32 {
   __device__ static __forceinline__ f32x4 mma(half8 a, half8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
+};
+// 16x16x32 bf16 family (the prep's Grams, as products of bfloat16 hi / lo halves)
+struct MmaBF {
   __device__ static __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -198,6 +202,69 @@ __device__ __forceinline__ void prep_load(const PrepIn& p, int64_t base, int nt,
   }
 }
 
+// Row-coalesced loading of r, a, b, k: lane l loads the 16-byte piece l % 8 (keys
+// 8 (l % 8) .. + 7) of token l / 8 + 8 h of each tensor, so the 16 lanes of a
+// quarter-wave read two whole 128-byte token rows instead of one 8-byte piece of
+// 16 rows. The pieces then pass through LDS (prep_rows_to_raw) into the token layout.
+// w is loaded in the key layout as by prep_load (whole rows already).
+struct PrepRows {
+  uint4 q[4][2];  // r, a, b, k; h = 0, 1
+};
+constexpr int kStageRow = 144;             // bytes per staged token row (128 + 16: 16-byte aligned, and rows
+                                           // 8 apart share banks, so the token-layout reads conflict 2-way)
+constexpr int kStageT = kC * kStageRow;    // one tensor: 2,304 bytes
+constexpr int kStageBytes = 4 * kStageT;   // 9,216 bytes
+static_assert(kStageBytes <= kRecD, "staged rows end before e^gamma_15 and the record's v");
+
+template <int MODE>
+__device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, int nt, PrepRows& rows, PrepRaw& x) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tstride = (uint32_t)p.H * kN;
+  x.nt = nt;
+  const uint16_t* src[4] = {p.r, p.a, p.b, p.k};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tok = min((lane >> 3) + 8 * h, nt - 1);
+    const uint32_t off = (uint32_t)(tok * tstride + 8 * (lane & 7)) * 2u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rows.q[q][h] = ld_off<uint4>(src[q] + base, off);
+  }
+#pragma unroll
+  for (int t = 0; t < kC; ++t) {
+    const int tt = min(t, nt - 1);
+    if constexpr (MODE == kPrepTmix)
+      x.wr[t] = __float_as_uint(ld_off<float>(p.w_raw + base, (uint32_t)(tt * tstride + lane) * 4u));
+    else
+      x.wr[t] = ld_off<uint16_t>(p.w + base, (uint32_t)(tt * tstride + lane) * 2u);
+  }
+}
+
+// Writes the loaded rows to stage (kStageBytes of this wave's LDS) and reads them back
+// in the token layout of PrepRaw.
+__device__ __forceinline__ void prep_rows_to_raw(const PrepRows& rows, unsigned char* stage, PrepRaw& x) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      st_off<uint4>(stage, (uint32_t)(q * kStageT + ((lane >> 3) + 8 * h) * kStageRow + 16 * (lane & 7)),
+                    rows.q[q][h]);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every piece is in LDS before other lanes read it
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const uint32_t off = (uint32_t)(li * kStageRow + 32 * kt + 8 * g);
+    x.rr[kt] = ld_off<uint2>(stage, 0 * kStageT + off);
+    x.ar[kt] = ld_off<uint2>(stage, 1 * kStageT + off);
+    x.br[kt] = ld_off<uint2>(stage, 2 * kStageT + off);
+    x.kr[kt] = ld_off<uint2>(stage, 3 * kStageT + off);
+  }
+  // every read has returned before the caller overwrites the stage
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
+}
+
 // The prep of one chunk from its raw inputs. fac: kPrepScratch bytes of this wave's
 // LDS. rec: the chunk's record (device memory or LDS); written as nine 1 KiB blocks,
 // 16 bytes per lane, plus e^{gamma_15}. rec may hold fac at its start (see above).
@@ -268,6 +335,7 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
   half4 Ahat[4];
   f32x4 Rhat[4];
   f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
+  bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
   // time-mix: 1 / max(|kk|, 1e-12) of this lane's token (its 64 channels are spread over
   // the four lanes li, li + 16, li + 32, li + 48)
   float inv = 1.f;
@@ -284,7 +352,6 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
     n2 += __shfl_xor(n2, 32);
     inv = 1.f / fmaxf(sqrtf(n2), 1e-12f);
   }
-  bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int col = 16 * kt + 4 * g;
@@ -305,8 +372,9 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
       }
       const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
       const float suf = el(g15, e) * f;                  // e^{gamma_15 - gamma_t}
+      // Gram operands: a and r scaled to token 7 from below, b and k from above
+      const float ag = av * el(gqm1, e), rg = rv * el(gq, e);
       const int q8 = 4 * (kt & 1) + e;
-      const float ag = av * el(gqm1, e), rg = rv * el(gq, e);  // Gram operands
       split_bf16(ag, ahH, ahL, q8);
       split_bf16(rg, rhH, rhL, q8);
       split_bf16(bv * f, bhH, bhL, q8);
@@ -320,18 +388,18 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
     const half4 KT = to_h4(Mma16::mma(kbar, eye, zero4()));
     st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT, KT));
     if (kt & 1) {
-      Lab = Mma32::mma(ahH, bhH, Lab);
-      Lak = Mma32::mma(ahH, khH, Lak);
-      Lrb = Mma32::mma(rhH, bhH, Lrb);
-      LrkT = Mma32::mma(khH, rhH, LrkT);
-      Lab = Mma32::mma(ahH, bhL, Lab);
-      Lak = Mma32::mma(ahH, khL, Lak);
-      Lrb = Mma32::mma(rhH, bhL, Lrb);
-      LrkT = Mma32::mma(khH, rhL, LrkT);
-      Lab = Mma32::mma(ahL, bhH, Lab);
-      Lak = Mma32::mma(ahL, khH, Lak);
-      Lrb = Mma32::mma(rhL, bhH, Lrb);
-      LrkT = Mma32::mma(khL, rhH, LrkT);
+      Lab = MmaBF::mma(ahH, bhH, Lab);
+      Lak = MmaBF::mma(ahH, khH, Lak);
+      Lrb = MmaBF::mma(rhH, bhH, Lrb);
+      LrkT = MmaBF::mma(khH, rhH, LrkT);
+      Lab = MmaBF::mma(ahH, bhL, Lab);
+      Lak = MmaBF::mma(ahH, khL, Lak);
+      Lrb = MmaBF::mma(rhH, bhL, Lrb);
+      LrkT = MmaBF::mma(khH, rhL, LrkT);
+      Lab = MmaBF::mma(ahL, bhH, Lab);
+      Lak = MmaBF::mma(ahL, khH, Lak);
+      Lrb = MmaBF::mma(rhL, bhH, Lrb);
+      LrkT = MmaBF::mma(khL, rhH, LrkT);
     }
   }
 #pragma unroll

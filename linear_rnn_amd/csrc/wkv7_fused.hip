@@ -20,8 +20,10 @@
 // every consumed[w] > c - kRing. The smallest unfinished chunk never waits on a later
 // one, so the hand-off cannot deadlock; every wait is also bounded (kSpinMax polls),
 // so a wave never spins forever even if the protocol were broken.
+#include <atomic>
 #include <cstdint>
 
+#include "rwkv7_wkv.h"
 #include "wkv7_chunk_ops.hpp"
 #include "wkv7_internal.hpp"
 
@@ -38,7 +40,12 @@ constexpr int kVRow = kN + 4;                // v row in the slot, bfloat16 elem
                                              // hit 32 distinct banks)
 constexpr int kVSlot = kC * kVRow * 2;       // 2,176 bytes
 constexpr int kSlot = kRecBytes + kVSlot;    // 11,648 bytes
-constexpr int kCtrlOff = kRing * kSlot;      // ready[kRing], then consumed[kScanW]
+// y of a scan wave's chunk passes through an LDS tile of its own, [token][16 values] float32
+// with 80-byte rows, so that its stores cover 4 tokens per quarter-wave instead of 16
+constexpr int kYRow = 80;
+constexpr int kYTile = kC * kYRow;           // 1,280 bytes per scan wave
+constexpr int kYOff = kRing * kSlot;
+constexpr int kCtrlOff = kYOff + kScanW * kYTile;  // ready[kRing], then consumed[kScanW]
 constexpr int kLds = kCtrlOff + 4 * (kRing + kScanW);
 constexpr int kThreads = 64 * (kScanW + kPrepW);
 constexpr int kSpinMax = 1 << 20;            // polls of 100-200 cycles: well over any legitimate wait
@@ -111,7 +118,8 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
       const int nt = min(kC, T - t0);
       const int64_t base = seq_base + (int64_t)t0 * tstride;
       PrepRaw x;
-      prep_load<MODE>(p.in, base, nt, x);
+      PrepRows rows;
+      prep_load_rows<MODE>(p.in, base, nt, rows, x);
       // v of the chunk for the scan: lane l holds token l / 8 (+ 8) columns 8 (l % 8) .. + 7;
       // tokens past the end repeat the last one (their record coefficients are zero)
       uint4 vq[2];
@@ -121,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
         vq[h2] = ld_off<uint4>(p.v + base, (uint32_t)(tv * tstride + 8 * (lane & 7)) * 2u);
       }
       wait_all_at_least(consumed, c - kRing + 1);  // the slot's previous chunk has been read
+      prep_rows_to_raw(rows, rec, x);              // the slot's start stages the rows
       prep_compute<MODE>(x, reinterpret_cast<float*>(rec), rec);
       uint16_t* vs = reinterpret_cast<uint16_t*>(rec + kRecBytes);
 #pragma unroll
@@ -149,7 +158,9 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
-  float* ybase = p.y + seq_base + 16 * w + 4 * g;
+  // stores: lane l writes token l / 4 of the chunk, values 16 w + 4 (l % 4) .. + 3
+  float* ybase = p.y + seq_base + 16 * w + 4 * (lane & 3);
+  unsigned char* ytile = ring + kYOff + w * kYTile;
   auto slot_of = [&](int c) { return ring + (c % kRing) * kSlot; };
   auto read = [&](int c, Frag& f) {
     const unsigned char* s = slot_of(c);
@@ -168,8 +179,15 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
     wait_at_least(&ready[cn % kRing], cn);
     read(cn, nxt);
     const f32x4 yv = scan_step(St, cur);
-    const int t = c * kC + li;
-    if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    // y through the wave's tile: written as lane (token li, values 4g..), read as lane
+    // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before the
+    // previous post (its wait covers every LDS access of this wave).
+    st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    const float4 yq = ld_off<float4>(ytile, (uint32_t)((lane >> 2) * kYRow + 16 * (lane & 3)));
+    const int t = c * kC + (lane >> 2);
+    if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
     post(&consumed[w], cn + 1);  // every fragment up to chunk cn is in registers
     ++c;
     return c < nc;
@@ -197,7 +215,23 @@ hipError_t launch_fused(const FusedParams& fp, int64_t units, hipStream_t stream
 // Offsets inside a sequence are 32-bit element counts (T * H * 64 below 2^31).
 bool fused_domain(int64_t T, int64_t H) { return T * H * kN < (int64_t(1) << 31); }
 
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+int auto_prefill_algo(int64_t B, int64_t T, int64_t H, int dtype) {
+  if (dtype != RWKV7_DTYPE_BF16 || !fused_domain(T, H)) return RWKV7_ALGO_SEQUENTIAL;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  if (cus <= 0) cus = 256;
+  return B * H * 16 >= (int64_t)cus * 7 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_CHUNKED_SPLIT;
+}
 
 hipError_t launch_chunked(const WkvCall& c) {
   // bfloat16 inputs only: float32 inputs keep float32 accuracy on the sequential kernel

@@ -18,6 +18,17 @@ struct WkvCall {
   hipStream_t stream;
 };
 
+// The prefill algorithm that RWKV7_ALGO_AUTO runs (an RWKV7_ALGO_* value):
+//   float32 inputs                           sequential (their 1e-5 bar needs float32 operands)
+//   bfloat16, T * H * 64 >= 2^31             sequential (the chunked kernels use 32-bit offsets
+//                                            inside a sequence; the sequential one does not)
+//   bfloat16, B * H >= 7/16 of the CU count  the one-kernel chunked prefill (a workgroup per head
+//                                            keeps most compute units busy)
+//   bfloat16, fewer heads                    the split chunked prefill (its prep kernel spreads
+//                                            the chunks of few heads over the whole chip)
+// The CU count comes from the current device (256 if it cannot be queried).
+int auto_prefill_algo(int64_t B, int64_t T, int64_t H, int dtype);
+
 // Token-by-token recurrence with the state resident in registers. Also the
 // single-token step (T == 1), the only shape that takes a 16-bit stored state.
 // Returns the launch status.
@@ -102,7 +113,9 @@ hipError_t launch_stack(const StackCall& c);
 
 // Device memory cached per (device, stream), shared by the launchers that need
 // scratch: calls on one stream run in order, so they can share it. Grown on
-// demand (synchronising the stream first), never shrunk.
+// demand (at least doubling); a replaced buffer stays allocated until the process
+// ends, since a HIP graph captured earlier may still use it. Growing while the
+// stream is being captured returns hipErrorStreamCaptureUnsupported.
 // Two independent buffers per (device, stream): the chunked kernels' records use
 // their own, so a caller holding the general one (the layer stack) can run them.
 constexpr int kWorkspaceGeneral = 0, kWorkspaceChunks = 1;

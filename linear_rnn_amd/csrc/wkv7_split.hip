@@ -64,6 +64,7 @@
 #include <tuple>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "wkv7_chunk_ops.hpp"
 #include "wkv7_internal.hpp"
@@ -333,15 +334,19 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
 // ============================================================================ host side
 
 // Device workspace (records of the chunked split prefill, checkpoints of the
-// backward) cached per (device, stream):
-// calls on one stream run in order, so they can share it; calls on different
-// streams get different buffers. Grown on demand, never shrunk.
+// backward, the layer stack's intermediates) cached per (device, stream): calls on
+// one stream run in order, so they can share it; calls on different streams get
+// different buffers. A buffer that a larger call replaces is retired, not freed: a
+// HIP graph captured earlier on that stream may still hold its address, so it stays
+// allocated until the process ends. Growth is at least geometric (x2), so retired
+// buffers add at most the size of the live one.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::tuple<int, uintptr_t, int>, Workspace> g_ws;
+std::vector<void*> g_ws_retired;  // never freed (see above)
 
 
 // Record-buffer budget per slab: the scan of a slab reads what its prep wrote
@@ -367,21 +372,19 @@ hipError_t device_workspace(hipStream_t stream, size_t bytes, void** out, int sl
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace& ws = g_ws[std::make_tuple(dev, reinterpret_cast<uintptr_t>(stream), slot)];
   if (ws.bytes < bytes) {
-    if (ws.ptr) {
-      // work already queued on this stream may still use the old buffer
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return e;
-      e = hipFree(ws.ptr);
-      if (e != hipSuccess) return e;
-      ws.ptr = nullptr;
-      ws.bytes = 0;
-    }
-    e = hipMalloc(&ws.ptr, bytes);
-    if (e != hipSuccess) {
-      ws.ptr = nullptr;
-      return e;
-    }
-    ws.bytes = bytes;
+    // growing allocates, which a stream under graph capture cannot record: such a call
+    // must be preceded by an eager call of at least its size on the same stream
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    const size_t grow = ws.bytes > bytes / 2 ? 2 * ws.bytes : bytes;
+    void* p = nullptr;
+    e = hipMalloc(&p, grow);
+    if (e != hipSuccess) return e;
+    if (ws.ptr) g_ws_retired.push_back(ws.ptr);
+    ws.ptr = p;
+    ws.bytes = grow;
   }
   *out = ws.ptr;
   return hipSuccess;

@@ -193,7 +193,7 @@ hipError_t launch_stack(const StackCall& c) {
     TmixCall tc{{in[0], w_raw, in[1], in[2], in[3], in[4], vecs + 3 * D, vecs + 4 * D, state, o, state, c.T,
                  (int32_t)c.H},
                 c.B, c.H, c.dtype, c.stream};
-    tc.algo = bf16 && c.T >= kChunkedPromptMin ? RWKV7_ALGO_CHUNKED_SPLIT : RWKV7_ALGO_SEQUENTIAL;
+    tc.algo = bf16 && c.T >= kChunkedPromptMin ? auto_prefill_algo(c.B, c.T, c.H, c.dtype) : RWKV7_ALGO_SEQUENTIAL;
     e = launch_tmix(tc);
     if (e != hipSuccess) return e;
     const void* oin = o;

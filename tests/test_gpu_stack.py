@@ -132,3 +132,44 @@ def test_step_in_a_hip_graph(torch):
         wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], tmp.copy_(x), s_warm)
         torch.cuda.synchronize()
     assert torch.equal(s_buf, s_ref)
+
+
+def test_graph_survives_workspace_growth(torch):
+    """A step captured in a graph keeps working after a larger eager call on the same stream has grown
+    the per-stream workspace: the buffer the graph holds is retired, not freed."""
+    say("stack step graph, then a larger eager prompt on the capture stream, then replays")
+    z = make_stack_inputs(2, 4, 1, 2, "bf16", seed=23)
+    d = dev(torch, z)
+    xs = [torch.randn((4, 1, 128), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(i))
+          for i in range(3)]
+    s_ref = d["states"].clone()
+    outs_ref = []
+    for x in xs:
+        xx = x.clone()
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], xx, s_ref)
+        outs_ref.append(xx)
+    torch.cuda.synchronize()
+    x_buf = torch.zeros((4, 1, 128), dtype=torch.float32, device="cuda")
+    s_buf = d["states"].clone()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], x_buf.clone(), d["states"].clone())
+        st.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], x_buf, s_buf)
+        # a 300-token prompt (chunked operator, far larger intermediates) on the capture stream
+        zp = make_stack_inputs(2, 4, 300, 2, "bf16", seed=24, with_state=False)
+        xp = torch.from_numpy(zp["x"]).cuda()
+        sp = torch.zeros_like(d["states"])
+        wkv.rwkv7_stack_forward(d["w_in"], d["w_out"], d["vecs"], xp, sp)
+        st.synchronize()
+    torch.cuda.synchronize()
+    assert torch.isfinite(xp).all()
+    s_buf.copy_(d["states"])
+    for i, x in enumerate(xs):
+        x_buf.copy_(x)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x_buf, outs_ref[i]), i
+    assert torch.equal(s_buf, s_ref)
