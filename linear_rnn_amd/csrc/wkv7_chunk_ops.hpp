@@ -151,12 +151,22 @@ constexpr int kPrepScratch = kFacBytes > kTmOffBytes + 2 * 16 * 16 * 2 ? kFacByt
 // are written only after T and M_r have been read into registers.
 static_assert(kPrepScratch <= kRecBK * 1024, "prep scratch overlaps the B-/K- blocks");
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 // x = hi + lo with both halves bfloat16 (round to nearest even): 16 significant bits and
 // the float32 exponent range, which the Gram operands need (factors up to w_min^-8).
-__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int i) {
-  const __bf16 h = (__bf16)x;
-  hi[i] = h;
-  lo[i] = (__bf16)(x - (float)h);
+// Two values at a time (elements i, i + 1 of the operands): one packed conversion for
+// both high halves, the exact widening of each (a shift, a mask), the two remainders,
+// one packed conversion for both low halves.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, bf16x8& hi, bf16x8& lo, int i) {
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const f32x2 r{x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u)};
+  const bf16x2 l = __builtin_convertvector(r, bf16x2);
+  hi[i] = h[0];
+  hi[i + 1] = h[1];
+  lo[i] = l[0];
+  lo[i + 1] = l[1];
 }
 // An ordering point for the values in x and for memory: the compiler computes x
 // before it and issues no later memory access ahead of it.
@@ -216,11 +226,10 @@ constexpr int kStageT = kC * kStageRow;    // one tensor: 2,304 bytes
 constexpr int kStageBytes = 4 * kStageT;   // 9,216 bytes
 static_assert(kStageBytes <= kRecD, "staged rows end before e^gamma_15 and the record's v");
 
-template <int MODE>
-__device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, int nt, PrepRows& rows, PrepRaw& x) {
+// r, a, b, k rows of chunk (base, nt)
+__device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, int nt, PrepRows& rows) {
   const int lane = threadIdx.x & 63;
   const uint32_t tstride = (uint32_t)p.H * kN;
-  x.nt = nt;
   const uint16_t* src[4] = {p.r, p.a, p.b, p.k};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -229,6 +238,13 @@ __device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, in
 #pragma unroll
     for (int q = 0; q < 4; ++q) rows.q[q][h] = ld_off<uint4>(src[q] + base, off);
   }
+}
+// w of chunk (base, nt) in the key layout
+template <int MODE>
+__device__ __forceinline__ void prep_load_w(const PrepIn& p, int64_t base, int nt, PrepRaw& x) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tstride = (uint32_t)p.H * kN;
+  x.nt = nt;
 #pragma unroll
   for (int t = 0; t < kC; ++t) {
     const int tt = min(t, nt - 1);
@@ -265,11 +281,24 @@ __device__ __forceinline__ void prep_rows_to_raw(const PrepRows& rows, unsigned 
   asm volatile("" ::: "memory");
 }
 
-// The prep of one chunk from its raw inputs. fac: kPrepScratch bytes of this wave's
-// LDS. rec: the chunk's record (device memory or LDS); written as nine 1 KiB blocks,
-// 16 bytes per lane, plus e^{gamma_15}. rec may hold fac at its start (see above).
+// What the first phase of a chunk's prep hands to the second: the four Grams in the D
+// layout, A^ (float16) and R^ (float32) in the token layout, and the identity operand.
+struct PrepMid {
+  f32x4 Lab, Lak, Lrb, LrkT;
+  half4 Ahat[4];
+  f32x4 Rhat[4];
+  half4 eye;
+};
+
+// The prep of one chunk from its raw inputs, in two phases (prep_grams, then
+// prep_finish; prep_compute runs both), so that a caller can issue the loads of its
+// next chunk in between. fac: kPrepScratch bytes of this wave's LDS. rec: the chunk's
+// record (device memory or LDS); written as nine 1 KiB blocks, 16 bytes per lane, plus
+// e^{gamma_15}. rec may hold fac at its start (see above).
+//
+// Phase 1: decay factors, operands, the four Grams; B-, K- and e^{gamma_15} stored.
 template <int MODE>
-__device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned char* rec) {
+__device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char* rec, PrepMid& m) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
   const int nt = x.nt;
@@ -283,7 +312,7 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
       w = expf(-expf(__uint_as_float(x.wr[t])));
     else
       w = bfw(x.wr[t]);
-    wc[t] = w < kWMin ? kWMin : w;  // clamp (a NaN passes through)
+    wc[t] = fmaxf(w, kWMin);  // clamp (a NaN decay becomes w_min)
   }
   // The last chunk of a sequence may run past its end: its tokens t >= nt become
   // identity tokens (w = 1, r = k = a = b = 0). The branch is the same for the whole wave.
@@ -328,13 +357,17 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
   // two key blocks per product: K index 8g + 4(kt % 2) + e. The Grams land in the D layout:
   // lane (s = li, g) holds t = 4g + e; L_rk is formed transposed (operands swapped).
   // Identity as a B operand: B[k = 4g+e][n = li] = (4g + e == li).
-  half4 eye;
+  half4& eye = m.eye;
 #pragma unroll
   for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
   const uint32_t lo = (uint32_t)lane * 16u;  // record blocks: 16 bytes per lane
-  half4 Ahat[4];
-  f32x4 Rhat[4];
-  f32x4 Lab = zero4(), Lak = zero4(), Lrb = zero4(), LrkT = zero4();
+  half4 (&Ahat)[4] = m.Ahat;
+  f32x4 (&Rhat)[4] = m.Rhat;
+  f32x4& Lab = m.Lab;
+  f32x4& Lak = m.Lak;
+  f32x4& Lrb = m.Lrb;
+  f32x4& LrkT = m.LrkT;
+  Lab = Lak = Lrb = LrkT = zero4();
   bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
   // time-mix: 1 / max(|kk|, 1e-12) of this lane's token (its 64 channels are spread over
   // the four lanes li, li + 16, li + 32, li + 48)
@@ -361,6 +394,7 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
     const float4 e7 = lds4(&fac[kRowE7 * kFacRow + col]);    // e^{gamma_7}
     const uint2 ra = x.ar[kt], rv2 = x.rr[kt], rb = x.br[kt], rk = x.kr[kt];
     half4 bbar, kbar;
+    float ag[4], rg[4], bg[4], kg[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float av = bf4(ra, e), bv = bf4(rb, e);
@@ -371,18 +405,23 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
         bv = kh1 * bv;
       }
       const float f = __builtin_amdgcn_rcpf(el(gq, e));  // e^{gamma_7 - gamma_t}
-      const float suf = el(g15, e) * f;                  // e^{gamma_15 - gamma_t}
       // Gram operands: a and r scaled to token 7 from below, b and k from above
-      const float ag = av * el(gqm1, e), rg = rv * el(gq, e);
+      ag[e] = av * el(gqm1, e);
+      rg[e] = rv * el(gq, e);
+      bg[e] = bv * f;
+      kg[e] = kv * f;
+      Ahat[kt][e] = (_Float16)(ag[e] * el(e7, e));  // a e^{gamma_{t-1}}
+      Rhat[kt][e] = rg[e] * el(e7, e);              // r e^{gamma_t}
+      bbar[e] = (_Float16)(bg[e] * el(g15, e));     // b e^{gamma_15 - gamma_t}
+      kbar[e] = (_Float16)(kg[e] * el(g15, e));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
       const int q8 = 4 * (kt & 1) + e;
-      split_bf16(ag, ahH, ahL, q8);
-      split_bf16(rg, rhH, rhL, q8);
-      split_bf16(bv * f, bhH, bhL, q8);
-      split_bf16(kv * f, khH, khL, q8);
-      Ahat[kt][e] = (_Float16)(ag * el(e7, e));  // a e^{gamma_{t-1}}
-      Rhat[kt][e] = rg * el(e7, e);              // r e^{gamma_t}
-      bbar[e] = (_Float16)(bv * suf);
-      kbar[e] = (_Float16)(kv * suf);
+      split_bf16x2(ag[e], ag[e + 1], ahH, ahL, q8);
+      split_bf16x2(rg[e], rg[e + 1], rhH, rhL, q8);
+      split_bf16x2(bg[e], bg[e + 1], bhH, bhL, q8);
+      split_bf16x2(kg[e], kg[e + 1], khH, khL, q8);
     }
     const half4 BT = to_h4(Mma16::mma(bbar, eye, zero4()));  // lane (j = li, g): B-[4g+e][16kt + li]
     const half4 KT = to_h4(Mma16::mma(kbar, eye, zero4()));
@@ -410,6 +449,15 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
     Lrb[e] = li <= t ? Lrb[e] : 0.f;    // lower with the diagonal
     LrkT[e] = t <= li ? LrkT[e] : 0.f;  // element (s = 4g+e, t = li) of L_rk^T
   }
+}
+
+// Phase 2: T, M_r and the products A', R', G_u, G_y, stored.
+__device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsigned char* rec) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const uint32_t lo = (uint32_t)lane * 16u;
+  const half4 eye = m.eye;
+  const f32x4 Lab = m.Lab, Lak = m.Lak, Lrb = m.Lrb, LrkT = m.LrkT;
 
   // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
   // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
@@ -474,9 +522,9 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kt = 2 * kp + u;
-      const half4 AT = to_h4(Mma16::mma(Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
-      ApT[u] = to_h4(Mma16::mma(AT, tB, zero4()));                 // lane (t = li, g): A'[t][16kt + 4g + e]
-      RpT[u] = to_h4(Mma16::mma(AT, mB, Rhat[kt]));                // R'[t][16kt + 4g + e]
+      const half4 AT = to_h4(Mma16::mma(m.Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
+      ApT[u] = to_h4(Mma16::mma(AT, tB, zero4()));                   // lane (t = li, g): A'[t][16kt + 4g + e]
+      RpT[u] = to_h4(Mma16::mma(AT, mB, m.Rhat[kt]));                // R'[t][16kt + 4g + e]
     }
     st_off<half8>(rec, (kRecA0 + kp) * 1024 + lo, cat8(ApT[0], ApT[1]));
     st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
@@ -485,6 +533,13 @@ __device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned ch
   const half4 GuT = to_h4(Mma16::mma(LakH, tB, zero4()));     // lane (t = li, g): G_u[t][4g + e]
   const half4 GyT = to_h4(Mma16::mma(LakH, mB, zero4()) + LrkT);  // G_y[t][4g + e]
   st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
+}
+
+template <int MODE>
+__device__ __forceinline__ void prep_compute(PrepRaw& x, float* fac, unsigned char* rec) {
+  PrepMid m;
+  prep_grams<MODE>(x, fac, rec, m);
+  prep_finish(m, fac, rec);
 }
 
 // ============================================================================ scan
@@ -497,15 +552,20 @@ struct Frag {
   uint32_t v[4];  // V[t = 4g + e][i = the wave's row li], raw bfloat16 bits (widened when used)
 };
 
-// Reads a chunk's fragments from its record in LDS. vrow: the record's v for this
-// wave, [token][vcols] bfloat16, at this wave's first value column.
-__device__ __forceinline__ void read_frag(const unsigned char* slot, const uint16_t* vrow, int vcols, Frag& f) {
+// Reads v of a chunk from LDS into f.v. vrow: [token][vcols] bfloat16, at this wave's
+// first value column.
+__device__ __forceinline__ void read_v(const uint16_t* vrow, int vcols, Frag& f) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.v[e] = vrow[(4 * g + e) * vcols + li];
+}
+// Reads a chunk's record fragments (not v) from its record in LDS.
+__device__ __forceinline__ void read_frag(const unsigned char* slot, Frag& f) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
   const uint32_t lo = (uint32_t)lane * 16u;
   // in the order of use (the next chunk's first products take v and G)
-#pragma unroll
-  for (int e = 0; e < 4; ++e) f.v[e] = vrow[(4 * g + e) * vcols + li];
   f.gl = *reinterpret_cast<const half8*>(slot + kRecG * 1024 + lo);
   f.a0 = *reinterpret_cast<const half8*>(slot + kRecA0 * 1024 + lo);
   f.r0 = *reinterpret_cast<const half8*>(slot + kRecR0 * 1024 + lo);

@@ -10,7 +10,7 @@
 //               store per lane (RWKV-7 G0 7.2B notes, lshu.cn/news/198401, section
 //               7.1: y is read out with r after the update).
 //   waves 4-11  prep: wave p takes chunks p, p + 8, p + 16, ...; it loads the chunk's
-//               r, w, k, a, b (and v for the scan), waits for its ring slot to be free,
+//               r, w, k, a, b, waits for its ring slot to be free,
 //               forms the record in the slot (its factor and solve scratch lives at the
 //               slot's start) and marks the slot ready.
 // Hand-off through LDS words, no workgroup barrier after the first: ready[slot] holds
@@ -35,11 +35,7 @@ using namespace chunk;
 constexpr int kScanW = 4;                    // scan waves (16 value rows each)
 constexpr int kPrepW = 8;                    // prep waves (one chunk each at a time)
 constexpr int kRing = 10;                    // record slots
-constexpr int kVRow = kN + 4;                // v row in the slot, bfloat16 elements (136 bytes: rows
-                                             // 4 apart start 8 banks apart, so a scan wave's v reads
-                                             // hit 32 distinct banks)
-constexpr int kVSlot = kC * kVRow * 2;       // 2,176 bytes
-constexpr int kSlot = kRecBytes + kVSlot;    // 11,648 bytes
+constexpr int kSlot = kRecBytes;             // 9,472 bytes (a scan wave loads its v itself)
 // y of a scan wave's chunk passes through an LDS tile of its own, [token][16 values] float32
 // with 80-byte rows, so that its stores cover 4 tokens per quarter-wave instead of 16
 constexpr int kYRow = 80;
@@ -111,34 +107,39 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
 
   if (wave >= kScanW) {
     // ---------------------------------------------------------------- prep waves
-    for (int c = wave - kScanW; c < nc; c += kPrepW) {
+    // The wave's chunks are c0, c0 + kPrepW, ... Two sets of row registers alternate: the
+    // r, a, b, k rows of the next chunk are loaded between the two phases of the current
+    // chunk's prep, so their latency passes during its solve and products and the next
+    // slot wait (w and v, a fifth of the bytes, are loaded when the chunk starts). Past the
+    // wave's last chunk the loads repeat its last chunk (unconditional, no branch).
+    const int c0 = wave - kScanW;
+    if (c0 >= nc) return;
+    const int last = c0 + (nc - 1 - c0) / kPrepW * kPrepW;  // this wave's last chunk
+    auto nt_of = [&](int c) { return min(kC, T - c * kC); };
+    auto base_of = [&](int c) { return seq_base + (int64_t)c * kC * tstride; };
+    // one chunk; returns false after the wave's last chunk
+    auto item = [&](int& c, PrepRows& cur, PrepRows& nxt) {
       const int slot = c % kRing;
       unsigned char* rec = ring + slot * kSlot;
-      const int t0 = c * kC;
-      const int nt = min(kC, T - t0);
-      const int64_t base = seq_base + (int64_t)t0 * tstride;
+      const int nt = nt_of(c);
+      const int64_t base = base_of(c);
       PrepRaw x;
-      PrepRows rows;
-      prep_load_rows<MODE>(p.in, base, nt, rows, x);
-      // v of the chunk for the scan: lane l holds token l / 8 (+ 8) columns 8 (l % 8) .. + 7;
-      // tokens past the end repeat the last one (their record coefficients are zero)
-      uint4 vq[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int tv = min((lane >> 3) + 8 * h2, nt - 1);
-        vq[h2] = ld_off<uint4>(p.v + base, (uint32_t)(tv * tstride + 8 * (lane & 7)) * 2u);
-      }
+      prep_load_w<MODE>(p.in, base, nt, x);
       wait_all_at_least(consumed, c - kRing + 1);  // the slot's previous chunk has been read
-      prep_rows_to_raw(rows, rec, x);              // the slot's start stages the rows
-      prep_compute<MODE>(x, reinterpret_cast<float*>(rec), rec);
-      uint16_t* vs = reinterpret_cast<uint16_t*>(rec + kRecBytes);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        uint2* d = reinterpret_cast<uint2*>(vs + ((lane >> 3) + 8 * h2) * kVRow + 8 * (lane & 7));
-        d[0] = make_uint2(vq[h2].x, vq[h2].y);
-        d[1] = make_uint2(vq[h2].z, vq[h2].w);
-      }
+      prep_rows_to_raw(cur, rec, x);               // the slot's start stages the rows
+      PrepMid m;
+      prep_grams<MODE>(x, reinterpret_cast<float*>(rec), rec, m);
+      const int cn = min(c + kPrepW, last);
+      prep_load_rows(p.in, base_of(cn), nt_of(cn), nxt);
+      prep_finish(m, reinterpret_cast<float*>(rec), rec);
       post(&ready[slot], c);
+      c += kPrepW;
+      return c < nc;
+    };
+    PrepRows ra, rb;
+    prep_load_rows(p.in, base_of(c0), nt_of(c0), ra);
+    int c = c0;
+    while (item(c, ra, rb) && item(c, rb, ra)) {
     }
     return;
   }
@@ -162,23 +163,36 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
   float* ybase = p.y + seq_base + 16 * w + 4 * (lane & 3);
   unsigned char* ytile = ring + kYOff + w * kYTile;
   auto slot_of = [&](int c) { return ring + (c % kRing) * kSlot; };
-  auto read = [&](int c, Frag& f) {
-    const unsigned char* s = slot_of(c);
-    read_frag(s, reinterpret_cast<const uint16_t*>(s + kRecBytes) + 16 * w, kVRow, f);
+  // v of chunk c for this wave: V[t = 4g + e][i = 16 w + li], raw bfloat16 bits (a
+  // quarter-wave reads 32 contiguous bytes of one token row); tokens past the end read
+  // the last token (their record coefficients are zero)
+  const uint16_t* vbase = p.v + seq_base + 16 * w + li;
+  auto load_v = [&](int c, uint32_t (&vr)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = min(c * kC + 4 * g + e, T - 1);
+      vr[e] = vbase[(int64_t)t * tstride];
+    }
   };
   Frag fa, fb;
+  uint32_t va[4], vb[4];  // v two chunks ahead: the set of chunk c is reloaded with chunk c + 2
+  load_v(0, va);
+  load_v(min(1, nc - 1), vb);
   wait_at_least(&ready[0], 0);
-  read(0, fa);
+  read_frag(slot_of(0), fa);
   int c = 0;
   // One chunk: the next chunk's fragments are read (its slot waited for) before this
-  // chunk's products are issued. Past the last chunk the read repeats the last chunk's
-  // slot, so the reads are unconditional (a read inside a branch would make the
-  // compiler wait for it at the join). Returns false after the last chunk.
-  auto body = [&](Frag& cur, Frag& nxt) {
+  // chunk's products are issued. Past the last chunk the reads repeat the last chunk, so
+  // they are unconditional (a read inside a branch would make the compiler wait for it at
+  // the join). Returns false after the last chunk.
+  auto body = [&](Frag& cur, Frag& nxt, uint32_t (&vc)[4]) {
     const int cn = min(c + 1, nc - 1);
     wait_at_least(&ready[cn % kRing], cn);
-    read(cn, nxt);
+    read_frag(slot_of(cn), nxt);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cur.v[e] = vc[e];
     const f32x4 yv = scan_step(St, cur);
+    load_v(min(c + 2, nc - 1), vc);
     // y through the wave's tile: written as lane (token li, values 4g..), read as lane
     // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before the
     // previous post (its wait covers every LDS access of this wave).
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
     ++c;
     return c < nc;
   };
-  while (body(fa, fb) && body(fb, fa)) {
+  while (body(fa, fb, va) && body(fb, fa, vb)) {
   }
   if (p.s_out) {
 #pragma unroll

@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   // address a fixed offset from the lane's base.
   auto read = [&](auto slot_index, Frag& f) {
     const unsigned char* slot = ring + decltype(slot_index)::value * kSlotBytes;
-    read_frag(slot, reinterpret_cast<const uint16_t*>(slot + kRecBytes) + 16 * wave, kVCols, f);
+    read_v(reinterpret_cast<const uint16_t*>(slot + kRecBytes) + 16 * wave, kVCols, f);
+    read_frag(slot, f);
   };
   // y of chunk c goes through LDS: each compute wave stages its 16 columns (lane: token li,
   // columns 16 wave + 4g .. + 3), and after the next barrier wave q stores tokens 8q .. 8q + 7
