@@ -67,6 +67,7 @@ extern "C" {
 #define RWKV7_ERR_ALIAS (-6)     /* outputs overlap inputs or each other (other than state_out == state_in) */
 #define RWKV7_ERR_ALGO (-7)      /* unknown algorithm, or one that does not support the arguments */
 #define RWKV7_ERR_HIP (-8)       /* a HIP runtime call or kernel launch failed */
+#define RWKV7_ERR_SCRATCH (-9)   /* rwkv7_wkv_prefill_noalloc: the call does not fit its static scratch array */
 
 /* Input dtype of r, w, k, v, a, b. y is always float32; so is the state except in rwkv7_wkv_step_q. */
 #define RWKV7_DTYPE_F32 0
@@ -344,6 +345,30 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  */
 int rwkv7_stack_forward(const void *w_in, const void *w_out, const float *vecs, float *x, float *states, int64_t L,
                         int64_t B, int64_t T, int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * rwkv7_wkv_prefill_ex with RWKV7_ALGO_CHUNKED_SPLIT, same arguments, layouts,
+ * domain and results, except that the chunk records passing from the prep
+ * kernel to the scan kernel live in a fixed device array of
+ * RWKV7_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends. The call allocates nothing (no hipMalloc, no
+ * library workspace). The array limits the size: one chunk of records
+ * (9,472 bytes) for every (b, h) unit, plus B*H*16 KiB for the carried state
+ * when state_out is NULL, must fit (B*H up to about 7,000 with state_out,
+ * 2,500 without); a longer sequence runs in slabs of chunks that fit. A call
+ * beyond that returns RWKV7_ERR_SCRATCH before any launch. bfloat16 inputs only
+ * (RWKV7_ERR_ALGO otherwise, as for the split algorithm).
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (other streams, other host threads) race and give wrong
+ * results; serialise them. No part of the array needs clearing between calls
+ * (every record is written before it is read).
+ */
+#define RWKV7_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int rwkv7_wkv_prefill_noalloc(const void *r, const void *w, const void *k, const void *v, const void *a,
+                              const void *b, const float *state_in, float *y, float *state_out, int64_t B,
+                              int64_t T, int64_t H, int64_t N, int dtype, void *stream);
 
 /*
  * The algorithm rwkv7_wkv_prefill would run for a bfloat16 or float32 prefill of

@@ -313,6 +313,30 @@ int rwkv7_wkv_prefill_ex(const void* r, const void* w, const void* k, const void
   return run(r, w, k, v, a, b, state_in, y, state_out, B, T, H, N, dtype, RWKV7_STATE_F32, algo, false, stream);
 }
 
+int rwkv7_wkv_prefill_noalloc(const void* r, const void* w, const void* k, const void* v, const void* a,
+                              const void* b, const float* state_in, float* y, float* state_out, int64_t B, int64_t T,
+                              int64_t H, int64_t N, int dtype, void* stream) {
+  const void* in[6] = {r, w, k, v, a, b};
+  const int st = validate(in, state_in, y, state_out, B, T, H, N, dtype, RWKV7_STATE_F32);
+  if (st != RWKV7_OK) return st;
+  if (dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_ALGO;
+  if (B * H == 0) return RWKV7_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    const hipError_t e = state_out && state_out != state_in ? rwkv7::launch_state_copy(state_in, state_out, B * H, s)
+                                                            : hipSuccess;
+    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+  }
+  if (T * H * 64 >= (int64_t(1) << 31)) return RWKV7_ERR_ALGO;
+  if (rwkv7::noalloc_scratch_need(B * H, state_out != nullptr) > rwkv7::kNoallocScratchBytes)
+    return RWKV7_ERR_SCRATCH;
+  WkvCall c{{r, w, k, v, a, b}, state_in, y, state_out, B, T, H, dtype, RWKV7_STATE_F32, s};
+  const hipError_t e = rwkv7::launch_chunked_split_noalloc(c);
+  if (e == hipErrorInvalidValue) return RWKV7_ERR_SCRATCH;
+  if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;
+  return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
+
 int rwkv7_wkv_prefill_algo(int64_t B, int64_t T, int64_t H, int64_t N, int dtype) {
   if (dtype != RWKV7_DTYPE_F32 && dtype != RWKV7_DTYPE_BF16) return RWKV7_ERR_DTYPE;
   if (B < 0 || T < 0 || H < 0) return RWKV7_ERR_SHAPE;
@@ -336,6 +360,7 @@ const char* rwkv7_wkv_strerror(int status) {
     case RWKV7_ERR_ALIAS: return "outputs overlap inputs or each other";
     case RWKV7_ERR_ALGO: return "unknown or unsupported algorithm for these arguments";
     case RWKV7_ERR_HIP: return "HIP runtime error";
+    case RWKV7_ERR_SCRATCH: return "the call needs more than the static scratch array of rwkv7_wkv_prefill_noalloc";
     default: return "unknown status";
   }
 }

@@ -44,6 +44,16 @@ hipError_t launch_chunked(const WkvCall& c);
 // kernel, with a record buffer cached per (device, stream).
 hipError_t launch_chunked_split(const WkvCall& c);
 
+// The split chunked prefill with its records in a static device array of
+// kNoallocScratchBytes (one per device) instead of the per-stream workspace: it
+// allocates nothing. hipErrorInvalidValue if one chunk of records for every head
+// (plus the carried state when s_out is null) does not fit, before any launch.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t launch_chunked_split_noalloc(const WkvCall& c);
+// Bytes of the static array a call with B * H == units needs at least (one chunk of
+// records per head, plus the carried state when state_out is null).
+size_t noalloc_scratch_need(int64_t units, bool state_out);
+
 // The time-mix operator with its prologue (decay, normalised removal key, the
 // a and b slots) and epilogue (ln_x GroupNorm) fused around the recurrence.
 struct TmixParams {

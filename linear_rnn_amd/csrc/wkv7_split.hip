@@ -424,13 +424,25 @@ struct SplitJob {
   hipStream_t stream;
 };
 
-hipError_t run_split(const SplitJob& j) {
+// One chunked pass, slab by slab. With fixed == nullptr the records live in the
+// per-(device, stream) workspace and a slab's records fit slab_budget_bytes(); otherwise
+// the records (and, when state_out is null, the state carried between slabs) live in
+// fixed, cap bytes of device memory, which must hold one chunk of records for every
+// head (hipErrorInvalidValue before any launch otherwise).
+hipError_t run_split(const SplitJob& j, unsigned char* fixed = nullptr, size_t cap = 0) {
   const int64_t units = j.B * j.H;
   const int64_t nch = (j.T + kC - 1) / kC;
   // In-sequence offsets are 32-bit: T * H * 64 elements must stay below 2^31.
   if (j.T * j.H * kN >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int64_t per_chunk = units * kRecBytes;
-  int64_t slab = (int64_t)(slab_budget_bytes() / (size_t)per_chunk);
+  const size_t carry_bytes = (size_t)units * kN * kN * 4;
+  size_t budget = slab_budget_bytes();
+  if (fixed) {
+    const size_t reserve = j.s_out ? 0 : carry_bytes;
+    if (cap < reserve + (size_t)per_chunk) return hipErrorInvalidValue;
+    budget = cap - reserve;
+  }
+  int64_t slab = (int64_t)(budget / (size_t)per_chunk);
   slab = slab < 1 ? 1 : slab;
   if (slab < nch) {
     // Every prep item takes about the same time, so a slab whose items fill
@@ -445,10 +457,15 @@ hipError_t run_split(const SplitJob& j) {
   if (units * slab > (int64_t(1) << 30)) return hipErrorNotSupported;
   const bool tmp_state = nslab > 1 && j.s_out == nullptr;
   const size_t rec_bytes = (size_t)(units * slab * kRecBytes);
-  const size_t bytes = rec_bytes + (tmp_state ? (size_t)units * kN * kN * 4 : 0);
-  void* ws = nullptr;
-  hipError_t e = device_workspace(j.stream, bytes, &ws, kWorkspaceChunks);
-  if (e != hipSuccess) return e;
+  const size_t bytes = rec_bytes + (tmp_state ? carry_bytes : 0);
+  void* ws = fixed;
+  hipError_t e = hipSuccess;
+  if (fixed) {
+    if (bytes > cap) return hipErrorInvalidValue;
+  } else {
+    e = device_workspace(j.stream, bytes, &ws, kWorkspaceChunks);
+    if (e != hipSuccess) return e;
+  }
   unsigned char* rec = static_cast<unsigned char*>(ws);
   float* carry = tmp_state ? reinterpret_cast<float*>(rec + rec_bytes) : j.s_out;
 
@@ -540,6 +557,57 @@ hipError_t launch_chunked_split(const WkvCall& c) {
   SplitJob j{in, kPrepPlain, static_cast<const uint16_t*>(c.in[3]), c.y, static_cast<const float*>(c.s_in),
              static_cast<float*>(c.s_out), c.B, c.T, c.H, c.stream};
   return run_split(j);
+}
+
+// ---------------------------------------------------------------------------- no-allocation variant
+// The chunk records of rwkv7_wkv_prefill_noalloc live in this array, one copy per
+// device (the runtime provides it when it loads this code object). Host code never
+// passes the array's name to a kernel: on the host the name is a stand-in, not a
+// device address. Each device's address is looked up once, with that device current,
+// and only that address reaches kernels.
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_addr[kMaxScratchDevices];  // per device, null until looked up
+
+hipError_t scratch_address(unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_chunked_split_noalloc(const WkvCall& c) {
+  if (c.dtype != 1) return hipErrorNotSupported;  // bfloat16 inputs only
+  unsigned char* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  PrepIn in{};
+  in.r = static_cast<const uint16_t*>(c.in[0]);
+  in.w = static_cast<const uint16_t*>(c.in[1]);
+  in.k = static_cast<const uint16_t*>(c.in[2]);
+  in.a = static_cast<const uint16_t*>(c.in[4]);
+  in.b = static_cast<const uint16_t*>(c.in[5]);
+  SplitJob j{in, kPrepPlain, static_cast<const uint16_t*>(c.in[3]), c.y, static_cast<const float*>(c.s_in),
+             static_cast<float*>(c.s_out), c.B, c.T, c.H, c.stream};
+  return run_split(j, ws, kNoallocScratchBytes);
+}
+
+size_t noalloc_scratch_need(int64_t units, bool state_out) {
+  return (size_t)units * kRecBytes + (state_out ? 0 : (size_t)units * kN * kN * 4);
 }
 
 hipError_t launch_tmix_chunked(const TmixCall& c) {

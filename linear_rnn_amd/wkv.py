@@ -29,10 +29,13 @@ RWKV7_ALGO_AUTO = 0
 RWKV7_ALGO_SEQUENTIAL = 1
 RWKV7_ALGO_CHUNKED = 2
 RWKV7_ALGO_CHUNKED_SPLIT = 3
+RWKV7_ERR_SCRATCH = -9
+RWKV7_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
             "rwkv7_tmix_prefill", "rwkv7_tmix_prefill_ex", "rwkv7_tmix_step", "rwkv7_wkv_backward",
-            "rwkv7_stack_forward", "rwkv7_wkv_prefill_algo", "rwkv7_wkv_strerror")
+            "rwkv7_stack_forward", "rwkv7_wkv_prefill_algo", "rwkv7_wkv_prefill_noalloc",
+            "rwkv7_wkv_strerror")
 
 _lib = None
 _lock = threading.Lock()
@@ -54,7 +57,7 @@ def lib() -> ctypes.CDLL:
             L = ctypes.CDLL(LIB_PATH)
             vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
             sig = [vp] * 9 + [i64] * 4 + [ci]
-            for name in ("rwkv7_wkv_prefill", "rwkv7_wkv_step"):
+            for name in ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_prefill_noalloc"):
                 f = getattr(L, name)
                 f.restype = ci
                 f.argtypes = sig + [vp]
@@ -186,6 +189,13 @@ def rwkv7_wkv_prefill(r, w, k, v, a, b, state_in, y, state_out, stream=None):
     """Whole-sequence prefill. Tensors as in include/rwkv7_wkv.h ([B,T,H,64] inputs, float32 y and state)."""
     args = _args(r, w, k, v, a, b, state_in, y, state_out, stream)
     _check(lib().rwkv7_wkv_prefill(*args, _stream(stream)))
+
+
+def rwkv7_wkv_prefill_noalloc(r, w, k, v, a, b, state_in, y, state_out, stream=None):
+    """The split chunked prefill with its records in the library's static device array (allocates nothing;
+    bfloat16 inputs; calls on one device must not overlap)."""
+    args = _args(r, w, k, v, a, b, state_in, y, state_out, stream)
+    _check(lib().rwkv7_wkv_prefill_noalloc(*args, _stream(stream)))
 
 
 def rwkv7_wkv_step(r, w, k, v, a, b, state_in, y, state_out, stream=None):

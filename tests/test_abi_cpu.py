@@ -312,3 +312,28 @@ def test_stack_validation(L):
     p[4] = p[3] + 64  # states inside x
     assert scall(L, p=p) == E_ALIAS
     assert scall(L, n_layers=0) == OK and scall(L, T=0) == OK and scall(L, p=[None] * 5, B=0) == OK
+
+
+# ---- the allocation-free prefill: refusals happen before any HIP call
+
+def test_noalloc_refusals(L):
+    def nc(p=None, B=2, T=3, H=4, dtype=BF16):
+        p = ptrs() if p is None else p
+        return L.rwkv7_wkv_prefill_noalloc(*(list(p) + [B, T, H, 64, dtype, None]))
+    assert nc(dtype=F32) == E_ALGO               # bfloat16 inputs only, as the split algorithm
+    assert nc(dtype=7) == E_DTYPE
+    assert nc(B=0) == OK and nc(H=0) == OK      # no work
+    # one chunk of records (9,472 bytes) per head must fit the 64 MiB array
+    cap = wkv.RWKV7_NOALLOC_SCRATCH_BYTES
+    too_many = cap // 9472 + 1
+    assert nc(B=too_many, H=1) == wkv.RWKV7_ERR_SCRATCH
+    # without state_out the carried state (16 KiB per head) must fit as well
+    p = ptrs()
+    p[8] = None
+    heads = cap // (9472 + 16384) + 1
+    assert nc(p=p, B=heads, H=1) == wkv.RWKV7_ERR_SCRATCH
+    # the ordinary argument checks come first
+    p = ptrs()
+    p[7] = None
+    assert nc(p=p) == E_NULL
+    assert "static scratch" in wkv.rwkv7_wkv_strerror(wkv.RWKV7_ERR_SCRATCH)
