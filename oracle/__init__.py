@@ -25,7 +25,8 @@ float64; tests/test_oracle_tmix.py pins those pieces to closed forms and to
 torch's normalize and group_norm.
 
 ``stack_forward`` runs L time-mix layers over a residual stream (projections in numpy float64,
-the operator above), rounding to the weights' dtype at the points where the GPU rounds;
+the operator above), rounding at the points that the model's precision fixes (read from the G0
+notes' half-precision model and the README's fp32 note; see its docstring), or nowhere ("f64");
 tests/test_oracle_stack.py pins it to the GPT/RNN-mode equivalence and to a composition of torch's
 own softplus, sigmoid and matmul.
 
@@ -298,12 +299,22 @@ def _softplus(z):
 
 def stack_forward(w_in, w_out, vecs, x, states, dtype: str = "f32", nthreads: int | None = None):
     """L layers in float64. x [B, T, D] float32, states [L, B, H, N, N] (float32 or float64),
-    w_in [L, D, 5D] / w_out [L, D, D] float32 or bfloat16 bits (`dtype` names which), vecs [L, 5, D]
-    float32 (w0, a0, k_k, ln_w, ln_b). Per layer: P = q(x) W_in (blocks r|k|v|w|a, each rounded to
-    float32 as the projection's output); w_raw = -softplus(-(w0 + P_w)) - 0.5 (float32);
-    kk = P_k * k_k; a_lr = sigmoid(a0 + P_a); r, k, v, kk, a_lr rounded to `dtype`; the operator
-    with ln_x; x += q(o) W_out. q() rounds to bfloat16 for "bf16" and is the identity for "f32"
-    (float32 activations feed the float32 projections unrounded). Returns (x float64, states float64).
+    w_in [L, D, 5D] / w_out [L, D, D] float32 or bfloat16 bits, vecs [L, 5, D] float32 (w0, a0, k_k,
+    ln_w, ln_b). Per layer: P = q(x) W_in (blocks r|k|v|w|a); w_raw = -softplus(-(w0 + P_w)) - 0.5;
+    kk = P_k * k_k; a_lr = sigmoid(a0 + P_a); the operator on r, k, v, kk, a_lr with ln_x; x += q(o) W_out.
+
+    `dtype` is the model's precision and fixes the rounding points, read from the RWKV-7 G0 7.2B
+    notes (lshu.cn/news/198401) sections 3.2-3.4 (a model runs in one dtype, half on that page:
+    weights and the activations that enter a product are in it; w0 and the [H, N, N] state stay
+    float32) and the README's fp32 note (oa0.com/c/1004164: the state and w stay float32, kv is
+    converted to float32), with the residual stream float32 as the stack's ABI takes it:
+      "f32"  every product's output and every operator input rounded to float32 (the float32 model);
+      "bf16" x and o rounded to bfloat16 where they enter a product, P rounded to float32 (a float32
+             accumulation), w_raw float32 (the decay input stays float32), r, k, v, kk, a_lr rounded
+             to bfloat16 (the operator takes the model's dtype);
+      "f64"  no rounding anywhere (the same weights, exact arithmetic to float64): the reference
+             against which a model's own rounding is measured.
+    Returns (x float64, states float64).
     """
     x = np.asarray(x, dtype=np.float64).copy()
     st = np.asarray(states, dtype=np.float64).copy()
@@ -312,14 +323,15 @@ def stack_forward(w_in, w_out, vecs, x, states, dtype: str = "f32", nthreads: in
     M = B * T
     Wi, Wo, V = _widen_any(w_in), _widen_any(w_out), _widen_any(vecs)
     q = (lambda a: _widen_any(_as_dtype(a, "bf16"))) if dtype == "bf16" else (lambda a: a)
+    f32 = (lambda a: a) if dtype == "f64" else (lambda a: a.astype(np.float32).astype(np.float64))
     for l in range(L):
-        P = (q(x).reshape(M, D) @ Wi[l]).astype(np.float32).astype(np.float64)
+        P = f32(q(x).reshape(M, D) @ Wi[l])
         pr, pk, pv, pw, pa = (P[:, i * D:(i + 1) * D] for i in range(5))
-        w_raw = (-_softplus(-(V[l, 0] + pw)) - 0.5).astype(np.float32)
+        w_raw = f32(-_softplus(-(V[l, 0] + pw)) - 0.5)
         kk = pk * V[l, 2]
         a_lr = 1.0 / (1.0 + np.exp(-(V[l, 1] + pa)))
         shp = (B, T, H, N)
-        ops = [_as_dtype(t, dtype).reshape(shp) for t in (pr, pk, pv, kk, a_lr)]
+        ops = [(t if dtype == "f64" else _as_dtype(t, dtype)).reshape(shp) for t in (pr, pk, pv, kk, a_lr)]
         out, s = tmix(ops[0], w_raw.reshape(shp), ops[1], ops[2], ops[3], ops[4], vecs[l, 3], vecs[l, 4],
                       state_in=st[l], nthreads=nthreads)
         st[l] = s
