@@ -74,20 +74,50 @@ struct InTraits<false> {
 // Stored-state element formats (RWKV7_STATE_* codes).
 enum { kStF32 = 0, kStBF16 = 1, kStF16 = 2 };
 
+// State traffic of a step, streamed once per call. With NT the loads and stores carry the
+// non-temporal hint, so a state larger than the last-level cache does not displace
+// everything else from it on every step (measured: 1 GiB float32 state 400 -> 368 us per
+// step; a 128 MiB bfloat16 state 57 -> 49 us). A state that fits the cache is read back
+// from it by the next step, and plain accesses keep that (256 MiB float32: 78 us plain
+// against 91 us non-temporal).
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld_state16(const void* p) {
+  if constexpr (NT) {
+    const u32x4v q = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(q[0], q[1], q[2], q[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ void st_state16(void* p, uint4 o) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(u32x4v{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4v*>(p));
+  else
+    *reinterpret_cast<uint4*>(p) = o;
+}
+
 // Four consecutive state elements of one row: load widened, store rounded.
 template <int SQ>
 struct StateIO;
 template <>
 struct StateIO<kStF32> {
+  template <bool NT = false>
   __device__ static float4 load4(const void* base, int64_t idx) {
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const uint4 q = ld_state16<NT>(static_cast<const float*>(base) + idx);
+    return make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
   }
+  template <bool NT = false>
   __device__ static void store4(void* base, int64_t idx, float4 s) {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = s;
+    st_state16<NT>(static_cast<float*>(base) + idx,
+                   make_uint4(__float_as_uint(s.x), __float_as_uint(s.y), __float_as_uint(s.z), __float_as_uint(s.w)));
   }
 };
 template <>
 struct StateIO<kStBF16> {
+  template <bool NT = false>
   __device__ static float4 load4(const void* base, int64_t idx) {
     const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
     return make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
@@ -96,12 +126,14 @@ struct StateIO<kStBF16> {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
   }
+  template <bool NT = false>
   __device__ static void store4(void* base, int64_t idx, float4 s) {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = make_uint2(pack(s.x, s.y), pack(s.z, s.w));
   }
 };
 template <>
 struct StateIO<kStF16> {
+  template <bool NT = false>
   __device__ static float4 load4(const void* base, int64_t idx) {
     const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
     return make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(q.x & 0xffffu)),
@@ -113,12 +145,13 @@ struct StateIO<kStF16> {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
   }
+  template <bool NT = false>
   __device__ static void store4(void* base, int64_t idx, float4 s) {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = make_uint2(pack(s.x, s.y), pack(s.z, s.w));
   }
 };
 
-template <bool BF16, int WAVES, int RPW, int TB, int SQ>
+template <bool BF16, int WAVES, int RPW, int TB, int SQ, bool NT = false>
 __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
   using Tr = InTraits<BF16>;
   using St = StateIO<SQ>;
@@ -166,7 +199,7 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
   for (int m = 0; m < kMr; ++m) {
     const int row = row0 + 4 * m + ri;
     if (p.s_in)
-      S[m] = St::load4(p.s_in, (unit * kN + row) * kN + 4 * c);
+      S[m] = St::template load4<NT>(p.s_in, (unit * kN + row) * kN + 4 * c);
     else
       S[m] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -277,7 +310,7 @@ __global__ __launch_bounds__(kWave* WAVES) void wkv7_seq_kernel(SeqParams p) {
 #pragma unroll
     for (int m = 0; m < kMr; ++m) {
       const int row = row0 + 4 * m + ri;
-      St::store4(p.s_out, (unit * kN + row) * kN + 4 * c, S[m]);
+      St::template store4<NT>(p.s_out, (unit * kN + row) * kN + 4 * c, S[m]);
     }
   }
 }
@@ -318,7 +351,7 @@ struct StepRaw {
   typename std::conditional<BF16, uint16_t, float>::type v[2];
 };
 
-template <bool BF16, int SQ>
+template <bool BF16, int SQ, bool NT>
 __global__ __launch_bounds__(4 * kWave) void wkv7_step_kernel(SeqParams p, int64_t units) {
   using St = StateIO<SQ>;
   using Raw = StepRaw<BF16, SQ>;
@@ -336,8 +369,7 @@ __global__ __launch_bounds__(4 * kWave) void wkv7_step_kernel(SeqParams p, int64
   auto load = [&](Raw& x, int64_t u) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
-      x.s[m] = p.s_in ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.s_in) +
-                                                        (u * kN + row_a + 8 * m) * kN + 8 * c8)
+      x.s[m] = p.s_in ? ld_state16<NT>(static_cast<const uint16_t*>(p.s_in) + (u * kN + row_a + 8 * m) * kN + 8 * c8)
                       : make_uint4(0u, 0u, 0u, 0u);
     const int64_t ib = u * kN + 8 * c8;
 #pragma unroll
@@ -412,7 +444,7 @@ __global__ __launch_bounds__(4 * kWave) void wkv7_step_kernel(SeqParams p, int64
         o.y = St::pack(S[m][2], S[m][3]);
         o.z = St::pack(S[m][4], S[m][5]);
         o.w = St::pack(S[m][6], S[m][7]);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.s_out) + (u * kN + row_a + 8 * m) * kN + 8 * c8) = o;
+        st_state16<NT>(static_cast<uint16_t*>(p.s_out) + (u * kN + row_a + 8 * m) * kN + 8 * c8, o);
       }
     }
   };
@@ -436,15 +468,21 @@ __global__ void state_copy_kernel(const float4* __restrict__ src, float4* __rest
   if (i < n4) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <bool BF16, int WAVES, int RPW, int TB, int SQ = kStF32>
+template <bool BF16, int WAVES, int RPW, int TB, int SQ = kStF32, bool NT = false>
 hipError_t launch_seq_cfg(const WkvCall& c) {
   SeqParams p{c.in[0], c.in[1], c.in[2], c.in[3], c.in[4], c.in[5], c.s_in, c.y, c.s_out, c.T, (int32_t)c.H};
   constexpr int kNrb = kN / (WAVES * RPW);
   const int64_t blocks = c.B * c.H * kNrb;
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_seq_kernel<BF16, WAVES, RPW, TB, SQ>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_seq_kernel<BF16, WAVES, RPW, TB, SQ, NT>),
                          dim3((uint32_t)blocks), dim3(kWave * WAVES), args, 0, c.stream);
 }
+
+// Stored-state size from which a step streams its state with non-temporal accesses: the
+// measured crossovers on MI355X (256 MB last-level cache) lie between 256 and 320 MiB for a
+// float32 state and between 64 and 128 MiB for a 16-bit one.
+constexpr int64_t kNtStateF32 = int64_t(288) << 20;
+constexpr int64_t kNtState16 = int64_t(96) << 20;
 
 // Measured on the D2048 step (B=512, H=32): 8192 workgroups (two heads each)
 // beat both one workgroup per head and fully resident grids for 16-bit states.
@@ -458,8 +496,10 @@ hipError_t launch_step(const WkvCall& c) {
   // 256 CUs busy with several waves, each walking heads with a stride of the grid.
   const int64_t grid = units < kStepGrid ? units : kStepGrid;
   void* args[] = {&p, &units};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&wkv7_step_kernel<BF16, SQ>), dim3((uint32_t)grid),
-                         dim3(4 * kWave), args, 0, c.stream);
+  const bool nt = units * kN * kN * 2 > kNtState16;
+  const void* fn = nt ? reinterpret_cast<const void*>(&wkv7_step_kernel<BF16, SQ, true>)
+                      : reinterpret_cast<const void*>(&wkv7_step_kernel<BF16, SQ, false>);
+  return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(4 * kWave), args, 0, c.stream);
 }
 
 template <bool BF16>
@@ -470,6 +510,7 @@ hipError_t launch_seq_dtype(const WkvCall& c, bool decode_shape) {
     // for 16 KiB state rows (78 us against 87 us per D2048 step).
     if (c.sdtype == kStBF16) return launch_step<BF16, kStBF16>(c);
     if (c.sdtype == kStF16) return launch_step<BF16, kStF16>(c);
+    if (c.B * c.H * kN * kN * 4 > kNtStateF32) return launch_seq_cfg<BF16, 4, 16, 1, kStF32, true>(c);
     return launch_seq_cfg<BF16, 4, 16, 1>(c);
   }
   if (c.sdtype != kStF32) return hipErrorNotSupported;

@@ -138,6 +138,38 @@ def test_d2048_decode_steps(torch):
     assert worst_y <= 1e-5 and worst_s <= 1e-5, (worst_y, worst_s)
 
 
+def test_large_state_step_streams_the_same_bits(torch):
+    """A float32 state above the last-level cache's size (B=640, H=32: 320 MiB) takes the step with
+    non-temporal state accesses. Its results equal, bit for bit, the same heads stepped in a small
+    batch (plain accesses), and match the oracle on sampled heads; three in-place steps."""
+    cfg = CONFIGS["D2048-decode"]
+    B, H = 640, 32
+    say("large-state step (320 MiB float32 state), 3 steps", B, H)
+    units = sample_units(B, H, 8, seed=5)
+    bsel = sorted({u[0] for u in units})
+    xs = [make_inputs(cfg, B=B, H=H, step=s, with_state=(s == 0)) for s in range(3)]
+    state = torch.from_numpy(xs[0]["state_in"]).cuda()
+    small = torch.from_numpy(np.ascontiguousarray(xs[0]["state_in"][bsel])).cuda()
+    y = torch.empty((B, 1, H, 64), dtype=torch.float32, device="cuda")
+    ys = torch.empty((len(bsel), 1, H, 64), dtype=torch.float32, device="cuda")
+    s_ref = {u: xs[0]["state_in"][u[0], u[1]].copy() for u in units}
+    for x in xs:
+        d = to_dev(x)
+        wkv.rwkv7_wkv_step(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], state, y, state)
+        ds = {n: d[n][bsel].contiguous() for n in "rwkvab"}
+        wkv.rwkv7_wkv_step(ds["r"], ds["w"], ds["k"], ds["v"], ds["a"], ds["b"], small, ys, small)
+        torch.cuda.synchronize()
+        assert torch.equal(y[bsel], ys)
+        for (b, h) in units:
+            sub = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1]) for n in "rwkvab"}
+            yr, sr = oracle.wkv7(*(sub[n] for n in "rwkvab"), state_in=s_ref[(b, h)][None, None])
+            s_ref[(b, h)] = sr[0, 0]
+            assert rel(y[b, 0, h].cpu().numpy(), yr[0, 0, 0]) <= 1e-5
+    assert torch.equal(state[bsel], small)
+    st = state.cpu().numpy()
+    assert max(rel(st[b, h], s_ref[(b, h)]) for (b, h) in units) <= 1e-5
+
+
 def test_prefill_equals_steps_bit_identical(torch):
     say("prefill vs steps")
     x = make_inputs(CONFIGS["L12-D768-prefill"], B=3, T=50, H=4, seed=9)
