@@ -404,7 +404,10 @@ def bench_decode_large(torch, wkv, args, B=2048, H=32, S=64, distinct=16):
                                % (B, H, N, S, distinct), "B": B, "H": H, "N": N, "state": "f32"},
         "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "kernel": "wkv7_seq_kernel (step tiling)", "algorithmic_bytes": nbytes, "traffic": None},
+                     "kernel": "wkv7_seq_kernel (step tiling, non-temporal state)", "algorithmic_bytes": nbytes,
+                     "traffic": measured_traffic("wkv7_seq_kernel:D2048-decode-large-state",
+                                                 ["linear_rnn_amd/csrc/wkv7_seq.hip",
+                                                  "linear_rnn_amd/csrc/wkv7_device.hpp"])},
     }
 
 
@@ -588,12 +591,19 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
     tm()
     ms_tmix = time_region(torch, tm, 5)
 
-    def tmc():
-        wkv.rwkv7_tmix_prefill_ex(*(dt[n] for n in names), dt["ln_w"], dt["ln_b"], dt["state_in"], o, so,
-                                  algo=wkv.RWKV7_ALGO_CHUNKED_SPLIT)
+    # the chunked form the stack's prompt runs at this shape, and the other one beside it
+    stack_algo = wkv.rwkv7_wkv_prefill_algo(B, T, H)
+    ms_by_algo = {}
+    for a in (wkv.RWKV7_ALGO_CHUNKED, wkv.RWKV7_ALGO_CHUNKED_SPLIT):
+        def tmc(a=a):
+            wkv.rwkv7_tmix_prefill_ex(*(dt[n] for n in names), dt["ln_w"], dt["ln_b"], dt["state_in"], o, so,
+                                      algo=a)
 
-    tmc()
-    ms_tmix_ch = time_region(torch, tmc, 5)
+        tmc()
+        ms_by_algo[a] = time_region(torch, tmc, 5)
+    ms_tmix_ch = ms_by_algo[stack_algo]
+    tm_kernel = {wkv.RWKV7_ALGO_CHUNKED: "wkv7_fused_kernel<time-mix> + tmix_ln_kernel",
+                 wkv.RWKV7_ALGO_CHUNKED_SPLIT: "wkv7_prep_kernel<time-mix> + wkv7_scan_kernel + tmix_ln_kernel"}
     # algorithmic bytes: r, k, v, kk, a_lr (bf16), w_raw and out (float32) per element, the state in and out
     tm_bytes = B * T * H * N * (5 * 2 + 4 + 4) + 2 * B * H * N * N * 4
     flops = FLOP_REC * B * T * H
@@ -605,11 +615,11 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
                                "synthetic bf16 weights, fp32 residual stream and states" % (B, T),
                    "L": L, "B": B, "T": T, "H": H, "N": N},
         "tmix_prefill_chunked": {
-            "ms": ms_tmix_ch, "share_of_prompt": ms_tmix_ch * L / ms_prompt,
+            "ms": ms_tmix_ch, "algo": ALGO_NAMES[stack_algo], "share_of_prompt": ms_tmix_ch * L / ms_prompt,
+            "by_algorithm": {ALGO_NAMES[a]: {"ms": t} for a, t in ms_by_algo.items()},
             "roofline": {"bound": "hbm", "achieved": tm_bytes / (ms_tmix_ch * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": tm_bytes / (ms_tmix_ch * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "kernel": "wkv7_prep_kernel<time-mix> + wkv7_scan_kernel + tmix_ln_kernel",
-                         "algorithmic_bytes": tm_bytes, "traffic": None}},
+                         "kernel": tm_kernel[stack_algo], "algorithmic_bytes": tm_bytes, "traffic": None}},
         "tmix_prefill_sequential": {
             "ms": ms_tmix,
             "roofline": {"bound": "alu", "achieved": flops / (ms_tmix * 1e-3) / 1e12,

@@ -106,7 +106,7 @@ extern "C" {
  * Algorithm (what RWKV7_ALGO_AUTO picks; rwkv7_wkv_prefill_algo reports it):
  *   float32 inputs                      RWKV7_ALGO_SEQUENTIAL (float32 throughout);
  *   bfloat16, T * H * 64 >= 2^31        RWKV7_ALGO_SEQUENTIAL (outside the chunked domain);
- *   bfloat16, B * H >= 7/16 of the      RWKV7_ALGO_CHUNKED (one workgroup per head);
+ *   bfloat16, B * H >= 3/8 of the       RWKV7_ALGO_CHUNKED (one workgroup per head);
  *     current device's compute units
  *   bfloat16, fewer heads               RWKV7_ALGO_CHUNKED_SPLIT (prep spread over the chip).
  * The chunked algorithms carry the state in float32 but round intra-chunk
@@ -241,14 +241,19 @@ int rwkv7_tmix_prefill(const void *r, const float *w_raw, const void *k, const v
  * rwkv7_tmix_prefill with a choice of algorithm:
  *   RWKV7_ALGO_AUTO, RWKV7_ALGO_SEQUENTIAL  the token-by-token kernel (what
  *                      rwkv7_tmix_prefill runs; bit-identical to T single steps)
- *   RWKV7_ALGO_CHUNKED_SPLIT  bfloat16 inputs only: the chunked prefill of
- *                      rwkv7_wkv_prefill_ex (prep and scan kernels, its cached device
- *                      workspace), with the decay exp(-exp(w_raw)), the unit key and
- *                      the two slots formed inside the prep, y written to out and
- *                      ln_x applied to out in place. Decays below 2^-15 are clamped
- *                      there (as in that prefill); results match the definition to the
- *                      chunked tolerance, not bit for bit with the steps.
- * Any other algo, or CHUNKED_SPLIT with float32 inputs: RWKV7_ERR_ALGO.
+ *   RWKV7_ALGO_CHUNKED  bfloat16 inputs only: the one-kernel chunked prefill of
+ *                      rwkv7_wkv_prefill_ex (one workgroup per head, no workspace),
+ *                      with the decay exp(-exp(w_raw)), the unit key and the two
+ *                      slots formed in its prep waves and y written to out; a
+ *                      second kernel applies ln_x to out in place. Its domain is
+ *                      that of the chunked prefill (T*H*64 < 2^31).
+ *   RWKV7_ALGO_CHUNKED_SPLIT  bfloat16 inputs only: the same prologue in the split
+ *                      prefill (prep and scan kernels, the cached device workspace),
+ *                      then ln_x in place.
+ * Both chunked forms clamp decays below 2^-15 (as the chunked prefill does) and
+ * match the definition to the chunked tolerance, not bit for bit with the steps.
+ * Any other algo, a chunked algo with float32 inputs, or CHUNKED outside its
+ * domain: RWKV7_ERR_ALGO.
  */
 int rwkv7_tmix_prefill_ex(const void *r, const float *w_raw, const void *k, const void *v, const void *kk,
                           const void *a_lr, const float *ln_w, const float *ln_b, const float *state_in, float *out,
@@ -325,9 +330,11 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  *
  * With bfloat16 weights, x and o are rounded to bfloat16 for the projections and
  * r, k, v, kk, a_lr are bfloat16 operator inputs; projections accumulate in
- * float32. A bfloat16 call of T >= 32 tokens runs the operator as
- * rwkv7_tmix_prefill_ex with RWKV7_ALGO_CHUNKED_SPLIT (a prompt); other calls run
- * it token by token. Token shift, the channel mix, the output gate and the low-rank
+ * float32. A bfloat16 call of T >= 32 tokens (a prompt) runs the operator as
+ * rwkv7_tmix_prefill_ex with the chunked algorithm that RWKV7_ALGO_AUTO picks for
+ * rwkv7_wkv_prefill_ex at the same B, T, H (the one-kernel form when B*H is at
+ * least 3/8 of the compute unit count, else the split form; sequential outside
+ * the chunked domain); other calls run it token by token. Token shift, the channel mix, the output gate and the low-rank
  * projections of the full model are not included. Every pointer is 16-byte
  * aligned; x and states may not overlap each other or the weights. B*T must be
  * below 2^31. L == 0 or an empty x does nothing. The projections run on rocBLAS

@@ -3,8 +3,33 @@
 // without touching the device.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "rwkv7_wkv.h"
 #include "wkv7_internal.hpp"
+
+namespace rwkv7 {
+
+int auto_prefill_algo(int64_t B, int64_t T, int64_t H, int dtype) {
+  // the chunked kernels use 32-bit element offsets inside a sequence
+  if (dtype != RWKV7_DTYPE_BF16 || T * H * 64 >= (int64_t(1) << 31)) return RWKV7_ALGO_SEQUENTIAL;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      cached[dev].store(cus, std::memory_order_relaxed);
+  }
+  if (cus <= 0) cus = 256;
+  // measured on MI355X (256 CUs): the one-kernel prefill takes about 0.9 us per chunk on a CU of its
+  // own whatever the head count up to one head per CU; the split one about 0.4 us per chunk of scan
+  // plus 5 ns per chunk and head of prep; they meet near 96 heads
+  return B * H * 8 >= (int64_t)cus * 3 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_CHUNKED_SPLIT;
+}
+
+}  // namespace rwkv7
 
 namespace {
 

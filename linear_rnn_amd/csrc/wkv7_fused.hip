@@ -20,10 +20,8 @@
 // every consumed[w] > c - kRing. The smallest unfinished chunk never waits on a later
 // one, so the hand-off cannot deadlock; every wait is also bounded (kSpinMax polls),
 // so a wave never spins forever even if the protocol were broken.
-#include <atomic>
 #include <cstdint>
 
-#include "rwkv7_wkv.h"
 #include "wkv7_chunk_ops.hpp"
 #include "wkv7_internal.hpp"
 
@@ -229,23 +227,8 @@ hipError_t launch_fused(const FusedParams& fp, int64_t units, hipStream_t stream
 // Offsets inside a sequence are 32-bit element counts (T * H * 64 below 2^31).
 bool fused_domain(int64_t T, int64_t H) { return T * H * kN < (int64_t(1) << 31); }
 
-constexpr int kMaxDevices = 64;
 
 }  // namespace
-
-int auto_prefill_algo(int64_t B, int64_t T, int64_t H, int dtype) {
-  if (dtype != RWKV7_DTYPE_BF16 || !fused_domain(T, H)) return RWKV7_ALGO_SEQUENTIAL;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
-    cus = cached[dev].load(std::memory_order_relaxed);
-    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0)
-      cached[dev].store(cus, std::memory_order_relaxed);
-  }
-  if (cus <= 0) cus = 256;
-  return B * H * 16 >= (int64_t)cus * 7 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_CHUNKED_SPLIT;
-}
 
 hipError_t launch_chunked(const WkvCall& c) {
   // bfloat16 inputs only: float32 inputs keep float32 accuracy on the sequential kernel

@@ -22,8 +22,8 @@ struct WkvCall {
 //   float32 inputs                           sequential (their 1e-5 bar needs float32 operands)
 //   bfloat16, T * H * 64 >= 2^31             sequential (the chunked kernels use 32-bit offsets
 //                                            inside a sequence; the sequential one does not)
-//   bfloat16, B * H >= 7/16 of the CU count  the one-kernel chunked prefill (a workgroup per head
-//                                            keeps most compute units busy)
+//   bfloat16, B * H >= 3/8 of the CU count   the one-kernel chunked prefill (a workgroup per head
+//                                            keeps enough compute units busy)
 //   bfloat16, fewer heads                    the split chunked prefill (its prep kernel spreads
 //                                            the chunks of few heads over the whole chip)
 // The CU count comes from the current device (256 if it cannot be queried).
