@@ -106,9 +106,11 @@ extern "C" {
  * Algorithm (what RWKV7_ALGO_AUTO picks; rwkv7_wkv_prefill_algo reports it):
  *   float32 inputs                      RWKV7_ALGO_SEQUENTIAL (float32 throughout);
  *   bfloat16, T * H * 64 >= 2^31        RWKV7_ALGO_SEQUENTIAL (outside the chunked domain);
- *   bfloat16, B * H >= 3/8 of the       RWKV7_ALGO_CHUNKED (one workgroup per head);
- *     current device's compute units
- *   bfloat16, fewer heads               RWKV7_ALGO_CHUNKED_SPLIT (prep spread over the chip).
+ *   bfloat16, B * H >= CUs * (0.3 + 12.8 / ceil(T / 16)), with CUs the current
+ *     device's compute units            RWKV7_ALGO_CHUNKED (one workgroup per head;
+ *                                       on 256 CUs: 96 heads from about 2,700 tokens,
+ *                                       128 heads from 1,024, 256 heads from about 290);
+ *   bfloat16, otherwise                 RWKV7_ALGO_CHUNKED_SPLIT (prep spread over the chip).
  * The chunked algorithms carry the state in float32 but round intra-chunk
  * operands, the state operand of a chunk's products included, to float16: the
  * domain described under rwkv7_wkv_prefill_ex applies (magnitudes below 2^15,
@@ -332,9 +334,8 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  * r, k, v, kk, a_lr are bfloat16 operator inputs; projections accumulate in
  * float32. A bfloat16 call of T >= 32 tokens (a prompt) runs the operator as
  * rwkv7_tmix_prefill_ex with the chunked algorithm that RWKV7_ALGO_AUTO picks for
- * rwkv7_wkv_prefill_ex at the same B, T, H (the one-kernel form when B*H is at
- * least 3/8 of the compute unit count, else the split form; sequential outside
- * the chunked domain); other calls run it token by token. Token shift, the channel mix, the output gate and the low-rank
+ * rwkv7_wkv_prefill_ex at the same B, T, H (the one-kernel or the split form;
+ * sequential outside the chunked domain); other calls run it token by token. Token shift, the channel mix, the output gate and the low-rank
  * projections of the full model are not included. Every pointer is 16-byte
  * aligned; x and states may not overlap each other or the weights. B*T must be
  * below 2^31. L == 0 or an empty x does nothing. The projections run on rocBLAS

@@ -23,10 +23,12 @@ int auto_prefill_algo(int64_t B, int64_t T, int64_t H, int dtype) {
       cached[dev].store(cus, std::memory_order_relaxed);
   }
   if (cus <= 0) cus = 256;
-  // measured on MI355X (256 CUs): the one-kernel prefill takes about 0.9 us per chunk on a CU of its
-  // own whatever the head count up to one head per CU; the split one about 0.4 us per chunk of scan
-  // plus 5 ns per chunk and head of prep; they meet near 96 heads
-  return B * H * 8 >= (int64_t)cus * 3 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_CHUNKED_SPLIT;
+  // measured on MI355X (256 CUs), up to one head per CU: the one-kernel prefill takes about 16 us
+  // to fill and drain its pipeline plus 0.79 us per chunk; the split one 0.43 us per chunk of scan
+  // plus 1.2 us*CUs per chunk and head of prep (4.8 ns on 256 CUs). The one-kernel form wins when
+  // B*H >= CUs * (0.3 + 12.8 / chunks): 96 heads from about 2,700 tokens, 128 from 1,024, 256 from about 290.
+  const int64_t nc = (T + 15) / 16;
+  return B * H * nc * 10 >= (int64_t)cus * (3 * nc + 128) ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_CHUNKED_SPLIT;
 }
 
 }  // namespace rwkv7

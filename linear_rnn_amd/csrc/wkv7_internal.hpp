@@ -22,9 +22,11 @@ struct WkvCall {
 //   float32 inputs                           sequential (their 1e-5 bar needs float32 operands)
 //   bfloat16, T * H * 64 >= 2^31             sequential (the chunked kernels use 32-bit offsets
 //                                            inside a sequence; the sequential one does not)
-//   bfloat16, B * H >= 3/8 of the CU count   the one-kernel chunked prefill (a workgroup per head
-//                                            keeps enough compute units busy)
-//   bfloat16, fewer heads                    the split chunked prefill (its prep kernel spreads
+//   bfloat16, B * H >= CUs * (0.3 + 12.8 / chunks), chunks = ceil(T / 16)
+//                                            the one-kernel chunked prefill (a workgroup per head
+//                                            keeps enough compute units busy, and the sequence is
+//                                            long enough to hide its pipeline's fill and drain)
+//   bfloat16, otherwise                      the split chunked prefill (its prep kernel spreads
 //                                            the chunks of few heads over the whole chip)
 // The CU count comes from the current device (256 if it cannot be queried).
 int auto_prefill_algo(int64_t B, int64_t T, int64_t H, int dtype);

@@ -337,3 +337,38 @@ def test_noalloc_refusals(L):
     p[7] = None
     assert nc(p=p) == E_NULL
     assert "static scratch" in wkv.rwkv7_wkv_strerror(wkv.RWKV7_ERR_SCRATCH)
+
+
+def _device_cus():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.get_device_properties(0).multi_processor_count
+    except Exception:
+        pass
+    return 256  # the library's assumption when no device can be queried
+
+
+@pytest.mark.parametrize("B,T,H", [(8, 4096, 12), (8, 1024, 12), (4, 16384, 64), (16, 4096, 16), (16, 1024, 16),
+                                   (1, 4096, 8), (8, 2720, 12), (8, 2736, 12), (16, 288, 16), (16, 304, 16),
+                                   (1, 16, 1)])
+def test_auto_prefill_rule(L, B, T, H):
+    """AUTO: float32 and over-limit bfloat16 calls run sequentially; bfloat16 runs the one-kernel chunked
+    prefill once B*H >= CUs * (0.3 + 12.8 / ceil(T / 16)), else the split one."""
+    cus = _device_cus()
+    nc = -(-T // 16)
+    want = wkv.RWKV7_ALGO_CHUNKED if B * H * nc * 10 >= cus * (3 * nc + 128) else wkv.RWKV7_ALGO_CHUNKED_SPLIT
+    assert wkv.rwkv7_wkv_prefill_algo(B, T, H) == want
+    assert wkv.rwkv7_wkv_prefill_algo(B, T, H, dtype=wkv.RWKV7_DTYPE_F32) == wkv.RWKV7_ALGO_SEQUENTIAL
+
+
+def test_auto_prefill_rule_at_256_cus(L):
+    if _device_cus() != 256:
+        pytest.skip("the fixed points below are for a 256-CU device")
+    # the prompt shapes the rule was measured on
+    assert wkv.rwkv7_wkv_prefill_algo(8, 1024, 12) == wkv.RWKV7_ALGO_CHUNKED_SPLIT
+    assert wkv.rwkv7_wkv_prefill_algo(8, 4096, 12) == wkv.RWKV7_ALGO_CHUNKED
+    assert wkv.rwkv7_wkv_prefill_algo(4, 16384, 64) == wkv.RWKV7_ALGO_CHUNKED
+    # 32-bit element offsets inside a sequence: T*H*64 must stay below 2^31
+    assert wkv.rwkv7_wkv_prefill_algo(1, 1 << 22, 8) == wkv.RWKV7_ALGO_SEQUENTIAL
+    assert wkv.rwkv7_wkv_prefill_algo(1, (1 << 22) - 16, 8) != wkv.RWKV7_ALGO_SEQUENTIAL
