@@ -41,15 +41,18 @@
 // the same permutation: the 64-key contractions below take key 16kt + 4g + e for
 // (step, lane group, element), matching the state tiles' D layout.
 //
-// One MFMA shape per dependent chain. Chains that mixed 16x16x32 and 16x16x16 f16
-// products gave wrong values on gfx950 in whichever product the register
-// allocation placed last; the same chains in one shape are exact. The wrappers
-// below therefore come in three families that take distinct operand types: Mma16
-// (16x16x16 f16, half4 operands: the prep's transposes and 16-token products), MmaBF
-// (16x16x32 bf16, bf16x8 operands: the prep's Grams) and Mma32 (16x16x32 f16, half8
-// operands: the scan). Each chain in this file accumulates through exactly one of
-// them; a result of one family reaches another only as a converted operand or through
-// a vector-unit addition, never as another family's accumulator.
+// One MFMA instruction per dependent chain. When an MFMA takes the result of the
+// MFMA just before it as its accumulator (the same registers), the compiler issues it
+// with no wait in between, whatever the two instructions are; chains of one
+// instruction are exact that way, but chains that mixed 16x16x32 and 16x16x16 f16
+// products gave wrong values on gfx950 in the product placed second. The wrappers
+// below therefore come in three families, each with its own operand types and its
+// own accumulator type (Acc<family>): Mma16 (16x16x16 f16, half4 operands: the
+// prep's transposes and 16-token products), MmaBF (16x16x32 bf16, bf16x8 operands:
+// the prep's Grams) and Mma32 (16x16x32 f16, half8 operands: the scan). A result of
+// one family can reach another family's product only through an explicit .v (as a
+// converted operand, or after a vector-unit addition), never as its accumulator by
+// accident.
 #pragma once
 
 #include "wkv7_device.hpp"
@@ -72,26 +75,43 @@ constexpr int kRecD = kRecBlocks * 1024;
 constexpr int kRecBytes = kRecD + kN * 4;  // 9472
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// A 16x16 float32 accumulator tile of one MFMA family, in the D layout (element e of
+// lane (li, g) is row 4g + e, column li).
+enum { kFam16 = 0, kFamBF = 1, kFam32 = 2 };
+template <int FAMILY>
+struct Acc {
+  f32x4 v;
+};
 // 16x16x16 f16 family (the prep's transposes and 16-token products)
 struct Mma16 {
-  __device__ static __forceinline__ f32x4 mma(half4 a, half4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  typedef Acc<kFam16> acc;
+  __device__ static __forceinline__ acc zero() { return acc{zero4()}; }
+  __device__ static __forceinline__ acc mma(half4 a, half4 b, acc c) {
+    return acc{__builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c.v, 0, 0, 0)};
   }
 };
 // 16x16x32 f16 family (the scan)
 struct Mma32 {
-  __device__ static __forceinline__ f32x4 mma(half8 a, half8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  typedef Acc<kFam32> acc;
+  __device__ static __forceinline__ acc zero() { return acc{zero4()}; }
+  __device__ static __forceinline__ acc mma(half8 a, half8 b, acc c) {
+    return acc{__builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c.v, 0, 0, 0)};
   }
 };
 // 16x16x32 bf16 family (the prep's Grams, as products of bfloat16 hi / lo halves)
 struct MmaBF {
-  __device__ static __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  typedef Acc<kFamBF> acc;
+  __device__ static __forceinline__ acc zero() { return acc{zero4()}; }
+  __device__ static __forceinline__ acc mma(bf16x8 a, bf16x8 b, acc c) {
+    return acc{__builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c.v, 0, 0, 0)};
   }
 };
 __device__ __forceinline__ half4 to_h4(f32x4 x) {
   return half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+template <int F>
+__device__ __forceinline__ half4 to_h4(const Acc<F>& x) {
+  return to_h4(x.v);
 }
 __device__ __forceinline__ half8 cat8(half4 lo, half4 hi) {
   return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -284,7 +304,7 @@ __device__ __forceinline__ void prep_rows_to_raw(const PrepRows& rows, unsigned 
 // What the first phase of a chunk's prep hands to the second: the four Grams in the D
 // layout, A^ (float16) and R^ (float32) in the token layout, and the identity operand.
 struct PrepMid {
-  f32x4 Lab, Lak, Lrb, LrkT;
+  MmaBF::acc Lab, Lak, Lrb, LrkT;
   half4 Ahat[4];
   f32x4 Rhat[4];
   half4 eye;
@@ -363,11 +383,11 @@ __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char
   const uint32_t lo = (uint32_t)lane * 16u;  // record blocks: 16 bytes per lane
   half4 (&Ahat)[4] = m.Ahat;
   f32x4 (&Rhat)[4] = m.Rhat;
-  f32x4& Lab = m.Lab;
-  f32x4& Lak = m.Lak;
-  f32x4& Lrb = m.Lrb;
-  f32x4& LrkT = m.LrkT;
-  Lab = Lak = Lrb = LrkT = zero4();
+  MmaBF::acc& Lab = m.Lab;
+  MmaBF::acc& Lak = m.Lak;
+  MmaBF::acc& Lrb = m.Lrb;
+  MmaBF::acc& LrkT = m.LrkT;
+  Lab = Lak = Lrb = LrkT = MmaBF::zero();
   bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
   // time-mix: 1 / max(|kk|, 1e-12) of this lane's token (its 64 channels are spread over
   // the four lanes li, li + 16, li + 32, li + 48)
@@ -423,8 +443,8 @@ __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char
       split_bf16x2(bg[e], bg[e + 1], bhH, bhL, q8);
       split_bf16x2(kg[e], kg[e + 1], khH, khL, q8);
     }
-    const half4 BT = to_h4(Mma16::mma(bbar, eye, zero4()));  // lane (j = li, g): B-[4g+e][16kt + li]
-    const half4 KT = to_h4(Mma16::mma(kbar, eye, zero4()));
+    const half4 BT = to_h4(Mma16::mma(bbar, eye, Mma16::zero()));  // lane (j = li, g): B-[4g+e][16kt + li]
+    const half4 KT = to_h4(Mma16::mma(kbar, eye, Mma16::zero()));
     st_off<half8>(rec, (kRecBK + kt) * 1024 + lo, cat8(BT, KT));
     if (kt & 1) {
       Lab = MmaBF::mma(ahH, bhH, Lab);
@@ -444,10 +464,10 @@ __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int t = 4 * g + e;            // row of Lab, Lak, Lrb; column li is s
-    Lab[e] = li < t ? Lab[e] : 0.f;     // strictly lower
-    Lak[e] = li < t ? Lak[e] : 0.f;
-    Lrb[e] = li <= t ? Lrb[e] : 0.f;    // lower with the diagonal
-    LrkT[e] = t <= li ? LrkT[e] : 0.f;  // element (s = 4g+e, t = li) of L_rk^T
+    Lab.v[e] = li < t ? Lab.v[e] : 0.f;     // strictly lower
+    Lak.v[e] = li < t ? Lak.v[e] : 0.f;
+    Lrb.v[e] = li <= t ? Lrb.v[e] : 0.f;    // lower with the diagonal
+    LrkT.v[e] = t <= li ? LrkT.v[e] : 0.f;  // element (s = 4g+e, t = li) of L_rk^T
   }
 }
 
@@ -457,7 +477,7 @@ __device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsign
   const int li = lane & 15, g = lane >> 4;
   const uint32_t lo = (uint32_t)lane * 16u;
   const half4 eye = m.eye;
-  const f32x4 Lab = m.Lab, Lak = m.Lak, Lrb = m.Lrb, LrkT = m.LrkT;
+  const MmaBF::acc Lab = m.Lab, Lak = m.Lak, Lrb = m.Lrb, LrkT = m.LrkT;
 
   // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
   // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
@@ -469,9 +489,9 @@ __device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsign
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    lab[(4 * g + e) * 16 + li] = Lab[e];
+    lab[(4 * g + e) * 16 + li] = Lab.v[e];
     rhs[(4 * g + e) * 16 + li] = 4 * g + e == li ? 1.f : 0.f;  // identity: the rows of T
-    rhs[(16 + 4 * g + e) * 16 + li] = Lrb[e];                 // L_rb: the rows of M_r
+    rhs[(16 + 4 * g + e) * 16 + li] = Lrb.v[e];               // L_rb: the rows of M_r
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
@@ -515,23 +535,24 @@ __device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsign
   asm volatile("" ::: "memory");
 
   // ---- products, stored per block. L_rk^T is added on the vector unit (a 16x16x32
-  // Gram result is not fed to a 16x16x16 product as its accumulator).
+  // Gram result is not fed to a 16x16x16 product as its accumulator). R^ comes from the
+  // vector unit, so it may start a 16x16x16 chain.
 #pragma unroll
   for (int kp = 0; kp < 2; ++kp) {
     half4 ApT[2], RpT[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kt = 2 * kp + u;
-      const half4 AT = to_h4(Mma16::mma(m.Ahat[kt], eye, zero4()));  // lane (j = li, g): A^[4g+e][16kt + li]
-      ApT[u] = to_h4(Mma16::mma(AT, tB, zero4()));                   // lane (t = li, g): A'[t][16kt + 4g + e]
-      RpT[u] = to_h4(Mma16::mma(AT, mB, m.Rhat[kt]));                // R'[t][16kt + 4g + e]
+      const half4 AT = to_h4(Mma16::mma(m.Ahat[kt], eye, Mma16::zero()));  // lane (j = li, g): A^[4g+e][16kt + li]
+      ApT[u] = to_h4(Mma16::mma(AT, tB, Mma16::zero()));                   // lane (t = li, g): A'[t][16kt + 4g + e]
+      RpT[u] = to_h4(Mma16::mma(AT, mB, Mma16::acc{m.Rhat[kt]}));          // R'[t][16kt + 4g + e]
     }
     st_off<half8>(rec, (kRecA0 + kp) * 1024 + lo, cat8(ApT[0], ApT[1]));
     st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
   }
   const half4 LakH = to_h4(Lak);  // as an A operand: L_ak^T (M = s', K = s)
-  const half4 GuT = to_h4(Mma16::mma(LakH, tB, zero4()));     // lane (t = li, g): G_u[t][4g + e]
-  const half4 GyT = to_h4(Mma16::mma(LakH, mB, zero4()) + LrkT);  // G_y[t][4g + e]
+  const half4 GuT = to_h4(Mma16::mma(LakH, tB, Mma16::zero()));          // lane (t = li, g): G_u[t][4g + e]
+  const half4 GyT = to_h4(Mma16::mma(LakH, mB, Mma16::zero()).v + LrkT.v);  // G_y[t][4g + e]
   st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
 }
 
@@ -592,13 +613,13 @@ __device__ __forceinline__ float row_bcast(float x) {
 // come first: they do not depend on the state, so they need not wait for the previous
 // chunk's update. Y is formed transposed (operands swapped: the state and V fragments
 // serve as A operands, R' and G as B operands, from the same registers).
-__device__ __forceinline__ f32x4 scan_step(f32x4 (&St)[4], const Frag& f) {
+__device__ __forceinline__ f32x4 scan_step(Mma32::acc (&St)[4], const Frag& f) {
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
   half4 vB;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
-  f32x4 u = Mma32::mma(f.gl, cat8(vB, hz), zero4());
-  f32x4 yv = Mma32::mma(cat8(hz, vB), f.gl, zero4());
+  Mma32::acc u = Mma32::mma(f.gl, cat8(vB, hz), Mma32::zero());
+  Mma32::acc yv = Mma32::mma(cat8(hz, vB), f.gl, Mma32::zero());
   const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
   const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
   u = Mma32::mma(f.a0, sB0, u);
@@ -607,27 +628,27 @@ __device__ __forceinline__ f32x4 scan_step(f32x4 (&St)[4], const Frag& f) {
   yv = Mma32::mma(sB1, f.r1, yv);
   const half8 uv = cat8(to_h4(u), vB);
   // the decays by row broadcasts (one 4-byte LDS read per lane instead of four 16-byte ones)
-  St[0][0] *= row_bcast<0>(f.dv);
-  St[0][1] *= row_bcast<1>(f.dv);
-  St[0][2] *= row_bcast<2>(f.dv);
-  St[0][3] *= row_bcast<3>(f.dv);
+  St[0].v[0] *= row_bcast<0>(f.dv);
+  St[0].v[1] *= row_bcast<1>(f.dv);
+  St[0].v[2] *= row_bcast<2>(f.dv);
+  St[0].v[3] *= row_bcast<3>(f.dv);
   St[0] = Mma32::mma(f.bk[0], uv, St[0]);
-  St[1][0] *= row_bcast<4>(f.dv);
-  St[1][1] *= row_bcast<5>(f.dv);
-  St[1][2] *= row_bcast<6>(f.dv);
-  St[1][3] *= row_bcast<7>(f.dv);
+  St[1].v[0] *= row_bcast<4>(f.dv);
+  St[1].v[1] *= row_bcast<5>(f.dv);
+  St[1].v[2] *= row_bcast<6>(f.dv);
+  St[1].v[3] *= row_bcast<7>(f.dv);
   St[1] = Mma32::mma(f.bk[1], uv, St[1]);
-  St[2][0] *= row_bcast<8>(f.dv);
-  St[2][1] *= row_bcast<9>(f.dv);
-  St[2][2] *= row_bcast<10>(f.dv);
-  St[2][3] *= row_bcast<11>(f.dv);
+  St[2].v[0] *= row_bcast<8>(f.dv);
+  St[2].v[1] *= row_bcast<9>(f.dv);
+  St[2].v[2] *= row_bcast<10>(f.dv);
+  St[2].v[3] *= row_bcast<11>(f.dv);
   St[2] = Mma32::mma(f.bk[2], uv, St[2]);
-  St[3][0] *= row_bcast<12>(f.dv);
-  St[3][1] *= row_bcast<13>(f.dv);
-  St[3][2] *= row_bcast<14>(f.dv);
-  St[3][3] *= row_bcast<15>(f.dv);
+  St[3].v[0] *= row_bcast<12>(f.dv);
+  St[3].v[1] *= row_bcast<13>(f.dv);
+  St[3].v[2] *= row_bcast<14>(f.dv);
+  St[3].v[3] *= row_bcast<15>(f.dv);
   St[3] = Mma32::mma(f.bk[3], uv, St[3]);
-  return yv;
+  return yv.v;
 }
 
 }  // namespace chunk

@@ -145,15 +145,15 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
   // ------------------------------------------------------------------ scan waves
   __builtin_amdgcn_s_setprio(2);  // the chain of the state, ahead of the prep's work on this SIMD
   const int w = wave;
-  f32x4 St[4];  // element e of St[kt] = S[i = 16 w + li][j = 16 kt + 4 g + e]
+  Mma32::acc St[4];  // element e of St[kt] = S[i = 16 w + li][j = 16 kt + 4 g + e]
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) St[kt] = zero4();
+  for (int kt = 0; kt < 4; ++kt) St[kt] = Mma32::zero();
   if (p.s_in) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const float4 s = *reinterpret_cast<const float4*>(p.s_in + ((int64_t)unit * kN + 16 * w + li) * kN +
                                                         16 * kt + 4 * g);
-      St[kt] = f32x4{s.x, s.y, s.z, s.w};
+      St[kt] = Mma32::acc{f32x4{s.x, s.y, s.z, s.w}};
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
       *reinterpret_cast<float4*>(p.s_out + ((int64_t)unit * kN + 16 * w + li) * kN + 16 * kt + 4 * g) =
-          make_float4(St[kt][0], St[kt][1], St[kt][2], St[kt][3]);
+          make_float4(St[kt].v[0], St[kt].v[1], St[kt].v[2], St[kt].v[3]);
   }
 }
 

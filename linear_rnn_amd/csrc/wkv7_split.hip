@@ -226,15 +226,15 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
   }
 
   // element e of St[kt] = S[i = 16 rb + li][j = 16kt + 4g + e]
-  f32x4 St[4];
+  Mma32::acc St[4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) St[kt] = zero4();
+  for (int kt = 0; kt < 4; ++kt) St[kt] = Mma32::zero();
   if (p.s_src) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const float4 s = *reinterpret_cast<const float4*>(p.s_src + ((int64_t)unit * kN + 16 * rb + li) * kN +
                                                         16 * kt + 4 * g);
-      St[kt] = f32x4{s.x, s.y, s.z, s.w};
+      St[kt] = Mma32::acc{f32x4{s.x, s.y, s.z, s.w}};
     }
   }
   // vmcnt(0) as a builtin, so the compiler's own wait counting knows the state has landed
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
       *reinterpret_cast<float4*>(p.s_dst + ((int64_t)unit * kN + 16 * rb + li) * kN + 16 * kt + 4 * g) =
-          make_float4(St[kt][0], St[kt][1], St[kt][2], St[kt][3]);
+          make_float4(St[kt].v[0], St[kt].v[1], St[kt].v[2], St[kt].v[3]);
   }
 }
 
