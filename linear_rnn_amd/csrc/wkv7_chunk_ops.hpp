@@ -244,7 +244,7 @@ constexpr int kStageRow = 144;             // bytes per staged token row (128 + 
                                            // 8 apart share banks, so the token-layout reads conflict 2-way)
 constexpr int kStageT = kC * kStageRow;    // one tensor: 2,304 bytes
 constexpr int kStageBytes = 4 * kStageT;   // 9,216 bytes
-static_assert(kStageBytes <= kRecD, "staged rows end before e^gamma_15 and the record's v");
+static_assert(kStageBytes <= kRecD, "staged rows end before e^gamma_15");
 
 // r, a, b, k rows of chunk (base, nt)
 __device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, int nt, PrepRows& rows) {

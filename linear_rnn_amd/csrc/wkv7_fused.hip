@@ -108,8 +108,9 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
     // The wave's chunks are c0, c0 + kPrepW, ... Two sets of row registers alternate: the
     // r, a, b, k rows of the next chunk are loaded between the two phases of the current
     // chunk's prep, so their latency passes during its solve and products and the next
-    // slot wait (w and v, a fifth of the bytes, are loaded when the chunk starts). Past the
-    // wave's last chunk the loads repeat its last chunk (unconditional, no branch).
+    // slot wait (w, a fifth of the prep's input bytes, is loaded when the chunk starts; the
+    // scan waves load v themselves). Past the wave's last chunk the loads repeat its last
+    // chunk (unconditional, no branch).
     const int c0 = wave - kScanW;
     if (c0 >= nc) return;
     const int last = c0 + (nc - 1 - c0) / kPrepW * kPrepW;  // this wave's last chunk
