@@ -293,19 +293,52 @@ int rwkv7_tmix_step(const void *r, const float *w_raw, const void *k, const void
  *
  * Every pointer 16-byte aligned; outputs may not overlap any input or each
  * other (dstate_in == dstate_out exactly is allowed); T == 0 copies dstate_out
- * to dstate_in (zeros when NULL). The forward pass is recomputed inside: a
- * first kernel stores the state every 16 tokens, a second walks the sequence
- * backwards, rebuilding each 8-token stretch of states from its checkpoint.
- * The checkpoints (B*H*ceil(T/16) * 16 KiB) live in the per-(device, stream)
- * workspace described for rwkv7_wkv_prefill_ex, grown as needed (an
- * allocation failure, or growth during graph capture, returns RWKV7_ERR_HIP
- * before any launch). Arithmetic is float32 throughout (bfloat16 inputs widened
- * exactly); results match the float64 derivatives to float32 rounding.
+ * to dstate_in (zeros when NULL). The algorithm is RWKV7_ALGO_AUTO of
+ * rwkv7_wkv_backward_ex below: the chunked backward for bfloat16 inputs (results
+ * to the bfloat16 bar, in its decay domain), the token-by-token one otherwise.
+ * The token-by-token backward recomputes the forward pass inside: a first kernel
+ * stores the float32 state every 8 tokens, a second walks the sequence backwards,
+ * rebuilding each 8-token stretch of states from its checkpoint; arithmetic is
+ * float32 throughout (bfloat16 inputs widened exactly) and results match the
+ * float64 derivatives to float32 rounding. Either algorithm keeps its stored
+ * states in the per-(device, stream) workspace described for
+ * rwkv7_wkv_prefill_ex, grown as needed (an allocation failure, or growth during
+ * graph capture, returns RWKV7_ERR_HIP before any launch).
  */
 int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v, const void *a, const void *b,
                        const float *state_in, const float *dy, const float *dstate_out, float *dr, float *dw,
                        float *dk, float *dv, float *da, float *db, float *dstate_in, int64_t B, int64_t T,
                        int64_t H, int64_t N, int dtype, void *stream);
+
+/*
+ * rwkv7_wkv_backward with a choice of algorithm (rwkv7_wkv_backward runs
+ * RWKV7_ALGO_AUTO):
+ *   RWKV7_ALGO_SEQUENTIAL  the checkpointed token-by-token reverse pass above, float32
+ *                      throughout, any dtype (AUTO for float32 inputs and for bfloat16
+ *                      with T*H*64 >= 2^31).
+ *   RWKV7_ALGO_CHUNKED  bfloat16 inputs with T*H*64 < 2^31 (else RWKV7_ERR_ALGO); AUTO for
+ *                      them. The derivatives of the chunked prefill's chunk form, on
+ *                      16x16 MFMA tiles: a checkpoint pass of the one-kernel chunked
+ *                      prefill stores the float16 state at every 16-token chunk start; a
+ *                      second kernel carries dL/dS back through the chunks (one
+ *                      workgroup per head) and stores it, in float16, at every chunk end;
+ *                      a third forms each chunk's input gradients (one wave per chunk and
+ *                      head). Both stored arrays (B*H*ceil(T/16) * 8 KiB each) live in the
+ *                      per-(device, stream) workspace of rwkv7_wkv_prefill_ex. Intra-chunk
+ *                      operands are float16 and the state gradient is carried in float32,
+ *                      so results agree with the float64 derivatives to about 1e-3
+ *                      relative (the bfloat16 bar). Domain: that of the chunked prefill
+ *                      (decays below 2^-15 are clamped, and the gradient is that of the
+ *                      clamped function) and, since the key-scaled inputs of a chunk enter
+ *                      float16 products, every product of eight consecutive decays above
+ *                      2^-15 (every decay above 0.28; the model's soft clamp keeps decays
+ *                      above exp(-exp(-0.5)) = 0.545). Outside it, use RWKV7_ALGO_SEQUENTIAL.
+ * Any other algo: RWKV7_ERR_ALGO.
+ */
+int rwkv7_wkv_backward_ex(const void *r, const void *w, const void *k, const void *v, const void *a,
+                          const void *b, const float *state_in, const float *dy, const float *dstate_out, float *dr,
+                          float *dw, float *dk, float *dv, float *da, float *db, float *dstate_in, int64_t B,
+                          int64_t T, int64_t H, int64_t N, int dtype, int algo, void *stream);
 
 /*
  * A stack of L time-mix layers over a residual stream: the hybrid ("fast")

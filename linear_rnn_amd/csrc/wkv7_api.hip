@@ -272,10 +272,21 @@ int rwkv7_wkv_backward(const void* r, const void* w, const void* k, const void* 
                        const float* state_in, const float* dy, const float* dstate_out, float* dr, float* dw,
                        float* dk, float* dv, float* da, float* db, float* dstate_in, int64_t B, int64_t T,
                        int64_t H, int64_t N, int dtype, void* stream) {
+  return rwkv7_wkv_backward_ex(r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in, B, T,
+                               H, N, dtype, RWKV7_ALGO_AUTO, stream);
+}
+
+int rwkv7_wkv_backward_ex(const void* r, const void* w, const void* k, const void* v, const void* a,
+                          const void* b, const float* state_in, const float* dy, const float* dstate_out, float* dr,
+                          float* dw, float* dk, float* dv, float* da, float* db, float* dstate_in, int64_t B,
+                          int64_t T, int64_t H, int64_t N, int dtype, int algo, void* stream) {
   const void* in[6] = {r, w, k, v, a, b};
   float* const grad[6] = {dr, dw, dk, dv, da, db};
   const int st = validate_backward(in, state_in, dy, dstate_out, grad, dstate_in, B, T, H, N, dtype);
   if (st != RWKV7_OK) return st;
+  if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SEQUENTIAL && algo != RWKV7_ALGO_CHUNKED) return RWKV7_ERR_ALGO;
+  if (algo == RWKV7_ALGO_CHUNKED && (dtype != RWKV7_DTYPE_BF16 || T * H * 64 >= (int64_t(1) << 31)))
+    return RWKV7_ERR_ALGO;
   if (B * H == 0) return RWKV7_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -285,6 +296,15 @@ int rwkv7_wkv_backward(const void* r, const void* w, const void* k, const void* 
   }
   rwkv7::BwdCall c{{r, w, k, v, a, b}, state_in, dy, dstate_out, {dr, dw, dk, dv, da, db}, dstate_in, B, T, H,
                    dtype, s};
+  // AUTO: the chunked backward for bfloat16 inputs inside its domain (as the prefill's AUTO),
+  // the float32 token-by-token one otherwise
+  if (algo == RWKV7_ALGO_AUTO && dtype == RWKV7_DTYPE_BF16 && T * H * 64 < (int64_t(1) << 31))
+    algo = RWKV7_ALGO_CHUNKED;
+  if (algo == RWKV7_ALGO_CHUNKED) {
+    e = rwkv7::launch_backward_chunked(c);
+    if (e == hipErrorNotSupported) return RWKV7_ERR_ALGO;
+    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+  }
   e = rwkv7::launch_backward(c);
   if (e == hipErrorNotSupported) return RWKV7_ERR_SHAPE;
   return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;

@@ -316,11 +316,12 @@ struct PrepMid {
 // record (device memory or LDS); written as nine 1 KiB blocks, 16 bytes per lane, plus
 // e^{gamma_15}. rec may hold fac at its start (see above).
 //
-// Phase 1: decay factors, operands, the four Grams; B-, K- and e^{gamma_15} stored.
+// The decay factor rows of a chunk into fac (kFacBytes), e^{gamma_15} (64 floats) at
+// e15; tokens past the end of the sequence become identity tokens in x.
 template <int MODE>
-__device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char* rec, PrepMid& m) {
+__device__ __forceinline__ void prep_factors(PrepRaw& x, float* fac, unsigned char* e15) {
   const int lane = threadIdx.x & 63;
-  const int li = lane & 15, g = lane >> 4;
+  const int li = lane & 15;
   const int nt = x.nt;
   const bool live = li < nt;
 
@@ -366,10 +367,18 @@ __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char
         fac[(7 - q) * kFacRow + j] = gd;
       }
     }
-    st_off<float>(rec, (uint32_t)(kRecD + 4 * j), e);  // e^{gamma_15}
+    st_off<float>(e15, (uint32_t)(4 * j), e);  // e^{gamma_15}
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS before other lanes read them
   __builtin_amdgcn_wave_barrier();
+}
+
+// Phase 1: decay factors, operands, the four Grams; B-, K- and e^{gamma_15} stored.
+template <int MODE>
+__device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char* rec, PrepMid& m) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+  prep_factors<MODE>(x, fac, rec + kRecD);
 
   // ---- token layout: operands, the four Grams and B-, K- (stored at once). Key 16kt + 4g + e
   // of the lane's token. Each Gram contracts 64 keys on 16x16x32 bfloat16 MFMAs as
@@ -471,13 +480,16 @@ __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char
   }
 }
 
-// Phase 2: T, M_r and the products A', R', G_u, G_y, stored.
-__device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsigned char* rec) {
+// T = (I - L_ab)^{-1} and M_r = L_rb T of a chunk, by float32 back substitution in fac
+// (the factor rows are no longer read). Returns them as float16 fragments: lane (li, g)
+// holds T[li][4g + e] in tB and M_r[li][4g + e] in mB (T^T and M_r^T as B operands, T
+// and M_r as A operands). Every LDS access of the solve has completed on return.
+struct TmFrags {
+  half4 tB, mB;
+};
+__device__ __forceinline__ TmFrags prep_solve(const MmaBF::acc Lab, const MmaBF::acc Lrb, float* fac) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
-  const uint32_t lo = (uint32_t)lane * 16u;
-  const half4 eye = m.eye;
-  const MmaBF::acc Lab = m.Lab, Lak = m.Lak, Lrb = m.Lrb, LrkT = m.LrkT;
 
   // ---- rows of T = (I - L_ab)^{-1} (lanes 0-15) and M_r = L_rb T (lanes 16-31):
   // x (I - L_ab) = rhs, solved right-looking: once x[s2] is final it is folded into
@@ -533,6 +545,17 @@ __device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsign
   // scratch is the record's own start)
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
+  return TmFrags{tB, mB};
+}
+
+// Phase 2: T, M_r and the products A', R', G_u, G_y, stored.
+__device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsigned char* rec) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = (uint32_t)lane * 16u;
+  const half4 eye = m.eye;
+  const MmaBF::acc Lak = m.Lak, LrkT = m.LrkT;
+  const TmFrags tm = prep_solve(m.Lab, m.Lrb, fac);
+  const half4 tB = tm.tB, mB = tm.mB;
 
   // ---- products, stored per block. L_rk^T is added on the vector unit (a 16x16x32
   // Gram result is not fed to a 16x16x16 product as its accumulator). R^ comes from the
@@ -613,19 +636,22 @@ __device__ __forceinline__ float row_bcast(float x) {
 // come first: they do not depend on the state, so they need not wait for the previous
 // chunk's update. Y is formed transposed (operands swapped: the state and V fragments
 // serve as A operands, R' and G as B operands, from the same registers).
+// Y = false skips the readout (the state alone is carried; zero is returned).
+template <bool Y = true>
 __device__ __forceinline__ f32x4 scan_step(Mma32::acc (&St)[4], const Frag& f) {
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
   half4 vB;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vB[e] = (_Float16)bfw(f.v[e]);
   Mma32::acc u = Mma32::mma(f.gl, cat8(vB, hz), Mma32::zero());
-  Mma32::acc yv = Mma32::mma(cat8(hz, vB), f.gl, Mma32::zero());
+  Mma32::acc yv = Mma32::zero();
+  if constexpr (Y) yv = Mma32::mma(cat8(hz, vB), f.gl, yv);
   const half8 sB0 = cat8(to_h4(St[0]), to_h4(St[1]));
   const half8 sB1 = cat8(to_h4(St[2]), to_h4(St[3]));
   u = Mma32::mma(f.a0, sB0, u);
-  yv = Mma32::mma(sB0, f.r0, yv);
+  if constexpr (Y) yv = Mma32::mma(sB0, f.r0, yv);
   u = Mma32::mma(f.a1, sB1, u);
-  yv = Mma32::mma(sB1, f.r1, yv);
+  if constexpr (Y) yv = Mma32::mma(sB1, f.r1, yv);
   const half8 uv = cat8(to_h4(u), vB);
   // the decays by row broadcasts (one 4-byte LDS read per lane instead of four 16-byte ones)
   St[0].v[0] *= row_bcast<0>(f.dv);
@@ -649,6 +675,23 @@ __device__ __forceinline__ f32x4 scan_step(Mma32::acc (&St)[4], const Frag& f) {
   St[3].v[3] *= row_bcast<15>(f.dv);
   St[3] = Mma32::mma(f.bk[3], uv, St[3]);
   return yv.v;
+}
+
+// ====================================================================== checkpoints
+// A 64x64 state (or state gradient) in float16, [row i][key j], stored in the order
+// in which MFMA fragments read it: row-major over rows, and within a row the 64 keys
+// as [kp][g][h][e] with key = 16 (2 kp + h) + 4 g + e. Lane (li, g) of a wave that owns
+// rows i0 .. i0 + 15 (element e of tile kt holding key 16 kt + 4 g + e of row i0 + li)
+// writes and reads its 8 keys of each kp as one 16-byte piece.
+constexpr int kCkHalves = kN * kN;  // 8 KiB per state
+__device__ __forceinline__ uint32_t ck_off(int row, int kp, int g) { return (uint32_t)(row * kN + kp * 32 + g * 8); }
+template <int F>
+__device__ __forceinline__ void ck_store(_Float16* dst, int i0, const Acc<F> (&tile)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp)
+    *reinterpret_cast<half8*>(dst + ck_off(i0 + li, kp, g)) = cat8(to_h4(tile[2 * kp]), to_h4(tile[2 * kp + 1]));
 }
 
 }  // namespace chunk

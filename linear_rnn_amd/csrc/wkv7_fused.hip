@@ -53,6 +53,7 @@ struct FusedParams {
   float* y;
   const float* s_in;  // may be null (zero state)
   float* s_out;       // may be null
+  _Float16* ck;       // checkpoint form only: the state at every chunk start (kCkHalves each)
   int32_t nc;         // chunks per sequence
 };
 
@@ -86,7 +87,9 @@ __device__ __forceinline__ void post(int* flag, int value) {
   __atomic_store_n(flag, value, __ATOMIC_RELAXED);
 }
 
-template <int MODE>
+// CK: the checkpoint form used by the backward. It stores, for every chunk, the
+// float16 state the chunk's products start from (ck_store) and writes no y.
+template <int MODE, bool CK = false>
 __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
   extern __shared__ __align__(16) unsigned char ring[];
   const int lane = threadIdx.x & 63;
@@ -190,17 +193,20 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
     read_frag(slot_of(cn), nxt);
 #pragma unroll
     for (int e = 0; e < 4; ++e) cur.v[e] = vc[e];
-    const f32x4 yv = scan_step(St, cur);
+    if constexpr (CK) ck_store(p.ck + ((int64_t)unit * nc + c) * kCkHalves, 16 * w, St);
+    const f32x4 yv = scan_step<!CK>(St, cur);
     load_v(min(c + 2, nc - 1), vc);
-    // y through the wave's tile: written as lane (token li, values 4g..), read as lane
-    // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before the
-    // previous post (its wait covers every LDS access of this wave).
-    st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    const float4 yq = ld_off<float4>(ytile, (uint32_t)((lane >> 2) * kYRow + 16 * (lane & 3)));
-    const int t = c * kC + (lane >> 2);
-    if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
+    if constexpr (!CK) {
+      // y through the wave's tile: written as lane (token li, values 4g..), read as lane
+      // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before the
+      // previous post (its wait covers every LDS access of this wave).
+      st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      const float4 yq = ld_off<float4>(ytile, (uint32_t)((lane >> 2) * kYRow + 16 * (lane & 3)));
+      const int t = c * kC + (lane >> 2);
+      if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
+    }
     post(&consumed[w], cn + 1);  // every fragment up to chunk cn is in registers
     ++c;
     return c < nc;
@@ -215,9 +221,9 @@ __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
   }
 }
 
-template <int MODE>
+template <int MODE, bool CK = false>
 hipError_t launch_fused(const FusedParams& fp, int64_t units, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&wkv7_fused_kernel<MODE>);
+  const void* fn = reinterpret_cast<const void*>(&wkv7_fused_kernel<MODE, CK>);
   static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return attr;
   FusedParams q = fp;
@@ -248,6 +254,24 @@ hipError_t launch_chunked(const WkvCall& c) {
   fp.s_out = static_cast<float*>(c.s_out);
   fp.nc = (int32_t)((c.T + kC - 1) / kC);
   return launch_fused<kPrepPlain>(fp, c.B * c.H, c.stream);
+}
+
+hipError_t launch_chunked_ckpt(const WkvCall& c, _Float16* ck) {
+  if (c.dtype != 1 || !fused_domain(c.T, c.H)) return hipErrorNotSupported;
+  FusedParams fp{};
+  fp.in.r = static_cast<const uint16_t*>(c.in[0]);
+  fp.in.w = static_cast<const uint16_t*>(c.in[1]);
+  fp.in.k = static_cast<const uint16_t*>(c.in[2]);
+  fp.in.a = static_cast<const uint16_t*>(c.in[4]);
+  fp.in.b = static_cast<const uint16_t*>(c.in[5]);
+  fp.in.T = (int32_t)c.T;
+  fp.in.H = (int32_t)c.H;
+  fp.v = static_cast<const uint16_t*>(c.in[3]);
+  fp.s_in = static_cast<const float*>(c.s_in);
+  fp.s_out = static_cast<float*>(c.s_out);
+  fp.ck = ck;
+  fp.nc = (int32_t)((c.T + kC - 1) / kC);
+  return launch_fused<kPrepPlain, true>(fp, c.B * c.H, c.stream);
 }
 
 hipError_t launch_tmix_fused(const TmixCall& c) {

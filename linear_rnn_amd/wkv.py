@@ -34,6 +34,7 @@ RWKV7_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("rwkv7_wkv_prefill", "rwkv7_wkv_step", "rwkv7_wkv_step_q", "rwkv7_wkv_prefill_ex",
             "rwkv7_tmix_prefill", "rwkv7_tmix_prefill_ex", "rwkv7_tmix_step", "rwkv7_wkv_backward",
+            "rwkv7_wkv_backward_ex",
             "rwkv7_stack_forward", "rwkv7_wkv_prefill_algo", "rwkv7_wkv_prefill_noalloc",
             "rwkv7_wkv_strerror")
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
             L.rwkv7_tmix_prefill_ex.argtypes = [vp] * 11 + [i64] * 4 + [ci, ci, vp]
             L.rwkv7_wkv_backward.restype = ci
             L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [i64] * 4 + [ci, vp]
+            L.rwkv7_wkv_backward_ex.restype = ci
+            L.rwkv7_wkv_backward_ex.argtypes = [vp] * 16 + [i64] * 4 + [ci, ci, vp]
             L.rwkv7_stack_forward.restype = ci
             L.rwkv7_stack_forward.argtypes = [vp] * 5 + [i64] * 5 + [ci, vp]
             L.rwkv7_wkv_prefill_algo.restype = ci
@@ -296,6 +299,13 @@ def tmix(r, w_raw, k, v, kk, a_lr, ln_w=None, ln_b=None, state_in=None, want_sta
 def rwkv7_wkv_backward(r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in,
                        stream=None):
     """Gradients of the recurrence: dr..db ([B,T,H,64] float32) and dstate_in ([B,H,64,64] float32 or None)."""
+    rwkv7_wkv_backward_ex(r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in,
+                          RWKV7_ALGO_AUTO, stream)
+
+
+def rwkv7_wkv_backward_ex(r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in,
+                          algo=RWKV7_ALGO_AUTO, stream=None):
+    """rwkv7_wkv_backward with an explicit algorithm (RWKV7_ALGO_AUTO / _SEQUENTIAL / _CHUNKED)."""
     import torch
     if not isinstance(r, torch.Tensor) or r.dim() != 4:
         raise ValueError("r must be a [B, T, H, N] tensor")
@@ -311,18 +321,19 @@ def rwkv7_wkv_backward(r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, d
     _expect(dstate_in, "dstate_in", (B, H, N, N), _f32(), r, optional=True)
     _on_gpu(r, stream)
     args = [_ptr(x) for x in (r, w, k, v, a, b, state_in, dy, dstate_out, dr, dw, dk, dv, da, db, dstate_in)]
-    _check(lib().rwkv7_wkv_backward(*args, B, T, H, N, _dtype_code(r), _stream(stream)))
+    _check(lib().rwkv7_wkv_backward_ex(*args, B, T, H, N, _dtype_code(r), int(algo), _stream(stream)))
 
 
-def wkv7_backward(r, w, k, v, a, b, dy, state_in=None, dstate_out=None, want_dstate=True, stream=None):
+def wkv7_backward(r, w, k, v, a, b, dy, state_in=None, dstate_out=None, want_dstate=True, stream=None,
+                  algo=RWKV7_ALGO_AUTO):
     """Allocate the gradients, run the backward, return dict dr, dw, dk, dv, da, db, dstate_in."""
     import torch
     B, T, H, N = r.shape
     out = {n: torch.empty((B, T, H, N), dtype=torch.float32, device=r.device)
            for n in ("dr", "dw", "dk", "dv", "da", "db")}
     out["dstate_in"] = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device) if want_dstate else None
-    rwkv7_wkv_backward(r, w, k, v, a, b, state_in, dy, dstate_out, *(out[n] for n in
-                       ("dr", "dw", "dk", "dv", "da", "db", "dstate_in")), stream=stream)
+    rwkv7_wkv_backward_ex(r, w, k, v, a, b, state_in, dy, dstate_out, *(out[n] for n in
+                          ("dr", "dw", "dk", "dv", "da", "db", "dstate_in")), algo=algo, stream=stream)
     return out
 
 
