@@ -18,16 +18,19 @@
 //
 // Three kernels:
 //   1. the one-kernel chunked prefill in its checkpoint form stores the float16 state at
-//      every chunk start (wkv7_fused.hip);
-//   2. wkv7_bchain_kernel, one workgroup per head: prep waves rebuild each chunk's
-//      chain record (B-, L_rb^T, T^T, [R^^T | A^^T], e^{gamma_15}) into an LDS ring,
-//      last chunk first; scan waves carry G in float32 back through the chunks, store
-//      each chunk's end G (float16) and finally dL/dS_0;
+//      every chunk start (wkv7_fused.hpp);
+//   2. the chain, one workgroup per head: prep waves rebuild each chunk's chain record
+//      (B-, L_rb^T, T^T, [R^^T | A^^T], e^{gamma_15}) into an LDS ring, last chunk
+//      first; scan waves carry G in float32 back through the chunks, store each chunk's
+//      end G (float16) and finally dL/dS_0.
+//   1 and 2 need only the inputs and dY, so one launch (wkv7_bpass_kernel) runs both,
+//   a workgroup per head for each;
 //   3. wkv7_bgrad_kernel, one wave per (head, chunk) over the whole chip, forms the
 //      chunk's input gradients from its inputs, dY, S0 and end G.
 #include <cstdint>
 
 #include "wkv7_chunk_ops.hpp"
+#include "wkv7_fused.hpp"
 #include "wkv7_internal.hpp"
 
 namespace rwkv7 {
@@ -136,13 +139,18 @@ __device__ __forceinline__ void chain_prep(PrepRaw& x, unsigned char* rec) {
   st_off<half8>(rec, kCbLrb * 1024 + lo, cat8(to_h4(Lrb), hz));  // lane (tau = li, g): L_rb[4g + e][tau]
 }
 
-constexpr int kScanW = 4;
-constexpr int kPrepW = 8;
-constexpr int kRing = 10;
+// The chain's workgroup has the shape of the one-kernel prefill's (fused::kScanW scan
+// waves, fused::kPrepW prep waves, the same hand-off and bounded waits), with a ring of
+// chain records.
+using fused::kScanW;
+using fused::kPrepW;
+using fused::kRing;
+using fused::kThreads;
+using fused::post;
+using fused::wait_all_at_least;
+using fused::wait_at_least;
 constexpr int kCtrlOff = kRing * kCbBytes;
 constexpr int kLds = kCtrlOff + 4 * (kRing + kScanW);
-constexpr int kThreads = 64 * (kScanW + kPrepW);
-constexpr int kSpinMax = 1 << 20;
 static_assert(kLds <= 160 * 1024, "LDS per compute unit");
 
 struct ChainParams {
@@ -154,43 +162,14 @@ struct ChainParams {
   int32_t nc;
 };
 
-__device__ __forceinline__ int lds_peek(const int* p) {
-  return __builtin_amdgcn_readfirstlane(__atomic_load_n(p, __ATOMIC_RELAXED));
-}
-__device__ __forceinline__ void wait_at_least(const int* flag, int target) {
-#pragma clang loop unroll(disable)
-  for (int n = 0; n < kSpinMax; ++n) {
-    if (lds_peek(flag) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_all_at_least(const int* flags, int target) {
-#pragma clang loop unroll(disable)
-  for (int n = 0; n < kSpinMax; ++n) {
-    int m = lds_peek(flags);
-#pragma unroll
-    for (int w = 1; w < kScanW; ++w) m = min(m, lds_peek(flags + w));
-    if (m >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void post(int* flag, int value) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __atomic_store_n(flag, value, __ATOMIC_RELAXED);
-}
-
 // Chunks are taken last first: step q handles chunk nc - 1 - q. The hand-off is that
 // of the one-kernel prefill (wkv7_fused.hip): ready[slot] = the last step whose record
 // is complete there, consumed[w] = the steps whose fragments scan wave w holds; the
 // smallest unfinished step never waits on a later one, and every wait is bounded.
-__global__ __launch_bounds__(kThreads) void wkv7_bchain_kernel(ChainParams p) {
-  extern __shared__ __align__(16) unsigned char ring[];
+__device__ __forceinline__ void chain_body(const ChainParams& p, unsigned char* ring, int unit) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, g = lane >> 4;
-  const int unit = blockIdx.x;
   const int H = p.in.H, T = p.in.T, nc = p.nc;
   const int bb = unit / H, hh = unit % H;
   const uint32_t tstride = (uint32_t)H * kN;
@@ -314,13 +293,27 @@ __global__ __launch_bounds__(kThreads) void wkv7_bchain_kernel(ChainParams p) {
   }
 }
 
-hipError_t launch_chain(const ChainParams& cp, int64_t units, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&wkv7_bchain_kernel);
-  static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+// The two passes that need only the inputs, in one launch: workgroups [0, units) run the
+// checkpoint form of the one-kernel prefill, workgroups [units, 2 units) the chain, so
+// the two run side by side when there are fewer heads than compute units.
+constexpr int kPassLds = fused::kLds > kLds ? fused::kLds : kLds;
+__global__ __launch_bounds__(kThreads) void wkv7_bpass_kernel(fused::FusedParams fp, ChainParams cp, int32_t units) {
+  extern __shared__ __align__(16) unsigned char ring[];
+  if ((int)blockIdx.x < units)
+    fused::fused_body<kPrepPlain, true>(fp, ring, blockIdx.x);
+  else
+    chain_body(cp, ring, blockIdx.x - units);
+}
+
+hipError_t launch_pass(const fused::FusedParams& fp, const ChainParams& cp, int64_t units, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&wkv7_bpass_kernel);
+  static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kPassLds);
   if (attr != hipSuccess) return attr;
+  fused::FusedParams f = fp;
   ChainParams q = cp;
-  void* args[] = {&q};
-  return hipLaunchKernel(fn, dim3((uint32_t)units), dim3(kThreads), args, kLds, stream);
+  int32_t u = (int32_t)units;
+  void* args[] = {&f, &q, &u};
+  return hipLaunchKernel(fn, dim3((uint32_t)(2 * units)), dim3(kThreads), args, kPassLds, stream);
 }
 
 // ============================================================================ gradients
@@ -365,20 +358,30 @@ __device__ __forceinline__ half4 f2h(float4 v) {
 __device__ __forceinline__ half4 b2h(uint2 q) {
   return half4{(_Float16)bf4(q, 0), (_Float16)bf4(q, 1), (_Float16)bf4(q, 2), (_Float16)bf4(q, 3)};
 }
-// 16-lane (one row of the wave) sum and suffix sum
+// Row (16-lane) data movement by DPP: lane li of a row reads lane li + N of the same row
+// (zero past its end), or lane (li + N) mod 16.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, true));
+}
+// sum over the row, in every lane of it
 __device__ __forceinline__ float row_sum16(float x) {
-  x += __shfl_xor(x, 1, 16);
-  x += __shfl_xor(x, 2, 16);
-  x += __shfl_xor(x, 4, 16);
-  x += __shfl_xor(x, 8, 16);
+  x += row_ror<1>(x);
+  x += row_ror<2>(x);
+  x += row_ror<4>(x);
+  x += row_ror<8>(x);
   return x;
 }
-__device__ __forceinline__ float row_suffix16(float x, int li) {
-#pragma unroll
-  for (int d = 1; d < 16; d *= 2) {
-    const float y = __shfl_down(x, d, 16);
-    x += li + d < 16 ? y : 0.f;
-  }
+// sum over lanes li .. 15 of the row
+__device__ __forceinline__ float row_suffix16(float x) {
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
   return x;
 }
 
@@ -580,24 +583,39 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   float* dkp = p.grad[2] + base;
   float* dap = p.grad[4] + base;
   float* dbp = p.grad[5] + base;
+  // the pieces a key tile reads from memory: its 16 x 16 blocks of S0 and G (row vectors,
+  // 8 bytes per lane and row tile) and the raw r, a, b, k (token layout; zero past the end
+  // of the sequence); loaded one key tile ahead
+  struct KtIn {
+    half4 s[4], g[4];
+    uint2 r, a, b, k;
+  };
+  auto kt_load = [&](int kt, KtIn& q) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const uint32_t o = ck_off(16 * rt + li, kt >> 1, g) + 4 * (kt & 1);
+      q.s[rt] = *reinterpret_cast<const half4*>(s0p + o);
+      q.g[rt] = *reinterpret_cast<const half4*>(gp + o);
+    }
+    const uint32_t ro = (uint32_t)(tl * tstride + 16 * kt + 4 * g) * 2u;
+    const uint2 z2 = make_uint2(0u, 0u);
+    q.r = li < nt ? ld_off<uint2>(p.in.r + base, ro) : z2;
+    q.a = li < nt ? ld_off<uint2>(p.in.a + base, ro) : z2;
+    q.b = li < nt ? ld_off<uint2>(p.in.b + base, ro) : z2;
+    q.k = li < nt ? ld_off<uint2>(p.in.k + base, ro) : z2;
+  };
+  KtIn kin[2];
+  kt_load(0, kin[0]);
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    // S0 and G tiles of key tile kt as column vectors over the rows (lane key 16 kt + li),
-    // from the row vectors of its four row tiles (8-byte pieces of the stored states)
+    const KtIn& cur = kin[kt & 1];
+    if (kt < 3) kt_load(kt + 1, kin[(kt + 1) & 1]);
+    // S0 and G tiles of key tile kt as column vectors over the rows (lane key 16 kt + li)
     half8 sC[2], gC[2];
-    {
-      half4 sq[4], gq4[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const uint32_t o = ck_off(16 * rt + li, kt >> 1, g) + 4 * (kt & 1);
-        sq[rt] = *reinterpret_cast<const half4*>(s0p + o);
-        gq4[rt] = *reinterpret_cast<const half4*>(gp + o);
-      }
-#pragma unroll
-      for (int rp = 0; rp < 2; ++rp) {
-        sC[rp] = cat8(tr16(sq[2 * rp], eye), tr16(sq[2 * rp + 1], eye));
-        gC[rp] = cat8(tr16(gq4[2 * rp], eye), tr16(gq4[2 * rp + 1], eye));
-      }
+    for (int rp = 0; rp < 2; ++rp) {
+      sC[rp] = cat8(tr16(cur.s[2 * rp], eye), tr16(cur.s[2 * rp + 1], eye));
+      gC[rp] = cat8(tr16(cur.g[2 * rp], eye), tr16(cur.g[2 * rp + 1], eye));
     }
     // sum over rows of S0 G for key 16 kt + li, times e^{gamma_15}, to the exchange
     {
@@ -643,20 +661,13 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
       dk[e] = iq * pk.v[e] + el(g15, e) * iq * vg.v[e];
       hv[e] = (float)bbar[kt][e] * ug.v[e] + (float)kbar[kt][e] * vg.v[e];
     }
-    // the raw inputs of this key tile in the token layout (zero past the end of the sequence)
-    const uint32_t ro = (uint32_t)(tl * tstride + col) * 2u;
-    const uint2 z2 = make_uint2(0u, 0u);
-    const uint2 rq = li < nt ? ld_off<uint2>(p.in.r + base, ro) : z2;
-    const uint2 aq = li < nt ? ld_off<uint2>(p.in.a + base, ro) : z2;
-    const uint2 bq = li < nt ? ld_off<uint2>(p.in.b + base, ro) : z2;
-    const uint2 kq = li < nt ? ld_off<uint2>(p.in.k + base, ro) : z2;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float an = __shfl_down(bf4(aq, e) * da[e], 1, 16);  // a_{t+1} da_{t+1}
-      dg[e] = bf4(rq, e) * dr[e] - bf4(bq, e) * db[e] - bf4(kq, e) * dk[e] + (li < kC - 1 ? an : 0.f);
+      const float an = row_shl<1>(bf4(cur.a, e) * da[e]);  // a_{t+1} da_{t+1} (zero at t = 15)
+      dg[e] = bf4(cur.r, e) * dr[e] - bf4(cur.b, e) * db[e] - bf4(cur.k, e) * dk[e] + an;
       const float tot = row_sum16(hv[e]) + el(e1, e);  // the chunk end's share, for every token
-      const float w = el(gq, e) * __builtin_amdgcn_rcpf(el(gqm1, e));
-      dg[e] = (row_suffix16(dg[e], li) + tot) / w;
+      // dw = dlog w / w, 1 / w = Gq_{t-1} / Gq_t
+      dg[e] = (row_suffix16(dg[e]) + tot) * el(gqm1, e) * __builtin_amdgcn_rcpf(el(gq, e));
     }
     if (li < nt) {
       const uint32_t o = (uint32_t)(li * tstride + col) * 4u;
@@ -690,12 +701,19 @@ hipError_t launch_backward_chunked(const BwdCall& c) {
   if (e != hipSuccess) return e;
   _Float16* s0 = static_cast<_Float16*>(ws);
   _Float16* gend = reinterpret_cast<_Float16*>(static_cast<char*>(ws) + ck_bytes);
-  // 1. the chunk start states
-  WkvCall f{{c.in[0], c.in[1], c.in[2], c.in[3], c.in[4], c.in[5]}, c.s_in, nullptr, nullptr, c.B, c.T, c.H,
-            c.dtype, 0, c.stream};
-  e = launch_chunked_ckpt(f, s0);
-  if (e != hipSuccess) return e;
-  // 2. the chain of state gradients
+  // 1. the chunk start states and 2. the chain of state gradients, side by side
+  fused::FusedParams fp{};
+  fp.in.r = static_cast<const uint16_t*>(c.in[0]);
+  fp.in.w = static_cast<const uint16_t*>(c.in[1]);
+  fp.in.k = static_cast<const uint16_t*>(c.in[2]);
+  fp.in.a = static_cast<const uint16_t*>(c.in[4]);
+  fp.in.b = static_cast<const uint16_t*>(c.in[5]);
+  fp.in.T = (int32_t)c.T;
+  fp.in.H = (int32_t)c.H;
+  fp.v = static_cast<const uint16_t*>(c.in[3]);
+  fp.s_in = c.s_in;
+  fp.ck = s0;
+  fp.nc = (int32_t)nc;
   ChainParams cp{};
   cp.in.r = static_cast<const uint16_t*>(c.in[0]);
   cp.in.w = static_cast<const uint16_t*>(c.in[1]);
@@ -709,7 +727,7 @@ hipError_t launch_backward_chunked(const BwdCall& c) {
   cp.ds_in = c.ds_in;
   cp.gend = gend;
   cp.nc = (int32_t)nc;
-  e = launch_chain(cp, units, c.stream);
+  e = launch_pass(fp, cp, units, c.stream);
   if (e != hipSuccess) return e;
   // 3. the input gradients, one wave per (head, chunk)
   GradParams gp{};

@@ -22,203 +22,19 @@
 // so a wave never spins forever even if the protocol were broken.
 #include <cstdint>
 
-#include "wkv7_chunk_ops.hpp"
+#include "wkv7_fused.hpp"
 #include "wkv7_internal.hpp"
 
 namespace rwkv7 {
 namespace {
 
 using namespace chunk;
+using namespace fused;
 
-constexpr int kScanW = 4;                    // scan waves (16 value rows each)
-constexpr int kPrepW = 8;                    // prep waves (one chunk each at a time)
-constexpr int kRing = 10;                    // record slots
-constexpr int kSlot = kRecBytes;             // 9,472 bytes (a scan wave loads its v itself)
-// y of a scan wave's chunk passes through an LDS tile of its own, [token][16 values] float32
-// with 80-byte rows, so that its stores cover 4 tokens per quarter-wave instead of 16
-constexpr int kYRow = 80;
-constexpr int kYTile = kC * kYRow;           // 1,280 bytes per scan wave
-constexpr int kYOff = kRing * kSlot;
-constexpr int kCtrlOff = kYOff + kScanW * kYTile;  // ready[kRing], then consumed[kScanW]
-constexpr int kLds = kCtrlOff + 4 * (kRing + kScanW);
-constexpr int kThreads = 64 * (kScanW + kPrepW);
-constexpr int kSpinMax = 1 << 20;            // polls of 100-200 cycles: well over any legitimate wait
-static_assert(kRing >= 3, "the scan reads one chunk ahead");
-static_assert(kLds <= 160 * 1024, "LDS per compute unit");
-static_assert(kRecBytes % 16 == 0 && kSlot % 16 == 0, "16-byte record blocks");
-
-struct FusedParams {
-  PrepIn in;  // r, w (or w_raw), k, a (or kk), b (or a_lr), T, H
-  const uint16_t* v;
-  float* y;
-  const float* s_in;  // may be null (zero state)
-  float* s_out;       // may be null
-  _Float16* ck;       // checkpoint form only: the state at every chunk start (kCkHalves each)
-  int32_t nc;         // chunks per sequence
-};
-
-__device__ __forceinline__ int lds_peek(const int* p) {
-  return __builtin_amdgcn_readfirstlane(__atomic_load_n(p, __ATOMIC_RELAXED));
-}
-// Waits until *flag >= target, then orders every later memory access after the wait.
-__device__ __forceinline__ void wait_at_least(const int* flag, int target) {
-#pragma clang loop unroll(disable)
-  for (int n = 0; n < kSpinMax; ++n) {
-    if (lds_peek(flag) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-}
-// Waits until every one of the kScanW words at flags is >= target.
-__device__ __forceinline__ void wait_all_at_least(const int* flags, int target) {
-#pragma clang loop unroll(disable)
-  for (int n = 0; n < kSpinMax; ++n) {
-    int m = lds_peek(flags);
-#pragma unroll
-    for (int w = 1; w < kScanW; ++w) m = min(m, lds_peek(flags + w));
-    if (m >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-}
-// Publishes value once every earlier LDS access of this wave has completed.
-__device__ __forceinline__ void post(int* flag, int value) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __atomic_store_n(flag, value, __ATOMIC_RELAXED);
-}
-
-// CK: the checkpoint form used by the backward. It stores, for every chunk, the
-// float16 state the chunk's products start from (ck_store) and writes no y.
 template <int MODE, bool CK = false>
 __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
   extern __shared__ __align__(16) unsigned char ring[];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, g = lane >> 4;
-  const int unit = blockIdx.x;
-  const int H = p.in.H, T = p.in.T, nc = p.nc;
-  const int bb = unit / H, hh = unit % H;
-  const uint32_t tstride = (uint32_t)H * kN;  // elements between tokens
-  const int64_t seq_base = (int64_t)bb * T * H * kN + (int64_t)hh * kN;  // element offset of (bb, 0, hh, 0)
-  int* ready = reinterpret_cast<int*>(ring + kCtrlOff);
-  int* consumed = ready + kRing;
-  if (threadIdx.x < kRing) ready[threadIdx.x] = -1;
-  if (threadIdx.x < kScanW) consumed[threadIdx.x] = 0;
-  __syncthreads();
-
-  if (wave >= kScanW) {
-    // ---------------------------------------------------------------- prep waves
-    // The wave's chunks are c0, c0 + kPrepW, ... Two sets of row registers alternate: the
-    // r, a, b, k rows of the next chunk are loaded between the two phases of the current
-    // chunk's prep, so their latency passes during its solve and products and the next
-    // slot wait (w, a fifth of the prep's input bytes, is loaded when the chunk starts; the
-    // scan waves load v themselves). Past the wave's last chunk the loads repeat its last
-    // chunk (unconditional, no branch).
-    const int c0 = wave - kScanW;
-    if (c0 >= nc) return;
-    const int last = c0 + (nc - 1 - c0) / kPrepW * kPrepW;  // this wave's last chunk
-    auto nt_of = [&](int c) { return min(kC, T - c * kC); };
-    auto base_of = [&](int c) { return seq_base + (int64_t)c * kC * tstride; };
-    // one chunk; returns false after the wave's last chunk
-    auto item = [&](int& c, PrepRows& cur, PrepRows& nxt) {
-      const int slot = c % kRing;
-      unsigned char* rec = ring + slot * kSlot;
-      const int nt = nt_of(c);
-      const int64_t base = base_of(c);
-      PrepRaw x;
-      prep_load_w<MODE>(p.in, base, nt, x);
-      wait_all_at_least(consumed, c - kRing + 1);  // the slot's previous chunk has been read
-      prep_rows_to_raw(cur, rec, x);               // the slot's start stages the rows
-      PrepMid m;
-      prep_grams<MODE>(x, reinterpret_cast<float*>(rec), rec, m);
-      const int cn = min(c + kPrepW, last);
-      prep_load_rows(p.in, base_of(cn), nt_of(cn), nxt);
-      prep_finish(m, reinterpret_cast<float*>(rec), rec);
-      post(&ready[slot], c);
-      c += kPrepW;
-      return c < nc;
-    };
-    PrepRows ra, rb;
-    prep_load_rows(p.in, base_of(c0), nt_of(c0), ra);
-    int c = c0;
-    while (item(c, ra, rb) && item(c, rb, ra)) {
-    }
-    return;
-  }
-
-  // ------------------------------------------------------------------ scan waves
-  __builtin_amdgcn_s_setprio(2);  // the chain of the state, ahead of the prep's work on this SIMD
-  const int w = wave;
-  Mma32::acc St[4];  // element e of St[kt] = S[i = 16 w + li][j = 16 kt + 4 g + e]
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) St[kt] = Mma32::zero();
-  if (p.s_in) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const float4 s = *reinterpret_cast<const float4*>(p.s_in + ((int64_t)unit * kN + 16 * w + li) * kN +
-                                                        16 * kt + 4 * g);
-      St[kt] = Mma32::acc{f32x4{s.x, s.y, s.z, s.w}};
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
-  // stores: lane l writes token l / 4 of the chunk, values 16 w + 4 (l % 4) .. + 3
-  float* ybase = p.y + seq_base + 16 * w + 4 * (lane & 3);
-  unsigned char* ytile = ring + kYOff + w * kYTile;
-  auto slot_of = [&](int c) { return ring + (c % kRing) * kSlot; };
-  // v of chunk c for this wave: V[t = 4g + e][i = 16 w + li], raw bfloat16 bits (a
-  // quarter-wave reads 32 contiguous bytes of one token row); tokens past the end read
-  // the last token (their record coefficients are zero)
-  const uint16_t* vbase = p.v + seq_base + 16 * w + li;
-  auto load_v = [&](int c, uint32_t (&vr)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = min(c * kC + 4 * g + e, T - 1);
-      vr[e] = vbase[(int64_t)t * tstride];
-    }
-  };
-  Frag fa, fb;
-  uint32_t va[4], vb[4];  // v two chunks ahead: the set of chunk c is reloaded with chunk c + 2
-  load_v(0, va);
-  load_v(min(1, nc - 1), vb);
-  wait_at_least(&ready[0], 0);
-  read_frag(slot_of(0), fa);
-  int c = 0;
-  // One chunk: the next chunk's fragments are read (its slot waited for) before this
-  // chunk's products are issued. Past the last chunk the reads repeat the last chunk, so
-  // they are unconditional (a read inside a branch would make the compiler wait for it at
-  // the join). Returns false after the last chunk.
-  auto body = [&](Frag& cur, Frag& nxt, uint32_t (&vc)[4]) {
-    const int cn = min(c + 1, nc - 1);
-    wait_at_least(&ready[cn % kRing], cn);
-    read_frag(slot_of(cn), nxt);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) cur.v[e] = vc[e];
-    if constexpr (CK) ck_store(p.ck + ((int64_t)unit * nc + c) * kCkHalves, 16 * w, St);
-    const f32x4 yv = scan_step<!CK>(St, cur);
-    load_v(min(c + 2, nc - 1), vc);
-    if constexpr (!CK) {
-      // y through the wave's tile: written as lane (token li, values 4g..), read as lane
-      // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before the
-      // previous post (its wait covers every LDS access of this wave).
-      st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-      const float4 yq = ld_off<float4>(ytile, (uint32_t)((lane >> 2) * kYRow + 16 * (lane & 3)));
-      const int t = c * kC + (lane >> 2);
-      if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
-    }
-    post(&consumed[w], cn + 1);  // every fragment up to chunk cn is in registers
-    ++c;
-    return c < nc;
-  };
-  while (body(fa, fb, va) && body(fb, fa, vb)) {
-  }
-  if (p.s_out) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      *reinterpret_cast<float4*>(p.s_out + ((int64_t)unit * kN + 16 * w + li) * kN + 16 * kt + 4 * g) =
-          make_float4(St[kt].v[0], St[kt].v[1], St[kt].v[2], St[kt].v[3]);
-  }
+  fused_body<MODE, CK>(p, ring, blockIdx.x);
 }
 
 template <int MODE, bool CK = false>
@@ -254,24 +70,6 @@ hipError_t launch_chunked(const WkvCall& c) {
   fp.s_out = static_cast<float*>(c.s_out);
   fp.nc = (int32_t)((c.T + kC - 1) / kC);
   return launch_fused<kPrepPlain>(fp, c.B * c.H, c.stream);
-}
-
-hipError_t launch_chunked_ckpt(const WkvCall& c, _Float16* ck) {
-  if (c.dtype != 1 || !fused_domain(c.T, c.H)) return hipErrorNotSupported;
-  FusedParams fp{};
-  fp.in.r = static_cast<const uint16_t*>(c.in[0]);
-  fp.in.w = static_cast<const uint16_t*>(c.in[1]);
-  fp.in.k = static_cast<const uint16_t*>(c.in[2]);
-  fp.in.a = static_cast<const uint16_t*>(c.in[4]);
-  fp.in.b = static_cast<const uint16_t*>(c.in[5]);
-  fp.in.T = (int32_t)c.T;
-  fp.in.H = (int32_t)c.H;
-  fp.v = static_cast<const uint16_t*>(c.in[3]);
-  fp.s_in = static_cast<const float*>(c.s_in);
-  fp.s_out = static_cast<float*>(c.s_out);
-  fp.ck = ck;
-  fp.nc = (int32_t)((c.T + kC - 1) / kC);
-  return launch_fused<kPrepPlain, true>(fp, c.B * c.H, c.stream);
 }
 
 hipError_t launch_tmix_fused(const TmixCall& c) {

@@ -112,11 +112,6 @@ hipError_t launch_backward(const BwdCall& c);
 // hipErrorNotSupported before any launch): wkv7_bwd_chunk.hip.
 hipError_t launch_backward_chunked(const BwdCall& c);
 
-// The one-kernel chunked prefill (bfloat16 inputs) in its checkpoint form: no y; the
-// float16 state at the start of every chunk into ck ([B*H][ceil(T/16)] states of
-// 64 x 64 halves, in the fragment order of wkv7_chunk_ops.hpp); state_out if given.
-hipError_t launch_chunked_ckpt(const WkvCall& c, _Float16* ck);
-
 // L time-mix layers over a float32 residual stream x [B*T, H*64], in place, with
 // the per-layer states [L, B, H, 64, 64] updated in place.
 struct StackCall {
