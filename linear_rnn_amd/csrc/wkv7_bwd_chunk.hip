@@ -327,15 +327,13 @@ hipError_t launch_pass(const fused::FusedParams& fp, const ChainParams& cp, int6
 // Contractions over the 64 value rows take row 16 (2 rp + h) + 4 g + e for
 // (rp, h = element / 4, e), two 16-row tiles per 16x16x32 product.
 constexpr int kGW = 4;  // waves (items) per workgroup
-// Per wave: the row staging area (later the scaled operands' column vectors, four
-// tensors x four key tiles x 8 bytes per lane), the factor rows, the solve's scratch,
-// a 64-float key exchange.
-constexpr int kGOpnd = 0;
+// Per wave: the chunk's staged r, a, b, k rows (kept for the whole item), the factor
+// rows, the solve's scratch, a 64-float key exchange.
+constexpr int kGStage = 0;
 constexpr int kGFac = kStageBytes;
 constexpr int kGScr = kGFac + kFacBytes;
 constexpr int kGEx = kGScr + 4096;
 constexpr int kGWaveLds = kGEx + kN * 4;  // 18,464 bytes
-static_assert(16 * 512 <= kStageBytes, "operand columns fit the staging area");
 static_assert(kGScr % 16 == 0 && kGEx % 16 == 0 && kGWaveLds % 16 == 0, "16-byte aligned areas");
 
 struct GradParams {
@@ -385,6 +383,14 @@ __device__ __forceinline__ float row_suffix16(float x) {
   return x;
 }
 
+// One wave per (head, chunk). Fragment conventions (16x16 tiles; lane (li, g)):
+//   "row vector" X[li][4g + e] (A operand of X, B operand of X^T; the token layout when
+//   li is a token), "column vector" X[4g + e][li] (the D layout; B operand of X).
+// An identity product turns one into the other (tr16). A product with its operands
+// swapped returns the transposed result (the same registers serve as A and B), so
+// key-space results land in the token layout: lane (t = li, g), keys 16 kt + 4 g + e.
+// The contractions over the 64 value rows accumulate one 16-row tile at a time
+// (16x16x16 products), while that tile's U, dX, S0 and G are in registers.
 __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63;
@@ -400,18 +406,17 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   const int64_t base = (int64_t)bb * T * H * kN + (int64_t)hh * kN + (int64_t)c * kC * tstride;
   const int nt = min(kC, T - c * kC);
   unsigned char* wl = lds + wave * kGWaveLds;
+  unsigned char* stage = wl + kGStage;
   float* fac = reinterpret_cast<float*>(wl + kGFac);
   float* scr = reinterpret_cast<float*>(wl + kGScr);
   float* ex = reinterpret_cast<float*>(wl + kGEx);
-  unsigned char* opnd = wl + kGOpnd;  // column vectors of a-, r-, b-, k- (slot q * 4 + kt)
-  auto opnd_off = [&](int q, int kt) { return (uint32_t)((q * 4 + kt) * 512 + lane * 8); };
   const half4 hz = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
   half4 eye;
 #pragma unroll
   for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * g + e == li ? 1.f : 0.f);
 
   // ---- loads: the chunk's rows, its v and dY as row vectors (lane t = li; t past the end
-  // reads the last token), its start state and end gradient
+  // reads the last token)
   PrepRows rows;
   prep_load_rows(p.in, base, nt, rows);
   PrepRaw x;
@@ -425,12 +430,12 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   }
   const _Float16* s0p = p.s0 + item * kCkHalves;
   const _Float16* gp = p.gend + item * kCkHalves;
-  prep_rows_to_raw(rows, wl, x);
+  prep_rows_to_raw(rows, stage, x);  // the staged rows stay in LDS for the end
   prep_factors<kPrepPlain>(x, fac, reinterpret_cast<unsigned char*>(ex));
 
-  // ---- chunk prep: scaled operands (token layout) and their column vectors, the Grams
-  half4 AT[4];                           // A^ as column vectors
-  half4 bbar[4], kbar[4];                // B-, K- row vectors (lane tau = li)
+  // ---- chunk prep: the Grams (column vectors: lane (s = li, g) holds L[t = 4g + e][s]),
+  // A^ column vectors, B-, K- row vectors
+  half4 AT[4], bbar[4], kbar[4];
   MmaBF::acc Lab = MmaBF::zero(), Lak = MmaBF::zero(), Lrb = MmaBF::zero(), Lrk = MmaBF::zero();
   {
     bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
       const float4 g15 = lds4(&fac[16 * kFacRow + col]);
       const float4 e7 = lds4(&fac[kRowE7 * kFacRow + col]);
       float ag[4], rg[4], bg[4], kg[4];
-      half4 ah, agh, rgh, bgh, kgh;
+      half4 ah;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float av = bf4(x.ar[kt], e), bv = bf4(x.br[kt], e), rv = bf4(x.rr[kt], e), kv = bf4(x.kr[kt], e);
@@ -454,10 +459,6 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
         ah[e] = (_Float16)(ag[e] * el(e7, e));
         bbar[kt][e] = (_Float16)(bg[e] * el(g15, e));
         kbar[kt][e] = (_Float16)(kg[e] * el(g15, e));
-        agh[e] = (_Float16)ag[e];
-        rgh[e] = (_Float16)rg[e];
-        bgh[e] = (_Float16)bg[e];
-        kgh[e] = (_Float16)kg[e];
       }
 #pragma unroll
       for (int e = 0; e < 4; e += 2) {
@@ -467,11 +468,6 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
         split_bf16x2(bg[e], bg[e + 1], bhH, bhL, q8);
         split_bf16x2(kg[e], kg[e + 1], khH, khL, q8);
       }
-      // lane (key 16 kt + li, g): X[t = 4g + e][key], into the (consumed) staging area
-      st_off<half4>(opnd, opnd_off(0, kt), tr16(agh, eye));
-      st_off<half4>(opnd, opnd_off(1, kt), tr16(rgh, eye));
-      st_off<half4>(opnd, opnd_off(2, kt), tr16(bgh, eye));
-      st_off<half4>(opnd, opnd_off(3, kt), tr16(kgh, eye));
       AT[kt] = tr16(ah, eye);
       if (kt & 1) {
         Lab = MmaBF::mma(ahH, bhH, Lab);
@@ -490,7 +486,7 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     }
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {  // column vectors: lane (s = li, g) holds L[t = 4g + e][s]
+  for (int e = 0; e < 4; ++e) {
     const int t = 4 * g + e;
     Lab.v[e] = li < t ? Lab.v[e] : 0.f;
     Lak.v[e] = li < t ? Lak.v[e] : 0.f;
@@ -498,8 +494,8 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     Lrk.v[e] = li <= t ? Lrk.v[e] : 0.f;
   }
   const TmFrags tmf = prep_solve(Lab, Lrb, scr);
-  const half4 tB = tmf.tB;                      // T row vectors
-  const half8 ttA = cat8(tr16(tB, eye), hz);    // T^T as an A operand
+  const half4 tB = tmf.tB;                    // T row vectors
+  const half8 ttA = cat8(tr16(tB, eye), hz);  // T^T as an A operand
   const half4 lakC = to_h4(Lak), lrbC = to_h4(Lrb), lrkC = to_h4(Lrk);  // L^T as A operands
   const half8 guA = cat8(to_h4(Mma16::mma(lakC, tB, Mma16::zero())), hz);  // lane t: G_u[t][4g + e]
   half8 apA[2];  // A' = T A^ as A operands over the key pairs
@@ -513,13 +509,22 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   const half8 bbA[2] = {cat8(bbar[0], bbar[1]), cat8(bbar[2], bbar[3])};
   const half8 kbA[2] = {cat8(kbar[0], kbar[1]), cat8(kbar[2], kbar[3])};
 
-  // ---- value-row quantities per 16-row tile rt (column vectors, lane = value row):
-  // U = A' S0^T + G_u V, dU = L_rb^T dY + B- G^T, dX = T^T dU; dV written from here
-  half4 uR[4], dxR[4];  // U, dX as row vectors (lane tau / t = li)
+  // ---- per 16-row tile rt: U = A' S0^T + G_u V, dU = L_rb^T dY + B- G^T, dX = T^T dU (column
+  // vectors, lane = value row), dV (stored), and this tile's share of every contraction over
+  // the rows: (dY S0), (dX S0), (U G), (V G) per key tile in the token layout, the four C x C
+  // Gram gradients, and sum_i S0 G
+  Mma16::acc ys[4], xs[4], ug[4], vg[4];
+  Mma16::acc dLrb = Mma16::zero(), dLrk = Mma16::zero(), dLab = Mma16::zero(), dLak = Mma16::zero();
+  float endp[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    ys[kt] = xs[kt] = ug[kt] = vg[kt] = Mma16::zero();
+    endp[kt] = 0.f;
+  }
   float* dvp = p.grad[3] + base;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    half8 sr[2], gr[2];  // lane (row 16 rt + li, g): the keys of key pair kp
+    half8 sr[2], gr[2];  // lane (row 16 rt + li, g): the keys of key pair kp (row vectors)
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
       sr[kp] = *reinterpret_cast<const half8*>(s0p + ck_off(16 * rt + li, kp, g));
@@ -534,8 +539,8 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     du = Mma32::mma(bbA[0], gr[0], du);
     du = Mma32::mma(bbA[1], gr[1], du);
     const half4 dxC = to_h4(Mma32::mma(ttA, cat8(to_h4(du), hz), Mma32::zero()));
-    uR[rt] = tr16(to_h4(u), eye);  // lane (tau = li, g): U[tau][row 16 rt + 4g + e]
-    dxR[rt] = tr16(dxC, eye);
+    const half4 uR = tr16(to_h4(u), eye);  // lane (tau = li, g): U[tau][row 16 rt + 4g + e]
+    const half4 dxR = tr16(dxC, eye);      // lane (t = li, g): dX[t][row 16 rt + 4g + e]
     // dV^T = [dY ; dX]^T [L_rk | L_ak] + G K-^T (operands swapped): lane (tau = li, g)
     // holds dV[tau][row 16 rt + 4g + e]
     Mma32::acc dv = Mma32::mma(cat8(dyC, dxC), cat8(lrkC, lakC), Mma32::zero());
@@ -544,132 +549,111 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     if (li < nt)
       st_off<float4>(dvp, (uint32_t)(li * tstride + 16 * rt + 4 * g) * 4u,
                      make_float4(dv.v[0], dv.v[1], dv.v[2], dv.v[3]));
-    __builtin_amdgcn_sched_barrier(0);  // one row tile at a time: bounded register pressure
-  }
-  // row vectors over the 64 rows as 16x16x32 operands (row perm)
-  const half8 dyA[2] = {cat8(dyh[0], dyh[1]), cat8(dyh[2], dyh[3])};
-  const half8 vA[2] = {cat8(vh[0], vh[1]), cat8(vh[2], vh[3])};
-  const half8 uA[2] = {cat8(uR[0], uR[1]), cat8(uR[2], uR[3])};
-  const half8 dxA[2] = {cat8(dxR[0], dxR[1]), cat8(dxR[2], dxR[3])};
-
-  // ---- the four C x C Gram gradients, as row vectors (lane t: dL[t][tau = 4g + e]) and
-  // their transposes (lane tau: dL[t = 4g + e][tau])
-  half4 dLrb, dLrk, dLab, dLak;
-  {
-    Mma32::acc a = Mma32::mma(uA[0], dyA[0], Mma32::zero());
-    a = Mma32::mma(uA[1], dyA[1], a);
-    Mma32::acc b = Mma32::mma(vA[0], dyA[0], Mma32::zero());
-    b = Mma32::mma(vA[1], dyA[1], b);
-    Mma32::acc cc = Mma32::mma(uA[0], dxA[0], Mma32::zero());
-    cc = Mma32::mma(uA[1], dxA[1], cc);
-    Mma32::acc d = Mma32::mma(vA[0], dxA[0], Mma32::zero());
-    d = Mma32::mma(vA[1], dxA[1], d);
+    // Gram gradients, as row vectors over tau (lane t): dL[t][tau] = sum_rows X[t] Y[tau]
+    dLrb = Mma16::mma(uR, dyh[rt], dLrb);
+    dLrk = Mma16::mma(vh[rt], dyh[rt], dLrk);
+    dLab = Mma16::mma(uR, dxR, dLab);
+    dLak = Mma16::mma(vh[rt], dxR, dLak);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tau = 4 * g + e;
-      dLrb[e] = (_Float16)(tau <= li ? a.v[e] : 0.f);
-      dLrk[e] = (_Float16)(tau <= li ? b.v[e] : 0.f);
-      dLab[e] = (_Float16)(tau < li ? cc.v[e] : 0.f);
-      dLak[e] = (_Float16)(tau < li ? d.v[e] : 0.f);
+    for (int kt = 0; kt < 4; ++kt) {
+      // this row tile of S0 and G, key tile kt, as column vectors over its rows (lane key)
+      const half4 sC = tr16((kt & 1) ? hi4(sr[kt >> 1]) : lo4(sr[kt >> 1]), eye);
+      const half4 gC = tr16((kt & 1) ? hi4(gr[kt >> 1]) : lo4(gr[kt >> 1]), eye);
+      ys[kt] = Mma16::mma(sC, dyh[rt], ys[kt]);  // (dY S0)[t][key]
+      xs[kt] = Mma16::mma(sC, dxR, xs[kt]);      // (dX S0)[t][key]
+      ug[kt] = Mma16::mma(gC, uR, ug[kt]);       // (U G)[tau][key]
+      vg[kt] = Mma16::mma(gC, vh[rt], vg[kt]);   // (V G)[tau][key]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) endp[kt] = fmaf((float)sC[e], (float)gC[e], endp[kt]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // one row tile at a time (the accumulators stay live)
   }
-  const half8 rbk = cat8(dLrb, dLrk), abk = cat8(dLab, dLak);
-  const half8 abT = cat8(tr16(dLab, eye), tr16(dLrb, eye)), akT = cat8(tr16(dLak, eye), tr16(dLrk, eye));
+  // the Gram gradients masked (dL_rb, dL_rk: tau <= t; dL_ab, dL_ak: tau < t), as A operands
+  // over tau (lane t) and, transposed, over t (lane tau)
+  half4 hrb, hrk, hab, hak;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int tau = 4 * g + e;
+    hrb[e] = (_Float16)(tau <= li ? dLrb.v[e] : 0.f);
+    hrk[e] = (_Float16)(tau <= li ? dLrk.v[e] : 0.f);
+    hab[e] = (_Float16)(tau < li ? dLab.v[e] : 0.f);
+    hak[e] = (_Float16)(tau < li ? dLak.v[e] : 0.f);
+  }
+  const half8 rbk = cat8(hrb, hrk), abk = cat8(hab, hak);
+  const half8 abT = cat8(tr16(hab, eye), tr16(hrb, eye)), akT = cat8(tr16(hak, eye), tr16(hrk, eye));
+  // sum over the rows of S0 G, times e^{gamma_15}, to the key exchange (lane key 16 kt + li)
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    float acc = endp[kt];
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    const int j = 16 * kt + li;
+    if (g == 0) ex[j] = acc * fac[16 * kFacRow + j] * fac[kRowE7 * kFacRow + j];
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
 
-  // ---- per key tile: the key-space products (token layout), the end term, the decay's
-  // gradient, and the stores
+  // ---- per key tile, in the token layout (lane t = li, keys 16 kt + 4g + e): the scaled
+  // operands again (from the staged rows), the Gram-gradient products, the input gradients,
+  // the decay's gradient, and the stores
   float* drp = p.grad[0] + base;
   float* dwp = p.grad[1] + base;
   float* dkp = p.grad[2] + base;
   float* dap = p.grad[4] + base;
   float* dbp = p.grad[5] + base;
-  // the pieces a key tile reads from memory: its 16 x 16 blocks of S0 and G (row vectors,
-  // 8 bytes per lane and row tile) and the raw r, a, b, k (token layout; zero past the end
-  // of the sequence); loaded one key tile ahead
-  struct KtIn {
-    half4 s[4], g[4];
-    uint2 r, a, b, k;
-  };
-  auto kt_load = [&](int kt, KtIn& q) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const uint32_t o = ck_off(16 * rt + li, kt >> 1, g) + 4 * (kt & 1);
-      q.s[rt] = *reinterpret_cast<const half4*>(s0p + o);
-      q.g[rt] = *reinterpret_cast<const half4*>(gp + o);
-    }
-    const uint32_t ro = (uint32_t)(tl * tstride + 16 * kt + 4 * g) * 2u;
-    const uint2 z2 = make_uint2(0u, 0u);
-    q.r = li < nt ? ld_off<uint2>(p.in.r + base, ro) : z2;
-    q.a = li < nt ? ld_off<uint2>(p.in.a + base, ro) : z2;
-    q.b = li < nt ? ld_off<uint2>(p.in.b + base, ro) : z2;
-    q.k = li < nt ? ld_off<uint2>(p.in.k + base, ro) : z2;
-  };
-  KtIn kin[2];
-  kt_load(0, kin[0]);
+  const bool live = li < nt;
+  const uint2 z2 = make_uint2(0u, 0u);
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const KtIn& cur = kin[kt & 1];
-    if (kt < 3) kt_load(kt + 1, kin[(kt + 1) & 1]);
-    // S0 and G tiles of key tile kt as column vectors over the rows (lane key 16 kt + li)
-    half8 sC[2], gC[2];
-#pragma unroll
-    for (int rp = 0; rp < 2; ++rp) {
-      sC[rp] = cat8(tr16(cur.s[2 * rp], eye), tr16(cur.s[2 * rp + 1], eye));
-      gC[rp] = cat8(tr16(cur.g[2 * rp], eye), tr16(cur.g[2 * rp + 1], eye));
-    }
-    // sum over rows of S0 G for key 16 kt + li, times e^{gamma_15}, to the exchange
-    {
-      float acc = 0.f;
-#pragma unroll
-      for (int rp = 0; rp < 2; ++rp)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)sC[rp][e], (float)gC[rp][e], acc);
-      acc += __shfl_xor(acc, 16);
-      acc += __shfl_xor(acc, 32);
-      const int j = 16 * kt + li;
-      if (g == 0) ex[j] = acc * fac[16 * kFacRow + j] * fac[kRowE7 * kFacRow + j];
-    }
-    Mma32::acc ys = Mma32::mma(sC[0], dyA[0], Mma32::zero());  // (dY S0)[t][keys]
-    ys = Mma32::mma(sC[1], dyA[1], ys);
-    Mma32::acc xs = Mma32::mma(sC[0], dxA[0], Mma32::zero());  // (dX S0)
-    xs = Mma32::mma(sC[1], dxA[1], xs);
-    Mma32::acc ug = Mma32::mma(gC[0], uA[0], Mma32::zero());   // (U G)[tau][keys]
-    ug = Mma32::mma(gC[1], uA[1], ug);
-    Mma32::acc vg = Mma32::mma(gC[0], vA[0], Mma32::zero());   // (V G)
-    vg = Mma32::mma(gC[1], vA[1], vg);
-    const half8 bk = cat8(ld_off<half4>(opnd, opnd_off(2, kt)), ld_off<half4>(opnd, opnd_off(3, kt)));
-    const half8 ar = cat8(ld_off<half4>(opnd, opnd_off(0, kt)), ld_off<half4>(opnd, opnd_off(1, kt)));
-    const Mma32::acc pr = Mma32::mma(bk, rbk, Mma32::zero());  // dL_rb b- + dL_rk k- (scaled operands)
-    const Mma32::acc pa = Mma32::mma(bk, abk, Mma32::zero());  // dL_ab b- + dL_ak k-
-    const Mma32::acc pb = Mma32::mma(ar, abT, Mma32::zero());  // dL_ab^T a- + dL_rb^T r-
-    const Mma32::acc pk = Mma32::mma(ar, akT, Mma32::zero());  // dL_ak^T a- + dL_rk^T r-
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
     const int col = 16 * kt + 4 * g;
+    const uint32_t so = (uint32_t)(li * kStageRow + 32 * kt + 8 * g);
+    const uint2 rq = live ? ld_off<uint2>(stage, 0 * kStageT + so) : z2;
+    const uint2 aq = live ? ld_off<uint2>(stage, 1 * kStageT + so) : z2;
+    const uint2 bq = live ? ld_off<uint2>(stage, 2 * kStageT + so) : z2;
+    const uint2 kq = live ? ld_off<uint2>(stage, 3 * kStageT + so) : z2;
     const float4 gqm1 = lds4(&fac[li * kFacRow + col]);
     const float4 gq = lds4(&fac[(li + 1) * kFacRow + col]);
     const float4 g15 = lds4(&fac[16 * kFacRow + col]);
     const float4 e7 = lds4(&fac[kRowE7 * kFacRow + col]);
     const float4 e1 = lds4(&ex[col]);
-    float dr[4], da[4], db[4], dk[4], dg[4], hv[4];
+    half4 agh, rgh, bgh, kgh;
+    float bs[4], ks[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float f = __builtin_amdgcn_rcpf(el(gq, e));
+      const float bg = bf4(bq, e) * f, kg = bf4(kq, e) * f;
+      agh[e] = (_Float16)(bf4(aq, e) * el(gqm1, e));
+      rgh[e] = (_Float16)(bf4(rq, e) * el(gq, e));
+      bgh[e] = (_Float16)bg;
+      kgh[e] = (_Float16)kg;
+      bs[e] = bg * el(g15, e);  // B- and K- of this token
+      ks[e] = kg * el(g15, e);
+    }
+    // column vectors of the scaled operands: lane (key 16 kt + li, g) holds X[t = 4g + e][key]
+    const half8 bk = cat8(tr16(bgh, eye), tr16(kgh, eye)), ar = cat8(tr16(agh, eye), tr16(rgh, eye));
+    const Mma32::acc pr = Mma32::mma(bk, rbk, Mma32::zero());  // dL_rb b- + dL_rk k- (scaled operands)
+    const Mma32::acc pa = Mma32::mma(bk, abk, Mma32::zero());  // dL_ab b- + dL_ak k-
+    const Mma32::acc pb = Mma32::mma(ar, abT, Mma32::zero());  // dL_ab^T a- + dL_rb^T r-
+    const Mma32::acc pk = Mma32::mma(ar, akT, Mma32::zero());  // dL_ak^T a- + dL_rk^T r-
+    float dr[4], da[4], db[4], dk[4], dg[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float q = el(gq, e), qm = el(gqm1, e), E7 = el(e7, e), iq = __builtin_amdgcn_rcpf(q);
-      dr[e] = q * E7 * ys.v[e] + q * pr.v[e];
-      da[e] = qm * E7 * xs.v[e] + qm * pa.v[e];
-      db[e] = iq * pb.v[e] + el(g15, e) * iq * ug.v[e];
-      dk[e] = iq * pk.v[e] + el(g15, e) * iq * vg.v[e];
-      hv[e] = (float)bbar[kt][e] * ug.v[e] + (float)kbar[kt][e] * vg.v[e];
+      dr[e] = q * E7 * ys[kt].v[e] + q * pr.v[e];
+      da[e] = qm * E7 * xs[kt].v[e] + qm * pa.v[e];
+      db[e] = iq * pb.v[e] + el(g15, e) * iq * ug[kt].v[e];
+      dk[e] = iq * pk.v[e] + el(g15, e) * iq * vg[kt].v[e];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float an = row_shl<1>(bf4(cur.a, e) * da[e]);  // a_{t+1} da_{t+1} (zero at t = 15)
-      dg[e] = bf4(cur.r, e) * dr[e] - bf4(cur.b, e) * db[e] - bf4(cur.k, e) * dk[e] + an;
-      const float tot = row_sum16(hv[e]) + el(e1, e);  // the chunk end's share, for every token
+      const float an = row_shl<1>(bf4(aq, e) * da[e]);  // a_{t+1} da_{t+1} (zero at t = 15)
+      dg[e] = bf4(rq, e) * dr[e] - bf4(bq, e) * db[e] - bf4(kq, e) * dk[e] + an;
+      // the chunk end's share, for every token: e^{gamma_15} sum_i S0 G + sum_tau (B- dB- + K- dK-)
+      const float tot = row_sum16(bs[e] * ug[kt].v[e] + ks[e] * vg[kt].v[e]) + el(e1, e);
       // dw = dlog w / w, 1 / w = Gq_{t-1} / Gq_t
       dg[e] = (row_suffix16(dg[e]) + tot) * el(gqm1, e) * __builtin_amdgcn_rcpf(el(gq, e));
     }
-    if (li < nt) {
+    if (live) {
       const uint32_t o = (uint32_t)(li * tstride + col) * 4u;
       st_off<float4>(drp, o, make_float4(dr[0], dr[1], dr[2], dr[3]));
       st_off<float4>(dwp, o, make_float4(dg[0], dg[1], dg[2], dg[3]));
@@ -677,7 +661,6 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
       st_off<float4>(dap, o, make_float4(da[0], da[1], da[2], da[3]));
       st_off<float4>(dbp, o, make_float4(db[0], db[1], db[2], db[3]));
     }
-    __builtin_amdgcn_sched_barrier(0);  // one key tile at a time
   }
 }
 
