@@ -506,8 +506,13 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     apA[0] = cat8(ap[0], ap[1]);
     apA[1] = cat8(ap[2], ap[3]);
   }
-  const half8 bbA[2] = {cat8(bbar[0], bbar[1]), cat8(bbar[2], bbar[3])};
-  const half8 kbA[2] = {cat8(kbar[0], kbar[1]), cat8(kbar[2], kbar[3])};
+  // B- and K- row vectors (A operands over the key pairs) wait in the solve's scratch,
+  // free from here on: four 16-byte pieces per lane, read back in every row tile
+  unsigned char* bk_l = reinterpret_cast<unsigned char*>(scr);
+  st_off<half8>(bk_l, (uint32_t)lane * 16u, cat8(bbar[0], bbar[1]));
+  st_off<half8>(bk_l, 1024u + (uint32_t)lane * 16u, cat8(bbar[2], bbar[3]));
+  st_off<half8>(bk_l, 2048u + (uint32_t)lane * 16u, cat8(kbar[0], kbar[1]));
+  st_off<half8>(bk_l, 3072u + (uint32_t)lane * 16u, cat8(kbar[2], kbar[3]));
 
   // ---- per 16-row tile rt: U = A' S0^T + G_u V, dU = L_rb^T dY + B- G^T, dX = T^T dU (column
   // vectors, lane = value row), dV (stored), and this tile's share of every contraction over
@@ -536,16 +541,16 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     u = Mma32::mma(apA[0], sr[0], u);
     u = Mma32::mma(apA[1], sr[1], u);
     Mma32::acc du = Mma32::mma(cat8(lrbC, hz), cat8(dyC, hz), Mma32::zero());
-    du = Mma32::mma(bbA[0], gr[0], du);
-    du = Mma32::mma(bbA[1], gr[1], du);
+    du = Mma32::mma(ld_off<half8>(bk_l, (uint32_t)lane * 16u), gr[0], du);
+    du = Mma32::mma(ld_off<half8>(bk_l, 1024u + (uint32_t)lane * 16u), gr[1], du);
     const half4 dxC = to_h4(Mma32::mma(ttA, cat8(to_h4(du), hz), Mma32::zero()));
     const half4 uR = tr16(to_h4(u), eye);  // lane (tau = li, g): U[tau][row 16 rt + 4g + e]
     const half4 dxR = tr16(dxC, eye);      // lane (t = li, g): dX[t][row 16 rt + 4g + e]
     // dV^T = [dY ; dX]^T [L_rk | L_ak] + G K-^T (operands swapped): lane (tau = li, g)
     // holds dV[tau][row 16 rt + 4g + e]
     Mma32::acc dv = Mma32::mma(cat8(dyC, dxC), cat8(lrkC, lakC), Mma32::zero());
-    dv = Mma32::mma(gr[0], kbA[0], dv);
-    dv = Mma32::mma(gr[1], kbA[1], dv);
+    dv = Mma32::mma(gr[0], ld_off<half8>(bk_l, 2048u + (uint32_t)lane * 16u), dv);
+    dv = Mma32::mma(gr[1], ld_off<half8>(bk_l, 3072u + (uint32_t)lane * 16u), dv);
     if (li < nt)
       st_off<float4>(dvp, (uint32_t)(li * tstride + 16 * rt + 4 * g) * 4u,
                      make_float4(dv.v[0], dv.v[1], dv.v[2], dv.v[3]));
@@ -554,6 +559,7 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     dLrk = Mma16::mma(vh[rt], dyh[rt], dLrk);
     dLab = Mma16::mma(uR, dxR, dLab);
     dLak = Mma16::mma(vh[rt], dxR, dLak);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       // this row tile of S0 and G, key tile kt, as column vectors over its rows (lane key)
@@ -565,6 +571,7 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
       vg[kt] = Mma16::mma(gC, vh[rt], vg[kt]);   // (V G)[tau][key]
 #pragma unroll
       for (int e = 0; e < 4; ++e) endp[kt] = fmaf((float)sC[e], (float)gC[e], endp[kt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);  // one row tile at a time (the accumulators stay live)
   }
