@@ -253,7 +253,7 @@ def main(argv=None):
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer prompt-then-steps leg")
     ap.add_argument("--stack-steps", type=int, default=32)
-    ap.add_argument("--backward-reps", type=int, default=5)
+    ap.add_argument("--backward-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -342,7 +342,7 @@ def main(argv=None):
         c = CONFIGS["L12-D768-prefill"]
         xb = make_inputs(c)
         out["backward"] = bench_backward(torch, wkv, xb, to_dev(xb, torch), torch.from_numpy(xb["state_in"]).cuda(),
-                                         c, args)
+                                         c, args, flush)
 
     if not args.no_stack:
         log("timing the layer stack")
@@ -499,9 +499,16 @@ def bench_decode_fused(torch, wkv, cfg, args, distinct=32):
     }
 
 
-def bench_backward(torch, wkv, x, d, s_in, cfg, args):
+BWD_SRC = ["linear_rnn_amd/csrc/wkv7_bwd_chunk.hip", "linear_rnn_amd/csrc/wkv7_fused.hpp",
+           "linear_rnn_amd/csrc/wkv7_chunk_ops.hpp", "linear_rnn_amd/csrc/wkv7_device.hpp"]
+
+
+def bench_backward(torch, wkv, x, d, s_in, cfg, args, flush=None):
     """Gradients of the recurrence (dr, dw, dk, dv, da, db, dstate_in) at the prefill shape, from seeded
-    dy and dstate_out; one call = checkpoint forward, reverse pass and (two row blocks) column-sum add."""
+    dy and dstate_out. The default (AUTO, bfloat16 inputs) is the chunked backward on MFMA: one launch
+    runs the checkpoint forward and the chain of state gradients side by side, a second forms the input
+    gradients; each call between its own HIP events, after a write of `flush` (median and min). The
+    token-by-token backward (float32 throughout) is timed beside it."""
     from linear_rnn_amd.inputs import make_cotangents
     B, T, H = cfg.B, cfg.T, cfg.H
     ct = make_cotangents(B, T, H, seed=cfg.seed)
@@ -509,29 +516,33 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args):
     ds = torch.from_numpy(ct["dstate_out"]).cuda()
     grads = [torch.empty((B, T, H, N), dtype=torch.float32, device="cuda") for _ in range(6)]
     dsi = torch.empty_like(ds)
+    if flush is None:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
 
-    def bwd():
-        wkv.rwkv7_wkv_backward(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], s_in, dy, ds, *grads, dsi)
+    def bwd(algo):
+        wkv.rwkv7_wkv_backward_ex(d["r"], d["w"], d["k"], d["v"], d["a"], d["b"], s_in, dy, ds, *grads, dsi,
+                                  algo=algo)
 
-    for _ in range(2):
-        bwd()
-    ms = time_region(torch, bwd, args.backward_reps)
+    algo = wkv.RWKV7_ALGO_AUTO
+    ts = time_steps(torch, lambda: bwd(algo), args.backward_reps + 3, flush)[3:]
+    ms, ms_min = med(ts), min(ts)
+    tseq = time_steps(torch, lambda: bwd(wkv.RWKV7_ALGO_SEQUENTIAL), 3, flush)[1:]
     tok_heads = B * T * H
-    flops = FLOP_BWD * tok_heads
-    # inputs (bf16) and dy read, six float32 gradients written, states in and out
+    # inputs (bf16) and dy read, six float32 gradients written, state_in and dstate_out read, dstate_in written
     nbytes = tok_heads * N * (6 * 2 + 4 + 6 * 4) + 3 * B * H * N * N * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
     return {
-        "value": tok_heads / (ms * 1e-3), "unit": UNIT, "ms_per_call": ms, "reps": args.backward_reps,
+        "value": tok_heads / (ms * 1e-3), "unit": UNIT, "ms_per_call": ms, "ms_min": ms_min, "reps": len(ts),
+        "algo": "chunked (MFMA)" if d["r"].dtype == torch.bfloat16 else "sequential",
         "config": {"workload": "%s: B=%d T=%d H=%d N=%d bf16 inputs, fp32 state_in, dy, dstate_out; fp32 "
                                "gradients" % (cfg.name, B, T, H, N), "B": B, "T": T, "H": H, "N": N},
-        "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VECTOR_TFLOPS,
-                     "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,
-                     "traffic": measured_traffic("wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel:" + cfg.name,
-                                                 ["linear_rnn_amd/csrc/wkv7_bwd.hip",
-                                                  "linear_rnn_amd/csrc/wkv7_device.hpp"]),
-                     "kernel": "wkv7_ckpt_kernel+wkv7_bwd_kernel+wkv7_colsum_kernel",
-                     "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
-                     "hbm_frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("wkv7_bpass_kernel+wkv7_bgrad_kernel:" + cfg.name, BWD_SRC),
+                     "kernel": "wkv7_bpass_kernel+wkv7_bgrad_kernel", "algorithmic_bytes": nbytes},
+        "by_algorithm": {
+            "sequential": {"ms": med(tseq), "alu_frac": FLOP_BWD * tok_heads / (med(tseq) * 1e-3) / 1e12 /
+                           PEAK_FP32_VECTOR_TFLOPS, "note": "float32 throughout; 26 N^2 flop per token*head"}},
     }
 
 

@@ -374,7 +374,9 @@ __device__ __forceinline__ void prep_factors(PrepRaw& x, float* fac, unsigned ch
 }
 
 // Phase 1: decay factors, operands, the four Grams; B-, K- and e^{gamma_15} stored.
-template <int MODE>
+// Y = false: a record for carrying the state alone (no readout): L_rb and L_rk are not
+// formed (zero), so neither is anything of R' and G_y.
+template <int MODE, bool Y = true>
 __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char* rec, PrepMid& m) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
@@ -458,16 +460,16 @@ __device__ __forceinline__ void prep_grams(PrepRaw& x, float* fac, unsigned char
     if (kt & 1) {
       Lab = MmaBF::mma(ahH, bhH, Lab);
       Lak = MmaBF::mma(ahH, khH, Lak);
-      Lrb = MmaBF::mma(rhH, bhH, Lrb);
-      LrkT = MmaBF::mma(khH, rhH, LrkT);
+      if constexpr (Y) Lrb = MmaBF::mma(rhH, bhH, Lrb);
+      if constexpr (Y) LrkT = MmaBF::mma(khH, rhH, LrkT);
       Lab = MmaBF::mma(ahH, bhL, Lab);
       Lak = MmaBF::mma(ahH, khL, Lak);
-      Lrb = MmaBF::mma(rhH, bhL, Lrb);
-      LrkT = MmaBF::mma(khH, rhL, LrkT);
+      if constexpr (Y) Lrb = MmaBF::mma(rhH, bhL, Lrb);
+      if constexpr (Y) LrkT = MmaBF::mma(khH, rhL, LrkT);
       Lab = MmaBF::mma(ahL, bhH, Lab);
       Lak = MmaBF::mma(ahL, khH, Lak);
-      Lrb = MmaBF::mma(rhL, bhH, Lrb);
-      LrkT = MmaBF::mma(khL, rhH, LrkT);
+      if constexpr (Y) Lrb = MmaBF::mma(rhL, bhH, Lrb);
+      if constexpr (Y) LrkT = MmaBF::mma(khL, rhH, LrkT);
     }
   }
 #pragma unroll
@@ -548,7 +550,9 @@ __device__ __forceinline__ TmFrags prep_solve(const MmaBF::acc Lab, const MmaBF:
   return TmFrags{tB, mB};
 }
 
-// Phase 2: T, M_r and the products A', R', G_u, G_y, stored.
+// Phase 2: T, M_r and the products A', R', G_u, G_y, stored (Y = false: A' and G_u;
+// G_y stored as zeros, R' not stored).
+template <bool Y = true>
 __device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsigned char* rec) {
   const int lane = threadIdx.x & 63;
   const uint32_t lo = (uint32_t)lane * 16u;
@@ -568,14 +572,15 @@ __device__ __forceinline__ void prep_finish(const PrepMid& m, float* fac, unsign
       const int kt = 2 * kp + u;
       const half4 AT = to_h4(Mma16::mma(m.Ahat[kt], eye, Mma16::zero()));  // lane (j = li, g): A^[4g+e][16kt + li]
       ApT[u] = to_h4(Mma16::mma(AT, tB, Mma16::zero()));                   // lane (t = li, g): A'[t][16kt + 4g + e]
-      RpT[u] = to_h4(Mma16::mma(AT, mB, Mma16::acc{m.Rhat[kt]}));          // R'[t][16kt + 4g + e]
+      if constexpr (Y) RpT[u] = to_h4(Mma16::mma(AT, mB, Mma16::acc{m.Rhat[kt]}));  // R'[t][16kt + 4g + e]
     }
     st_off<half8>(rec, (kRecA0 + kp) * 1024 + lo, cat8(ApT[0], ApT[1]));
-    st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
+    if constexpr (Y) st_off<half8>(rec, (kRecR0 + kp) * 1024 + lo, cat8(RpT[0], RpT[1]));
   }
   const half4 LakH = to_h4(Lak);  // as an A operand: L_ak^T (M = s', K = s)
   const half4 GuT = to_h4(Mma16::mma(LakH, tB, Mma16::zero()));          // lane (t = li, g): G_u[t][4g + e]
-  const half4 GyT = to_h4(Mma16::mma(LakH, mB, Mma16::zero()).v + LrkT.v);  // G_y[t][4g + e]
+  half4 GyT = half4{(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+  if constexpr (Y) GyT = to_h4(Mma16::mma(LakH, mB, Mma16::zero()).v + LrkT.v);  // G_y[t][4g + e]
   st_off<half8>(rec, kRecG * 1024 + lo, cat8(GuT, GyT));
 }
 

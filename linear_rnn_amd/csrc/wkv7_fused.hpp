@@ -109,10 +109,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
       wait_all_at_least(consumed, c - kRing + 1);  // the slot's previous chunk has been read
       prep_rows_to_raw(cur, rec, x);               // the slot's start stages the rows
       PrepMid m;
-      prep_grams<MODE>(x, reinterpret_cast<float*>(rec), rec, m);
+      prep_grams<MODE, !CK>(x, reinterpret_cast<float*>(rec), rec, m);
       const int cn = min(c + kPrepW, last);
       prep_load_rows(p.in, base_of(cn), nt_of(cn), nxt);
-      prep_finish(m, reinterpret_cast<float*>(rec), rec);
+      prep_finish<!CK>(m, reinterpret_cast<float*>(rec), rec);
       post(&ready[slot], c);
       c += kPrepW;
       return c < nc;
