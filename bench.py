@@ -57,8 +57,8 @@ FLUSH_BYTES = 1 << 30
 ALGO_NAMES = {1: "sequential", 2: "chunked (one kernel per head)", 3: "chunked (split prep / scan)"}
 KERNELS = {  # algorithm -> (kernel names in a trace, source files whose hash keys the counter table)
     1: ("wkv7_seq_kernel", ["linear_rnn_amd/csrc/wkv7_seq.hip", "linear_rnn_amd/csrc/wkv7_device.hpp"]),
-    2: ("wkv7_fused_kernel", ["linear_rnn_amd/csrc/wkv7_fused.hip", "linear_rnn_amd/csrc/wkv7_chunk_ops.hpp",
-                              "linear_rnn_amd/csrc/wkv7_device.hpp"]),
+    2: ("wkv7_fused_kernel", ["linear_rnn_amd/csrc/wkv7_fused.hip", "linear_rnn_amd/csrc/wkv7_fused.hpp",
+                              "linear_rnn_amd/csrc/wkv7_chunk_ops.hpp", "linear_rnn_amd/csrc/wkv7_device.hpp"]),
     3: ("wkv7_prep_kernel+wkv7_scan_kernel", ["linear_rnn_amd/csrc/wkv7_split.hip",
                                                "linear_rnn_amd/csrc/wkv7_chunk_ops.hpp",
                                                "linear_rnn_amd/csrc/wkv7_device.hpp"]),

@@ -185,6 +185,7 @@ __device__ __forceinline__ void chain_body(const ChainParams& p, unsigned char* 
     // ---------------------------------------------------------------- prep waves
     const int q0 = wave - kScanW;
     if (q0 >= nc) return;
+    constexpr unsigned kRows = kRowR | kRowA | kRowB;  // the chain needs no k
     const int last = q0 + (nc - 1 - q0) / kPrepW * kPrepW;
     auto nt_of = [&](int q) { return min(kC, T - (nc - 1 - q) * kC); };
     auto base_of = [&](int q) { return seq_base + (int64_t)(nc - 1 - q) * kC * tstride; };
@@ -193,16 +194,16 @@ __device__ __forceinline__ void chain_body(const ChainParams& p, unsigned char* 
       PrepRaw x;
       prep_load_w<kPrepPlain>(p.in, base_of(q), nt_of(q), x);
       wait_all_at_least(consumed, q - kRing + 1);
-      prep_rows_to_raw(cur, rec, x);
+      prep_rows_to_raw<kRows>(cur, rec, x);
       const int qn = min(q + kPrepW, last);
-      prep_load_rows(p.in, base_of(qn), nt_of(qn), nxt);
+      prep_load_rows<kRows>(p.in, base_of(qn), nt_of(qn), nxt);
       chain_prep(x, rec);
       post(&ready[q % kRing], q);
       q += kPrepW;
       return q < nc;
     };
     PrepRows ra, rb;
-    prep_load_rows(p.in, base_of(q0), nt_of(q0), ra);
+    prep_load_rows<kRows>(p.in, base_of(q0), nt_of(q0), ra);
     int q = q0;
     while (item(q, ra, rb) && item(q, rb, ra)) {
     }

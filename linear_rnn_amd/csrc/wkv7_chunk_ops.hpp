@@ -239,6 +239,7 @@ __device__ __forceinline__ void prep_load(const PrepIn& p, int64_t base, int nt,
 // w is loaded in the key layout as by prep_load (whole rows already).
 struct PrepRows {
   uint4 q[4][2];  // r, a, b, k; h = 0, 1
+  uint4 wq[2];    // w (bfloat16) in the same form, when the caller takes w with the rows
 };
 constexpr int kStageRow = 144;             // bytes per staged token row (128 + 16: 16-byte aligned, and rows
                                            // 8 apart share banks, so the token-layout reads conflict 2-way)
@@ -246,7 +247,14 @@ constexpr int kStageT = kC * kStageRow;    // one tensor: 2,304 bytes
 constexpr int kStageBytes = 4 * kStageT;   // 9,216 bytes
 static_assert(kStageBytes <= kRecD, "staged rows end before e^gamma_15");
 
+// Which of r, a, b, k a caller needs (bit q of a row mask: r = 1, a = 2, b = 4, k = 8).
+// A form of the prep that never reads a tensor skips its loads and staging; its
+// registers then hold zeros.
+enum : unsigned { kRowR = 1u, kRowA = 2u, kRowB = 4u, kRowK = 8u, kRowsAll = 15u };
+
 // r, a, b, k rows of chunk (base, nt)
+// W: also w (plain bfloat16 form), so that its latency passes with the rows'.
+template <unsigned ROWS = kRowsAll, bool W = false>
 __device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, int nt, PrepRows& rows) {
   const int lane = threadIdx.x & 63;
   const uint32_t tstride = (uint32_t)p.H * kN;
@@ -256,7 +264,9 @@ __device__ __forceinline__ void prep_load_rows(const PrepIn& p, int64_t base, in
     const int tok = min((lane >> 3) + 8 * h, nt - 1);
     const uint32_t off = (uint32_t)(tok * tstride + 8 * (lane & 7)) * 2u;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rows.q[q][h] = ld_off<uint4>(src[q] + base, off);
+    for (int q = 0; q < 4; ++q)
+      rows.q[q][h] = (ROWS >> q) & 1u ? ld_off<uint4>(src[q] + base, off) : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (W) rows.wq[h] = ld_off<uint4>(p.w + base, off);
   }
 }
 // w of chunk (base, nt) in the key layout
@@ -277,6 +287,7 @@ __device__ __forceinline__ void prep_load_w(const PrepIn& p, int64_t base, int n
 
 // Writes the loaded rows to stage (kStageBytes of this wave's LDS) and reads them back
 // in the token layout of PrepRaw.
+template <unsigned ROWS = kRowsAll, bool W = false>
 __device__ __forceinline__ void prep_rows_to_raw(const PrepRows& rows, unsigned char* stage, PrepRaw& x) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
@@ -284,21 +295,35 @@ __device__ __forceinline__ void prep_rows_to_raw(const PrepRows& rows, unsigned 
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      st_off<uint4>(stage, (uint32_t)(q * kStageT + ((lane >> 3) + 8 * h) * kStageRow + 16 * (lane & 7)),
-                    rows.q[q][h]);
+      if ((ROWS >> q) & 1u)
+        st_off<uint4>(stage, (uint32_t)(q * kStageT + ((lane >> 3) + 8 * h) * kStageRow + 16 * (lane & 7)),
+                      rows.q[q][h]);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every piece is in LDS before other lanes read it
   __builtin_amdgcn_wave_barrier();
+  const uint2 z2 = make_uint2(0u, 0u);
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const uint32_t off = (uint32_t)(li * kStageRow + 32 * kt + 8 * g);
-    x.rr[kt] = ld_off<uint2>(stage, 0 * kStageT + off);
-    x.ar[kt] = ld_off<uint2>(stage, 1 * kStageT + off);
-    x.br[kt] = ld_off<uint2>(stage, 2 * kStageT + off);
-    x.kr[kt] = ld_off<uint2>(stage, 3 * kStageT + off);
+    x.rr[kt] = ROWS & kRowR ? ld_off<uint2>(stage, 0 * kStageT + off) : z2;
+    x.ar[kt] = ROWS & kRowA ? ld_off<uint2>(stage, 1 * kStageT + off) : z2;
+    x.br[kt] = ROWS & kRowB ? ld_off<uint2>(stage, 2 * kStageT + off) : z2;
+    x.kr[kt] = ROWS & kRowK ? ld_off<uint2>(stage, 3 * kStageT + off) : z2;
   }
-  // every read has returned before the caller overwrites the stage
+  // every read has returned before the stage is overwritten
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
+  if constexpr (W) {
+    // w through the first tensor's stage, read back in the key layout (lane = key)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      st_off<uint4>(stage, (uint32_t)(((lane >> 3) + 8 * h) * kStageRow + 16 * (lane & 7)), rows.wq[h]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < kC; ++t) x.wr[t] = ld_off<uint16_t>(stage, (uint32_t)(t * kStageRow + 2 * lane));
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+  }
 }
 
 // What the first phase of a chunk's prep hands to the second: the four Grams in the D

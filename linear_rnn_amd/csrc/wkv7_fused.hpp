@@ -95,6 +95,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
     // chunk (unconditional, no branch).
     const int c0 = wave - kScanW;
     if (c0 >= nc) return;
+    constexpr unsigned kRows = CK ? kRowA | kRowB | kRowK : kRowsAll;  // no readout, no r
+    // the checkpoint form takes w with the rows (measured: backward 0.571 -> 0.560 ms at 96
+    // heads; the prefill measured no gain at 96 heads and a 1% loss at 256)
+    constexpr bool kW = CK && MODE == kPrepPlain;
     const int last = c0 + (nc - 1 - c0) / kPrepW * kPrepW;  // this wave's last chunk
     auto nt_of = [&](int c) { return min(kC, T - c * kC); };
     auto base_of = [&](int c) { return seq_base + (int64_t)c * kC * tstride; };
@@ -105,20 +109,21 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
       const int nt = nt_of(c);
       const int64_t base = base_of(c);
       PrepRaw x;
-      prep_load_w<MODE>(p.in, base, nt, x);
+      x.nt = nt;
+      if constexpr (!kW) prep_load_w<MODE>(p.in, base, nt, x);
       wait_all_at_least(consumed, c - kRing + 1);  // the slot's previous chunk has been read
-      prep_rows_to_raw(cur, rec, x);               // the slot's start stages the rows
+      prep_rows_to_raw<kRows, kW>(cur, rec, x);    // the slot's start stages the rows
       PrepMid m;
       prep_grams<MODE, !CK>(x, reinterpret_cast<float*>(rec), rec, m);
       const int cn = min(c + kPrepW, last);
-      prep_load_rows(p.in, base_of(cn), nt_of(cn), nxt);
+      prep_load_rows<kRows, kW>(p.in, base_of(cn), nt_of(cn), nxt);
       prep_finish<!CK>(m, reinterpret_cast<float*>(rec), rec);
       post(&ready[slot], c);
       c += kPrepW;
       return c < nc;
     };
     PrepRows ra, rb;
-    prep_load_rows(p.in, base_of(c0), nt_of(c0), ra);
+    prep_load_rows<kRows, kW>(p.in, base_of(c0), nt_of(c0), ra);
     int c = c0;
     while (item(c, ra, rb) && item(c, rb, ra)) {
     }
