@@ -613,8 +613,10 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
         tmc()
         ms_by_algo[a] = time_region(torch, tmc, 5)
     ms_tmix_ch = ms_by_algo[stack_algo]
-    tm_kernel = {wkv.RWKV7_ALGO_CHUNKED: "wkv7_fused_kernel<time-mix> + tmix_ln_kernel",
-                 wkv.RWKV7_ALGO_CHUNKED_SPLIT: "wkv7_prep_kernel<time-mix> + wkv7_scan_kernel + tmix_ln_kernel"}
+    # (kernel names as traced, sources keying the counter table); ln_x runs inside the scan in both
+    tm_kernel = {wkv.RWKV7_ALGO_CHUNKED: ("wkv7_fused_kernel<1>", KERNELS[2][1]),
+                 wkv.RWKV7_ALGO_CHUNKED_SPLIT: ("wkv7_prep_kernel<1>+wkv7_scan_kernel<4, true>", KERNELS[3][1])}
+    tm_key = "%s:tmix-B%d-T%d-H%d" % (tm_kernel[stack_algo][0], B, T, H)
     # algorithmic bytes: r, k, v, kk, a_lr (bf16), w_raw and out (float32) per element, the state in and out
     tm_bytes = B * T * H * N * (5 * 2 + 4 + 4) + 2 * B * H * N * N * 4
     flops = FLOP_REC * B * T * H
@@ -630,7 +632,8 @@ def bench_stack(torch, wkv, args, L=12, H=12, B=8, T=1024):
             "by_algorithm": {ALGO_NAMES[a]: {"ms": t} for a, t in ms_by_algo.items()},
             "roofline": {"bound": "hbm", "achieved": tm_bytes / (ms_tmix_ch * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": tm_bytes / (ms_tmix_ch * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "kernel": tm_kernel[stack_algo], "algorithmic_bytes": tm_bytes, "traffic": None}},
+                         "kernel": tm_kernel[stack_algo][0], "algorithmic_bytes": tm_bytes,
+                         "traffic": measured_traffic(tm_key, tm_kernel[stack_algo][1])}},
         "tmix_prefill_sequential": {
             "ms": ms_tmix,
             "roofline": {"bound": "alu", "achieved": flops / (ms_tmix * 1e-3) / 1e12,

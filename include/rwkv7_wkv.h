@@ -246,12 +246,13 @@ int rwkv7_tmix_prefill(const void *r, const float *w_raw, const void *k, const v
  *   RWKV7_ALGO_CHUNKED  bfloat16 inputs only: the one-kernel chunked prefill of
  *                      rwkv7_wkv_prefill_ex (one workgroup per head, no workspace),
  *                      with the decay exp(-exp(w_raw)), the unit key and the two
- *                      slots formed in its prep waves and y written to out; a
- *                      second kernel applies ln_x to out in place. Its domain is
- *                      that of the chunked prefill (T*H*64 < 2^31).
+ *                      slots formed in its prep waves, and ln_x applied by its scan
+ *                      waves before out is written (no second pass over out). Its
+ *                      domain is that of the chunked prefill (T*H*64 < 2^31).
  *   RWKV7_ALGO_CHUNKED_SPLIT  bfloat16 inputs only: the same prologue in the split
- *                      prefill (prep and scan kernels, the cached device workspace),
- *                      then ln_x in place.
+ *                      prefill (prep and scan kernels, the cached device workspace;
+ *                      one scan workgroup per head, so that ln_x is applied as out is
+ *                      written).
  * Both chunked forms clamp decays below 2^-15 (as the chunked prefill does) and
  * match the definition to the chunked tolerance, not bit for bit with the steps.
  * Any other algo, a chunked algo with float32 inputs, or CHUNKED outside its

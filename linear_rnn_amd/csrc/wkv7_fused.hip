@@ -88,9 +88,9 @@ hipError_t launch_tmix_fused(const TmixCall& c) {
   fp.s_in = t.s_in;
   fp.s_out = t.s_out;
   fp.nc = (int32_t)((t.T + kC - 1) / kC);
-  const hipError_t e = launch_fused<kPrepTmix>(fp, c.B * c.H, c.stream);
-  if (e != hipSuccess) return e;
-  return launch_tmix_ln(t.out, t.ln_w, t.ln_b, c.B * t.T * c.H, (int32_t)c.H, c.stream);
+  fp.ln_w = t.ln_w;  // ln_x is applied by the scan waves before y is stored
+  fp.ln_b = t.ln_b;
+  return launch_fused<kPrepTmix>(fp, c.B * c.H, c.stream);
 }
 
 }  // namespace rwkv7

@@ -20,8 +20,13 @@ constexpr int kSlot = kRecBytes;             // 9,472 bytes (a scan wave loads i
 constexpr int kYRow = 80;
 constexpr int kYTile = kC * kYRow;           // 1,280 bytes per scan wave
 constexpr int kYOff = kRing * kSlot;
-constexpr int kCtrlOff = kYOff + kScanW * kYTile;  // ready[kRing], then consumed[kScanW]
-constexpr int kLds = kCtrlOff + 4 * (kRing + kScanW);
+// ln_x of the time-mix form: per chunk parity, scan wave and token, the mean and centred sum
+// of squares of the wave's 16 channels; one progress word per scan wave
+constexpr int kLnOff = kYOff + kScanW * kYTile;
+constexpr int kLnBytes = 2 * kScanW * kC * 8;  // [chunk parity][wave][token] (mean, sum of squares)
+constexpr int kCtrlOff = kLnOff + kLnBytes;  // ready[kRing], consumed[kScanW], ln_done[kScanW]
+constexpr int kLds = kCtrlOff + 4 * (kRing + 2 * kScanW);
+constexpr float kLnEps = 64e-5f;  // the GroupNorm eps of ln_x
 constexpr int kThreads = 64 * (kScanW + kPrepW);
 constexpr int kSpinMax = 1 << 20;            // polls of 100-200 cycles: well over any legitimate wait
 static_assert(kRing >= 3, "the scan reads one chunk ahead");
@@ -36,6 +41,8 @@ struct FusedParams {
   float* s_out;       // may be null
   _Float16* ck;       // checkpoint form only: the state at every chunk start (kCkHalves each)
   int32_t nc;         // chunks per sequence
+  const float* ln_w;  // time-mix form: ln_x's affine per (head, channel), may be null (1)
+  const float* ln_b;  // may be null (0)
 };
 
 __device__ __forceinline__ int lds_peek(const int* p) {
@@ -81,8 +88,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
   const int64_t seq_base = (int64_t)bb * T * H * kN + (int64_t)hh * kN;  // element offset of (bb, 0, hh, 0)
   int* ready = reinterpret_cast<int*>(ring + kCtrlOff);
   int* consumed = ready + kRing;
+  int* ln_done = consumed + kScanW;
   if (threadIdx.x < kRing) ready[threadIdx.x] = -1;
   if (threadIdx.x < kScanW) consumed[threadIdx.x] = 0;
+  if (threadIdx.x < kScanW) ln_done[threadIdx.x] = 0;
   __syncthreads();
 
   if (wave >= kScanW) {
@@ -160,6 +169,49 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
       vr[e] = vbase[(int64_t)t * tstride];
     }
   };
+  // y of a chunk through the wave's tile: written as lane (token li, values 4g..), read as lane
+  // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before this wave's
+  // previous post (its wait covers every LDS access of the wave).
+  auto store_y = [&](const f32x4 yv, int cy) {
+    st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    const float4 yq = ld_off<float4>(ytile, (uint32_t)((lane >> 2) * kYRow + 16 * (lane & 3)));
+    const int t = cy * kC + (lane >> 2);
+    if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
+  };
+  // ln_x (time-mix form): the GroupNorm of each token's 64 outputs. Each scan wave posts, per
+  // token, the mean and centred sum of squares of its 16 channels (ln_done[w] = chunks posted);
+  // a chunk is normalised and stored one chunk later, once all four have posted, by combining
+  // the four pairs (equal counts: mean of the means; sum of squares plus 16 times the squared
+  // deviations of the means), the same order in every wave. Partials alternate between two
+  // buffers by chunk parity: a wave writes chunk c's only after every wave has posted chunk
+  // c - 1, so every read of chunk c - 2's buffer has completed.
+  constexpr bool kLn = MODE == kPrepTmix && !CK;
+  float ln_g[4] = {1.f, 1.f, 1.f, 1.f}, ln_o[4] = {0.f, 0.f, 0.f, 0.f};
+  float2* ln_part = reinterpret_cast<float2*>(ring + kLnOff);  // [2][kScanW][kC]
+  f32x4 y_prev = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kLn) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = hh * kN + 16 * w + 4 * g + e;
+      if (p.ln_w) ln_g[e] = p.ln_w[ch];
+      if (p.ln_b) ln_o[e] = p.ln_b[ch];
+    }
+  }
+  auto finish_ln = [&](int cp) {
+    wait_all_at_least(ln_done, cp + 1);
+    const float2* pp = ln_part + (cp & 1) * kScanW * kC + li;
+    const float2 q0 = pp[0], q1 = pp[kC], q2 = pp[2 * kC], q3 = pp[3 * kC];
+    const float mu = ((q0.x + q1.x) + (q2.x + q3.x)) * 0.25f;
+    const float d0 = q0.x - mu, d1 = q1.x - mu, d2 = q2.x - mu, d3 = q3.x - mu;
+    const float m2 = ((q0.y + q1.y) + (q2.y + q3.y)) + 16.f * ((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
+    const float inv = 1.f / sqrtf(m2 * (1.f / kN) + kLnEps);
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = fmaf((y_prev[e] - mu) * inv, ln_g[e], ln_o[e]);
+    store_y(o, cp);
+  };
   Frag fa, fb;
   uint32_t va[4], vb[4];  // v two chunks ahead: the set of chunk c is reloaded with chunk c + 2
   load_v(0, va);
@@ -180,16 +232,24 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
     if constexpr (CK) ck_store(p.ck + ((int64_t)unit * nc + c) * kCkHalves, 16 * w, St);
     const f32x4 yv = scan_step<!CK>(St, cur);
     load_v(min(c + 2, nc - 1), vc);
-    if constexpr (!CK) {
-      // y through the wave's tile: written as lane (token li, values 4g..), read as lane
-      // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before the
-      // previous post (its wait covers every LDS access of this wave).
-      st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-      const float4 yq = ld_off<float4>(ytile, (uint32_t)((lane >> 2) * kYRow + 16 * (lane & 3)));
-      const int t = c * kC + (lane >> 2);
-      if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
+    if constexpr (kLn) {
+      // this wave's 16 channels of each token: their mean and centred sum of squares (lane
+      // (token li, g) holds channels 16 w + 4 g + e), to be combined over the four scan waves
+      float s1 = (yv[0] + yv[1]) + (yv[2] + yv[3]);
+      s1 += __shfl_xor(s1, 16);
+      s1 += __shfl_xor(s1, 32);
+      const float m_loc = s1 * (1.f / 16);
+      float s2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s2 = fmaf(yv[e] - m_loc, yv[e] - m_loc, s2);
+      s2 += __shfl_xor(s2, 16);
+      s2 += __shfl_xor(s2, 32);
+      if (c > 0) finish_ln(c - 1);  // the previous chunk, whose partials every wave has posted
+      if (g == 0) ln_part[((c & 1) * kScanW + w) * kC + li] = make_float2(m_loc, s2);
+      post(&ln_done[w], c + 1);
+      y_prev = yv;
+    } else if constexpr (!CK) {
+      store_y(yv, c);
     }
     post(&consumed[w], cn + 1);  // every fragment up to chunk cn is in registers
     ++c;
@@ -197,6 +257,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
   };
   while (body(fa, fb, va) && body(fb, fa, vb)) {
   }
+  if constexpr (kLn) finish_ln(nc - 1);
   if (p.s_out) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)

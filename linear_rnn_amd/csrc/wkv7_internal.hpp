@@ -82,17 +82,13 @@ struct TmixCall {
 };
 hipError_t launch_tmix(const TmixCall& c);
 // The fused operator as a chunked prefill (bfloat16 inputs): the prep forms the
-// decay, the unit key and the two slots, the scan writes y into out, and ln_x
-// normalises it in place. Decays below 2^-15 are clamped, as in the chunked
+// decay, the unit key and the two slots, and the scan (one workgroup per head) applies
+// ln_x to y as it writes out. Decays below 2^-15 are clamped, as in the chunked
 // prefill of the recurrence.
 hipError_t launch_tmix_chunked(const TmixCall& c);
 // The same with the one-kernel chunked prefill (the prep's time-mix mode in the
-// fused kernel), then ln_x in place.
+// fused kernel), its scan waves applying ln_x before out is written.
 hipError_t launch_tmix_fused(const TmixCall& c);
-// ln_x in place on rows of 64 (one token of one head each): GroupNorm per head with
-// eps 64e-5, then the per-channel affine (ln_w / ln_b may be null).
-hipError_t launch_tmix_ln(float* out, const float* ln_w, const float* ln_b, int64_t rows, int32_t H,
-                          hipStream_t stream);
 
 // Reverse-mode derivatives of the recurrence: a checkpointing forward pass and
 // a reverse pass over the checkpoints, all gradients float32.

@@ -121,33 +121,40 @@ struct ScanParams {
   float* s_dst;        // state at the slab end, or null
   int32_t T, H;
   int32_t c0, nc;
+  const float* ln_w;  // time-mix form: ln_x's affine per (head, channel), may be null (1)
+  const float* ln_b;  // may be null (0)
 };
 
 // A head's 64 value rows are independent: four compute waves of 16 rows each, two
-// per workgroup (one workgroup per CU keeps every compute wave on a SIMD of its
-// own). A third wave streams the workgroup's chunks straight into an LDS ring with
-// global-to-LDS loads (no register staging), kDist chunks ahead of the reads; the
-// compute waves issue no global loads, so nothing they wait on is behind a load.
-// One barrier per chunk.
-constexpr int kScanWaves = 2;  // compute waves per workgroup
-constexpr int kWgPerHead = 4 / kScanWaves;
-constexpr int kDist = 5;                          // chunks in flight ahead of the one read next
+// per workgroup for the plain recurrence (one workgroup per CU keeps every compute wave on
+// a SIMD of its own), all four in one workgroup for the time-mix form, so that a token's
+// 64 outputs meet in one workgroup for ln_x. A further wave streams the workgroup's chunks
+// straight into an LDS ring with global-to-LDS loads (no register staging), kDist chunks
+// ahead of the reads; the compute waves issue no global loads, so nothing they wait on is
+// behind a load. One barrier per chunk.
+constexpr int kDist = 5;  // chunks in flight ahead of the one read next
 // ring slots: the chunk being read, the kDist in flight and one spare, so that a slot is
 // reloaded only once the compute waves have used what they read from it (no wait on
 // outstanding LDS reads at the barrier)
 constexpr int kSlots = kDist + 2;
-constexpr int kVCols = 16 * kScanWaves;           // value columns of v this workgroup needs
-constexpr int kVBytes = kC * kVCols * 2;          // bfloat16, [token][kVCols]: 1 KiB
-constexpr int kSlotBytes = kRecBytes + kVBytes;   // 10,496
-// y staging: two chunks (by parity) of [token][kVCols] float32, so that a workgroup's y rows
-// leave in whole 128-byte lines rather than one 64-byte half per compute wave
-constexpr int kYStageBytes = kC * kVCols * 4;  // 2 KiB
-constexpr int kScanLds = kSlots * kSlotBytes + 2 * kYStageBytes;  // 77,568: two workgroups fit a compute unit
-constexpr int kLoads = kRecBlocks + 2;  // loads per lane per chunk: record blocks, e^gamma, v
-constexpr int kScanThreads = 64 * (kScanWaves + 1);
-// the load counter holds at most 63 outstanding operations: never more are in flight
-static_assert(kDist * kLoads < 64, "load counter");
-static_assert(kVBytes == 64 * 16 && kRecBlocks == 9, "one 16-byte piece of v per lane");
+template <int WAVES>
+struct ScanCfg {
+  static constexpr int kWgPerHead = 4 / WAVES;
+  static constexpr int kVCols = 16 * WAVES;           // value columns of v this workgroup needs
+  static constexpr int kVBytes = kC * kVCols * 2;     // bfloat16, [token][kVCols]: 1 or 2 KiB
+  static constexpr int kVLoads = kVBytes / 1024;      // one 16-byte piece per lane each
+  static constexpr int kSlotBytes = kRecBytes + kVBytes;  // 10,496 / 11,520
+  // y staging: two chunks (by parity) of [token][kVCols] float32, so that a workgroup's y
+  // rows leave in whole 128-byte lines rather than one 64-byte half per compute wave
+  static constexpr int kYStageBytes = kC * kVCols * 4;
+  static constexpr int kLds = kSlots * kSlotBytes + 2 * kYStageBytes;  // 77,568 (two per CU) / 88,832
+  static constexpr int kLoads = kRecBlocks + 1 + kVLoads;  // loads per lane per chunk: blocks, e^gamma, v
+  static constexpr int kThreads = 64 * (WAVES + 1);
+  // the load counter holds at most 63 outstanding operations: never more are in flight
+  static_assert(kDist * kLoads < 64, "load counter");
+  static_assert(kRecBlocks == 9 && kVBytes % 1024 == 0, "whole-wave pieces of v");
+};
+constexpr float kLnEps = 64e-5f;  // the GroupNorm eps of ln_x
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -171,7 +178,13 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
+// WAVES compute waves per workgroup; LN: ln_x on y before it is stored (WAVES == 4).
+template <int WAVES, bool LN>
+__global__ __launch_bounds__(64 * (WAVES + 1)) void wkv7_scan_kernel(ScanParams p) {
+  using Cfg = ScanCfg<WAVES>;
+  static_assert(!LN || WAVES == 4, "ln_x needs a token's 64 outputs in one workgroup");
+  constexpr int kScanWaves = WAVES, kWgPerHead = Cfg::kWgPerHead, kVCols = Cfg::kVCols;
+  constexpr int kSlotBytes = Cfg::kSlotBytes, kYStageBytes = Cfg::kYStageBytes, kLoads = Cfg::kLoads;
   extern __shared__ __align__(16) unsigned char ring[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
 
   // ---- loader wave: chunk x (clamped to the last one: past the end the loads repeat it)
   // into slot x % kSlots: the record as it is (nine 1 KiB blocks, then e^{gamma_15}),
-  // then v [token][kVCols] (lane l: token l / 4, eight columns). Tokens past the end of
+  // then v [token][kVCols] (16-byte pieces of eight columns, in token order). Tokens past the end of
   // the sequence repeat the last one; their coefficients in the record are zero.
   // Chunk x + kDist reuses the slot of chunk x + kDist - kSlots = x - 2: the compute
   // waves used what they read from it in the step of chunk x - 2, before the barrier
@@ -206,8 +219,12 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
       for (int b = 0; b < kRecBlocks; ++b) to_lds<16>(src + b * 1024 + lane * 16, slot + b * 1024);
       to_lds<4>(src + kRecD + lane * 4, slot + kRecD);
       const int nt = min(kC, p.T - (p.c0 + xc) * kC);
-      const int t = min(lane >> 2, nt - 1);
-      to_lds<16>(vbase + ((int64_t)(xc * kC + t) * tstride + 8 * (lane & 3)), slot + kRecBytes);
+      constexpr int ppt = kVCols / 8;  // pieces per token
+#pragma unroll
+      for (int h = 0; h < Cfg::kVLoads; ++h) {
+        const int t = min(lane / ppt + h * (64 / ppt), nt - 1);
+        to_lds<16>(vbase + ((int64_t)(xc * kC + t) * tstride + 8 * (lane % ppt)), slot + kRecBytes + 1024 * h);
+      }
     };
     // once chunk c + kDist is issued, chunk c + 1 has landed when at most the loads of
     // kDist - 1 chunks are outstanding (they complete in issue order)
@@ -250,17 +267,40 @@ __global__ __launch_bounds__(kScanThreads) void wkv7_scan_kernel(ScanParams p) {
     read_frag(slot, f);
   };
   // y of chunk c goes through LDS: each compute wave stages its 16 columns (lane: token li,
-  // columns 16 wave + 4g .. + 3), and after the next barrier wave q stores tokens 8q .. 8q + 7
-  // of all kVCols columns, eight lanes (128 contiguous bytes) per token; tokens past the end
-  // of the sequence are not stored
+  // columns 16 wave + 4g .. + 3), and after the next barrier wave q stores its 16 / WAVES
+  // tokens of all kVCols columns, kVCols / 4 lanes (whole 128-byte lines) per token; tokens
+  // past the end of the sequence are not stored. LN: those kVCols / 4 = 16 lanes are one DPP
+  // row holding a token's 64 outputs, so ln_x (mean, then the population variance of the
+  // centred values, then the affine) is two row sums before the store.
+  constexpr int lpt = kVCols / 4;  // lanes per token in the store
+  const int cc = 4 * (lane % lpt);
+  float ln_g[4] = {1.f, 1.f, 1.f, 1.f}, ln_o[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (LN) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (p.ln_w) ln_g[e] = p.ln_w[hh * kN + cc + e];
+      if (p.ln_b) ln_o[e] = p.ln_b[hh * kN + cc + e];
+    }
+  }
   unsigned char* ystage = ring + kSlots * kSlotBytes;
   auto stage_y = [&](auto par, const f32x4& yv) {
     *reinterpret_cast<f32x4*>(ystage + decltype(par)::value * kYStageBytes + (li * kVCols + 16 * wave + 4 * g) * 4) = yv;
   };
   auto flush_y = [&](auto par, int c) {
-    const int tt = 8 * wave + (lane >> 3), cc = 4 * (lane & 7);
-    const f32x4 v =
-        *reinterpret_cast<const f32x4*>(ystage + decltype(par)::value * kYStageBytes + (tt * kVCols + cc) * 4);
+    const int tt = (kC / kScanWaves) * wave + lane / lpt;
+    f32x4 v = *reinterpret_cast<const f32x4*>(ystage + decltype(par)::value * kYStageBytes + (tt * kVCols + cc) * 4);
+    if constexpr (LN) {
+      const float mu = row16_sum((v[0] + v[1]) + (v[2] + v[3])) * (1.f / kN);
+      float d[4], q = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d[e] = v[e] - mu;
+        q = fmaf(d[e], d[e], q);
+      }
+      const float inv = 1.f / sqrtf(row16_sum(q) * (1.f / kN) + kLnEps);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(d[e] * inv, ln_g[e], ln_o[e]);
+    }
     const int nt = min(kC, p.T - (p.c0 + c) * kC);
     const uint32_t off = (uint32_t)(((c * kC + tt) * tstride + cc) * 4u);
     if (nt == kC)  // the same for the whole wave: a whole chunk stores with no lane masked
@@ -415,13 +455,15 @@ namespace {
 // One chunked pass: the prep (in the given input mode) and the scan, slab by slab.
 struct SplitJob {
   PrepIn in;  // input pointers (T and H are filled in from the call)
-  int mode;
+  int mode;   // kPrepTmix: the time-mix form, with ln_x applied before y is stored
   const uint16_t* v;
   float* y;
   const float* s_in;
   float* s_out;
   int64_t B, T, H;
   hipStream_t stream;
+  const float* ln_w = nullptr;
+  const float* ln_b = nullptr;
 };
 
 // One chunked pass, slab by slab. With fixed == nullptr the records live in the
@@ -471,17 +513,25 @@ hipError_t run_split(const SplitJob& j, unsigned char* fixed = nullptr, size_t c
 
   const void* prep_fn = j.mode == kPrepTmix ? reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepTmix>)
                                             : reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>);
-  const void* scan_fn = reinterpret_cast<const void*>(&wkv7_scan_kernel);
+  const bool tmix = j.mode == kPrepTmix;
+  const void* scan_plain = reinterpret_cast<const void*>(&wkv7_scan_kernel<2, false>);
+  const void* scan_ln = reinterpret_cast<const void*>(&wkv7_scan_kernel<4, true>);
+  const void* scan_fn = tmix ? scan_ln : scan_plain;
   const int prep_lds = kPrepWaves * kPrepScratch;
-  const int scan_lds = kScanLds;
+  const int scan_lds = tmix ? ScanCfg<4>::kLds : ScanCfg<2>::kLds;
+  const int scan_threads = tmix ? ScanCfg<4>::kThreads : ScanCfg<2>::kThreads;
+  const int64_t scan_blocks = units * (tmix ? ScanCfg<4>::kWgPerHead : ScanCfg<2>::kWgPerHead);
   static const hipError_t a0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepPlain>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
   static const hipError_t a1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&wkv7_prep_kernel<kPrepTmix>),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, prep_lds);
-  static const hipError_t a2 = hipFuncSetAttribute(scan_fn, hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
+  static const hipError_t a2 =
+      hipFuncSetAttribute(scan_plain, hipFuncAttributeMaxDynamicSharedMemorySize, ScanCfg<2>::kLds);
+  static const hipError_t a3 = hipFuncSetAttribute(scan_ln, hipFuncAttributeMaxDynamicSharedMemorySize, ScanCfg<4>::kLds);
   if (a0 != hipSuccess) return a0;
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
+  if (a3 != hipSuccess) return a3;
 
   for (int64_t s = 0; s < nslab; ++s) {
     const int64_t c0 = s * slab;
@@ -506,42 +556,14 @@ hipError_t run_split(const SplitJob& j, unsigned char* fixed = nullptr, size_t c
                   (int32_t)j.T,
                   (int32_t)j.H,
                   (int32_t)c0,
-                  (int32_t)ncs};
+                  (int32_t)ncs,
+                  j.ln_w,
+                  j.ln_b};
     void* sargs[] = {&sp};
-    e = hipLaunchKernel(scan_fn, dim3((uint32_t)(units * kWgPerHead)), dim3(kScanThreads), sargs, scan_lds,
-                        j.stream);
+    e = hipLaunchKernel(scan_fn, dim3((uint32_t)scan_blocks), dim3(scan_threads), sargs, scan_lds, j.stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
-}
-
-// Sum over the 64 lanes of a wave (every lane ends with the same bits).
-__device__ __forceinline__ float wave_sum64(float x) {
-  x = row16_sum(x);
-  x = x + __shfl_xor(x, 16);
-  x = x + __shfl_xor(x, 32);
-  return x;
-}
-
-// ln_x in place on y [rows, 64] (a row is one token of one head): a GroupNorm with
-// one group per head, mean and population variance over the 64 channels, then the
-// per-channel affine. One wave per row, lane = channel.
-constexpr float kGroupNormEps = 64e-5f;
-__global__ __launch_bounds__(256) void tmix_ln_kernel(float* y, const float* ln_w, const float* ln_b, int64_t rows,
-                                                      int32_t H) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;  // wave-uniform
-  const int h = (int)(row % H);
-  float* yr = y + row * kN;
-  const float v = yr[lane];
-  const float mu = wave_sum64(v) * (1.f / kN);
-  const float d = v - mu;
-  const float var = wave_sum64(d * d) * (1.f / kN);
-  const float o = d * (1.f / sqrtf(var + kGroupNormEps));
-  const float gw = ln_w ? ln_w[h * kN + lane] : 1.f;
-  const float gb = ln_b ? ln_b[h * kN + lane] : 0.f;
-  yr[lane] = fmaf(o, gw, gb);
 }
 
 }  // namespace
@@ -619,19 +641,10 @@ hipError_t launch_tmix_chunked(const TmixCall& c) {
   in.k = static_cast<const uint16_t*>(t.k);
   in.a = static_cast<const uint16_t*>(t.kk);
   in.b = static_cast<const uint16_t*>(t.a_lr);
-  // the scan writes y into out; ln_x then normalises it in place
-  SplitJob j{in, kPrepTmix, static_cast<const uint16_t*>(t.v), t.out, t.s_in, t.s_out, c.B, t.T, c.H, c.stream};
-  hipError_t e = run_split(j);
-  if (e != hipSuccess) return e;
-  return launch_tmix_ln(t.out, t.ln_w, t.ln_b, c.B * t.T * c.H, (int32_t)c.H, c.stream);
-}
-
-hipError_t launch_tmix_ln(float* out, const float* ln_w, const float* ln_b, int64_t rows, int32_t H,
-                          hipStream_t stream) {
-  if (rows <= 0) return hipSuccess;
-  void* args[] = {&out, &ln_w, &ln_b, &rows, &H};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&tmix_ln_kernel), dim3((uint32_t)((rows + 3) / 4)),
-                         dim3(256), args, 0, stream);
+  // the scan applies ln_x to y before it stores it into out
+  SplitJob j{in, kPrepTmix, static_cast<const uint16_t*>(t.v), t.out, t.s_in, t.s_out, c.B, t.T, c.H, c.stream,
+             t.ln_w, t.ln_b};
+  return run_split(j);
 }
 
 }  // namespace rwkv7
