@@ -31,20 +31,29 @@ namespace {
 using namespace chunk;
 using namespace fused;
 
-template <int MODE, bool CK = false>
+template <int MODE, bool CK = false, bool ROWS = true>
 __global__ __launch_bounds__(kThreads) void wkv7_fused_kernel(FusedParams p) {
   extern __shared__ __align__(16) unsigned char ring[];
-  fused_body<MODE, CK>(p, ring, blockIdx.x);
+  fused_body<MODE, CK, ROWS>(p, ring, blockIdx.x);
 }
 
-template <int MODE, bool CK = false>
+template <int MODE, bool CK = false, bool ROWS = true>
 hipError_t launch_fused(const FusedParams& fp, int64_t units, hipStream_t stream) {
-  const void* fn = reinterpret_cast<const void*>(&wkv7_fused_kernel<MODE, CK>);
+  const void* fn = reinterpret_cast<const void*>(&wkv7_fused_kernel<MODE, CK, ROWS>);
   static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return attr;
   FusedParams q = fp;
   void* args[] = {&q};
   return hipLaunchKernel(fn, dim3((uint32_t)units), dim3(kThreads), args, kLds, stream);
+}
+
+// Compute units of the current device (256 if the query fails).
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
 }
 
 // Offsets inside a sequence are 32-bit element counts (T * H * 64 below 2^31).
@@ -69,7 +78,10 @@ hipError_t launch_chunked(const WkvCall& c) {
   fp.s_in = static_cast<const float*>(c.s_in);
   fp.s_out = static_cast<float*>(c.s_out);
   fp.nc = (int32_t)((c.T + kC - 1) / kC);
-  return launch_fused<kPrepPlain>(fp, c.B * c.H, c.stream);
+  // y as whole token rows when the heads fill the chip, else through each scan wave's tile
+  const int64_t units = c.B * c.H;
+  if (units >= cu_count()) return launch_fused<kPrepPlain, false, true>(fp, units, c.stream);
+  return launch_fused<kPrepPlain, false, false>(fp, units, c.stream);
 }
 
 hipError_t launch_tmix_fused(const TmixCall& c) {

@@ -15,16 +15,19 @@ constexpr int kScanW = 4;                    // scan waves (16 value rows each)
 constexpr int kPrepW = 8;                    // prep waves (one chunk each at a time)
 constexpr int kRing = 10;                    // record slots
 constexpr int kSlot = kRecBytes;             // 9,472 bytes (a scan wave loads its v itself)
-// y of a scan wave's chunk passes through an LDS tile of its own, [token][16 values] float32
-// with 80-byte rows, so that its stores cover 4 tokens per quarter-wave instead of 16
+// y leaves the scan waves in one of two ways (ROWS below):
+// - staged as whole token rows, [chunk parity][token][64 values] float32 (rows padded to 272
+//   bytes against bank conflicts), each scan wave storing four whole 256-byte rows per chunk one
+//   chunk later; a progress word per scan wave counts the chunks it has staged;
+// - through a tile of each wave's own, [token][16 values] float32 with 80-byte rows, so that its
+//   stores cover 4 tokens per quarter-wave instead of 16 (no wait on the other scan waves).
+constexpr int kYRowF = kN + 4;               // floats per staged row
+constexpr int kYOff = kRing * kSlot;
+constexpr int kYBytes = 2 * kC * kYRowF * 4;  // 8,704 bytes
 constexpr int kYRow = 80;
 constexpr int kYTile = kC * kYRow;           // 1,280 bytes per scan wave
-constexpr int kYOff = kRing * kSlot;
-// ln_x of the time-mix form: per chunk parity, scan wave and token, the mean and centred sum
-// of squares of the wave's 16 channels; one progress word per scan wave
-constexpr int kLnOff = kYOff + kScanW * kYTile;
-constexpr int kLnBytes = 2 * kScanW * kC * 8;  // [chunk parity][wave][token] (mean, sum of squares)
-constexpr int kCtrlOff = kLnOff + kLnBytes;  // ready[kRing], consumed[kScanW], ln_done[kScanW]
+constexpr int kYTileOff = kYOff + kYBytes;
+constexpr int kCtrlOff = kYTileOff + kScanW * kYTile;  // ready[kRing], consumed[kScanW], y_done[kScanW]
 constexpr int kLds = kCtrlOff + 4 * (kRing + 2 * kScanW);
 constexpr float kLnEps = 64e-5f;  // the GroupNorm eps of ln_x
 constexpr int kThreads = 64 * (kScanW + kPrepW);
@@ -77,7 +80,11 @@ __device__ __forceinline__ void post(int* flag, int value) {
 
 // CK: the checkpoint form used by the backward. It stores, for every chunk, the
 // float16 state the chunk's products start from (ck_store) and writes no y.
-template <int MODE, bool CK>
+// ROWS: y staged as whole token rows (the time-mix form always: ln_x needs a token's 64
+// outputs together); otherwise through each scan wave's own tile. Measured on the plain form:
+// rows 0.920 -> 0.910 ms at D4096-long and 0.245 -> 0.237 ms at L24-D1024 (256 heads), but
+// 0.193 -> 0.200 ms at L12-D768 (96 heads), where each scan wave's extra steps per chunk cost.
+template <int MODE, bool CK, bool ROWS = true>
 __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* ring, int unit) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -88,10 +95,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
   const int64_t seq_base = (int64_t)bb * T * H * kN + (int64_t)hh * kN;  // element offset of (bb, 0, hh, 0)
   int* ready = reinterpret_cast<int*>(ring + kCtrlOff);
   int* consumed = ready + kRing;
-  int* ln_done = consumed + kScanW;
+  int* y_done = consumed + kScanW;
   if (threadIdx.x < kRing) ready[threadIdx.x] = -1;
   if (threadIdx.x < kScanW) consumed[threadIdx.x] = 0;
-  if (threadIdx.x < kScanW) ln_done[threadIdx.x] = 0;
+  if (threadIdx.x < kScanW) y_done[threadIdx.x] = 0;
   __syncthreads();
 
   if (wave >= kScanW) {
@@ -154,9 +161,12 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the state has landed
-  // stores: lane l writes token l / 4 of the chunk, values 16 w + 4 (l % 4) .. + 3
-  float* ybase = p.y + seq_base + 16 * w + 4 * (lane & 3);
-  unsigned char* ytile = ring + kYOff + w * kYTile;
+  // row stores: lane l writes token 4 w + l / 16 of a chunk, values 4 (l % 16) .. + 3;
+  // tile stores: lane l writes token l / 4, values 16 w + 4 (l % 4) .. + 3
+  constexpr bool kRows = ROWS || (MODE == kPrepTmix && !CK);
+  float* ybase = kRows ? p.y + seq_base + 4 * (lane & 15) : p.y + seq_base + 16 * w + 4 * (lane & 3);
+  float* ystage = reinterpret_cast<float*>(ring + kYOff);
+  unsigned char* ytile = ring + kYTileOff + w * kYTile;
   auto slot_of = [&](int c) { return ring + (c % kRing) * kSlot; };
   // v of chunk c for this wave: V[t = 4g + e][i = 16 w + li], raw bfloat16 bits (a
   // quarter-wave reads 32 contiguous bytes of one token row); tokens past the end read
@@ -169,10 +179,30 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
       vr[e] = vbase[(int64_t)t * tstride];
     }
   };
-  // y of a chunk through the wave's tile: written as lane (token li, values 4g..), read as lane
-  // (token l / 4, values 4 (l % 4) ..). The tile's previous reads completed before this wave's
-  // previous post (its wait covers every LDS access of the wave).
-  auto store_y = [&](const f32x4 yv, int cy) {
+  // y of chunk c: each scan wave writes its 16 values of every token into the staged rows of
+  // buffer c % 2 and posts; one chunk later, once all four have posted, wave w stores tokens
+  // 4w .. 4w + 3 whole (16 lanes per token, one DPP row). A wave writes buffer c % 2 only after
+  // every wave has posted chunk c - 1, so every read of chunk c - 2's rows has completed.
+  // Time-mix form: ln_x (mean, then the population variance of the centred values, then the
+  // affine) on the whole row before the store, by two row sums.
+  constexpr bool kLn = MODE == kPrepTmix && !CK;
+  float ln_g[4] = {1.f, 1.f, 1.f, 1.f}, ln_o[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kLn) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = hh * kN + 4 * (lane & 15) + e;
+      if (p.ln_w) ln_g[e] = p.ln_w[ch];
+      if (p.ln_b) ln_o[e] = p.ln_b[ch];
+    }
+  }
+  auto stage_y = [&](const f32x4 yv, int cy) {
+    st_off<float4>(ystage, (uint32_t)((((cy & 1) * kC + li) * kYRowF + 16 * w + 4 * g) * 4),
+                   make_float4(yv[0], yv[1], yv[2], yv[3]));
+    post(&y_done[w], cy + 1);
+  };
+  // the tile's previous reads completed before this wave's previous post (its wait covers every
+  // LDS access of the wave)
+  auto tile_y = [&](const f32x4 yv, int cy) {
     st_off<float4>(ytile, (uint32_t)(li * kYRow + 16 * g), make_float4(yv[0], yv[1], yv[2], yv[3]));
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
@@ -180,37 +210,20 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
     const int t = cy * kC + (lane >> 2);
     if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = yq;
   };
-  // ln_x (time-mix form): the GroupNorm of each token's 64 outputs. Each scan wave posts, per
-  // token, the mean and centred sum of squares of its 16 channels (ln_done[w] = chunks posted);
-  // a chunk is normalised and stored one chunk later, once all four have posted, by combining
-  // the four pairs (equal counts: mean of the means; sum of squares plus 16 times the squared
-  // deviations of the means), the same order in every wave. Partials alternate between two
-  // buffers by chunk parity: a wave writes chunk c's only after every wave has posted chunk
-  // c - 1, so every read of chunk c - 2's buffer has completed.
-  constexpr bool kLn = MODE == kPrepTmix && !CK;
-  float ln_g[4] = {1.f, 1.f, 1.f, 1.f}, ln_o[4] = {0.f, 0.f, 0.f, 0.f};
-  float2* ln_part = reinterpret_cast<float2*>(ring + kLnOff);  // [2][kScanW][kC]
-  f32x4 y_prev = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (kLn) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ch = hh * kN + 16 * w + 4 * g + e;
-      if (p.ln_w) ln_g[e] = p.ln_w[ch];
-      if (p.ln_b) ln_o[e] = p.ln_b[ch];
+  auto flush_y = [&](int cy) {
+    wait_all_at_least(y_done, cy + 1);
+    const int tt = 4 * w + (lane >> 4);
+    float4 q = ld_off<float4>(ystage, (uint32_t)((((cy & 1) * kC + tt) * kYRowF + 4 * (lane & 15)) * 4));
+    if constexpr (kLn) {
+      const float mu = row16_sum((q.x + q.y) + (q.z + q.w)) * (1.f / kN);
+      const float d0 = q.x - mu, d1 = q.y - mu, d2 = q.z - mu, d3 = q.w - mu;
+      const float var = row16_sum(fmaf(d0, d0, fmaf(d1, d1, fmaf(d2, d2, d3 * d3)))) * (1.f / kN);
+      const float inv = 1.f / sqrtf(var + kLnEps);
+      q = make_float4(fmaf(d0 * inv, ln_g[0], ln_o[0]), fmaf(d1 * inv, ln_g[1], ln_o[1]),
+                      fmaf(d2 * inv, ln_g[2], ln_o[2]), fmaf(d3 * inv, ln_g[3], ln_o[3]));
     }
-  }
-  auto finish_ln = [&](int cp) {
-    wait_all_at_least(ln_done, cp + 1);
-    const float2* pp = ln_part + (cp & 1) * kScanW * kC + li;
-    const float2 q0 = pp[0], q1 = pp[kC], q2 = pp[2 * kC], q3 = pp[3 * kC];
-    const float mu = ((q0.x + q1.x) + (q2.x + q3.x)) * 0.25f;
-    const float d0 = q0.x - mu, d1 = q1.x - mu, d2 = q2.x - mu, d3 = q3.x - mu;
-    const float m2 = ((q0.y + q1.y) + (q2.y + q3.y)) + 16.f * ((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
-    const float inv = 1.f / sqrtf(m2 * (1.f / kN) + kLnEps);
-    f32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = fmaf((y_prev[e] - mu) * inv, ln_g[e], ln_o[e]);
-    store_y(o, cp);
+    const int t = cy * kC + tt;
+    if (t < T) *reinterpret_cast<float4*>(ybase + (int64_t)t * tstride) = q;
   };
   Frag fa, fb;
   uint32_t va[4], vb[4];  // v two chunks ahead: the set of chunk c is reloaded with chunk c + 2
@@ -232,24 +245,11 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
     if constexpr (CK) ck_store(p.ck + ((int64_t)unit * nc + c) * kCkHalves, 16 * w, St);
     const f32x4 yv = scan_step<!CK>(St, cur);
     load_v(min(c + 2, nc - 1), vc);
-    if constexpr (kLn) {
-      // this wave's 16 channels of each token: their mean and centred sum of squares (lane
-      // (token li, g) holds channels 16 w + 4 g + e), to be combined over the four scan waves
-      float s1 = (yv[0] + yv[1]) + (yv[2] + yv[3]);
-      s1 += __shfl_xor(s1, 16);
-      s1 += __shfl_xor(s1, 32);
-      const float m_loc = s1 * (1.f / 16);
-      float s2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s2 = fmaf(yv[e] - m_loc, yv[e] - m_loc, s2);
-      s2 += __shfl_xor(s2, 16);
-      s2 += __shfl_xor(s2, 32);
-      if (c > 0) finish_ln(c - 1);  // the previous chunk, whose partials every wave has posted
-      if (g == 0) ln_part[((c & 1) * kScanW + w) * kC + li] = make_float2(m_loc, s2);
-      post(&ln_done[w], c + 1);
-      y_prev = yv;
+    if constexpr (!CK && kRows) {
+      if (c > 0) flush_y(c - 1);  // the previous chunk, which every wave has staged
+      stage_y(yv, c);
     } else if constexpr (!CK) {
-      store_y(yv, c);
+      tile_y(yv, c);
     }
     post(&consumed[w], cn + 1);  // every fragment up to chunk cn is in registers
     ++c;
@@ -257,7 +257,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
   };
   while (body(fa, fb, va) && body(fb, fa, vb)) {
   }
-  if constexpr (kLn) finish_ln(nc - 1);
+  if constexpr (!CK && kRows) flush_y(nc - 1);
   if (p.s_out) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
