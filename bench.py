@@ -198,7 +198,7 @@ def prefill_leg(torch, wkv, cfg, d, s_in, steps, warmup, flush, other_algos=True
     if other_algos:
         alt = {}
         for a in (wkv.RWKV7_ALGO_CHUNKED, wkv.RWKV7_ALGO_CHUNKED_SPLIT):
-            time_steps(torch, call(a), 3, flush)
+            time_steps(torch, call(a), 10, flush)
             t = time_steps(torch, call(a), reps_alt, flush)
             alt[ALGO_NAMES[a]] = {"ms_median": med(t), "ms_min": min(t),
                                   "hbm_frac": algo_bytes(B, T, H) / (med(t) * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -206,7 +206,7 @@ def prefill_leg(torch, wkv, cfg, d, s_in, steps, warmup, flush, other_algos=True
     return res
 
 
-def resume_leg(torch, wkv, cfg, d, s_in, steps, flush, segments=4):
+def resume_leg(torch, wkv, cfg, d, s_in, steps, flush, segments=4, warmup=10):
     """The sequence as `segments` consecutive calls with the state carried in place (one step = all calls)."""
     B, T, H = cfg.B, cfg.T, cfg.H
     L = T // segments
@@ -221,7 +221,7 @@ def resume_leg(torch, wkv, cfg, d, s_in, steps, flush, segments=4):
         for p, y in zip(parts, ys):
             wkv.rwkv7_wkv_prefill(p["r"], p["w"], p["k"], p["v"], p["a"], p["b"], st, y, st)
 
-    time_steps(torch, run, 3, flush, before=reset)
+    time_steps(torch, run, warmup, flush, before=reset)
     ms_all = time_steps(torch, run, steps, flush, before=reset)
     ms = med(ms_all)
     nbytes = algo_bytes(B, T, H) + 2 * (segments - 1) * B * H * N * N * 4
@@ -238,7 +238,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--algo", type=int, default=0,
                     help="headline algorithm: 0 automatic, 1 sequential, 2 chunked (one kernel), 3 chunked (split)")
     ap.add_argument("--workload", default="D4096-long-prefill",
@@ -321,7 +321,7 @@ def main(argv=None):
             si = torch.from_numpy(xs["state_in"]).cuda()
             shapes[name] = prefill_leg(torch, wkv, c, ds, si, args.steps, args.warmup, flush)
             if name.startswith("L24"):
-                shapes[name + ":4x1024"] = resume_leg(torch, wkv, c, ds, si, args.steps, flush)
+                shapes[name + ":4x1024"] = resume_leg(torch, wkv, c, ds, si, args.steps, flush, warmup=args.warmup)
             del ds, xs
         out["prefill_shapes"] = shapes
 

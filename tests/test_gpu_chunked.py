@@ -48,6 +48,17 @@ def test_ragged_vs_oracle(torch, CH, B, T, H):
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
 
 
+# At least as many heads as compute units: the fused kernel stages y as whole token rows
+# (one chunk late) instead of per-wave tiles; ragged ends, 1-token last chunks, more heads than CUs
+@pytest.mark.parametrize("B,T,H", [(16, 33, 16), (4, 161, 64), (20, 17, 16)])
+def test_ragged_many_heads_vs_oracle(torch, CH, B, T, H):
+    say("algo", CH, "chunked ragged, many heads", B, T, H)
+    x = make_inputs(CONFIGS["L24-D1024-prefill-resume"], B=B, T=T, H=H, seed=300 + T)
+    y, s = run(torch, to_dev(x), CH)
+    yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
+    assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
+
+
 def test_zero_initial_state(torch, CH):
     say("algo", CH, "chunked, state_in NULL")
     x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=77, H=4, seed=3)
