@@ -18,15 +18,17 @@
 //
 // Three kernels:
 //   1. the one-kernel chunked prefill in its checkpoint form stores the float16 state at
-//      every chunk start (wkv7_fused.hpp);
+//      the start of every even chunk (wkv7_fused.hpp);
 //   2. the chain, one workgroup per head: prep waves rebuild each chunk's chain record
 //      (B-, L_rb^T, T^T, [R^^T | A^^T], e^{gamma_15}) into an LDS ring, last chunk
-//      first; scan waves carry G in float32 back through the chunks, store each chunk's
-//      end G (float16) and finally dL/dS_0.
+//      first; scan waves carry G in float32 back through the chunks, store the end G
+//      (float16) of every odd chunk and of the last one, and finally dL/dS_0.
 //   1 and 2 need only the inputs and dY, so one launch (wkv7_bpass_kernel) runs both,
 //   a workgroup per head for each;
 //   3. wkv7_bgrad_kernel, one wave per (head, chunk) over the whole chip, forms the
-//      chunk's input gradients from its inputs, dY, S0 and end G.
+//      chunk's input gradients from its inputs, dY, S0 and end G; the two waves of a
+//      chunk pair rebuild the odd chunk's S0 and the even chunk's G from what is stored
+//      (one more chunk step each way), which halves the float16 arrays.
 #include <cstdint>
 
 #include "wkv7_chunk_ops.hpp"
@@ -158,7 +160,8 @@ struct ChainParams {
   const float* dy;     // [B, T, H, 64]
   const float* ds_out; // [B, H, 64, 64] or null (zero)
   float* ds_in;        // [B, H, 64, 64] or null
-  _Float16* gend;      // [B*H][nc] float16 G at every chunk's end (fragment order)
+  _Float16* gend;      // [B*H][(nc + 1) / 2] float16 G at the end of every odd chunk c and of the
+                       // last one, at index c / 2 (fragment order)
   int32_t nc;
 };
 
@@ -249,7 +252,8 @@ __device__ __forceinline__ void chain_body(const ChainParams& p, unsigned char* 
     wait_at_least(&ready[qn % kRing], qn);
     read_cfrag(slot_of(qn), nxt);
     const int c = nc - 1 - q;
-    ck_store(p.gend + ((int64_t)unit * nc + c) * kCkHalves, 16 * w, Gt);  // G at the end of chunk c
+    if ((c & 1) || c == nc - 1)  // G at the end of chunk c
+      ck_store(p.gend + ((int64_t)unit * ((nc + 1) >> 1) + (c >> 1)) * kCkHalves, 16 * w, Gt);
     half4 dyh;
 #pragma unroll
     for (int e = 0; e < 4; ++e) dyh[e] = (_Float16)dcur[e];
@@ -325,28 +329,46 @@ hipError_t launch_pass(const fused::FusedParams& fp, const ChainParams& cp, int6
 // An identity product turns one into the other (tr16). A product with its operands
 // swapped returns the transposed result (the same registers serve as A and B), so
 // key-space results land in the token layout: lane (t = li, g), keys 16 kt + 4 g + e.
-// Contractions over the 64 value rows take row 16 (2 rp + h) + 4 g + e for
-// (rp, h = element / 4, e), two 16-row tiles per 16x16x32 product.
-constexpr int kGW = 4;  // waves (items) per workgroup
+// The contractions over the 64 value rows accumulate one 16-row tile at a time
+// (16x16x16 products), while that tile's U, dX, S0 and G are in registers.
+constexpr int kGW = 2;  // waves per workgroup: one chunk pair (wave 0 the even chunk, wave 1 the odd)
 // Per wave: the chunk's staged r, a, b, k rows (kept for the whole item), the factor
-// rows, the solve's scratch, a 64-float key exchange.
+// rows, the solve's scratch, a 64-float key exchange, and the 64x64 float16 state (or
+// gradient) handed to the other wave of the pair.
 constexpr int kGStage = 0;
 constexpr int kGFac = kStageBytes;
 constexpr int kGScr = kGFac + kFacBytes;
 constexpr int kGEx = kGScr + 4096;
-constexpr int kGWaveLds = kGEx + kN * 4;  // 18,464 bytes
-static_assert(kGScr % 16 == 0 && kGEx % 16 == 0 && kGWaveLds % 16 == 0, "16-byte aligned areas");
+constexpr int kGX = kGEx + kN * 4;
+constexpr int kGWaveLds = kGX + kCkHalves * 2;  // 26,656 bytes
+static_assert(kGScr % 16 == 0 && kGX % 16 == 0 && kGWaveLds % 16 == 0, "16-byte aligned areas");
+static_assert(3 * kGW * kGWaveLds <= 160 * 1024, "three workgroups per compute unit");
 
 struct GradParams {
   PrepIn in;             // r, w, k, a, b (bfloat16), T, H
   const uint16_t* v;
   const float* dy;
-  const _Float16* s0;    // [units][nc] chunk start states (fragment order)
-  const _Float16* gend;  // [units][nc] gradients at chunk ends (fragment order)
+  const _Float16* s0;    // [units][np] start states of the even chunks (fragment order)
+  const _Float16* gend;  // [units][np] gradients at the ends of the odd chunks and the last one
   float* grad[6];        // dr, dw, dk, dv, da, db
-  int64_t items;         // units * nc
+  int64_t pairs;         // units * np, np = (nc + 1) / 2
   int32_t nc;
 };
+
+// The handed-over state: row-major rows of 128 bytes; the 16-byte piece (kp, g) of row i
+// sits at piece (4 kp + g) ^ (i & 7), so that the 16 rows of a row-vector access spread
+// over the banks.
+__device__ __forceinline__ uint32_t xt_off(int row, int kp, int g) {
+  return (uint32_t)(row * 128 + 16 * ((4 * kp + g) ^ (row & 7)));
+}
+// Workgroup barrier for the LDS hand-off: this wave's LDS accesses have completed, global
+// ones stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ half4 tr16(half4 x, half4 eye) { return to_h4(Mma16::mma(x, eye, Mma16::zero())); }
 __device__ __forceinline__ half4 lo4(half8 x) { return half4{x[0], x[1], x[2], x[3]}; }
@@ -384,23 +406,12 @@ __device__ __forceinline__ float row_suffix16(float x) {
   return x;
 }
 
-// One wave per (head, chunk). Fragment conventions (16x16 tiles; lane (li, g)):
-//   "row vector" X[li][4g + e] (A operand of X, B operand of X^T; the token layout when
-//   li is a token), "column vector" X[4g + e][li] (the D layout; B operand of X).
-// An identity product turns one into the other (tr16). A product with its operands
-// swapped returns the transposed result (the same registers serve as A and B), so
-// key-space results land in the token layout: lane (t = li, g), keys 16 kt + 4 g + e.
-// The contractions over the 64 value rows accumulate one 16-row tile at a time
-// (16x16x16 products), while that tile's U, dX, S0 and G are in registers.
-__global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
-  extern __shared__ __align__(16) unsigned char lds[];
+// The work of one wave: chunk c of head unit, the odd (ODD) or even chunk of its pair.
+template <bool ODD>
+__device__ __forceinline__ void grad_item(const GradParams& p, unsigned char* lds, int wave, int unit, int c) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
-  const int64_t item = (int64_t)blockIdx.x * kGW + wave;
-  if (item >= p.items) return;
-  const int nc = p.nc;
-  const int unit = (int)(item / nc), c = (int)(item % nc);
+  const int nc = p.nc, np = (nc + 1) >> 1;
   const int H = p.in.H, T = p.in.T;
   const int bb = unit / H, hh = unit % H;
   const uint32_t tstride = (uint32_t)H * kN;
@@ -429,14 +440,20 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     vh[rt] = b2h(ld_off<uint2>(p.v + base, (uint32_t)(tl * tstride + 16 * rt + 4 * g) * 2u));
     dyh[rt] = f2h(ld_off<float4>(p.dy + base, (uint32_t)(tl * tstride + 16 * rt + 4 * g) * 4u));
   }
-  const _Float16* s0p = p.s0 + item * kCkHalves;
-  const _Float16* gp = p.gend + item * kCkHalves;
   prep_rows_to_raw(rows, stage, x);  // the staged rows stay in LDS for the end
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(vh[rt]), "+v"(dyh[rt]));  // held as float16
+  const int64_t slot = ((int64_t)unit * np + (c >> 1)) * kCkHalves;
+  const _Float16* s0p = p.s0 + slot;    // even chunks
+  const _Float16* gp = p.gend + slot;   // odd chunks and the last one
+  const bool g_mem = ODD || c == nc - 1;
+  unsigned char* xown = wl + kGX;
+  const unsigned char* xpeer = lds + (wave ^ 1) * kGWaveLds + kGX;
   prep_factors<kPrepPlain>(x, fac, reinterpret_cast<unsigned char*>(ex));
 
   // ---- chunk prep: the Grams (column vectors: lane (s = li, g) holds L[t = 4g + e][s]),
   // A^ column vectors, B-, K- row vectors
-  half4 AT[4], bbar[4], kbar[4];
+  half4 AT[4], RT[4], bbar[4], kbar[4];  // RT: R^ column vectors (odd chunk only)
   MmaBF::acc Lab = MmaBF::zero(), Lak = MmaBF::zero(), Lrb = MmaBF::zero(), Lrk = MmaBF::zero();
   {
     bf16x8 ahH, ahL, rhH, rhL, bhH, bhL, khH, khL;
@@ -448,7 +465,7 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
       const float4 g15 = lds4(&fac[16 * kFacRow + col]);
       const float4 e7 = lds4(&fac[kRowE7 * kFacRow + col]);
       float ag[4], rg[4], bg[4], kg[4];
-      half4 ah;
+      half4 ah, rh;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float av = bf4(x.ar[kt], e), bv = bf4(x.br[kt], e), rv = bf4(x.rr[kt], e), kv = bf4(x.kr[kt], e);
@@ -457,7 +474,8 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
         rg[e] = rv * el(gq, e);
         bg[e] = bv * f;
         kg[e] = kv * f;
-        ah[e] = (_Float16)(ag[e] * el(e7, e));
+        ah[e] = (_Float16)(ag[e] * el(e7, e));  // A^ = a e^{gamma_{t-1}}
+        rh[e] = (_Float16)(rg[e] * el(e7, e));  // R^ = r e^{gamma_t}
         bbar[kt][e] = (_Float16)(bg[e] * el(g15, e));
         kbar[kt][e] = (_Float16)(kg[e] * el(g15, e));
       }
@@ -470,6 +488,7 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
         split_bf16x2(kg[e], kg[e + 1], khH, khL, q8);
       }
       AT[kt] = tr16(ah, eye);
+      if constexpr (ODD) RT[kt] = tr16(rh, eye);
       if (kt & 1) {
         Lab = MmaBF::mma(ahH, bhH, Lab);
         Lak = MmaBF::mma(ahH, khH, Lak);
@@ -495,6 +514,12 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
     Lrk.v[e] = li <= t ? Lrk.v[e] : 0.f;
   }
   const TmFrags tmf = prep_solve(Lab, Lrb, scr);
+  half8 owns[4][2];  // the stored G (odd) or S0 (even) of every row tile, in flight during the solve's tail
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+      owns[rt][kp] = *reinterpret_cast<const half8*>((ODD ? gp : s0p) + ck_off(16 * rt + li, kp, g));
   const half4 tB = tmf.tB;                    // T row vectors
   const half8 ttA = cat8(tr16(tB, eye), hz);  // T^T as an A operand
   const half4 lakC = to_h4(Lak), lrbC = to_h4(Lrb), lrkC = to_h4(Lrk);  // L^T as A operands
@@ -515,10 +540,75 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   st_off<half8>(bk_l, 2048u + (uint32_t)lane * 16u, cat8(kbar[0], kbar[1]));
   st_off<half8>(bk_l, 3072u + (uint32_t)lane * 16u, cat8(kbar[2], kbar[3]));
 
-  // ---- per 16-row tile rt: U = A' S0^T + G_u V, dU = L_rb^T dY + B- G^T, dX = T^T dU (column
-  // vectors, lane = value row), dV (stored), and this tile's share of every contraction over
-  // the rows: (dY S0), (dX S0), (U G), (V G) per key tile in the token layout, the four C x C
-  // Gram gradients, and sum_i S0 G
+  // U = A' S0^T + G_u V and dU = L_rb^T dY + B- G^T, dX = T^T dU of row tile rt (column
+  // vectors, lane = value row)
+  auto form_u = [&](const half8 (&sr)[2], half4 vC) {
+    Mma32::acc u = Mma32::mma(guA, cat8(vC, hz), Mma32::zero());
+    u = Mma32::mma(apA[0], sr[0], u);
+    return Mma32::mma(apA[1], sr[1], u);
+  };
+  auto form_dx = [&](const half8 (&gr)[2], half4 dyC) {
+    Mma32::acc du = Mma32::mma(cat8(lrbC, hz), cat8(dyC, hz), Mma32::zero());
+    du = Mma32::mma(ld_off<half8>(bk_l, (uint32_t)lane * 16u), gr[0], du);
+    du = Mma32::mma(ld_off<half8>(bk_l, 1024u + (uint32_t)lane * 16u), gr[1], du);
+    return to_h4(Mma32::mma(ttA, cat8(to_h4(du), hz), Mma32::zero()));
+  };
+  auto ld_ck = [&](const _Float16* src, int rt, half8 (&dst)[2]) {
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) dst[kp] = *reinterpret_cast<const half8*>(src + ck_off(16 * rt + li, kp, g));
+  };
+
+  // ---- for the other wave of the pair, per 16-row tile rt and key tile kt = 2 kp + h:
+  // the odd chunk's G0 = e^{gamma_15} G + [R^^T | A^^T] [dY ; dX] (the even chunk's end
+  // gradient), the even chunk's S_end = e^{gamma_15} S0 + [B-^T | K-^T] [U ; V] (the odd
+  // chunk's start state)
+  half8 xop[4];   // per key tile: [R^^T | A^^T] (odd) or [B-^T | K-^T] (even) as an A operand
+  float4 e15[4];  // e^{gamma_15} of keys 16 kt + 4g + e
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    if constexpr (ODD)
+      xop[kt] = cat8(RT[kt], AT[kt]);
+    else
+      xop[kt] = cat8(tr16(bbar[kt], eye), tr16(kbar[kt], eye));
+    const float4 g15 = lds4(&fac[16 * kFacRow + 16 * kt + 4 * g]);
+    const float4 e7 = lds4(&fac[kRowE7 * kFacRow + 16 * kt + 4 * g]);
+    e15[kt] = make_float4(g15.x * e7.x, g15.y * e7.y, g15.z * e7.z, g15.w * e7.w);
+  }
+  half4 kept[4];  // U (even) or dX (odd) of each row tile, for the row tiles below
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int row = 16 * rt + li;
+    const half8 (&own)[2] = owns[rt];
+    half4 pC, qC;  // [dY ; dX] or [U ; V] as a B operand
+    if constexpr (ODD) {
+      pC = tr16(dyh[rt], eye);
+      qC = form_dx(own, pC);
+      kept[rt] = qC;
+    } else {
+      qC = tr16(vh[rt], eye);
+      pC = to_h4(form_u(own, qC));
+      kept[rt] = pC;
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      half4 t2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kt = 2 * kp + h;
+        Mma32::acc o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.v[e] = (float)own[kp][4 * h + e] * el(e15[kt], e);
+        o = Mma32::mma(xop[kt], cat8(pC, qC), o);
+        t2[h] = to_h4(o);
+      }
+      st_off<half8>(xown, xt_off(row, kp, g), cat8(t2[0], t2[1]));
+    }
+  }
+  lds_barrier();  // both waves' states are in LDS
+
+  // ---- per 16-row tile rt: U, dU, dX, dV (stored), and this tile's share of every
+  // contraction over the rows: (dY S0), (dX S0), (U G), (V G) per key tile in the token
+  // layout, the four C x C Gram gradients, and sum_i S0 G
   Mma16::acc ys[4], xs[4], ug[4], vg[4];
   Mma16::acc dLrb = Mma16::zero(), dLrk = Mma16::zero(), dLab = Mma16::zero(), dLak = Mma16::zero();
   float endp[4];
@@ -530,22 +620,26 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
   float* dvp = p.grad[3] + base;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
+    const int row = 16 * rt + li;
     half8 sr[2], gr[2];  // lane (row 16 rt + li, g): the keys of key pair kp (row vectors)
+    if constexpr (ODD) {
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      sr[kp] = *reinterpret_cast<const half8*>(s0p + ck_off(16 * rt + li, kp, g));
-      gr[kp] = *reinterpret_cast<const half8*>(gp + ck_off(16 * rt + li, kp, g));
+      for (int kp = 0; kp < 2; ++kp) sr[kp] = ld_off<half8>(xpeer, xt_off(row, kp, g));
+      ld_ck(gp, rt, gr);
+    } else {
+      ld_ck(s0p, rt, sr);
+      if (g_mem) {
+        ld_ck(gp, rt, gr);  // the last chunk, alone in its pair
+      } else {
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) gr[kp] = ld_off<half8>(xpeer, xt_off(row, kp, g));
+      }
     }
     const half4 vC = tr16(vh[rt], eye);    // lane (row 16 rt + li, g): V[tau = 4g + e][row]
     const half4 dyC = tr16(dyh[rt], eye);  // dY[t = 4g + e][row]
-    Mma32::acc u = Mma32::mma(guA, cat8(vC, hz), Mma32::zero());
-    u = Mma32::mma(apA[0], sr[0], u);
-    u = Mma32::mma(apA[1], sr[1], u);
-    Mma32::acc du = Mma32::mma(cat8(lrbC, hz), cat8(dyC, hz), Mma32::zero());
-    du = Mma32::mma(ld_off<half8>(bk_l, (uint32_t)lane * 16u), gr[0], du);
-    du = Mma32::mma(ld_off<half8>(bk_l, 1024u + (uint32_t)lane * 16u), gr[1], du);
-    const half4 dxC = to_h4(Mma32::mma(ttA, cat8(to_h4(du), hz), Mma32::zero()));
-    const half4 uR = tr16(to_h4(u), eye);  // lane (tau = li, g): U[tau][row 16 rt + 4g + e]
+    const half4 uC = ODD ? to_h4(form_u(sr, vC)) : kept[rt];
+    const half4 dxC = ODD ? kept[rt] : form_dx(gr, dyC);
+    const half4 uR = tr16(uC, eye);  // lane (tau = li, g): U[tau][row 16 rt + 4g + e]
     const half4 dxR = tr16(dxC, eye);      // lane (t = li, g): dX[t][row 16 rt + 4g + e]
     // dV^T = [dY ; dX]^T [L_rk | L_ak] + G K-^T (operands swapped): lane (tau = li, g)
     // holds dV[tau][row 16 rt + 4g + e]
@@ -669,7 +763,31 @@ __global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
       st_off<float4>(dap, o, make_float4(da[0], da[1], da[2], da[3]));
       st_off<float4>(dbp, o, make_float4(db[0], db[1], db[2], db[3]));
     }
+    __builtin_amdgcn_sched_barrier(0);  // one key tile at a time
   }
+}
+
+// One workgroup per chunk pair (2j, 2j + 1) of a head, one wave per chunk. Only the even
+// chunk's S0 and the odd chunk's G are stored: before its row tiles, the even chunk's wave
+// forms its end state S_end = S0 e^{gamma_15} + U^T B- + V^T K- (the odd chunk's S0) and
+// the odd chunk's wave its start gradient G0 = G e^{gamma_15} + R^^T dY + A^^T dX (the even
+// chunk's end G), each into LDS for the other.
+__global__ __launch_bounds__(64 * kGW, 2) void wkv7_bgrad_kernel(GradParams p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nc = p.nc, np = (nc + 1) >> 1;
+  const bool odd = wave & 1;
+  const int64_t pair = blockIdx.x;
+  const int unit = (int)(pair / np);
+  const int c = 2 * (int)(pair % np) + (odd ? 1 : 0);
+  if (pair >= p.pairs || c >= nc) {  // the odd half of a last pair of one chunk: meets the one barrier
+    lds_barrier();
+    return;
+  }
+  if (odd)
+    grad_item<true>(p, lds, wave, unit, c);
+  else
+    grad_item<false>(p, lds, wave, unit, c);
 }
 
 hipError_t launch_grad(const GradParams& gp, hipStream_t stream) {
@@ -677,7 +795,7 @@ hipError_t launch_grad(const GradParams& gp, hipStream_t stream) {
   const int lds = kGW * kGWaveLds;
   GradParams q = gp;
   void* args[] = {&q};
-  return hipLaunchKernel(fn, dim3((uint32_t)((gp.items + kGW - 1) / kGW)), dim3(64 * kGW), args, lds, stream);
+  return hipLaunchKernel(fn, dim3((uint32_t)gp.pairs), dim3(64 * kGW), args, lds, stream);
 }
 
 }  // namespace
@@ -686,7 +804,8 @@ hipError_t launch_backward_chunked(const BwdCall& c) {
   if (c.dtype != 1 || c.T * c.H * kN >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int64_t units = c.B * c.H;
   const int64_t nc = (c.T + kC - 1) / kC;
-  const size_t ck_bytes = (size_t)(units * nc) * kCkHalves * sizeof(_Float16);
+  // the start states of the even chunks and the end gradients of the odd ones (and the last)
+  const size_t ck_bytes = (size_t)(units * ((nc + 1) / 2)) * kCkHalves * sizeof(_Float16);
   void* ws = nullptr;
   hipError_t e = device_workspace(c.stream, 2 * ck_bytes, &ws);
   if (e != hipSuccess) return e;
@@ -728,7 +847,7 @@ hipError_t launch_backward_chunked(const BwdCall& c) {
   gp.s0 = s0;
   gp.gend = gend;
   for (int i = 0; i < 6; ++i) gp.grad[i] = c.grad[i];
-  gp.items = units * nc;
+  gp.pairs = units * ((nc + 1) / 2);
   gp.nc = (int32_t)nc;
   return launch_grad(gp, c.stream);
 }

@@ -42,7 +42,8 @@ struct FusedParams {
   float* y;
   const float* s_in;  // may be null (zero state)
   float* s_out;       // may be null
-  _Float16* ck;       // checkpoint form only: the state at every chunk start (kCkHalves each)
+  _Float16* ck;       // checkpoint form only: the state at the start of every even chunk c, at
+                      // index c / 2 of (nc + 1) / 2 per sequence (kCkHalves each)
   int32_t nc;         // chunks per sequence
   const float* ln_w;  // time-mix form: ln_x's affine per (head, channel), may be null (1)
   const float* ln_b;  // may be null (0)
@@ -242,7 +243,9 @@ __device__ __forceinline__ void fused_body(const FusedParams& p, unsigned char* 
     read_frag(slot_of(cn), nxt);
 #pragma unroll
     for (int e = 0; e < 4; ++e) cur.v[e] = vc[e];
-    if constexpr (CK) ck_store(p.ck + ((int64_t)unit * nc + c) * kCkHalves, 16 * w, St);
+    if constexpr (CK) {
+      if (!(c & 1)) ck_store(p.ck + ((int64_t)unit * ((nc + 1) >> 1) + (c >> 1)) * kCkHalves, 16 * w, St);
+    }
     const f32x4 yv = scan_step<!CK>(St, cur);
     load_v(min(c + 2, nc - 1), vc);
     if constexpr (!CK && kRows) {
