@@ -253,7 +253,9 @@ def main(argv=None):
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the multi-layer prompt-then-steps leg")
     ap.add_argument("--stack-steps", type=int, default=32)
-    ap.add_argument("--backward-reps", type=int, default=10)
+    ap.add_argument("--backward-reps", type=int, default=20)
+    ap.add_argument("--backward-warmup", type=int, default=40,
+                    help="untimed backward calls first (the clock settles over the first tens of calls)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -507,7 +509,8 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args, flush=None):
     """Gradients of the recurrence (dr, dw, dk, dv, da, db, dstate_in) at the prefill shape, from seeded
     dy and dstate_out. The default (AUTO, bfloat16 inputs) is the chunked backward on MFMA: one launch
     runs the checkpoint forward and the chain of state gradients side by side, a second forms the input
-    gradients; each call between its own HIP events, after a write of `flush` (median and min). The
+    gradients; after untimed warm-up calls, each call between its own HIP events, after a write of
+    `flush` (median and min). The
     token-by-token backward (float32 throughout) is timed beside it."""
     from linear_rnn_amd.inputs import make_cotangents
     B, T, H = cfg.B, cfg.T, cfg.H
@@ -524,7 +527,7 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args, flush=None):
                                   algo=algo)
 
     algo = wkv.RWKV7_ALGO_AUTO
-    ts = time_steps(torch, lambda: bwd(algo), args.backward_reps + 3, flush)[3:]
+    ts = time_steps(torch, lambda: bwd(algo), args.backward_warmup + args.backward_reps, flush)[args.backward_warmup:]
     ms, ms_min = med(ts), min(ts)
     tseq = time_steps(torch, lambda: bwd(wkv.RWKV7_ALGO_SEQUENTIAL), 3, flush)[1:]
     tok_heads = B * T * H
@@ -533,6 +536,7 @@ def bench_backward(torch, wkv, x, d, s_in, cfg, args, flush=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {
         "value": tok_heads / (ms * 1e-3), "unit": UNIT, "ms_per_call": ms, "ms_min": ms_min, "reps": len(ts),
+        "warmup": args.backward_warmup, "ms_all": ts,
         "algo": "chunked (MFMA)" if d["r"].dtype == torch.bfloat16 else "sequential",
         "config": {"workload": "%s: B=%d T=%d H=%d N=%d bf16 inputs, fp32 state_in, dy, dstate_out; fp32 "
                                "gradients" % (cfg.name, B, T, H, N), "B": B, "T": T, "H": H, "N": N},
