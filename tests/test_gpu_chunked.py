@@ -59,6 +59,17 @@ def test_ragged_many_heads_vs_oracle(torch, CH, B, T, H):
     assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
 
 
+# Fewer heads than compute units but more than half of them (129 to 255 on 256 CUs): per-wave y
+# tiles, ragged ends, a 1-token last chunk
+@pytest.mark.parametrize("B,T,H", [(3, 40, 50), (1, 161, 200), (1, 33, 129)])
+def test_ragged_mid_heads_vs_oracle(torch, CH, B, T, H):
+    say("algo", CH, "chunked ragged, mid heads", B, T, H)
+    x = make_inputs(CONFIGS["L24-D1024-prefill-resume"], B=B, T=T, H=H, seed=400 + T)
+    y, s = run(torch, to_dev(x), CH)
+    yr, sr = oracle.wkv7(*(x[n] for n in "rwkvab"), state_in=x["state_in"])
+    assert rel(y, yr) <= TOL_BF16 and rel(s, sr) <= TOL_BF16, (rel(y, yr), rel(s, sr))
+
+
 def test_zero_initial_state(torch, CH):
     say("algo", CH, "chunked, state_in NULL")
     x = make_inputs(CONFIGS["L12-D768-prefill"], B=2, T=77, H=4, seed=3)
