@@ -320,12 +320,15 @@ int rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *
  *   RWKV7_ALGO_CHUNKED  bfloat16 inputs with T*H*64 < 2^31 (else RWKV7_ERR_ALGO); AUTO for
  *                      them. The derivatives of the chunked prefill's chunk form, on
  *                      16x16 MFMA tiles: a checkpoint pass of the one-kernel chunked
- *                      prefill stores the float16 state at every 16-token chunk start; a
- *                      second kernel carries dL/dS back through the chunks (one
- *                      workgroup per head) and stores it, in float16, at every chunk end;
- *                      a third forms each chunk's input gradients (one wave per chunk and
- *                      head). Both stored arrays (B*H*ceil(T/16) * 8 KiB each) live in the
- *                      per-(device, stream) workspace of rwkv7_wkv_prefill_ex. Intra-chunk
+ *                      prefill stores the float16 state at the start of every even
+ *                      16-token chunk; a second kernel carries dL/dS back through the
+ *                      chunks (one workgroup per head) and stores it, in float16, at the
+ *                      end of every odd chunk and of the last one; a third forms each
+ *                      chunk's input gradients (one wave per chunk and head, the two waves
+ *                      of a chunk pair rebuilding the missing state and gradient for each
+ *                      other). Both stored arrays (B*H*ceil(ceil(T/16)/2) * 8 KiB each)
+ *                      live in the per-(device, stream) workspace of
+ *                      rwkv7_wkv_prefill_ex. Intra-chunk
  *                      operands are float16 and the state gradient is carried in float32,
  *                      so results agree with the float64 derivatives to about 1e-3
  *                      relative (the bfloat16 bar). Domain: that of the chunked prefill
