@@ -225,3 +225,7 @@ def test_full_size_sampled(torch, name, algo):
         worst["dstate_in"] = max(worst.get("dstate_in", 0.0), rel(g["dstate_in"][b:b + 1, h:h + 1], r["dstate_in"]))
     say("backward full size errors", worst)
     assert max(worst.values()) <= TOL_BF16, worst
+    if algo == CHK and name == "L12-D768-prefill":
+        # a second call at full size is bit-identical (the chunk pairs' LDS hand-off, at scale)
+        g2 = run(torch, x, ct, algo=algo)
+        assert all(np.array_equal(g[n], g2[n]) for n in g), [n for n in g if not np.array_equal(g[n], g2[n])]
